@@ -1,0 +1,253 @@
+/*
+ * amk.h: C ABI of the MI355X batch-1 decode megakernel library (libamk.so).
+ *
+ * One call of amk_decode_step runs one batch-1 greedy decode step of a Llama-family
+ * transformer as a single persistent launch: one workgroup per compute unit walks a static
+ * task-DAG schedule, synchronised only by monotone counters, and the whole forward pass of one
+ * token happens inside that one launch (AutoMegaKernel pages: page 1, author's note, "one
+ * launch = one forward = one token", and "How it works"; page 3, "How it works", layer 0).
+ * A schedule is validated on the CPU before anything launches; an unsafe one is refused, never
+ * run (page 1, "Deadlock-free by construction"; page 2, "Statically verified schedule IR" and
+ * Table 1; page 4, "De Safety Gate").
+ *
+ * Conventions
+ *  - Every call returns an amk_status; nothing aborts, throws or exits across this ABI.
+ *    Out-parameters are written only on AMK_OK (verdicts are also written on AMK_E_REJECTED).
+ *  - "device" pointers are HIP device memory of the current device; "host" pointers are
+ *    ordinary CPU memory. All matrices are row-major [out, in].
+ *  - A context is not thread-safe; use it from one host thread and one stream at a time.
+ *  - The library is silent unless the environment variable AMK_LOG=1 is set.
+ */
+#ifndef AMK_H
+#define AMK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    AMK_OK = 0,
+    AMK_E_INVALID_ARG = 1,     /* null pointer, bad size, position out of range, bad struct_size */
+    AMK_E_UNSUPPORTED = 2,     /* model variant the kernel does not implement (see amk_create) */
+    AMK_E_REJECTED = 3,        /* the schedule failed validation; nothing was launched */
+    AMK_E_OOM = 4,             /* device or host allocation failed */
+    AMK_E_HIP = 5,             /* a HIP runtime call failed */
+    AMK_E_NOT_RESIDENT = 6,    /* one workgroup per CU cannot be co-resident on this device */
+    AMK_E_DEVICE_TIMEOUT = 7   /* a previous step hit the device watchdog (bounded spin-waits) */
+} amk_status;
+
+/* Weight format of the projection matrices (QKV, O, gate, up, down, LM head). */
+typedef enum {
+    AMK_F32 = 0,        /* fp32 weights; fp32 activations and KV cache when act_f32 = 1 */
+    AMK_BF16 = 1,       /* bf16 weights */
+    AMK_INT8_PC = 2,    /* int8, symmetric absmax per output row, fp16 scale (W8A16) */
+    AMK_INT4_G128 = 3   /* int4 in [-7, 7], symmetric absmax per 128 input columns, fp16 scales */
+} amk_wfmt;
+
+/* Model shape. The decode step is the standard Llama step (RMSNorm, QKV projections, rotary
+ * embedding on half-split pairs, grouped-query attention where query head h reads KV head
+ * floor(h * n_kv_heads / n_heads), O projection + residual, RMSNorm, SwiGLU MLP + residual,
+ * final RMSNorm, LM head, greedy argmax with the lowest index winning ties); pages: page 3,
+ * "How it works" (the instruction list), page 1 "What's built". Biased projections are not
+ * part of this family and cannot be expressed. */
+typedef struct {
+    uint32_t struct_size;     /* sizeof(amk_model_desc) */
+    int32_t hidden, n_layers, n_heads, n_kv_heads, head_dim, intermediate, vocab;
+    int32_t max_ctx;          /* KV cache rows per (layer, K/V, kv head) */
+    int32_t tied_embeddings;  /* 1: the LM head is the embedding matrix */
+    float rope_theta, rms_eps;
+    int32_t wfmt;             /* amk_wfmt */
+    int32_t act_f32;          /* 1: activations and KV cache fp32 (requires AMK_F32); 0: bf16 */
+} amk_model_desc;
+
+/* Canonical weights, device pointers, borrowed only for the duration of amk_create: the
+ * library quantises (int formats) and repacks them into its own buffers and synchronises
+ * before returning, so the caller may free them afterwards. Element type is fp32 when
+ * wfmt == AMK_F32, else bf16 (the master that int formats are quantised from). Norm gains
+ * and the embedding use the same element type. Per-layer entries are arrays of n_layers
+ * device pointers (the arrays themselves are host memory). */
+typedef struct {
+    uint32_t struct_size;     /* sizeof(amk_weights) */
+    const void* embed;        /* [vocab, hidden] */
+    const void* final_norm;   /* [hidden] */
+    const void* lm_head;      /* [vocab, hidden]; NULL when tied_embeddings */
+    const void* const* attn_norm;  /* [hidden] each */
+    const void* const* wq;         /* [n_heads*head_dim, hidden] */
+    const void* const* wk;         /* [n_kv_heads*head_dim, hidden] */
+    const void* const* wv;         /* [n_kv_heads*head_dim, hidden] */
+    const void* const* wo;         /* [hidden, n_heads*head_dim] */
+    const void* const* mlp_norm;   /* [hidden] */
+    const void* const* wg;         /* [intermediate, hidden] */
+    const void* const* wu;         /* [intermediate, hidden] */
+    const void* const* wd;         /* [hidden, intermediate] */
+} amk_weights;
+
+/* ---------------------------------------------------------------- schedule IR
+ * A schedule: tasks in per-CU queues; counters that tasks signal (+1 each per launch) and
+ * wait on (value >= threshold, counted from the start of the launch, i.e. thresholds are
+ * epoch-relative); the memory each task touches. The page-2 rule set (Table 1) decides
+ * deadlock and race freedom; see amk_validate for the exact rules. */
+
+#define AMK_ACC_WRITE 1u       /* access writes (else reads) */
+#define AMK_ACC_POST 2u        /* access happens after the task's signals */
+#define AMK_REGION_PLAIN 0u    /* ordinary memory */
+#define AMK_REGION_LL 1u       /* flag-carrying words: written once per launch, the write is observed from the data */
+#define AMK_REGION_RO 2u       /* read-only during a launch */
+#define AMK_SCHED_LL_PROTOCOL 1u   /* schedule flag: waits are observed through flag-carrying reads (rule V8) */
+
+/* opcodes of the kernel's instruction set (args in amk_task.arg[]) */
+enum {
+    AMK_OP_QKV = 1,      /* layer, arg0 = first row quad, arg1 = quad count: RMSNorm + QKV GEMV + RoPE + KV append */
+    AMK_OP_ATTN = 2,     /* layer, arg0 = first query head, arg1 = head count, arg2 = chunk, arg3 = chunks */
+    AMK_OP_MERGE = 3,    /* layer, arg0 = first query head, arg1 = head count, arg3 = chunks: split-context merge */
+    AMK_OP_OPROJ = 4,    /* layer, arg0 = first row, arg1 = row count: O GEMV + residual */
+    AMK_OP_GATEUP = 5,   /* layer, arg0 = first j, arg1 = count: RMSNorm + gate/up GEMV + SwiGLU */
+    AMK_OP_DOWN = 6,     /* layer, arg0 = first row, arg1 = row count: down GEMV + residual */
+    AMK_OP_LM = 7,       /* arg0 = first vocab row, arg1 = row count, arg2 = tile index: final RMSNorm + LM head + tile argmax */
+    AMK_OP_ARGMAX = 8    /* arg2 = number of LM tiles: greedy token */
+};
+
+typedef struct {
+    uint32_t opcode, layer;
+    uint32_t arg[4];
+    uint32_t wait_off, wait_cnt;    /* into amk_schedule.waits */
+    uint32_t sig_off, sig_cnt;      /* into amk_schedule.signals */
+    uint32_t acc_off, acc_cnt;      /* into amk_schedule.accesses */
+} amk_task;
+
+typedef struct { uint32_t counter, threshold; } amk_wait;
+typedef struct { uint32_t region, flags; uint64_t lo, hi; } amk_access;   /* element range [lo, hi) */
+typedef struct { uint32_t region, pad; uint64_t lo, hi; } amk_range;
+
+typedef struct {
+    uint32_t struct_size;      /* sizeof(amk_schedule) */
+    uint32_t flags;            /* AMK_SCHED_* */
+    uint32_t n_tasks, n_queues, n_counters, n_regions;
+    uint32_t n_waits, n_signals, n_accesses, n_inputs, n_outputs;
+    const amk_task* tasks;             /* [n_tasks] */
+    const uint32_t* queue_off;         /* [n_queues + 1]; queue q lists queue_tasks[queue_off[q] .. queue_off[q+1]) */
+    const uint32_t* queue_tasks;       /* task ids in execution order */
+    const amk_wait* waits;             /* [n_waits] */
+    const uint32_t* signals;           /* [n_signals] counter ids */
+    const amk_access* accesses;        /* [n_accesses] */
+    const uint32_t* region_kind;       /* [n_regions] AMK_REGION_* */
+    const amk_range* inputs;           /* [n_inputs] data defined before the launch */
+    const amk_range* outputs;          /* [n_outputs] data the launch must produce */
+} amk_schedule;
+
+/* Verdict. accepted == (rule_mask == 0). Bits: 1 << k for rule Vk (k = 0..8). task, counter
+ * and region name the first offender found (or -1); they are diagnostics only. */
+typedef struct { int32_t accepted; uint32_t rule_mask; int32_t task, counter, region; } amk_verdict;
+
+/* Knobs of the built-in lowering (the edit surface a schedule search varies; page 1,
+ * "Two autoresearch loops", loop 2: tiling, SM assignment, pipelining depth, page allocation).
+ * Zero means default. */
+typedef struct {
+    uint32_t struct_size;      /* sizeof(amk_schedule_config) */
+    int32_t n_cu;              /* queues = workgroups; 0 = the device's CU count (amk_lower: 256) */
+    int32_t tasks_qkv, tasks_o, tasks_gateup, tasks_down, tasks_lm;   /* tasks per GEMV phase (0 = min(n_cu, units)) */
+    int32_t attn_chunks;       /* context chunks per attention head group (0 = by max_ctx) */
+    int32_t attn_group_tasks;  /* 1: one attention task per KV group, 0: auto (per query head for short contexts) */
+    int32_t cu_assign;         /* 0 = XCD-aware (attention of one KV group on one XCD), 1 = plain round robin */
+    int32_t ring_kb;           /* LDS weight-ring size in KiB (0 = default) */
+    int32_t loader_depth;      /* 1 KiB loads kept in flight by the loader wave (0 = default) */
+} amk_schedule_config;
+
+/* ---------------------------------------------------------------- calls */
+
+/* Validate a schedule on the CPU. Reentrant, thread-safe, never touches a device. AMK_OK
+ * means the call ran; the verdict is in *out. Rules (1 << k in rule_mask):
+ *  V0 integrity: ids in range, every task in exactly one queue exactly once, lo < hi, no
+ *     duplicate signal in a task, no write to a read-only region, no declared input/output
+ *     and no post access on a flag-carrying region. When V0 fails nothing else is checked.
+ *  V1 a wait threshold outside [1, P(c)], P(c) = number of tasks signalling counter c.
+ *  V2 a partial wait (1 <= t < P(c)) on a counter with P(c) > 1.
+ *  V3 the producer->waiter graph has a cycle (self-waits included).
+ *  V4 the union graph (producer->waiter edges plus queue order) has a cycle although the
+ *     producer->waiter graph has none: a queue is not a linear extension of the DAG.
+ *  V5 (only without V3/V4) two accesses of different tasks overlap, one writes, and neither
+ *     happens before the other; on flag-carrying regions any two overlapping writes.
+ *  V6 a declared output is not covered by writes.
+ *  V7 (only without V3/V4) a read is not covered by declared inputs plus writes that happen
+ *     before it; on flag-carrying regions a write overlaps a read it does not precede.
+ *  V8 (AMK_SCHED_LL_PROTOCOL only) a task waits on a counter one of whose producers writes
+ *     nothing that the task reads from a flag-carrying region.
+ * Happens-before is reachability in the union graph where each task is split into a pre node
+ * (its waits enter, its signals leave) and a post node (AMK_ACC_POST accesses; queue order
+ * leaves from it). Returns AMK_E_INVALID_ARG for null pointers or a wrong struct_size. */
+amk_status amk_validate(const amk_schedule* sched, amk_verdict* out);
+
+/* Run the built-in lowering on the CPU (no device needed): model + config -> schedule. The
+ * result is library-owned; free it with amk_schedule_free. AMK_E_UNSUPPORTED for shapes the
+ * kernel does not implement (see amk_create). */
+amk_status amk_lower(const amk_model_desc* desc, const amk_schedule_config* cfg, amk_schedule** out);
+void amk_schedule_free(amk_schedule* sched);
+
+typedef struct amk_ctx amk_ctx;
+
+/* Build a context on the current device: lower (or take `sched`), validate, check that one
+ * 1024-thread workgroup per CU fits, quantise/repack the weights into library-owned device
+ * memory, upload the task table and synchronise `stream`.
+ *  desc      host; shape (AMK_E_UNSUPPORTED unless: head_dim in {16, 64, 128}; hidden, head
+ *            counts and intermediate even; n_heads % n_kv_heads == 0; act_f32 == 1 only with
+ *            AMK_F32; hidden and intermediate multiples of 128 for AMK_INT4_G128; vocab >= 2;
+ *            hidden <= 8192; intermediate <= 16384).
+ *  weights   host struct of device pointers, borrowed for this call only.
+ *  kv_cache  device, caller-owned for the context's lifetime, layout
+ *            [n_layers][2 (K, V)][n_kv_heads][max_ctx][head_dim] in the activation type
+ *            (fp32 or bf16). K rows are stored after rotary embedding. Row `pos` is written
+ *            by the step at `pos`; rows below `pos` are read; rows above are never touched.
+ *  sched     host, optional: a schedule to run instead of the built-in lowering. Its tasks'
+ *            access lists must equal what the kernel does for their opcodes (else V0).
+ *  cfg       host, optional lowering knobs.
+ *  stream    HIP stream for the set-up work (hipStream_t; NULL = default stream).
+ *  verdict   host, optional: the validator's verdict (written on AMK_OK and AMK_E_REJECTED).
+ * A rejected schedule returns AMK_E_REJECTED and allocates nothing. */
+amk_status amk_create(const amk_model_desc* desc, const amk_weights* weights, void* kv_cache,
+                      const amk_schedule* sched, const amk_schedule_config* cfg, void* stream,
+                      amk_verdict* verdict, amk_ctx** out);
+
+/* One decode step: enqueue exactly one cooperative launch on `stream` and return without
+ * synchronising.
+ *  token_in   device int32[1]: the input token (read at the start of the launch).
+ *  pos        host int, 0 <= pos < max_ctx (else AMK_E_INVALID_ARG and no launch).
+ *  token_out  device int32[1]: the greedy token (may equal token_in: decode chains on the
+ *             device with no host round trip).
+ *  logits     device fp32[vocab] or NULL: the step's logits (not rounded).
+ * A token outside [0, vocab) is replaced by 0 and flagged in the device status word. A
+ * watchdog timeout in an earlier step (bounded spin-waits; only reachable with an invalid
+ * schedule or broken hardware) is reported here as AMK_E_DEVICE_TIMEOUT without launching;
+ * destroy and re-create the context to recover. */
+amk_status amk_decode_step(amk_ctx* ctx, const int32_t* token_in, int32_t pos, int32_t* token_out,
+                           float* logits, void* stream);
+
+/* Device status word of the context (synchronises the context's last stream first):
+ * 0 = fine; bit 0 = watchdog timeout; bit 1 = token out of range. */
+uint32_t amk_device_status(amk_ctx* ctx);
+
+/* The schedule the context runs (library-owned, valid until amk_destroy). */
+const amk_schedule* amk_ctx_schedule(const amk_ctx* ctx);
+
+/* Synchronise the last stream, free every library-owned buffer; never touches caller
+ * buffers. NULL-safe. */
+void amk_destroy(amk_ctx* ctx);
+
+/* The library's own weight quantiser, exposed for bit-exact comparison with other
+ * implementations (symmetric absmax, fp16 scales, codes decided in fp32, page 2,
+ * "Quantisation support and performance"). master: device bf16 [rows, cols]. codes: device
+ * int8 [rows, cols] (one code per byte, int4 codes in [-7, 7]); scales: device fp32 (the fp16
+ * values widened) [rows] for AMK_INT8_PC, [rows, cols/128] for AMK_INT4_G128. Runs on
+ * `stream` and synchronises it. */
+amk_status amk_quantize(int32_t wfmt, const void* master, int64_t rows, int64_t cols, void* codes,
+                        void* scales, void* stream);
+
+/* Library version string. */
+const char* amk_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* AMK_H */

@@ -198,7 +198,10 @@ class OracleModel:
             self._keep = []
 
     def __del__(self):
-        self.close()
+        try:
+            self.close()
+        except Exception:   # interpreter shutdown: the library may already be gone
+            pass
 
     def set_kv(self, layer: int, kv_vals: np.ndarray, pos0: int = 0):
         """kv_vals: [2][nKV][n][hd] act-format values (fp32 or bf16 bits)."""

@@ -1,0 +1,136 @@
+// Internal definitions shared by the host lowering (lower.cpp, abi.cpp) and the device code
+// (megakernel.hip, prep.hip). Not part of the public ABI.
+#pragma once
+#include <stdint.h>
+
+#include "amk.h"
+
+#if defined(__HIPCC__)
+#define AMK_HD __host__ __device__
+#else
+#define AMK_HD
+#endif
+
+namespace amk {
+
+// Workgroup: one per CU. Wave 0 streams weights and KV blocks into the LDS ring; waves 1..15
+// walk the task queue.
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+constexpr int kComputeWaves = kWaves - 1;
+constexpr int kComputeThreads = kComputeWaves * 64;
+
+// LDS budget (bytes): ring + input-vector stage + row results + attention state + control.
+constexpr int kLdsTotal = 160 * 1024;
+constexpr int kHBytes = 32 * 1024;          // input vector stage (fp32 up to 8192, or 16-bit up to 16384 values)
+constexpr int kRedRows = 1024;              // row results per task
+constexpr int kAttnLds = 16 * 1024;         // attention: q, per-wave partial states, current row
+constexpr int kCtrlBytes = 1024;
+constexpr int kRingMaxBytes = kLdsTotal - kHBytes - kRedRows * 4 - kAttnLds - kCtrlBytes;  // 108 KiB
+constexpr int kRingDefaultKB = 104;
+constexpr int kLoaderDepthDefault = 40;     // 1 KiB loads in flight
+constexpr int kAttnBlock = 64;              // positions per attention unit
+constexpr int kMaxAttnHeads = 8;            // query heads per attention task
+constexpr int64_t kStageFloats = kHBytes / 4;   // fp32 values the input-vector stage holds
+
+// Limits the kernel supports (checked at create).
+constexpr int kMaxHidden = 8192;
+constexpr int kMaxInter = 16384;
+
+// Device task descriptor (32 bytes).
+struct DevTask {
+    uint16_t op;
+    uint16_t layer;
+    uint32_t arg[4];
+    uint32_t tile_rows;      // rows in the weight tile (GEMV ops)
+    uint64_t wofs;           // byte offset of the tile inside this CU's weight stream
+};
+static_assert(sizeof(DevTask) == 32, "DevTask layout");
+
+// Weight tile geometry for a GEMV with K inputs in format wfmt.
+AMK_HD inline uint32_t row_pitch(int wfmt, uint32_t K) {
+    uint32_t b;
+    switch (wfmt) {
+    case AMK_F32: b = 4 * K; break;
+    case AMK_BF16: b = 2 * K; break;
+    case AMK_INT8_PC: b = K + 2; break;              // int8: codes, then the row's fp16 scale
+    default: b = K / 2 + (K / 128) * 2; break;   // int4: group scales first, then nibbles
+    }
+    return (b + 15u) & ~15u;
+}
+// Rows are self-contained (scales travel inside their row), so a tile has no header and any
+// row can stream through the LDS ring on its own.
+AMK_HD inline uint32_t tile_header(int wfmt, uint32_t rows) {
+    (void)wfmt;
+    (void)rows;
+    return 0u;
+}
+AMK_HD inline uint64_t tile_bytes(int wfmt, uint32_t K, uint32_t rows) {
+    return (uint64_t)tile_header(wfmt, rows) + (uint64_t)rows * row_pitch(wfmt, K);
+}
+// int4 row: bytes [0, 2*K/128) hold the group scales (fp16), the nibbles start at this offset
+AMK_HD inline uint32_t int4_codes_off(uint32_t K) { return (K / 128) * 2; }
+
+// Flag-carrying ("LL") buffers: one 8-byte word = 32-bit payload + 32-bit flag; the flag of a
+// word written in launch e is e+1 (never 0). bf16 activations pack 2 values per word; fp32
+// activations and attention partial states hold one value per word.
+struct LLLayout {
+    uint32_t vpw;            // activation values per word (2 bf16, 1 fp32)
+    uint64_t qkv, part, o, xo, a, xd;   // word offsets inside one layer block
+    uint64_t layer_words;
+    uint64_t lmpart;         // word offset of the LM tile results (after all layers)
+    uint64_t total;
+};
+
+AMK_HD inline LLLayout ll_layout(int H, int L, int nH, int nKV, int hd, int I, int act_f32, int nchunks,
+                                               int lm_tiles) {
+    LLLayout y;
+    y.vpw = act_f32 ? 1 : 2;
+    uint64_t off = 0;
+    y.qkv = off; off += (uint64_t)(nH + 2 * nKV) * hd / y.vpw;
+    y.part = off; off += nchunks > 1 ? (uint64_t)nH * nchunks * (hd + 2) : 0;
+    y.o = off; off += (uint64_t)nH * hd / y.vpw;
+    y.xo = off; off += (uint64_t)H / y.vpw;
+    y.a = off; off += (uint64_t)I / y.vpw;
+    y.xd = off; off += (uint64_t)H / y.vpw;
+    off = (off + 15) & ~15ull;
+    y.layer_words = off;
+    y.lmpart = off * L;
+    y.total = y.lmpart + 2ull * lm_tiles;
+    return y;
+}
+
+// Kernel parameters (passed by value).
+struct KParams {
+    // shape
+    int32_t H, L, nH, nKV, hd, I, V, max_ctx, wfmt, act_f32;
+    float eps, attn_scale;
+    int32_t nchunks, lm_tiles;
+    // schedule
+    const DevTask* tasks;
+    const uint32_t* queue_off;       // [n_cu + 1]
+    const uint8_t* wstream;          // all CU streams
+    const uint64_t* cu_stream_off;   // [n_cu + 1] byte offsets into wstream
+    // buffers
+    unsigned long long* ll;          // LL words
+    void* kv;                        // [L][2][nKV][max_ctx][hd], act type
+    const void* embed;               // [V][H], act type
+    const float* norms;              // [L][2][H] (attn, mlp) then [H] final, fp32
+    const float* rope;               // [max_ctx][hd/2][2] (cos, sin), fp32
+    // step
+    const int32_t* tok_in;
+    int32_t* tok_out;
+    float* logits;                   // may be null
+    int32_t pos;
+    uint32_t flag;                   // epoch + 1 (never 0)
+    uint32_t* status;                // host-visible status word
+    uint32_t* abort_flag;            // device word: set on watchdog timeout
+    uint64_t watchdog_ticks;         // s_memrealtime ticks (100 MHz) before a spin-wait gives up
+    uint32_t ring_bytes;             // LDS ring size used
+    uint32_t loader_depth;
+};
+
+constexpr uint32_t kStatusTimeout = 1u;
+constexpr uint32_t kStatusBadToken = 2u;
+
+}  // namespace amk

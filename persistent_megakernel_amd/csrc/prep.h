@@ -1,0 +1,22 @@
+// Host launchers of the device code (defined in the .hip files, called from abi.cpp).
+#pragma once
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include "amk_internal.h"
+#include "lower.h"
+
+namespace amk {
+
+hipError_t launch_repack(const RowMap* d_rows, uint32_t n_rows, const void* const* d_src_tab, int L, int wfmt, uint8_t* d_stream,
+                         hipStream_t st);
+hipError_t launch_quantize(const uint16_t* master, int64_t rows, int64_t cols, int group, int qmax, int8_t* codes, float* scales,
+                           hipStream_t st);
+hipError_t launch_norms(const void* src, int wfmt, uint32_t n, float* dst, hipStream_t st);
+
+// The persistent kernel: one cooperative launch of n_cu workgroups of kThreads.
+hipError_t launch_megakernel(const KParams& p, int n_cu, hipStream_t st);
+// Workgroups of the megakernel that fit on one CU (0 = it cannot run).
+int megakernel_blocks_per_cu();
+
+}  // namespace amk

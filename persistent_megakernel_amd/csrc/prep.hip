@@ -1,0 +1,144 @@
+// One-off set-up kernels (run at amk_create, not per token): the weight quantiser and the repack
+// of the canonical weights into the per-CU weight streams the megakernel reads, plus the
+// conversion of norm gains to fp32.
+//
+// Quantisation (the pages' int8 W8A16 and int4 weight-only kernels, page 2, "Quantisation
+// support and performance"; page 1, "Results"): symmetric absmax over an output row (int8) or a
+// group of 128 input columns (int4); the scale is fp32(absmax / qmax) rounded to fp16; a code
+// is the nearest integer (ties to even) to fp32(w) / fp32(scale), clamped to [-qmax, qmax]; a
+// zero scale gives zero codes. Codes are decided in fp32.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "amk_internal.h"
+#include "prep.h"
+
+namespace amk {
+namespace {
+
+__device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
+__device__ __forceinline__ uint16_t f2h_bits(float f) {
+    _Float16 h = (_Float16)f;   // round to nearest even
+    uint16_t b;
+    __builtin_memcpy(&b, &h, 2);
+    return b;
+}
+__device__ __forceinline__ float h2f(uint16_t b) {
+    _Float16 h;
+    __builtin_memcpy(&h, &b, 2);
+    return (float)h;
+}
+
+// absmax of src[0, n) (bf16), reduced over the block (256 threads)
+__device__ float block_absmax(const uint16_t* src, uint32_t n, float* red) {
+    float m = 0.f;
+    for (uint32_t k = threadIdx.x; k < n; k += blockDim.x) m = fmaxf(m, fabsf(bf2f(src[k])));
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    float t = 0.f;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t = fmaxf(t, red[w]);
+    return t;
+}
+
+__device__ __forceinline__ int quant_code(float w, float s, int qmax) {
+    if (s == 0.f) return 0;
+    float n = __builtin_rintf(w / s);
+    n = fminf(fmaxf(n, (float)-qmax), (float)qmax);
+    return (int)n;
+}
+
+__device__ __forceinline__ float quant_scale(float absmax, int qmax) {
+    return h2f(f2h_bits(absmax / (float)qmax));
+}
+
+// One block per row of the repack plan.
+__global__ void __launch_bounds__(256) k_repack(const RowMap* rows, uint32_t n_rows, const void* const* src_tab, int L,
+                                                int wfmt, uint8_t* stream) {
+    __shared__ float red[4];
+    const uint32_t ri = blockIdx.x;
+    if (ri >= n_rows) return;
+    const RowMap m = rows[ri];
+    const uint32_t K = m.K;
+    const void* base = src_tab[m.mat * (uint32_t)(L + 1) + m.layer];
+    uint8_t* dst = stream + m.dst;
+    const uint32_t pitch = row_pitch(wfmt, K);
+    if (wfmt == AMK_F32) {
+        const float* s = (const float*)base + (uint64_t)m.src_row * K;
+        for (uint32_t k = threadIdx.x; k < pitch / 4; k += blockDim.x) ((float*)dst)[k] = k < K ? s[k] : 0.f;
+    } else if (wfmt == AMK_BF16) {
+        const uint16_t* s = (const uint16_t*)base + (uint64_t)m.src_row * K;
+        for (uint32_t k = threadIdx.x; k < pitch / 2; k += blockDim.x) ((uint16_t*)dst)[k] = k < K ? s[k] : 0;
+    } else if (wfmt == AMK_INT8_PC) {
+        const uint16_t* s = (const uint16_t*)base + (uint64_t)m.src_row * K;
+        const float sc = quant_scale(block_absmax(s, K, red), 127);
+        for (uint32_t k = threadIdx.x; k < pitch; k += blockDim.x) {
+            uint8_t v = 0;
+            if (k < K) v = (uint8_t)(int8_t)quant_code(bf2f(s[k]), sc, 127);
+            else if (k < K + 2) v = (uint8_t)(f2h_bits(sc) >> (8 * (k - K)));
+            dst[k] = v;
+        }
+    } else {
+        const uint16_t* s = (const uint16_t*)base + (uint64_t)m.src_row * K;
+        const uint32_t ng = K / 128, coff = int4_codes_off(K);
+        for (uint32_t b = 0; b < ng; ++b) {
+            const float sc = quant_scale(block_absmax(s + 128 * b, 128, red), 7);
+            if (threadIdx.x == 0) *(uint16_t*)(dst + 2 * b) = f2h_bits(sc);
+            if (threadIdx.x < 64) {   // 64 bytes: nibble pair (2k, 2k+1) -> byte k, low nibble first
+                const uint32_t k = threadIdx.x;
+                const int q0 = quant_code(bf2f(s[128 * b + 2 * k]), sc, 7) + 8;
+                const int q1 = quant_code(bf2f(s[128 * b + 2 * k + 1]), sc, 7) + 8;
+                dst[coff + 64 * b + k] = (uint8_t)(q0 | (q1 << 4));
+            }
+            __syncthreads();
+        }
+        for (uint32_t k = coff + K / 2 + threadIdx.x; k < pitch; k += blockDim.x) dst[k] = 0;
+    }
+}
+
+// The quantiser alone: codes (one int8 per element) and fp32-widened scales.
+__global__ void __launch_bounds__(256) k_quantize(const uint16_t* master, int64_t cols, int group, int qmax, int8_t* codes,
+                                                  float* scales) {
+    __shared__ float red[4];
+    const int64_t row = blockIdx.x;
+    const int64_t g = group > 0 ? group : cols;
+    const int64_t ng = cols / g;
+    const uint16_t* s = master + row * cols;
+    for (int64_t b = 0; b < ng; ++b) {
+        const float sc = quant_scale(block_absmax(s + b * g, (uint32_t)g, red), qmax);
+        if (threadIdx.x == 0) scales[row * ng + b] = sc;
+        for (int64_t k = threadIdx.x; k < g; k += blockDim.x)
+            codes[row * cols + b * g + k] = (int8_t)quant_code(bf2f(s[b * g + k]), sc, qmax);
+        __syncthreads();
+    }
+}
+
+__global__ void k_norms_to_f32(const void* src, int wfmt, uint32_t n, float* dst) {
+    const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    dst[i] = wfmt == AMK_F32 ? ((const float*)src)[i] : bf2f(((const uint16_t*)src)[i]);
+}
+
+}  // namespace
+
+hipError_t launch_repack(const RowMap* d_rows, uint32_t n_rows, const void* const* d_src_tab, int L, int wfmt, uint8_t* d_stream,
+                         hipStream_t st) {
+    if (!n_rows) return hipSuccess;
+    hipLaunchKernelGGL(k_repack, dim3(n_rows), dim3(256), 0, st, d_rows, n_rows, d_src_tab, L, wfmt, d_stream);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize(const uint16_t* master, int64_t rows, int64_t cols, int group, int qmax, int8_t* codes, float* scales,
+                           hipStream_t st) {
+    if (!rows) return hipSuccess;
+    hipLaunchKernelGGL(k_quantize, dim3((uint32_t)rows), dim3(256), 0, st, master, cols, group, qmax, codes, scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_norms(const void* src, int wfmt, uint32_t n, float* dst, hipStream_t st) {
+    hipLaunchKernelGGL(k_norms_to_f32, dim3((n + 255) / 256), dim3(256), 0, st, src, wfmt, n, dst);
+    return hipGetLastError();
+}
+
+}  // namespace amk

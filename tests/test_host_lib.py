@@ -1,0 +1,92 @@
+"""Host side of libamk.so, no GPU: the library loads and exports every call include/amk.h
+declares; the C++ validator's verdicts equal the reference validator's bit for bit; the
+built-in lowering of every workload (and of the lowering knobs the GPU tests use) is accepted;
+shapes the kernel does not implement are refused before anything reaches a device."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import amk_inputs as I
+from amk_inputs import schedules as S
+from oracle import validator_ref as VR
+
+import schedule_corpus
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def M():
+    import persistent_megakernel_amd as M
+    M.lib()
+    return M
+
+
+def test_exports_every_declared_symbol(M):
+    hdr = open(os.path.join(ROOT, "include", "amk.h")).read()
+    names = set(re.findall(r"^\s*(?:amk_status|void|uint32_t|const\s+\w+\s*\*|const char\s*\*)\s+(amk_\w+)\s*\(",
+                           hdr, re.M))
+    assert {"amk_validate", "amk_create", "amk_decode_step", "amk_destroy"} <= names
+    lib = C.CDLL(M._abi.LIB_PATH)
+    for n in sorted(names):
+        assert hasattr(lib, n), n
+        assert n in M._abi.SIGNATURES, n
+    assert M.amk_version().startswith("amk-mi355x")
+
+
+@pytest.mark.parametrize("name,sched,acc,mask", schedule_corpus.corpus(), ids=lambda x: x if isinstance(x, str) else "")
+def test_cpp_validator_equals_reference_on_hand_corpus(M, name, sched, acc, mask):
+    v = M.amk_validate(sched)
+    assert (bool(v.accepted), v.rule_mask) == (acc, mask), name
+
+
+def test_cpp_validator_equals_reference_on_random_schedules(M):
+    for seed in range(400):
+        s = S.random_schedule(seed)
+        v = M.amk_validate(s)
+        assert (bool(v.accepted), v.rule_mask) == VR.validate(s), seed
+        assert bool(v.accepted) == (v.rule_mask == 0)
+
+
+@pytest.mark.parametrize("name", sorted(I.SHAPES))
+def test_builtin_lowering_accepted(M, name):
+    v = M.amk_lower_verdict(M.model_desc(I.SHAPES[name]))
+    assert v.accepted and v.rule_mask == 0
+
+
+@pytest.mark.parametrize("kw", [dict(n_cu=1), dict(n_cu=7, cu_assign=1), dict(attn_chunks=3, attn_group_tasks=1),
+                                dict(tasks_qkv=3, tasks_o=5, tasks_gateup=2, tasks_down=9, tasks_lm=4)])
+def test_tiny_lowering_knobs_accepted_and_agree_with_reference(M, kw):
+    """The Python reference validator, run on the lowered schedule itself, agrees."""
+    sched = M.amk_lower(M.model_desc(I.SHAPES["tiny_fp32"]), M.schedule_config(**kw))
+    assert VR.validate(sched) == (True, 0)
+    assert M.amk_validate(sched).accepted
+
+
+def test_lowered_schedule_round_trip_and_mutation_rejected(M):
+    """A lowered schedule copied back into C is accepted; dropping one full wait (so a reader
+    is no longer ordered after its producers) is rejected by both validators."""
+    sched = M.amk_lower(M.model_desc(I.SHAPES["tiny_fp32"]), M.schedule_config(n_cu=4))
+    assert M.amk_validate(sched).accepted
+    bad = sched.copy()
+    i = next(k for k, t in enumerate(bad.tasks) if t.opcode == M.A.AMK_OP_OPROJ and t.waits)
+    bad.tasks[i].waits = []
+    v = M.amk_validate(bad)
+    assert not v.accepted
+    assert (bool(v.accepted), v.rule_mask) == VR.validate(bad)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=32), 2),                         # head_dim not in {16, 64, 128}
+    (dict(n_kv_heads=3), 2),                        # n_heads not a multiple of n_kv_heads
+    (dict(intermediate=180), 2),                    # not a multiple of 16
+    (dict(wfmt=I.WF_BF16), 2),                      # fp32 activations with bf16 weights
+    (dict(hidden=0), 1),
+])
+def test_unsupported_shapes_refused(M, kw, status):
+    shape = I.tiny_shape(**kw)
+    with pytest.raises(M.AmkError) as e:
+        M.amk_lower(M.model_desc(shape))
+    assert e.value.status == status
