@@ -149,11 +149,16 @@ typedef struct {
     uint32_t struct_size;      /* sizeof(amk_schedule_config) */
     int32_t n_cu;              /* queues = workgroups; 0 = the device's CU count (amk_lower: 256) */
     int32_t tasks_qkv, tasks_o, tasks_gateup, tasks_down, tasks_lm;   /* tasks per GEMV phase (0 = min(n_cu, units)) */
-    int32_t attn_chunks;       /* context chunks per attention head group (0 = by max_ctx) */
-    int32_t attn_group_tasks;  /* 1: one attention task per KV group, 0: auto (per query head for short contexts) */
-    int32_t cu_assign;         /* 0 = XCD-aware (attention of one KV group on one XCD), 1 = plain round robin */
+    int32_t attn_chunks;       /* context chunks per attention head group (0 = auto: 1 below 256 cache
+                                  rows, else enough chunks to give every CU one attention task) */
+    int32_t attn_group_tasks;  /* 1: one attention task per KV group (up to 8 query heads), 2: one per
+                                  query head, 0: auto (grouped whenever KV heads are shared) */
+    int32_t cu_assign;         /* 0 = XCD-aware (unchunked attention of one KV group on one XCD; chunked
+                                  attention round robin), 1 = plain round robin */
     int32_t ring_kb;           /* LDS weight-ring size in KiB (0 = default) */
     int32_t loader_depth;      /* 1 KiB loads kept in flight by the loader wave (0 = default) */
+    int32_t prefetch_kb;       /* how far ahead of its LDS loads the loader touches the CU's weight stream
+                                  to bring it into L2, in KiB (0 or -1 = off) */
 } amk_schedule_config;
 
 /* ---------------------------------------------------------------- calls */
@@ -230,6 +235,20 @@ uint32_t amk_device_status(amk_ctx* ctx);
 
 /* The schedule the context runs (library-owned, valid until amk_destroy). */
 const amk_schedule* amk_ctx_schedule(const amk_ctx* ctx);
+
+/* Per-task timestamp trace (for critical-path and synchronisation-cost attribution of the
+ * pages' per-tile sync overhead; page 2, "Performance analysis"; page 4, "Bottleneck
+ * analysis"). When `trace` is non-NULL, every later amk_decode_step on this context writes,
+ * for each task of the schedule, 6 uint64 values at trace[6 * k ...], where k is the task's
+ * index in queue order (queue 0's tasks first; amk_ctx_schedule gives the order):
+ *   [0] compute start, [1] inputs observed (all waits satisfied, prologue done),
+ *   [2] rows / attention blocks done, [3] task end, [4] loader's first issue for the task,
+ *   [5] loader's last issue for the task,
+ * in ticks of the device's constant 100 MHz realtime counter (one time base across CUs;
+ * slots a task has no event for keep their old value). trace: device memory of at least
+ * `capacity` uint64 values, caller-owned, borrowed until disabled; capacity must be at least
+ * 6 * n_tasks (else AMK_E_INVALID_ARG). trace = NULL disables (the default). */
+amk_status amk_set_trace(amk_ctx* ctx, uint64_t* trace, uint64_t capacity);
 
 /* Synchronise the last stream, free every library-owned buffer; never touches caller
  * buffers. NULL-safe. */

@@ -21,7 +21,7 @@ from ._abi import (AMK_BF16, AMK_F32, AMK_INT4_G128, AMK_INT8_PC, AmkError, STAT
                    STATUS_TIMEOUT, check, lib)
 
 __all__ = ["amk_validate", "amk_lower", "amk_create", "amk_decode_step", "amk_destroy",
-           "amk_quantize", "amk_device_status", "amk_ctx_schedule", "amk_version", "Decoder",
+           "amk_quantize", "amk_device_status", "amk_ctx_schedule", "amk_set_trace", "amk_version", "Decoder",
            "model_desc", "schedule_config", "AmkError"]
 
 
@@ -199,6 +199,10 @@ def amk_ctx_schedule(ctx: int):
     return schedule_from_c(lib().amk_ctx_schedule(C.c_void_p(ctx)))
 
 
+def amk_set_trace(ctx: int, trace_ptr: int, capacity: int) -> None:
+    check("amk_set_trace", lib().amk_set_trace(C.c_void_p(ctx), C.c_void_p(trace_ptr or None), int(capacity)))
+
+
 def amk_destroy(ctx: Optional[int]) -> None:
     lib().amk_destroy(C.c_void_p(ctx) if ctx else None)
 
@@ -285,6 +289,14 @@ class Decoder:
 
     def status(self) -> int:
         return amk_device_status(self.ctx)
+
+    def enable_trace(self):
+        """Allocate a trace buffer and make later steps record per-task timestamps into it;
+        returns the device uint64 tensor [n_tasks, 6] (see amk_set_trace)."""
+        n = len(self.schedule().tasks)
+        self.trace = self.torch.zeros((n, A.TRACE_SLOTS), dtype=self.torch.int64, device=self.device)
+        amk_set_trace(self.ctx, self.trace.data_ptr(), self.trace.numel())
+        return self.trace
 
     def schedule(self):
         return amk_ctx_schedule(self.ctx)

@@ -31,6 +31,7 @@ AMK_OP_GATEUP, AMK_OP_DOWN, AMK_OP_LM, AMK_OP_ARGMAX = 5, 6, 7, 8
 
 # device status bits
 STATUS_TIMEOUT, STATUS_BAD_TOKEN = 1, 2
+TRACE_SLOTS = 6
 
 
 class amk_model_desc(C.Structure):
@@ -87,7 +88,8 @@ class amk_schedule_config(C.Structure):
     _fields_ = [("struct_size", C.c_uint32), ("n_cu", C.c_int32), ("tasks_qkv", C.c_int32),
                 ("tasks_o", C.c_int32), ("tasks_gateup", C.c_int32), ("tasks_down", C.c_int32),
                 ("tasks_lm", C.c_int32), ("attn_chunks", C.c_int32), ("attn_group_tasks", C.c_int32),
-                ("cu_assign", C.c_int32), ("ring_kb", C.c_int32), ("loader_depth", C.c_int32)]
+                ("cu_assign", C.c_int32), ("ring_kb", C.c_int32), ("loader_depth", C.c_int32),
+                ("prefetch_kb", C.c_int32)]
 
 
 # every symbol include/amk.h declares, with (restype, argtypes)
@@ -103,6 +105,7 @@ SIGNATURES = {
     "amk_decode_step": (C.c_int, [_P, _P, C.c_int32, _P, _P, _P]),
     "amk_device_status": (C.c_uint32, [_P]),
     "amk_ctx_schedule": (C.POINTER(amk_schedule), [_P]),
+    "amk_set_trace": (C.c_int, [_P, _P, C.c_uint64]),
     "amk_destroy": (None, [_P]),
     "amk_quantize": (C.c_int, [C.c_int32, _P, C.c_int64, C.c_int64, _P, _P, _P]),
     "amk_version": (C.c_char_p, []),

@@ -15,6 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libamk.so")
+BENCH = os.path.join(HERE, "amk_bench")
 ARCH = "gfx950"
 
 HIP_SOURCES = ["megakernel.hip", "prep.hip"]
@@ -60,6 +61,12 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp%d" % os.getpid()
     _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs])
     os.replace(tmp, LIB)
+    # the C-ABI benchmark driver (links the library, no device code of its own)
+    tmp = BENCH + ".tmp%d" % os.getpid()
+    _run(["g++", "-O2", "-std=c++17", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include", *inc,
+          "-o", tmp, os.path.join(CSRC, "amk_bench.cpp"), "-L", HERE, "-lamk", "-L", "/opt/rocm/lib",
+          "-lamdhip64", "-Wl,-rpath,$ORIGIN", "-Wl,-rpath,/opt/rocm/lib"])
+    os.replace(tmp, BENCH)
     return LIB
 
 

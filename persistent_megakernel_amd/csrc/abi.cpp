@@ -35,6 +35,7 @@ struct amk_ctx {
     uint32_t* d_abort = nullptr;
     uint32_t epoch = 0;
     hipStream_t last = nullptr;
+    uint64_t* trace = nullptr;      // caller-owned, optional
     KParams base;
 };
 
@@ -55,16 +56,16 @@ void logf(const char* what, const std::string& msg) {
 
 void free_ctx(amk_ctx* c) {
     if (!c) return;
-    hipFree(c->d_wstream);
-    hipFree(c->d_tasks);
-    hipFree(c->d_qoff);
-    hipFree(c->d_cuoff);
-    hipFree(c->d_ll);
-    hipFree(c->d_embed);
-    hipFree(c->d_norms);
-    hipFree(c->d_rope);
-    hipFree(c->d_abort);
-    if (c->h_status) hipHostFree(c->h_status);
+    (void)hipFree(c->d_wstream);
+    (void)hipFree(c->d_tasks);
+    (void)hipFree(c->d_qoff);
+    (void)hipFree(c->d_cuoff);
+    (void)hipFree(c->d_ll);
+    (void)hipFree(c->d_embed);
+    (void)hipFree(c->d_norms);
+    (void)hipFree(c->d_rope);
+    (void)hipFree(c->d_abort);
+    if (c->h_status) (void)hipHostFree(c->h_status);
     delete c;
 }
 
@@ -84,7 +85,7 @@ uint64_t watchdog_ticks() {
     return (uint64_t)(ms * 1e5);   // s_memrealtime runs at 100 MHz
 }
 
-// Smallest ring the loader can always make progress with: the widest weight row, or the K and
+// Smallest ring the loader can always make progress with: two of the widest weight rows, or the K and
 // V segments of one attention block, plus one 1 KiB load in flight.
 uint32_t ring_need(const amk_model_desc& d) {
     const uint32_t qd = (uint32_t)(d.n_heads * d.head_dim);
@@ -92,7 +93,7 @@ uint32_t ring_need(const amk_model_desc& d) {
     for (uint32_t K : {(uint32_t)d.hidden, qd, (uint32_t)d.intermediate}) pitch = std::max(pitch, row_pitch(d.wfmt, K));
     const uint32_t rowb = (uint32_t)d.head_dim * (d.act_f32 ? 4u : 2u);
     const uint32_t blk = 2u * (((uint32_t)kAttnBlock * rowb + 1023u) & ~1023u);
-    const uint32_t row = ((pitch + 1023u) & ~1023u) + 1024u;
+    const uint32_t row = ((2u * pitch + 1023u) & ~1023u) + 1024u;   // a wave works on two rows at once
     return std::max(row, blk + 1024u);
 }
 
@@ -153,7 +154,7 @@ extern "C" amk_status amk_create(const amk_model_desc* desc, const amk_weights* 
     }
     // ---- co-residency of one workgroup per CU
     int coop = 0;
-    hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
+    (void)hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
     if (!coop || megakernel_blocks_per_cu() < 1) { delete c; return AMK_E_NOT_RESIDENT; }
 
     // ---- device buffers
@@ -223,8 +224,8 @@ extern "C" amk_status amk_create(const amk_model_desc* desc, const amk_weights* 
         ck(upload(&d_rows, c->L.rows, stream));
         ck(launch_repack(d_rows, (uint32_t)c->L.rows.size(), d_tab, L, d.wfmt, c->d_wstream, stream));
         ck(hipStreamSynchronize(stream));
-        hipFree(d_rows);
-        hipFree((void*)d_tab);
+        (void)hipFree(d_rows);
+        (void)hipFree((void*)d_tab);
     }
     if (e != hipSuccess) { logf("create", hipGetErrorString(e)); free_ctx(c); return e == hipErrorOutOfMemory ? AMK_E_OOM : AMK_E_HIP; }
     c->L.rows.clear();
@@ -255,11 +256,15 @@ extern "C" amk_status amk_create(const amk_model_desc* desc, const amk_weights* 
     if (ring_kb * 1024 > kRingMaxBytes) ring_kb = kRingMaxBytes / 1024;
     P.ring_bytes = (uint32_t)ring_kb * 1024u;
     if (P.ring_bytes < ring_need(d)) {
-        logf("create", "LDS ring smaller than one weight row or one attention block");
+        logf("create", "LDS ring smaller than two weight rows or one attention block");
         free_ctx(c);
         return AMK_E_INVALID_ARG;
     }
     P.loader_depth = (cfg && cfg->loader_depth > 0) ? (uint32_t)cfg->loader_depth : (uint32_t)kLoaderDepthDefault;
+    {
+        const int pf = cfg ? cfg->prefetch_kb : 0;
+        P.prefetch_bytes = pf < 0 ? 0u : 1024u * (uint32_t)(pf > 0 ? std::min(pf, 4096) : kPrefetchKBDefault);
+    }
     c->last = stream;
     *out = c;
     return AMK_OK;
@@ -276,6 +281,7 @@ extern "C" amk_status amk_decode_step(amk_ctx* c, const int32_t* token_in, int32
     P.logits = logits;
     P.pos = pos;
     P.flag = (c->epoch % 0xffffffffu) + 1u;
+    P.trace = c->trace;
     hipStream_t st = (hipStream_t)stream_v;
     hipError_t e = launch_megakernel(P, c->n_cu, st);
     if (e != hipSuccess) { logf("decode_step", hipGetErrorString(e)); return AMK_E_HIP; }
@@ -286,18 +292,25 @@ extern "C" amk_status amk_decode_step(amk_ctx* c, const int32_t* token_in, int32
 
 extern "C" uint32_t amk_device_status(amk_ctx* c) {
     if (!c) return 0;
-    hipStreamSynchronize(c->last);
+    (void)hipStreamSynchronize(c->last);
     uint32_t s = 0;
     if (__atomic_load_n(&c->h_status[0], __ATOMIC_ACQUIRE)) s |= kStatusTimeout;
     if (__atomic_load_n(&c->h_status[1], __ATOMIC_ACQUIRE)) s |= kStatusBadToken;
     return s;
 }
 
+extern "C" amk_status amk_set_trace(amk_ctx* c, uint64_t* trace, uint64_t capacity) {
+    if (!c) return AMK_E_INVALID_ARG;
+    if (trace && capacity < (uint64_t)kTraceSlots * c->L.dtasks.size()) return AMK_E_INVALID_ARG;
+    c->trace = trace;
+    return AMK_OK;
+}
+
 extern "C" const amk_schedule* amk_ctx_schedule(const amk_ctx* c) { return c ? &c->L.sched->box.view : nullptr; }
 
 extern "C" void amk_destroy(amk_ctx* c) {
     if (!c) return;
-    hipStreamSynchronize(c->last);
+    (void)hipStreamSynchronize(c->last);
     free_ctx(c);
 }
 

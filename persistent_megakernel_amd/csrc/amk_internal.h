@@ -24,13 +24,16 @@ constexpr int kComputeThreads = kComputeWaves * 64;
 constexpr int kLdsTotal = 160 * 1024;
 constexpr int kHBytes = 32 * 1024;          // input vector stage (fp32 up to 8192, or 16-bit up to 16384 values)
 constexpr int kRedRows = 1024;              // row results per task
-constexpr int kAttnLds = 16 * 1024;         // attention: q, per-wave partial states, current row
+constexpr int kAttnLds = 8 * 1024;          // attention: q, current k/v, combination weights; residual rows
+constexpr int kTaskCache = 256;             // task descriptors of a CU's queue kept in LDS (32 bytes each)
 constexpr int kCtrlBytes = 1024;
-constexpr int kRingMaxBytes = kLdsTotal - kHBytes - kRedRows * 4 - kAttnLds - kCtrlBytes;  // 108 KiB
+constexpr int kRingMaxBytes = kLdsTotal - kHBytes - kRedRows * 4 - kAttnLds - kTaskCache * 32 - kCtrlBytes;  // 107 KiB
 constexpr int kRingDefaultKB = 104;
-constexpr int kLoaderDepthDefault = 40;     // 1 KiB loads in flight
+constexpr int kPrefetchKBDefault = 0;       // L2 prefetch distance on the weight stream (off unless configured)
+constexpr int kLoaderDepthDefault = 48;     // loads in flight beyond the current group (at most 53)
 constexpr int kAttnBlock = 64;              // positions per attention unit
 constexpr int kMaxAttnHeads = 8;            // query heads per attention task
+constexpr int kChunkedCtx = 256;            // caches at least this long get context-split attention by default
 constexpr int64_t kStageFloats = kHBytes / 4;   // fp32 values the input-vector stage holds
 
 // Limits the kernel supports (checked at create).
@@ -128,7 +131,13 @@ struct KParams {
     uint64_t watchdog_ticks;         // s_memrealtime ticks (100 MHz) before a spin-wait gives up
     uint32_t ring_bytes;             // LDS ring size used
     uint32_t loader_depth;
+    uint32_t prefetch_bytes;         // L2 prefetch distance ahead of the weight stream's LDS loads (0 = off)
+    uint64_t* trace;                 // optional per-task timestamps (kTraceSlots per device task) or null
 };
+
+// Trace slots per device task (s_memrealtime ticks, 100 MHz): compute start, inputs observed,
+// rows/blocks done, end; loader first issue, loader last issue.
+constexpr int kTraceSlots = 6;
 
 constexpr uint32_t kStatusTimeout = 1u;
 constexpr uint32_t kStatusBadToken = 2u;

@@ -193,6 +193,11 @@ bool derive_accesses(const Shape& s, const GenTask& t, uint64_t w_off, uint64_t 
         const uint32_t g = (uint32_t)((uint64_t)h0 * s.nKV / s.nH);
         if ((uint64_t)(h0 + nh - 1) * s.nKV / s.nH != g) return false;   // one KV group per task
         if ((uint64_t)kComputeWaves * nh * (s.hd + 2) > kStageFloats) return false;   // per-wave states in LDS
+        {   // dims per lane of the attention lane layout: hd / min(64 / nh rounded up to 2^k, hd) <= 8
+            uint32_t nhp = 1;
+            while (nhp < nh) nhp <<= 1;
+            if ((uint32_t)s.hd / std::min<uint32_t>(64u / nhp, (uint32_t)s.hd) > 8u) return false;
+        }
         add_acc(a, s.reg(l, L_QKV), 0, (uint64_t)h0 * s.hd, (uint64_t)(h0 + nh) * s.hd);
         if (c == nc - 1) {
             add_acc(a, s.reg(l, L_QKV), 0, qd + (uint64_t)g * s.hd, qd + (uint64_t)(g + 1) * s.hd);
@@ -309,7 +314,7 @@ bool check_plan(const amk_model_desc& d, const Lowered& out, std::string* msg) {
             if (t.tile_rows > (uint32_t)kRedRows) return fail("tile with more rows than the LDS row buffer");
             const uint32_t K = t.op == AMK_OP_OPROJ ? (uint32_t)qd : t.op == AMK_OP_DOWN ? (uint32_t)d.intermediate : (uint32_t)H;
             if (t.wofs + tile_bytes(d.wfmt, K, t.tile_rows) > len) return fail("tile outside its CU stream");
-            if (row_pitch(d.wfmt, K) > (uint32_t)kRingMaxBytes / 2) return fail("weight row larger than half the LDS ring");
+            if (row_pitch(d.wfmt, K) > (uint32_t)kRingMaxBytes / 3) return fail("weight row larger than a third of the LDS ring");
         }
     }
     return true;
@@ -451,7 +456,8 @@ amk_status lower_model(const amk_model_desc& d, const amk_schedule_config* cfg, 
     Shape s = make_shape(d);
     const int nH = s.nH, nKV = s.nKV, gsz = nH / nKV, vpw = s.vpw;
     // attention grouping
-    const bool group_tasks = C.attn_group_tasks == 1 || (C.attn_group_tasks == 0 && d.max_ctx > 1024);
+    // one attention task per KV group (its query heads share the K/V stream) unless asked not to
+    const bool group_tasks = C.attn_group_tasks == 1 || (C.attn_group_tasks == 0 && gsz > 1);   // 2: per query head
     int heads_per_task = 1;
     if (group_tasks) {
         heads_per_task = gsz;
@@ -467,18 +473,19 @@ amk_status lower_model(const amk_model_desc& d, const amk_schedule_config* cfg, 
         heads_per_task = h;
     }
     const int n_head_tasks = nH / heads_per_task;
-    const int nc_max = std::max(1, (int)(kStageFloats / ((int64_t)heads_per_task * (s.hd + 2))));
+    // merges run one query head each: a head's chunk states must fit the LDS stage
+    const int nc_max = std::max(1, (int)(kStageFloats / (s.hd + 2)));
     int nc = C.attn_chunks;
     if (nc <= 0) {
         nc = 1;
-        if (group_tasks) {
-            int by_cu = std::max(1, n_cu / n_head_tasks);
-            int by_ctx = (d.max_ctx + 127) / 128;
+        if (d.max_ctx >= kChunkedCtx) {   // long caches: split the context so every CU streams a piece
+            const int by_cu = std::max(1, n_cu / n_head_tasks);
+            const int by_ctx = std::max(1, d.max_ctx / 128);   // about 128 positions per chunk at full cache
             nc = std::max(1, std::min(std::min(by_cu, by_ctx), nc_max));
         }
     }
     s.nchunks = nc;
-    const bool xcd = C.cu_assign == 0;
+    const bool xcd = C.cu_assign == 0 && nc == 1;   // chunked attention is spread over all CUs
 
     std::vector<GenTask> T;
     uint32_t nctr = 0;
@@ -539,11 +546,12 @@ amk_status lower_model(const amk_model_desc& d, const amk_schedule_config* cfg, 
                 if (c == nc - 1) T[id].waits.push_back({c_kv[g], UINT32_MAX});
                 T[id].sigs.push_back(nc == 1 ? c_att : c_part[m]);
             }
-            if (nc > 1) {
-                uint32_t id = mk(AMK_OP_MERGE, l, h0, heads_per_task, 0, nc, first_cu);
-                T[id].waits.push_back({c_part[m], UINT32_MAX});
-                T[id].sigs.push_back(c_att);
-            }
+            if (nc > 1)   // one merge per query head, next to the group's first chunk
+                for (int h = h0; h < h0 + heads_per_task; ++h) {
+                    uint32_t id = mk(AMK_OP_MERGE, l, h, 1, 0, nc, first_cu + (uint32_t)(h - h0));
+                    T[id].waits.push_back({c_part[m], UINT32_MAX});
+                    T[id].sigs.push_back(c_att);
+                }
         }
         // O projection
         const uint64_t uo = (uint64_t)s.H / vpw, to = ntasks(C.tasks_o, uo);

@@ -54,6 +54,8 @@ struct __attribute__((aligned(16))) Lds {
     uint32_t abort_;                   // this workgroup gives up
     float fpart[2 * kComputeWaves];
     int32_t ipart[2 * kComputeWaves];
+    uint32_t pf_sink[64];              // destination of the loader's L2 prefetches (never read)
+    DevTask tcache[kTaskCache];        // the first kTaskCache tasks of this CU's queue
 };
 static_assert(sizeof(Lds) <= kLdsTotal, "LDS budget");
 
@@ -104,6 +106,12 @@ DEV void dma16(const void* gptr, uint32_t lds_addr) {
                  : "memory", "m0");
 }
 DEV void vm_wait0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// L2 prefetch of 8 KiB: lane i touches the 128-byte line at gptr + 128 i with a 4-byte LDS-DMA
+// load into a sink (no VGPR result, so nothing in flight can clobber a register).
+DEV void prefetch_8k(const void* gptr, uint32_t sink_lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(sink_lds)
+                 : "memory", "m0");
+}
 
 struct Ctx {
     const KParams* P;
@@ -111,6 +119,11 @@ struct Ctx {
     uint64_t deadline;
     int cu;
 };
+
+// task t of this CU's queue (starting at q0): from the LDS copy when it holds it
+DEV DevTask task_at(const Ctx& c, uint32_t q0, uint32_t t) {
+    return t - q0 < (uint32_t)kTaskCache ? c.S->tcache[t - q0] : c.P->tasks[t];
+}
 
 DEV bool expired(const Ctx& c) {
     if (rt() > c.deadline) return true;
@@ -123,11 +136,16 @@ DEV void raise_timeout(const Ctx& c) {
     __hip_atomic_store(&c.P->status[0], kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-// spin step of every wait: bounded by the watchdog and by the global abort flag
+// spin step of every wait: bounded by the watchdog and by the global abort flag. The global
+// flag is a device-coherent load (a memory round trip), so it is read only once a wait has
+// lasted about 100 us (counted in 64-spin steps of the realtime clock); another workgroup sets
+// it only after its own watchdog (far longer) expired.
 DEV bool spin_ok(const Ctx& c, uint32_t& n) {
     if (((++n) & 63u) == 0) {
-        if (rt() > c.deadline) { raise_timeout(c); return false; }
-        if (__hip_atomic_load(c.P->abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+        const uint64_t now = rt();
+        if (now > c.deadline) { raise_timeout(c); return false; }
+        if ((n & 0xfffu) == 0 &&
+            __hip_atomic_load(c.P->abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
             __hip_atomic_store(&c.S->abort_, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             return false;
         }
@@ -199,52 +217,115 @@ DEV void for_segments(const KParams& P, const DevTask& T, int cu, F&& fn) {
     }
 }
 
+// Ring-stream bytes a task occupies (what for_segments streams, each segment rounded to 1 KiB),
+// computed without touching global memory.
+DEV uint32_t task_foot(const KParams& P, const DevTask& T) {
+    if (is_gemv(T.op)) return kb_round(tile_bytes(P.wfmt, K_of(P, T.op), T.tile_rows));
+    if (T.op != AMK_OP_ATTN) return 0;
+    uint32_t h0, h1;
+    chunk_range(P.pos, T.arg[2], T.arg[3], h0, h1);
+    const uint32_t n = h1 - h0, nb = (n + kAttnBlock - 1) / kAttnBlock, rowb = kv_row_bytes(P);
+    if (!nb) return 0;
+    return (nb - 1) * 2 * kb_round((uint64_t)kAttnBlock * rowb) + 2 * kb_round((uint64_t)(n - (nb - 1) * kAttnBlock) * rowb);
+}
+
 // ------------------------------------------------------------------ loader wave
 
+// smallest ring-stream position some compute wave still needs
+DEV uint32_t min_released(const Lds& S) {
+    uint32_t m = lds_ld(&S.released[0]);
+    for (int w = 1; w < kComputeWaves; ++w) {
+        const uint32_t r = lds_ld(&S.released[w]);
+        if ((int)(r - m) < 0) m = r;
+    }
+    return m;
+}
+
+constexpr uint32_t kLoadGroup = 8;   // 1 KiB loads issued back to back between bookkeeping
+constexpr uint32_t kMaxPrefetchPerGroup = 2;   // L2 prefetch instructions issued before one group
+
+// The loader wave: streams every segment of its queue into the ring, 1 KiB per LDS-DMA
+// instruction, in groups of kLoadGroup with one ring-space check and one publication per group.
+// At most DEPTH + kLoadGroup loads are in flight (the hardware counts up to 63). `filled` is
+// published DEPTH loads behind the issue point in steady state, and in full before the loader
+// blocks on ring space, so every landed byte a compute wave waits for is eventually published.
 template <int DEPTH>
 DEV void loader_run(const Ctx& c) {
+    static_assert(DEPTH + kLoadGroup + kMaxPrefetchPerGroup <= 63, "in-flight loads exceed the vmcnt range");
     const KParams& P = *c.P;
     Lds& S = *c.S;
     const int lane = lane_id();
     const uint32_t ring = P.ring_bytes;
     const uint32_t ring_lds = (uint32_t)(uintptr_t)S.ring;
-    uint32_t issued = 0, published = 0, consumed = 0;
+    uint32_t issued = 0, published = 0, consumed = 0;   // 1 KiB units issued/published; bytes consumed
+    uint32_t inflight = 0;                              // vector memory instructions possibly outstanding
+    uint32_t roff = 0;                                  // ring offset of the next 1 KiB
     bool ok = true;
     const uint32_t q0 = P.queue_off[c.cu], q1 = P.queue_off[c.cu + 1];
+    // the CU's weight stream is contiguous: it is touched prefetch_bytes ahead of the LDS loads
+    const uint8_t* wbase = P.wstream + P.cu_stream_off[c.cu];
+    const uint32_t wlen = (uint32_t)(P.cu_stream_off[c.cu + 1] - P.cu_stream_off[c.cu]);
+    const uint32_t sink = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)S.pf_sink);
+    uint32_t pf = 0;                                    // weight-stream bytes prefetched so far
     for (uint32_t t = q0; t < q1 && ok; ++t) {
-        const DevTask T = P.tasks[t];
+        const DevTask T = task_at(c, q0, t);
+        uint64_t* tr = P.trace ? P.trace + (uint64_t)t * kTraceSlots : nullptr;
+        if (tr && lane == 0) tr[4] = rt();
         for_segments(P, T, c.cu, [&](const uint8_t* g, uint64_t bytes) {
             const uint32_t n_inst = (uint32_t)((bytes + 1023) / 1024);
-            for (uint32_t k = 0; k < n_inst && ok; ++k) {
-                const uint32_t pos = issued * 1024u;
-                if ((int)(pos + 1024u - (consumed + ring)) > 0) {
-                    vm_wait0();
-                    published = issued;
-                    lds_st(&S.filled, published * 1024u);
-                    uint32_t n = 0;
-                    for (;;) {
-                        uint32_t m = lds_ld(&S.released[0]);
-                        for (int w = 1; w < kComputeWaves; ++w) {
-                            uint32_t r = lds_ld(&S.released[w]);
-                            if ((int)(r - m) < 0) m = r;
-                        }
-                        consumed = m;
-                        if ((int)(pos + 1024u - (consumed + ring)) <= 0) break;
-                        if (!spin_ok(c, n)) { ok = false; break; }
+            const uint32_t tail = (uint32_t)(bytes - (uint64_t)(n_inst - 1) * 1024u);   // bytes in the last 1 KiB
+            const uint8_t* src = g + (uint32_t)lane * 16u;
+            const bool weights = g >= wbase && g < wbase + wlen;
+            const uint32_t wofs = weights ? (uint32_t)(g - wbase) : 0u;
+            for (uint32_t k = 0; k < n_inst && ok;) {
+                const uint32_t grp = min(kLoadGroup, n_inst - k);
+                if (weights && P.prefetch_bytes) {   // keep the L2 prefetch ahead of this group
+                    const uint32_t want = min(wofs + (k + grp) * 1024u + P.prefetch_bytes, wlen);
+                    for (uint32_t n = 0; pf < want && n < kMaxPrefetchPerGroup; ++n) {
+                        if (pf + (uint32_t)lane * 128u < wlen) prefetch_8k(wbase + pf + (uint32_t)lane * 128u, sink);
+                        pf += 8192u;
+                        ++inflight;
                     }
-                    if (!ok) break;
                 }
-                const uint64_t off = (uint64_t)k * 1024u + (uint64_t)lane * 16u;
-                const uint32_t dst = __builtin_amdgcn_readfirstlane(ring_lds + pos % ring);
-                if (off < bytes) dma16(g + off, dst);
-                ++issued;
-                if (issued - published > (uint32_t)DEPTH) {
+                const uint32_t need = (issued + grp) * 1024u;   // stream end after this group
+                if ((int)(need - (consumed + ring)) > 0) {
+                    consumed = min_released(S);
+                    if ((int)(need - (consumed + ring)) > 0) {
+                        // blocked: publish everything in flight, then wait for the compute waves
+                        vm_wait0();
+                        inflight = 0;
+                        published = issued;
+                        lds_st(&S.filled, published * 1024u);
+                        uint32_t n = 0;
+                        for (;;) {
+                            consumed = min_released(S);
+                            if ((int)(need - (consumed + ring)) <= 0) break;
+                            if (!spin_ok(c, n)) { ok = false; break; }
+                        }
+                        if (!ok) break;
+                    }
+                }
+                for (uint32_t j = 0; j < grp; ++j, ++k) {
+                    const uint32_t dst = __builtin_amdgcn_readfirstlane(ring_lds + roff);
+                    if (k + 1 < n_inst || (uint32_t)lane * 16u < tail) dma16(src + (uint64_t)k * 1024u, dst);
+                    roff += 1024u;
+                    if (roff == ring) roff = 0;
+                }
+                issued += grp;
+                inflight += grp;
+                if (inflight > (uint32_t)DEPTH) {
+                    // the DEPTH most recent instructions hold at most DEPTH of these 1 KiB loads:
+                    // everything issued before them has landed
                     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DEPTH) : "memory");
-                    published = issued - DEPTH;
-                    lds_st(&S.filled, published * 1024u);
+                    inflight = DEPTH;
+                    if ((int)(issued - DEPTH - published) > 0) {
+                        published = issued - DEPTH;
+                        lds_st(&S.filled, published * 1024u);
+                    }
                 }
             }
         });
+        if (tr && lane == 0) tr[5] = rt();
     }
     vm_wait0();
     lds_st(&S.filled, issued * 1024u);
@@ -252,36 +333,42 @@ DEV void loader_run(const Ctx& c) {
 
 // ------------------------------------------------------------------ compute-side building blocks
 
-constexpr int kMaxWordsPerThread = 9;
+// Words each compute thread has in flight at once while gathering flag-carrying words. The
+// gather walks its words in chunks of this many, so its register use does not grow with the
+// vector length.
+constexpr int kGatherChunk = 4;
 
 // Wait until words [0, n) of a flag-carrying buffer all carry `flag`; hand each payload to fn.
-// Each compute thread polls words ctid + k * kComputeThreads.
+// Each compute thread polls words ctid + k * kComputeThreads, kGatherChunk of them at a time.
 template <typename F>
 DEV bool ll_gather(const Ctx& c, const u64* base, uint32_t n, int ctid, F&& fn) {
     const uint32_t flag = c.P->flag;
-    u64 w[kMaxWordsPerThread];
+    const uint32_t step = (uint32_t)kGatherChunk * kComputeThreads;
+    for (uint32_t i0 = (uint32_t)ctid; i0 < n; i0 += step) {
+        u64 w[kGatherChunk];
 #pragma unroll
-    for (int k = 0; k < kMaxWordsPerThread; ++k) {
-        const uint32_t i = (uint32_t)ctid + (uint32_t)k * kComputeThreads;
-        w[k] = i < n ? ll_load(base + i) : ((u64)flag << 32);
-    }
-    uint32_t spins = 0;
-    for (;;) {
-        bool done = true;
-#pragma unroll
-        for (int k = 0; k < kMaxWordsPerThread; ++k) done &= (uint32_t)(w[k] >> 32) == flag;
-        if (done) break;
-        if (!spin_ok(c, spins)) return false;
-#pragma unroll
-        for (int k = 0; k < kMaxWordsPerThread; ++k) {
-            const uint32_t i = (uint32_t)ctid + (uint32_t)k * kComputeThreads;
-            if ((uint32_t)(w[k] >> 32) != flag) w[k] = ll_load(base + i);
+        for (int k = 0; k < kGatherChunk; ++k) {
+            const uint32_t i = i0 + (uint32_t)k * kComputeThreads;
+            w[k] = i < n ? ll_load(base + i) : ((u64)flag << 32);
         }
-    }
+        uint32_t spins = 0;
+        for (;;) {
+            bool done = true;
 #pragma unroll
-    for (int k = 0; k < kMaxWordsPerThread; ++k) {
-        const uint32_t i = (uint32_t)ctid + (uint32_t)k * kComputeThreads;
-        if (i < n) fn(i, (uint32_t)w[k]);
+            for (int k = 0; k < kGatherChunk; ++k) done &= (uint32_t)(w[k] >> 32) == flag;
+            if (done) break;
+            if (!spin_ok(c, spins)) return false;
+#pragma unroll
+            for (int k = 0; k < kGatherChunk; ++k) {
+                const uint32_t i = i0 + (uint32_t)k * kComputeThreads;
+                if ((uint32_t)(w[k] >> 32) != flag) w[k] = ll_load(base + i);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kGatherChunk; ++k) {
+            const uint32_t i = i0 + (uint32_t)k * kComputeThreads;
+            if (i < n) fn(i, (uint32_t)w[k]);
+        }
     }
     return true;
 }
@@ -355,107 +442,131 @@ DEV bool stage_input(const Ctx& c, int ctid, uint32_t& gen, const u64* src, cons
     return cbar(c, gen);
 }
 
-// GEMV rows of one task out of the ring: S.red[r] = sum_k W[r][k] h[k] (x scale for int8).
-DEV bool gemv_rows(const Ctx& c, int cw, uint32_t tile_pos, uint32_t rows, uint32_t K) {
+DEV uint32_t wrap(uint32_t off, uint32_t ring) { return off >= ring ? off - ring : off; }
+
+// Partial dot products of two weight rows (ring offsets b0, b1) with the staged input vector
+// over this lane's 16-byte weight segments s = lane, lane + 64, ...; the input values of a
+// segment are read once for both rows. Weights are widened in registers: fp32 as is, bf16 by a
+// shift, int8 by a sign-extending byte conversion, int4 by nibble extraction minus the bias 8
+// with each 128-column group's partial sum scaled by its fp16 scale. Products are exact in fp32
+// (bf16 x bf16, int x bf16); sums are fp32.
+template <int FMT>
+DEV void dot2(const Lds& S, uint32_t b0, uint32_t b1, uint32_t K, uint32_t ring, int lane, float& acc0, float& acc1) {
+    const uint16_t* hb = (const uint16_t*)S.hb;
+    if constexpr (FMT == AMK_F32) {
+        for (uint32_t s = (uint32_t)lane; s < K / 4; s += 64) {
+            const u32x4 w0 = ring16(S, wrap(b0 + 16 * s, ring)), w1 = ring16(S, wrap(b1 + 16 * s, ring));
+            const u32x4 hv = *(const u32x4*)(S.hf + 4 * s);
+            const float h[4] = {__uint_as_float(hv.x), __uint_as_float(hv.y), __uint_as_float(hv.z), __uint_as_float(hv.w)};
+            const uint32_t a[4] = {w0.x, w0.y, w0.z, w0.w}, b[4] = {w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                acc0 += __uint_as_float(a[k]) * h[k];
+                acc1 += __uint_as_float(b[k]) * h[k];
+            }
+        }
+    } else if constexpr (FMT == AMK_BF16) {
+        for (uint32_t s = (uint32_t)lane; s < K / 8; s += 64) {
+            const u32x4 w0 = ring16(S, wrap(b0 + 16 * s, ring)), w1 = ring16(S, wrap(b1 + 16 * s, ring));
+            const u32x4 hv = *(const u32x4*)(hb + 8 * s);
+            const uint32_t hh[4] = {hv.x, hv.y, hv.z, hv.w}, a[4] = {w0.x, w0.y, w0.z, w0.w}, b[4] = {w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float hl = bf2f(hh[k] & 0xffffu), hu = bf2f(hh[k] >> 16);
+                acc0 += bf2f(a[k] & 0xffffu) * hl;
+                acc0 += bf2f(a[k] >> 16) * hu;
+                acc1 += bf2f(b[k] & 0xffffu) * hl;
+                acc1 += bf2f(b[k] >> 16) * hu;
+            }
+        }
+    } else if constexpr (FMT == AMK_INT8_PC) {
+        for (uint32_t s = (uint32_t)lane; s < K / 16; s += 64) {
+            const u32x4 w0 = ring16(S, wrap(b0 + 16 * s, ring)), w1 = ring16(S, wrap(b1 + 16 * s, ring));
+            const u32x4 h0 = *(const u32x4*)(hb + 16 * s), h1 = *(const u32x4*)(hb + 16 * s + 8);
+            const uint32_t hh[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+            const uint32_t a[4] = {w0.x, w0.y, w0.z, w0.w}, b[4] = {w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t hw = hh[(4 * k + j) >> 1];
+                    const float h = bf2f(((4 * k + j) & 1) ? (hw >> 16) : (hw & 0xffffu));
+                    acc0 += (float)(int8_t)((a[k] >> (8 * j)) & 0xffu) * h;
+                    acc1 += (float)(int8_t)((b[k] >> (8 * j)) & 0xffu) * h;
+                }
+        }
+    } else {   // int4 g128: row = [K/128 fp16 scales][K/2 bytes of nibbles, biased by 8]
+        const uint32_t coff = int4_codes_off(K);
+        for (uint32_t s = (uint32_t)lane; s < K / 32; s += 64) {
+            const u32x4 w0 = ring16(S, wrap(b0 + coff + 16 * s, ring)), w1 = ring16(S, wrap(b1 + coff + 16 * s, ring));
+            const float sc0 = h2f(*(const uint16_t*)(S.ring + wrap(b0 + 2 * (s / 4), ring)));
+            const float sc1 = h2f(*(const uint16_t*)(S.ring + wrap(b1 + 2 * (s / 4), ring)));
+            const uint32_t a[4] = {w0.x, w0.y, w0.z, w0.w}, b[4] = {w1.x, w1.y, w1.z, w1.w};
+            float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const u32x4 hv = *(const u32x4*)(hb + 32 * s + 8 * k);
+                const uint32_t hh[4] = {hv.x, hv.y, hv.z, hv.w};
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const uint32_t hw = hh[j >> 1];
+                    const float h = bf2f((j & 1) ? (hw >> 16) : (hw & 0xffffu));
+                    p0 += (float)((int)((a[k] >> (4 * j)) & 0xfu) - 8) * h;
+                    p1 += (float)((int)((b[k] >> (4 * j)) & 0xfu) - 8) * h;
+                }
+            }
+            acc0 += sc0 * p0;
+            acc1 += sc1 * p1;
+        }
+    }
+}
+
+// GEMV rows of one task out of the ring: S.red[r] = sum_k W[r][k] h[k] (times the row scale for
+// int8). Wave w takes the row pairs (2p, 2p+1), p = w, w + kComputeWaves, ...
+template <int FMT>
+DEV bool gemv_rows_fmt(const Ctx& c, int cw, uint32_t tile_pos, uint32_t rows, uint32_t K) {
     const KParams& P = *c.P;
     Lds& S = *c.S;
     const int lane = lane_id();
     const uint32_t ring = P.ring_bytes;
-    const uint32_t pitch = row_pitch(P.wfmt, K);
-    const uint32_t hdr = tile_header(P.wfmt, rows);
-    const uint16_t* hb = (const uint16_t*)S.hb;
+    const uint32_t pitch = row_pitch(FMT, K);
+    const uint32_t end = tile_pos + kb_round(tile_bytes(FMT, K, rows));
+    const uint32_t pairs = (rows + 1) / 2;
     // Advertise the first ring byte this wave still needs before waiting for any row: until
     // it does, the loader cannot run more than one ring past the task start, and a wave whose
     // first row lies beyond that would wait forever.
-    if (lane == 0)
-        lds_st(&S.released[cw], (uint32_t)cw < rows ? tile_pos + hdr + (uint32_t)cw * pitch
-                                                     : tile_pos + kb_round(tile_bytes(P.wfmt, K, rows)));
-    for (uint32_t r = (uint32_t)cw; r < rows; r += kComputeWaves) {
-        const uint32_t rpos = tile_pos + hdr + r * pitch;
-        if (!wait_filled(c, rpos + pitch)) return false;
-        const uint32_t base = rpos % ring;
-        float acc = 0.f;
-        if (P.wfmt == AMK_F32) {
-            const uint32_t nseg = K / 4;
-            for (uint32_t s = (uint32_t)lane; s < nseg; s += 64) {
-                uint32_t off = base + 16 * s;
-                if (off >= ring) off -= ring;
-                const u32x4 w = ring16(S, off);
-                const float* h = S.hf + 4 * s;
-                acc += __uint_as_float(w.x) * h[0];
-                acc += __uint_as_float(w.y) * h[1];
-                acc += __uint_as_float(w.z) * h[2];
-                acc += __uint_as_float(w.w) * h[3];
-            }
-        } else if (P.wfmt == AMK_BF16) {
-            const uint32_t nseg = K / 8;
-            for (uint32_t s = (uint32_t)lane; s < nseg; s += 64) {
-                uint32_t off = base + 16 * s;
-                if (off >= ring) off -= ring;
-                const u32x4 w = ring16(S, off);
-                const u32x4 h = *(const u32x4*)(hb + 8 * s);
-                uint32_t wv[4] = {w.x, w.y, w.z, w.w}, hv[4] = {h.x, h.y, h.z, h.w};
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    acc += bf2f(wv[k] & 0xffffu) * bf2f(hv[k] & 0xffffu);
-                    acc += bf2f(wv[k] >> 16) * bf2f(hv[k] >> 16);
-                }
-            }
-        } else if (P.wfmt == AMK_INT8_PC) {
-            const uint32_t nseg = K / 16;
-            for (uint32_t s = (uint32_t)lane; s < nseg; s += 64) {
-                uint32_t off = base + 16 * s;
-                if (off >= ring) off -= ring;
-                const u32x4 w = ring16(S, off);
-                const u32x4 h0 = *(const u32x4*)(hb + 16 * s);
-                const u32x4 h1 = *(const u32x4*)(hb + 16 * s + 8);
-                uint32_t wv[4] = {w.x, w.y, w.z, w.w}, hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
-#pragma unroll
-                for (int k = 0; k < 4; ++k)
-#pragma unroll
-                    for (int b = 0; b < 4; ++b) {
-                        const float q = (float)(int8_t)((wv[k] >> (8 * b)) & 0xffu);
-                        const uint32_t hw = hv[(4 * k + b) >> 1];
-                        acc += q * bf2f(((4 * k + b) & 1) ? (hw >> 16) : (hw & 0xffffu));
-                    }
-            }
-        } else {   // int4 g128: row = [K/128 fp16 scales][K/2 bytes of nibbles (biased by 8)]
-            const uint32_t nseg = K / 32, coff = int4_codes_off(K);
-            for (uint32_t s = (uint32_t)lane; s < nseg; s += 64) {
-                uint32_t off = base + coff + 16 * s;
-                if (off >= ring) off -= ring;
-                const u32x4 w = ring16(S, off);
-                uint32_t soff = base + 2 * (s / 4);
-                if (soff >= ring) soff -= ring;
-                const float sc = h2f(*(const uint16_t*)(S.ring + soff));
-                uint32_t wv[4] = {w.x, w.y, w.z, w.w};
-                float part = 0.f;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const u32x4 h = *(const u32x4*)(hb + 32 * s + 8 * k);
-                    uint32_t hv[4] = {h.x, h.y, h.z, h.w};
-#pragma unroll
-                    for (int b = 0; b < 8; ++b) {
-                        const float q = (float)((int)((wv[k] >> (4 * b)) & 0xfu) - 8);
-                        const uint32_t hw = hv[b >> 1];
-                        part += q * bf2f((b & 1) ? (hw >> 16) : (hw & 0xffffu));
-                    }
-                }
-                acc += sc * part;
-            }
+    if (lane == 0) lds_st(&S.released[cw], (uint32_t)cw < pairs ? tile_pos + 2u * (uint32_t)cw * pitch : end);
+    for (uint32_t p = (uint32_t)cw; p < pairs; p += kComputeWaves) {
+        const uint32_t r0 = 2 * p;
+        const bool two = r0 + 1 < rows;
+        const uint32_t rpos = tile_pos + r0 * pitch;
+        if (!wait_filled(c, rpos + (two ? 2 : 1) * pitch)) return false;
+        const uint32_t b0 = rpos % ring, b1 = wrap(b0 + pitch, ring);
+        float acc0 = 0.f, acc1 = 0.f;
+        dot2<FMT>(S, b0, two ? b1 : b0, K, ring, lane, acc0, acc1);
+        acc0 = wave_sum(acc0);
+        acc1 = wave_sum(acc1);
+        if constexpr (FMT == AMK_INT8_PC) {
+            acc0 *= h2f(*(const uint16_t*)(S.ring + wrap(b0 + K, ring)));
+            acc1 *= h2f(*(const uint16_t*)(S.ring + wrap(b1 + K, ring)));
         }
-        acc = wave_sum(acc);
-        if (P.wfmt == AMK_INT8_PC) {
-            uint32_t soff = base + K;
-            if (soff >= ring) soff -= ring;
-            acc *= h2f(*(const uint16_t*)(S.ring + soff));
+        if (lane == 0) {
+            S.red[r0] = acc0;
+            if (two) S.red[r0 + 1] = acc1;
+            const uint32_t pn = p + kComputeWaves;
+            lds_st(&S.released[cw], pn < pairs ? tile_pos + 2u * pn * pitch : end);
         }
-        if (lane == 0) S.red[r] = acc;
-        const uint32_t next = r + kComputeWaves < rows ? tile_pos + hdr + (r + kComputeWaves) * pitch
-                                                       : tile_pos + kb_round(tile_bytes(P.wfmt, K, rows));
-        if (lane == 0) lds_st(&S.released[cw], next);
     }
     return true;
+}
+
+DEV bool gemv_rows(const Ctx& c, int cw, uint32_t tile_pos, uint32_t rows, uint32_t K) {
+    switch (c.P->wfmt) {
+    case AMK_F32: return gemv_rows_fmt<AMK_F32>(c, cw, tile_pos, rows, K);
+    case AMK_BF16: return gemv_rows_fmt<AMK_BF16>(c, cw, tile_pos, rows, K);
+    case AMK_INT8_PC: return gemv_rows_fmt<AMK_INT8_PC>(c, cw, tile_pos, rows, K);
+    default: return gemv_rows_fmt<AMK_INT4_G128>(c, cw, tile_pos, rows, K);
+    }
 }
 
 // ------------------------------------------------------------------ the ops
@@ -467,7 +578,13 @@ struct TaskEnv {
     uint32_t tile_pos;   // ring-stream position of the task's first segment
     LLLayout y;
     int token;
+    uint64_t* tr;        // this task's trace slots, or null
 };
+
+// timestamp slot k of the current task (first compute thread only)
+DEV void mark(const TaskEnv& e, int k) {
+    if (e.tr && e.ctid == 0) e.tr[k] = rt();
+}
 
 DEV bool op_gemv(const TaskEnv& e, const DevTask& T) {
     const Ctx& c = *e.c;
@@ -492,6 +609,15 @@ DEV bool op_gemv(const TaskEnv& e, const DevTask& T) {
     case AMK_OP_DOWN: src = LLl + e.y.a; break;
     case AMK_OP_LM: src = ll_layer(P, e.y, P.L - 1) + e.y.xd; gains = P.norms + (uint64_t)P.L * 2 * P.H; break;
     }
+    // QKV: this thread's rotary cos/sin (quad ctid), loaded now so the load overlaps the input wait
+    float rc0 = 1.f, rs0 = 0.f, rc1 = 1.f, rs1 = 0.f;
+    if (op == AMK_OP_QKV && (uint32_t)ctid < T.arg[1]) {
+        const uint32_t u = T.arg[0] + (uint32_t)ctid, per = (uint32_t)P.hd / 4;
+        if (u / per < (uint32_t)(P.nH + P.nKV)) {   // q and k heads rotate, v heads do not
+            const float4 cs = *(const float4*)(P.rope + ((uint64_t)P.pos * (P.hd / 2) + 2 * (u % per)) * 2);
+            rc0 = cs.x; rs0 = cs.y; rc1 = cs.z; rs1 = cs.w;
+        }
+    }
     // residual rows (O and down): from the previous x (or the embedding row at layer 0)
     if (op == AMK_OP_OPROJ || op == AMK_OP_DOWN) {
         const uint32_t r0 = T.arg[0], n = T.arg[1];
@@ -508,8 +634,10 @@ DEV bool op_gemv(const TaskEnv& e, const DevTask& T) {
         }
     }
     if (!stage_input(c, ctid, *e.gen, src, emb, K, gains)) return false;
+    mark(e, 1);
     if (!gemv_rows(c, e.cw, e.tile_pos, rows, K)) return false;
     if (!cbar(c, *e.gen)) return false;
+    mark(e, 2);
     const uint32_t flag = P.flag;
     switch (op) {
     case AMK_OP_QKV: {
@@ -517,14 +645,15 @@ DEV bool op_gemv(const TaskEnv& e, const DevTask& T) {
         const uint32_t nq = T.arg[1], per = (uint32_t)P.hd / 4, half = (uint32_t)P.hd / 2;
         const uint32_t qd = (uint32_t)(P.nH * P.hd), kd = (uint32_t)(P.nKV * P.hd);
         u64* out = (u64*)(LLl + e.y.qkv);
-        for (uint32_t k = (uint32_t)ctid; k < nq; k += kComputeThreads) {
+        // one quad per thread (a task has at most kRedRows / 4 < kComputeThreads quads)
+        if ((uint32_t)ctid < nq) {
+            const uint32_t k = (uint32_t)ctid;
             const uint32_t u = T.arg[0] + k, head = u / per, m = u % per;
             const uint32_t base = head * (uint32_t)P.hd;
             float v0 = S.red[4 * k], v1 = S.red[4 * k + 1], v2 = S.red[4 * k + 2], v3 = S.red[4 * k + 3];
             const bool rot = base < qd + kd;
             if (rot) {
-                const float* cs = P.rope + ((uint64_t)P.pos * half + 2 * m) * 2;
-                const float c0 = cs[0], s0 = cs[1], c1 = cs[2], s1 = cs[3];
+                const float c0 = rc0, s0 = rs0, c1 = rc1, s1 = rs1;
                 const float a0 = v0 * c0 - v2 * s0, b0 = v2 * c0 + v0 * s0;
                 const float a1 = v1 * c1 - v3 * s1, b1 = v3 * c1 + v1 * s1;
                 v0 = a0; v2 = b0; v1 = a1; v3 = b1;
@@ -620,21 +749,48 @@ DEV bool op_gemv(const TaskEnv& e, const DevTask& T) {
     return true;
 }
 
-// Attention of query heads [h0, h0+nh) (one KV group g) over chunk c of the context.
+// LDS map of an attention task inside S.att (floats): q of the task's heads, the current k and v,
+// the cross-wave combination weights, the per-head maxima.
+constexpr int kAttQ = 0;                          // [nh][hd], nh * hd <= 1024
+constexpr int kAttKc = kMaxAttnHeads * 128;       // [hd]
+constexpr int kAttVc = kAttKc + 128;              // [hd]
+constexpr int kAttF = kAttVc + 128;               // [kComputeWaves][kMaxAttnHeads] weights exp(m_w - M)
+constexpr int kAttM = kAttF + kComputeWaves * kMaxAttnHeads;   // [kMaxAttnHeads] maxima
+static_assert(kAttM + kMaxAttnHeads <= kAttnLds / 4, "attention LDS map");
+constexpr int kAttMaxD = 8;                       // dims per lane: hd / lanes-per-head (the lowering keeps it <= 8)
+
+// One K or V element of ring row `roff` (activation format), as fp32.
+DEV float kv_at(const KParams& P, const Lds& S, uint32_t roff, uint32_t d) {
+    return P.act_f32 ? *(const float*)(S.ring + roff + 4 * d) : bf2f(*(const uint16_t*)(S.ring + roff + 2 * d));
+}
+
+// Attention of query heads [h0, h0+nh) (one KV group g) over chunk ch of nc of the context
+// positions [0, pos]: the softmax-weighted sum of V rows with weights from q.K / sqrt(hd)
+// (page 3, "How it works", the attention instruction over the persistent KV cache).
+//
+// Lane layout: the 64 lanes of a wave are (query head, dimension group) pairs: a head owns L
+// lanes (L = 64 / nh rounded to a power of two, at most hd), a lane owns D = hd / L
+// consecutive dims and keeps its q slice and its slice of the running output in registers. A
+// position's score is the lane-group sum of q.K over the group; softmax runs online (running
+// max m, running sum l, rescaled output o). Positions are dealt round robin to the compute
+// waves, so even a short chunk keeps every wave busy; the current position (last chunk only)
+// comes from the flag-carrying words, the history from the ring. At the end the per-wave
+// states (m, l, o) are combined with weights exp(m_w - M) computed once per (wave, head); a
+// single chunk writes the output row, a split context writes its (M, L, o) partial state.
 DEV bool op_attn(const TaskEnv& e, const DevTask& T) {
     const Ctx& c = *e.c;
     const KParams& P = *c.P;
     Lds& S = *c.S;
     const int l = T.layer, ctid = e.ctid, cw = e.cw, lane = lane_id();
     const uint32_t h0 = T.arg[0], nh = T.arg[1], ch = T.arg[2], nc = T.arg[3];
-    const int hd = P.hd;
+    const uint32_t hd = (uint32_t)P.hd;
     const int g = (int)((uint64_t)h0 * P.nKV / P.nH);
     const uint32_t vpw = P.act_f32 ? 1u : 2u;
     const u64* Lq = ll_layer(P, e.y, l) + e.y.qkv;
     const bool cur = ch == nc - 1;
-    float* qs = S.att;                       // [nh][hd]
-    float* kc = S.att + kMaxAttnHeads * 128; // [hd]
-    float* vc = kc + 128;                    // [hd]
+    float* qs = S.att + kAttQ;
+    float* kc = S.att + kAttKc;
+    float* vc = S.att + kAttVc;
     // inputs: q of the task's heads; the current k, v of the group (last chunk only)
     if (!ll_gather(c, Lq + (uint64_t)h0 * hd / vpw, nh * hd / vpw, ctid, [&](uint32_t i, uint32_t pl) {
             for (uint32_t j = 0; j < vpw; ++j) qs[i * vpw + j] = word_val(P, pl, (int)j);
@@ -652,202 +808,167 @@ DEV bool op_attn(const TaskEnv& e, const DevTask& T) {
             return false;
     }
     if (!cbar(c, *e.gen)) return false;
+    mark(e, 1);
+    // lane layout
+    uint32_t nhp = 1;
+    while (nhp < nh) nhp <<= 1;
+    const uint32_t L = min(64u / nhp, hd), D = hd / L;
+    const uint32_t hl = (uint32_t)lane / L, dg = (uint32_t)lane % L;
+    const bool active = hl < nh;
+    const uint32_t hq = active ? hl : 0;   // inactive lanes shadow head 0 and never store
+    float qr[kAttMaxD], o[kAttMaxD];
+#pragma unroll
+    for (int k = 0; k < kAttMaxD; ++k) {
+        qr[k] = (uint32_t)k < D ? qs[hq * hd + dg * D + k] : 0.f;
+        o[k] = 0.f;
+    }
+    float m = -INFINITY, lsum = 0.f;
+    // positions of this task: history [p0, p1) from the ring (blocks of kAttnBlock: K then V
+    // segment), then the current position
     uint32_t p0, p1;
     chunk_range(P.pos, ch, nc, p0, p1);
-    const uint32_t nb = (p1 - p0 + kAttnBlock - 1) / kAttnBlock;
+    const uint32_t nhist = p1 - p0, ntot = nhist + (cur ? 1u : 0u);
+    const uint32_t nb = (nhist + kAttnBlock - 1) / kAttnBlock;
     const uint32_t rowb = kv_row_bytes(P), ring = P.ring_bytes;
+    const uint32_t full = 2 * kb_round((uint64_t)kAttnBlock * rowb);
+    const uint32_t tend = e.tile_pos + (nb ? (nb - 1) * full + 2 * kb_round((uint64_t)(nhist - (nb - 1) * kAttnBlock) * rowb) : 0);
     const float scale = P.attn_scale;
-    // per-wave running state; lane owns dims d = lane + 64 j
-    float M[kMaxAttnHeads], Lsum[kMaxAttnHeads], O[kMaxAttnHeads][2];
-#pragma unroll
-    for (int h = 0; h < kMaxAttnHeads; ++h) { M[h] = -INFINITY; Lsum[h] = 0.f; O[h][0] = O[h][1] = 0.f; }
-    {   // advertise the first ring byte this wave needs (its first block, or the task's end)
-        const uint32_t full = 2 * kb_round((uint64_t)kAttnBlock * rowb);
-        uint32_t first = e.tile_pos;
-        if ((uint32_t)cw < nb) first += (uint32_t)cw * full;
-        else if (nb) first += (nb - 1) * full + 2 * kb_round((uint64_t)(p1 - p0 - (nb - 1) * kAttnBlock) * rowb);
-        if (lane == 0) lds_st(&S.released[cw], first);
-    }
-    uint32_t blk_pos = e.tile_pos;
-    for (uint32_t b = 0; b < nb; ++b) {
-        const uint32_t np = min((uint32_t)kAttnBlock, p1 - p0 - b * kAttnBlock);
-        const uint32_t seg = kb_round((uint64_t)np * rowb);
-        const uint32_t kpos = blk_pos, vpos = blk_pos + seg;
-        blk_pos += 2 * seg;
-        if ((int)(b % kComputeWaves) != cw) continue;
-        if (!wait_filled(c, vpos + np * rowb)) return false;
-        const uint32_t kbase = kpos % ring, vbase = vpos % ring;
-        // scores: lane j <-> position j of the block
-        float sc[kMaxAttnHeads];
-#pragma unroll
-        for (int h = 0; h < kMaxAttnHeads; ++h) sc[h] = -INFINITY;
-        if ((uint32_t)lane < np) {
-            uint32_t roff = kbase + (uint32_t)lane * rowb;
-            if (roff >= ring) roff -= ring;
-            float d[kMaxAttnHeads];
-#pragma unroll
-            for (int h = 0; h < kMaxAttnHeads; ++h) d[h] = 0.f;
-            for (int k = 0; k < hd; k += 8) {
-                float kv8[8];
-                if (P.act_f32) {
-                    const u32x4 a = ring16(S, roff + 4 * k), bq = ring16(S, roff + 4 * k + 16);
-                    kv8[0] = __uint_as_float(a.x); kv8[1] = __uint_as_float(a.y); kv8[2] = __uint_as_float(a.z); kv8[3] = __uint_as_float(a.w);
-                    kv8[4] = __uint_as_float(bq.x); kv8[5] = __uint_as_float(bq.y); kv8[6] = __uint_as_float(bq.z); kv8[7] = __uint_as_float(bq.w);
-                } else {
-                    const u32x4 a = ring16(S, roff + 2 * k);
-                    kv8[0] = bf2f(a.x & 0xffffu); kv8[1] = bf2f(a.x >> 16); kv8[2] = bf2f(a.y & 0xffffu); kv8[3] = bf2f(a.y >> 16);
-                    kv8[4] = bf2f(a.z & 0xffffu); kv8[5] = bf2f(a.z >> 16); kv8[6] = bf2f(a.w & 0xffffu); kv8[7] = bf2f(a.w >> 16);
-                }
-#pragma unroll
-                for (int h = 0; h < kMaxAttnHeads; ++h) {
-                    if ((uint32_t)h < nh) {
-                        const float* q = qs + h * hd + k;
-#pragma unroll
-                        for (int t = 0; t < 8; ++t) d[h] += q[t] * kv8[t];
-                    }
-                }
+    // advertise the first ring byte this wave needs (the block of its first position)
+    if (lane == 0) lds_st(&S.released[cw], (uint32_t)cw < nhist ? e.tile_pos + ((uint32_t)cw / kAttnBlock) * full : tend);
+    uint32_t have_blk = 0xffffffffu;
+    for (uint32_t i = (uint32_t)cw; i < ntot; i += kComputeWaves) {
+        uint32_t koff = 0, voff = 0;
+        const bool hist = i < nhist;
+        if (hist) {
+            const uint32_t b = i / kAttnBlock, r = i % kAttnBlock;
+            const uint32_t np = min((uint32_t)kAttnBlock, nhist - b * kAttnBlock);
+            const uint32_t kpos = e.tile_pos + b * full, vpos = kpos + kb_round((uint64_t)np * rowb);
+            if (b != have_blk) {
+                if (lane == 0) lds_st(&S.released[cw], kpos);
+                if (!wait_filled(c, vpos + np * rowb)) return false;
+                have_blk = b;
             }
+            koff = wrap(kpos % ring + r * rowb, ring);
+            voff = wrap(vpos % ring + r * rowb, ring);
+        }
+        float sdot = 0.f;
 #pragma unroll
-            for (int h = 0; h < kMaxAttnHeads; ++h) sc[h] = d[h] * scale;
-        }
+        for (int k = 0; k < kAttMaxD; ++k)
+            if ((uint32_t)k < D) sdot += qr[k] * (hist ? kv_at(P, S, koff, dg * D + k) : kc[dg * D + k]);
+        for (uint32_t off = L >> 1; off >= 1; off >>= 1) sdot += __shfl_xor(sdot, (int)off, 64);
+        const float sc = sdot * scale;
+        const float mn = fmaxf(m, sc);
+        const float alpha = expf(m - mn), pw = expf(sc - mn);
+        lsum = lsum * alpha + pw;
 #pragma unroll
-        for (int h = 0; h < kMaxAttnHeads; ++h) {
-            if ((uint32_t)h >= nh) continue;
-            const float mb = wave_max(sc[h]);
-            const float p = (uint32_t)lane < np ? expf(sc[h] - mb) : 0.f;
-            const float lb = wave_sum(p);
-            const float mn = fmaxf(M[h], mb);
-            const float al = expf(M[h] - mn), be = expf(mb - mn);
-            float acc0 = 0.f, acc1 = 0.f;
-            for (uint32_t j = 0; j < np; ++j) {
-                const float pj = __shfl(p, (int)j, 64);
-                uint32_t roff = vbase + j * rowb;
-                if (roff >= ring) roff -= ring;
-                if (lane < hd) {
-                    const float v = P.act_f32 ? *(const float*)(S.ring + roff + 4 * lane)
-                                              : bf2f(*(const uint16_t*)(S.ring + roff + 2 * lane));
-                    acc0 += pj * v;
-                }
-                if (lane + 64 < hd) {
-                    const float v = P.act_f32 ? *(const float*)(S.ring + roff + 4 * (lane + 64))
-                                              : bf2f(*(const uint16_t*)(S.ring + roff + 2 * (lane + 64)));
-                    acc1 += pj * v;
-                }
-            }
-            Lsum[h] = Lsum[h] * al + lb * be;
-            O[h][0] = O[h][0] * al + be * acc0;
-            O[h][1] = O[h][1] * al + be * acc1;
-            M[h] = mn;
-        }
-        // this wave no longer needs anything before its next block
-        uint32_t nxt = blk_pos;
-        for (uint32_t bb = b + 1; bb < nb && (int)(bb % kComputeWaves) != cw; ++bb) {
-            const uint32_t npp = min((uint32_t)kAttnBlock, p1 - p0 - bb * kAttnBlock);
-            nxt += 2 * kb_round((uint64_t)npp * rowb);
-        }
-        if (lane == 0) lds_st(&S.released[cw], nxt);
+        for (int k = 0; k < kAttMaxD; ++k)
+            if ((uint32_t)k < D) o[k] = o[k] * alpha + pw * (hist ? kv_at(P, S, voff, dg * D + k) : vc[dg * D + k]);
+        m = mn;
     }
-    // per-wave states -> LDS: hf[(cw * nh + h) * (hd + 2) + {0: M, 1: L, 2+d: O}]
-    const int st = hd + 2;
+    if (lane == 0) lds_st(&S.released[cw], tend);
+    // per-wave states -> LDS: hf[(cw * nh + h) * (hd + 2) + {0: m, 1: l, 2 + d: o}]
+    const uint32_t st = hd + 2;
+    if (active) {
+        float* w = S.hf + ((uint32_t)cw * nh + hl) * st;
+        if (dg == 0) { w[0] = m; w[1] = lsum; }
 #pragma unroll
-    for (int h = 0; h < kMaxAttnHeads; ++h) {
-        if ((uint32_t)h >= nh) continue;
-        float* w = S.hf + (cw * (int)nh + h) * st;
-        if (lane == 0) { w[0] = M[h]; w[1] = Lsum[h]; }
-        if (lane < hd) w[2 + lane] = O[h][0];
-        if (lane + 64 < hd) w[2 + lane + 64] = O[h][1];
+        for (int k = 0; k < kAttMaxD; ++k)
+            if ((uint32_t)k < D) w[2 + dg * D + k] = o[k];
     }
     if (!cbar(c, *e.gen)) return false;
-    // merge the waves (and the current position) per (head, dim)
+    mark(e, 2);
+    // combination weights, once per (wave, head)
+    for (uint32_t t = (uint32_t)ctid; t < (uint32_t)kComputeWaves * nh; t += kComputeThreads) {
+        const uint32_t w = t / nh, h = t % nh;
+        float M = -INFINITY;
+        for (int v = 0; v < kComputeWaves; ++v) M = fmaxf(M, S.hf[((uint32_t)v * nh + h) * st]);
+        const float mw = S.hf[(w * nh + h) * st];
+        S.att[kAttF + w * kMaxAttnHeads + h] = mw == -INFINITY ? 0.f : expf(mw - M);
+        if (w == 0) S.att[kAttM + h] = M;
+    }
+    if (!cbar(c, *e.gen)) return false;
     const uint32_t flag = P.flag;
-    const u64* unused = nullptr;
-    (void)unused;
-    for (uint32_t t = (uint32_t)ctid; t < nh * (uint32_t)hd; t += kComputeThreads) {
-        const int h = (int)(t / hd), d = (int)(t % hd);
-        float m = -INFINITY;
-        for (int w = 0; w < kComputeWaves; ++w) m = fmaxf(m, S.hf[(w * (int)nh + h) * st]);
-        float scur = -INFINITY;
-        if (cur) {
-            float dd = 0.f;
-            for (int k = 0; k < hd; ++k) dd += qs[h * hd + k] * kc[k];
-            scur = dd * scale;
-            m = fmaxf(m, scur);
-        }
-        float Ls = 0.f, Os = 0.f;
-        for (int w = 0; w < kComputeWaves; ++w) {
-            const float* ws = S.hf + (w * (int)nh + h) * st;
-            if (ws[0] == -INFINITY) continue;
-            const float f = expf(ws[0] - m);
-            Ls += ws[1] * f;
-            Os += ws[2 + d] * f;
-        }
-        if (cur) {
-            const float f = expf(scur - m);
-            Ls += f;
-            Os += f * vc[d];
-        }
-        S.att[kMaxAttnHeads * 128 + 256 + t] = Os;   // staged for the packed store
-        if (d == 0) S.fpart[h] = m, S.ipart[h] = 0;
-        if (d == 0) S.att[kMaxAttnHeads * 128 + 256 + kMaxAttnHeads * 128 + h] = Ls;
-    }
-    if (!cbar(c, *e.gen)) return false;
-    const float* Ost = S.att + kMaxAttnHeads * 128 + 256;
-    const float* Lst = Ost + kMaxAttnHeads * 128;
-    if (nc == 1) {
+    if (nc == 1) {   // the output rows, rounded once
         u64* out = ll_layer(P, e.y, l) + e.y.o + (uint64_t)h0 * hd / vpw;
-        for (uint32_t i = (uint32_t)ctid; i < nh * (uint32_t)hd / vpw; i += kComputeThreads) {
+        for (uint32_t i = (uint32_t)ctid; i < nh * hd / vpw; i += kComputeThreads) {
             float v[2] = {0.f, 0.f};
             for (uint32_t j = 0; j < vpw; ++j) {
-                const uint32_t t = i * vpw + j;
-                v[j] = rA(P, Ost[t] / Lst[t / hd]);
+                const uint32_t t = i * vpw + j, h = t / hd, d = t % hd;
+                float os = 0.f, ls = 0.f;
+                for (int w = 0; w < kComputeWaves; ++w) {
+                    const float f = S.att[kAttF + w * kMaxAttnHeads + h];
+                    const float* ws = S.hf + ((uint32_t)w * nh + h) * st;
+                    ls += f * ws[1];
+                    os += f * ws[2 + d];
+                }
+                v[j] = rA(P, os / ls);
             }
             ll_store(out + i, pack2(P, v[0], v[1]), flag);
         }
-    } else {
-        // partial state (M, L, O[hd]) per head, one fp32 per word
+    } else {   // partial state (M, L, o[hd]) per head, one fp32 per word
         u64* part = ll_layer(P, e.y, l) + e.y.part;
-        for (uint32_t t = (uint32_t)ctid; t < nh * (uint32_t)(hd + 2); t += kComputeThreads) {
-            const uint32_t h = t / (hd + 2), k = t % (hd + 2);
-            const float v = k == 0 ? S.fpart[h] : k == 1 ? Lst[h] : Ost[h * hd + (k - 2)];
-            ll_store(part + ((uint64_t)(h0 + h) * nc + ch) * (hd + 2) + k, __float_as_uint(v), flag);
+        for (uint32_t t = (uint32_t)ctid; t < nh * st; t += kComputeThreads) {
+            const uint32_t h = t / st, k = t % st;
+            float v;
+            if (k == 0) {
+                v = S.att[kAttM + h];
+            } else {
+                v = 0.f;
+                for (int w = 0; w < kComputeWaves; ++w)
+                    v += S.att[kAttF + w * kMaxAttnHeads + h] * S.hf[((uint32_t)w * nh + h) * st + k];
+            }
+            ll_store(part + ((uint64_t)(h0 + h) * nc + ch) * st + k, __float_as_uint(v), flag);
         }
     }
     return true;
 }
 
-// Merge of the context chunks of query heads [h0, h0+nh).
+// Merge of the context chunks of query heads [h0, h0+nh): o = sum_c exp(M_c - M) o_c divided by
+// sum_c exp(M_c - M) L_c, M = max_c M_c (the split-context form of the same softmax). The
+// weights are computed once per (head, chunk).
 DEV bool op_merge(const TaskEnv& e, const DevTask& T) {
     const Ctx& c = *e.c;
     const KParams& P = *c.P;
     Lds& S = *c.S;
     const int l = T.layer, ctid = e.ctid;
     const uint32_t h0 = T.arg[0], nh = T.arg[1], nc = T.arg[3];
-    const int hd = P.hd, st = hd + 2;
+    const uint32_t hd = (uint32_t)P.hd, st = hd + 2;
     const uint32_t vpw = P.act_f32 ? 1u : 2u;
     const u64* part = ll_layer(P, e.y, l) + e.y.part + (uint64_t)h0 * nc * st;
     if (!ll_gather(c, part, nh * nc * st, ctid, [&](uint32_t i, uint32_t pl) { S.hf[i] = __uint_as_float(pl); }))
         return false;
     if (!cbar(c, *e.gen)) return false;
-    float* Ost = S.att;
-    for (uint32_t t = (uint32_t)ctid; t < nh * (uint32_t)hd; t += kComputeThreads) {
-        const int h = (int)(t / hd), d = (int)(t % hd);
-        const float* base = S.hf + (uint64_t)h * nc * st;
-        float m = -INFINITY;
-        for (uint32_t k = 0; k < nc; ++k) m = fmaxf(m, base[k * st]);
-        float Ls = 0.f, Os = 0.f;
-        for (uint32_t k = 0; k < nc; ++k) {
-            const float* s = base + k * st;
-            if (s[0] == -INFINITY) continue;
-            const float f = expf(s[0] - m);
-            Ls += s[1] * f;
-            Os += s[2 + d] * f;
+    mark(e, 1);
+    // per head: M, then the chunk weights f_c = exp(M_c - M) (stored over M_c) and L
+    float* Lh = S.att;                       // [nh]
+    for (uint32_t h = (uint32_t)e.cw; h < nh; h += kComputeWaves) {
+        float* base = S.hf + (uint64_t)h * nc * st;
+        float M = -INFINITY;
+        for (uint32_t k = (uint32_t)lane_id(); k < nc; k += 64) M = fmaxf(M, base[k * st]);
+        M = wave_max(M);
+        float Ls = 0.f;
+        for (uint32_t k = (uint32_t)lane_id(); k < nc; k += 64) {
+            const float mk = base[k * st];
+            const float f = mk == -INFINITY ? 0.f : expf(mk - M);
+            Ls += f * base[k * st + 1];
+            base[k * st] = f;
         }
-        Ost[t] = rA(P, Os / Ls);
+        Ls = wave_sum(Ls);
+        if (lane_id() == 0) Lh[h] = Ls;
     }
     if (!cbar(c, *e.gen)) return false;
     u64* out = ll_layer(P, e.y, l) + e.y.o + (uint64_t)h0 * hd / vpw;
-    for (uint32_t i = (uint32_t)ctid; i < nh * (uint32_t)hd / vpw; i += kComputeThreads)
-        ll_store(out + i, pack2(P, Ost[i * vpw], vpw == 2 ? Ost[i * vpw + 1] : 0.f), P.flag);
+    for (uint32_t i = (uint32_t)ctid; i < nh * hd / vpw; i += kComputeThreads) {
+        float v[2] = {0.f, 0.f};
+        for (uint32_t j = 0; j < vpw; ++j) {
+            const uint32_t t = i * vpw + j, h = t / hd, d = t % hd;
+            const float* base = S.hf + (uint64_t)h * nc * st;
+            float os = 0.f;
+            for (uint32_t k = 0; k < nc; ++k) os += base[k * st] * base[k * st + 2 + d];
+            v[j] = rA(P, os / Lh[h]);
+        }
+        ll_store(out + i, pack2(P, v[0], v[1]), P.flag);
+    }
     return true;
 }
 
@@ -867,6 +988,7 @@ DEV bool op_argmax(const TaskEnv& e, const DevTask& T) {
         }))
         return false;
     if (!cbar(c, *e.gen)) return false;
+    mark(e, 1);
     for (uint32_t t = (uint32_t)ctid; t < nt; t += kComputeThreads) {
         const float v = S.hf[2 * t];
         const int i = __float_as_int(S.hf[2 * t + 1]);
@@ -915,8 +1037,10 @@ DEV void compute_run(const Ctx& c) {
     uint32_t pos = 0;   // ring-stream position of the current task
     const uint32_t q0 = P.queue_off[c.cu], q1 = P.queue_off[c.cu + 1];
     for (uint32_t t = q0; t < q1; ++t) {
-        const DevTask T = P.tasks[t];
+        const DevTask T = task_at(c, q0, t);
         e.tile_pos = pos;
+        e.tr = P.trace ? P.trace + (uint64_t)t * kTraceSlots : nullptr;
+        mark(e, 0);
         bool ok;
         switch (T.op) {
         case AMK_OP_ATTN: ok = op_attn(e, T); break;
@@ -924,15 +1048,14 @@ DEV void compute_run(const Ctx& c) {
         case AMK_OP_ARGMAX: ok = op_argmax(e, T); break;
         default: ok = op_gemv(e, T); break;
         }
-        uint32_t foot = 0;
-        for_segments(P, T, c.cu, [&](const uint8_t*, uint64_t bytes) { foot += kb_round(bytes); });
-        pos += foot;
+        pos += task_foot(P, T);
         if (lane_id() == 0) lds_st(&S.released[cw], pos);
         // all compute waves are done with this task's LDS data before the next task stages its input
         if (!ok || !cbar(c, gen)) {
             __hip_atomic_store(&S.abort_, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             return;
         }
+        mark(e, 3);
     }
 }
 
@@ -944,6 +1067,13 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) amk_megakernel(KParams
     if (tid < kComputeWaves + 1) {
         if (tid == 0) { S.filled = 0; S.bar = 0; S.abort_ = 0; }
         if (tid < kComputeWaves) S.released[tid] = 0;
+    }
+    {   // copy the head of this CU's task queue to LDS (8 dwords per task)
+        const uint32_t q0 = P.queue_off[blockIdx.x], q1 = P.queue_off[blockIdx.x + 1];
+        const uint32_t n = min(q1 - q0, (uint32_t)kTaskCache) * (uint32_t)(sizeof(DevTask) / 4);
+        const uint32_t* src = (const uint32_t*)(P.tasks + q0);
+        uint32_t* dst = (uint32_t*)S.tcache;
+        for (uint32_t i = (uint32_t)tid; i < n; i += kThreads) dst[i] = src[i];
     }
     __syncthreads();
     Ctx c;
@@ -958,8 +1088,9 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) amk_megakernel(KParams
         case 24: loader_run<24>(c); break;
         case 32: loader_run<32>(c); break;
         case 48: loader_run<48>(c); break;
-        case 56: loader_run<56>(c); break;
-        default: loader_run<40>(c); break;
+        case 40: loader_run<40>(c); break;
+        case 52: loader_run<52>(c); break;
+        default: loader_run<48>(c); break;
         }
     } else {
         compute_run(c);

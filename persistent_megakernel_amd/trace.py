@@ -1,0 +1,103 @@
+"""Per-task timestamp traces of the decode megakernel: where one launch spends its time.
+
+A trace row per task (queue order) holds six realtime-counter values (100 MHz): compute start,
+inputs observed, rows done, end, loader first issue, loader last issue (amk_set_trace). From
+them: per opcode the time spent waiting for inputs (producers on other CUs plus the staging
+prologue), computing out of LDS, and in the epilogue; per phase (opcode, layer) the moment the
+last CU finished, i.e. the critical path of the launch; and whether weight loads had been
+issued before the inputs arrived (prefetch ahead of the dependency).
+
+    python -m persistent_megakernel_amd.trace --workload tinyllama_int8 --pos 512
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import sys
+from collections import defaultdict
+
+import numpy as np
+
+from . import _abi as A
+
+TICK_US = 0.01          # one tick of the 100 MHz realtime counter
+OPNAMES = {A.AMK_OP_QKV: "qkv", A.AMK_OP_ATTN: "attn", A.AMK_OP_MERGE: "merge", A.AMK_OP_OPROJ: "oproj",
+           A.AMK_OP_GATEUP: "gateup", A.AMK_OP_DOWN: "down", A.AMK_OP_LM: "lm", A.AMK_OP_ARGMAX: "argmax"}
+
+
+def summarize(sched, trace) -> dict:
+    """sched: Python schedule (amk_ctx_schedule); trace: int array [n_tasks, 6] in queue order."""
+    tr = np.asarray(trace, dtype=np.int64)
+    order = [t for q in sched.queues for t in q]
+    cu_of = [cu for cu, q in enumerate(sched.queues) for _ in q]
+    t0 = int(tr[:, 0].min())
+    rel = (tr - t0) * TICK_US
+    by_op = defaultdict(lambda: defaultdict(list))
+    phase = defaultdict(lambda: [np.inf, 0.0, 0.0])     # (op, layer) -> [first start, last inputs, last end]
+    for k, tid in enumerate(order):
+        t = sched.tasks[tid]
+        op, layer = t.opcode, t.args[0]
+        s, ready, done, end, l0, l1 = rel[k]
+        d = by_op[OPNAMES.get(op, str(op))]
+        d["wait"].append(ready - s)
+        d["compute"].append(done - ready if op not in (A.AMK_OP_MERGE, A.AMK_OP_ARGMAX) else 0.0)
+        d["epilogue"].append(end - (done if op not in (A.AMK_OP_MERGE, A.AMK_OP_ARGMAX) else ready))
+        d["loader_late"].append(max(0.0, l1 - ready))
+        p = phase[(op, layer)]
+        p[0] = min(p[0], s)
+        p[1] = max(p[1], ready)
+        p[2] = max(p[2], end)
+    total = float(rel[:, 3].max())
+    ops = {name: {k: round(float(np.mean(v)), 3) for k, v in d.items()} | {"tasks": len(d["wait"])}
+           for name, d in by_op.items()}
+    seq = sorted(phase.items(), key=lambda kv: kv[1][2])
+    crit = []
+    prev = 0.0
+    for (op, layer), (s, ready, end) in seq:
+        crit.append({"op": OPNAMES.get(op, str(op)), "layer": int(layer), "last_end_us": round(end, 3),
+                     "span_us": round(end - prev, 3), "last_inputs_us": round(ready, 3)})
+        prev = end
+    return {"launch_us": round(total, 3), "ops_mean_us": ops, "phases": crit,
+            "n_cu": len(sched.queues), "cu_busy_end_us": round(float(np.median(rel[:, 3])), 3)}
+
+
+def main(argv=None) -> int:
+    import torch
+    import amk_inputs as I
+    from . import Decoder, run_steps
+
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--workload", default="tinyllama_int8", choices=sorted(I.SHAPES))
+    ap.add_argument("--pos", type=int, default=0)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = the workload's)")
+    ap.add_argument("--phases", action="store_true", help="print every phase of the critical path")
+    ap.add_argument("--cfg", nargs="*", default=[], help="lowering knobs, e.g. loader_depth=56 attn_chunks=8")
+    args = ap.parse_args(argv)
+    from . import schedule_config
+    cfg = schedule_config(**{k: int(v) for k, v in (kv.split("=") for kv in args.cfg)}) if args.cfg else None
+    shape = I.SHAPES[args.workload]
+    if args.layers:
+        shape = shape.replace(n_layers=args.layers)
+    shape = shape.replace(max_ctx=max(shape.max_ctx, args.pos + args.steps + 1))
+    w = I.make_weights(shape)
+    dec = Decoder(shape, w, cfg=cfg)
+    if args.pos:
+        for l in range(shape.n_layers):
+            dec.set_kv_prefix(l, I.kv_prefill(shape, args.pos, l))
+    trace = dec.enable_trace()
+    tok = int(I.prompt_tokens(shape, 1, stream=5)[0])
+    run_steps(dec, [tok] * args.steps, args.pos, chain_from=1)
+    torch.cuda.synchronize()
+    res = summarize(dec.schedule(), trace.cpu().numpy())
+    res["cfg"] = args.cfg
+    if not args.phases:
+        res["phases"] = res["phases"][:12] + res["phases"][-4:]
+    print(json.dumps(res, indent=1))
+    st = dec.status()
+    dec.close()
+    return 1 if st else 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
