@@ -155,10 +155,6 @@ typedef struct {
                                   query head, 0: auto (grouped whenever KV heads are shared) */
     int32_t cu_assign;         /* 0 = XCD-aware (unchunked attention of one KV group on one XCD; chunked
                                   attention round robin), 1 = plain round robin */
-    int32_t ring_kb;           /* LDS weight-ring size in KiB (0 = default) */
-    int32_t loader_depth;      /* 1 KiB loads kept in flight by the loader wave (0 = default) */
-    int32_t prefetch_kb;       /* how far ahead of its LDS loads the loader touches the CU's weight stream
-                                  to bring it into L2, in KiB (0 or -1 = off) */
 } amk_schedule_config;
 
 /* ---------------------------------------------------------------- calls */
@@ -242,8 +238,8 @@ const amk_schedule* amk_ctx_schedule(const amk_ctx* ctx);
  * for each task of the schedule, 6 uint64 values at trace[6 * k ...], where k is the task's
  * index in queue order (queue 0's tasks first; amk_ctx_schedule gives the order):
  *   [0] compute start, [1] inputs observed (all waits satisfied, prologue done),
- *   [2] rows / attention blocks done, [3] task end, [4] loader's first issue for the task,
- *   [5] loader's last issue for the task,
+ *   [2] rows / attention positions done (whole workgroup), [3] task end, [4] GEMV tasks: the
+ *   first wave's own rows done, [5] outputs written (before the task's closing barrier),
  * in ticks of the device's constant 100 MHz realtime counter (one time base across CUs;
  * slots a task has no event for keep their old value). trace: device memory of at least
  * `capacity` uint64 values, caller-owned, borrowed until disabled; capacity must be at least

@@ -88,8 +88,7 @@ class amk_schedule_config(C.Structure):
     _fields_ = [("struct_size", C.c_uint32), ("n_cu", C.c_int32), ("tasks_qkv", C.c_int32),
                 ("tasks_o", C.c_int32), ("tasks_gateup", C.c_int32), ("tasks_down", C.c_int32),
                 ("tasks_lm", C.c_int32), ("attn_chunks", C.c_int32), ("attn_group_tasks", C.c_int32),
-                ("cu_assign", C.c_int32), ("ring_kb", C.c_int32), ("loader_depth", C.c_int32),
-                ("prefetch_kb", C.c_int32)]
+                ("cu_assign", C.c_int32)]
 
 
 # every symbol include/amk.h declares, with (restype, argtypes)

@@ -85,18 +85,6 @@ uint64_t watchdog_ticks() {
     return (uint64_t)(ms * 1e5);   // s_memrealtime runs at 100 MHz
 }
 
-// Smallest ring the loader can always make progress with: two of the widest weight rows, or the K and
-// V segments of one attention block, plus one 1 KiB load in flight.
-uint32_t ring_need(const amk_model_desc& d) {
-    const uint32_t qd = (uint32_t)(d.n_heads * d.head_dim);
-    uint32_t pitch = 0;
-    for (uint32_t K : {(uint32_t)d.hidden, qd, (uint32_t)d.intermediate}) pitch = std::max(pitch, row_pitch(d.wfmt, K));
-    const uint32_t rowb = (uint32_t)d.head_dim * (d.act_f32 ? 4u : 2u);
-    const uint32_t blk = 2u * (((uint32_t)kAttnBlock * rowb + 1023u) & ~1023u);
-    const uint32_t row = ((2u * pitch + 1023u) & ~1023u) + 1024u;   // a wave works on two rows at once
-    return std::max(row, blk + 1024u);
-}
-
 }  // namespace
 
 extern "C" const char* amk_version(void) { return "amk-mi355x 0.1"; }
@@ -252,19 +240,6 @@ extern "C" amk_status amk_create(const amk_model_desc* desc, const amk_weights* 
     P.status = c->d_status;
     P.abort_flag = c->d_abort;
     P.watchdog_ticks = watchdog_ticks();
-    int ring_kb = (cfg && cfg->ring_kb > 0) ? cfg->ring_kb : kRingDefaultKB;
-    if (ring_kb * 1024 > kRingMaxBytes) ring_kb = kRingMaxBytes / 1024;
-    P.ring_bytes = (uint32_t)ring_kb * 1024u;
-    if (P.ring_bytes < ring_need(d)) {
-        logf("create", "LDS ring smaller than two weight rows or one attention block");
-        free_ctx(c);
-        return AMK_E_INVALID_ARG;
-    }
-    P.loader_depth = (cfg && cfg->loader_depth > 0) ? (uint32_t)cfg->loader_depth : (uint32_t)kLoaderDepthDefault;
-    {
-        const int pf = cfg ? cfg->prefetch_kb : 0;
-        P.prefetch_bytes = pf < 0 ? 0u : 1024u * (uint32_t)(pf > 0 ? std::min(pf, 4096) : kPrefetchKBDefault);
-    }
     c->last = stream;
     *out = c;
     return AMK_OK;

@@ -2,7 +2,8 @@
 // of the decode workloads' shapes with synthetic weights, then time back-to-back greedy decode
 // launches (the token chained on the device) with HIP events on the launch stream.
 //
-//   amk_bench [workload] [steps] [warmup] [start_pos]
+//   amk_bench [workload] [steps] [warmup] [start_pos] [cache_rows] [null_stream]
+//   amk_bench --copy MiB          (traffic-counter calibration: device-to-device copies)
 //   workloads: tiny_fp32 smollm2_135m_bf16 tinyllama_int8 llama7b_bf16 llama7b_int8 llama3_8b_int4
 //
 // Weights are filled on the host with a cheap counter-based hash (uniform in +-0.035, about the
@@ -77,7 +78,25 @@ void* dev_tensor(size_t n, bool f32, float amp, float bias, uint64_t salt, std::
 
 }  // namespace
 
+// `amk_bench --copy MiB`: three device-to-device copies of MiB mebibytes (the calibration of
+// the HBM traffic counters: each copy reads and writes exactly that many bytes).
+int copy_calibration(size_t mib) {
+    const size_t n = mib << 20;
+    void *a = nullptr, *b = nullptr;
+    CK(hipMalloc(&a, n));
+    CK(hipMalloc(&b, n));
+    CK(hipMemset(a, 1, n));
+    CK(hipDeviceSynchronize());
+    for (int i = 0; i < 3; ++i) CK(hipMemcpy(b, a, n, hipMemcpyDeviceToDevice));
+    CK(hipDeviceSynchronize());
+    std::printf("{\"copy_bytes\": %zu, \"copies\": 3}\n", n);
+    CK(hipFree(a));
+    CK(hipFree(b));
+    return 0;
+}
+
 int main(int argc, char** argv) {
+    if (argc > 2 && std::string(argv[1]) == "--copy") return copy_calibration((size_t)std::atoll(argv[2]));
     const std::string name = argc > 1 ? argv[1] : "tinyllama_int8";
     const int steps = argc > 2 ? std::atoi(argv[2]) : 200;
     const int warmup = argc > 3 ? std::atoi(argv[3]) : 20;
@@ -89,12 +108,16 @@ int main(int argc, char** argv) {
         return 2;
     }
     const int pos0 = argc > 4 ? std::atoi(argv[4]) : s->start_pos;
+    // optional: cache rows (0 = just enough for the run) and the launch stream (1 = the null stream)
+    const int ctx_rows = argc > 5 ? std::atoi(argv[5]) : 0;
+    const bool null_stream = argc > 6 && std::atoi(argv[6]) == 1;
     const bool f32 = s->wfmt == AMK_F32;
     amk_model_desc d;
     std::memset(&d, 0, sizeof(d));
     d.struct_size = sizeof(d);
     d.hidden = s->H; d.n_layers = s->L; d.n_heads = s->nH; d.n_kv_heads = s->nKV; d.head_dim = s->hd;
-    d.intermediate = s->I; d.vocab = s->V; d.max_ctx = pos0 + warmup + steps + 1; d.tied_embeddings = s->tied;
+    d.intermediate = s->I; d.vocab = s->V; d.tied_embeddings = s->tied;
+    d.max_ctx = ctx_rows > pos0 + warmup + steps ? ctx_rows : pos0 + warmup + steps + 1;
     d.rope_theta = s->theta; d.rms_eps = 1e-5f; d.wfmt = s->wfmt; d.act_f32 = s->act_f32;
 
     std::vector<void*> owned;
@@ -133,8 +156,8 @@ int main(int argc, char** argv) {
         for (size_t b = 0; b < (size_t)s->L * 2 * s->nKV; ++b)
             CK(hipMemcpy((uint8_t*)kv + b * d.max_ctx * s->hd * esz, tmp, blk * esz, hipMemcpyDeviceToDevice));
     }
-    hipStream_t st;
-    CK(hipStreamCreate(&st));
+    hipStream_t st = nullptr;
+    if (!null_stream) CK(hipStreamCreate(&st));
     amk_ctx* ctx = nullptr;
     amk_verdict v;
     amk_status rc = amk_create(&d, &w, kv, nullptr, nullptr, st, &v, &ctx);
@@ -170,6 +193,6 @@ int main(int argc, char** argv) {
     CK(hipFree(kv));
     CK(hipEventDestroy(a));
     CK(hipEventDestroy(b));
-    CK(hipStreamDestroy(st));
+    if (st) CK(hipStreamDestroy(st));
     return status ? 1 : 0;
 }

@@ -13,24 +13,30 @@
 
 namespace amk {
 
-// Workgroup: one per CU. Wave 0 streams weights and KV blocks into the LDS ring; waves 1..15
-// walk the task queue.
-constexpr int kThreads = 1024;
+// Workgroup: one per CU, 8 waves, all of which walk the task queue. Every wave streams the
+// weight rows it owns straight into registers (no loader wave, no LDS staging of weights).
+constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
-constexpr int kComputeWaves = kWaves - 1;
-constexpr int kComputeThreads = kComputeWaves * 64;
+constexpr int kComputeWaves = kWaves;
+constexpr int kComputeThreads = kThreads;
 
-// LDS budget (bytes): ring + input-vector stage + row results + attention state + control.
+// LDS budget (bytes): input-vector stage, attention K/V staging, row results, attention state,
+// task cache, control.
 constexpr int kLdsTotal = 160 * 1024;
 constexpr int kHBytes = 32 * 1024;          // input vector stage (fp32 up to 8192, or 16-bit up to 16384 values)
+constexpr int kKvBytes = 64 * 1024;         // attention: K and V rows of the positions being processed; int4 scales
 constexpr int kRedRows = 1024;              // row results per task
 constexpr int kAttnLds = 8 * 1024;          // attention: q, current k/v, combination weights; residual rows
 constexpr int kTaskCache = 256;             // task descriptors of a CU's queue kept in LDS (32 bytes each)
-constexpr int kCtrlBytes = 1024;
-constexpr int kRingMaxBytes = kLdsTotal - kHBytes - kRedRows * 4 - kAttnLds - kTaskCache * 32 - kCtrlBytes;  // 107 KiB
-constexpr int kRingDefaultKB = 104;
-constexpr int kPrefetchKBDefault = 0;       // L2 prefetch distance on the weight stream (off unless configured)
-constexpr int kLoaderDepthDefault = 48;     // loads in flight beyond the current group (at most 53)
+#ifndef AMK_LOAD_SLOTS
+#define AMK_LOAD_SLOTS 6
+#endif
+#ifndef AMK_AHEAD_GROUPS
+#define AMK_AHEAD_GROUPS 1
+#endif
+constexpr int kLoadSlots = AMK_LOAD_SLOTS;  // 1 KiB (16 B per lane) weight loads per register buffer (2 buffers per wave)
+constexpr int kAheadGroups = AMK_AHEAD_GROUPS;   // groups of the next task's weights issued ahead (1 or 2)
+static_assert(kAheadGroups == 1 || kAheadGroups == 2, "prefetch depth");
 constexpr int kAttnBlock = 64;              // positions per attention unit
 constexpr int kMaxAttnHeads = 8;            // query heads per attention task
 constexpr int kChunkedCtx = 256;            // caches at least this long get context-split attention by default
@@ -50,29 +56,26 @@ struct DevTask {
 };
 static_assert(sizeof(DevTask) == 32, "DevTask layout");
 
-// Weight tile geometry for a GEMV with K inputs in format wfmt.
+// Weight tile geometry for a GEMV with K inputs in format wfmt. A tile is its rows' codes, row
+// after row (row_pitch bytes each, a multiple of 16), then the scale block: int8 one fp16 scale
+// per row, int4 K/128 fp16 group scales per row (row-major), padded to 16 bytes.
 AMK_HD inline uint32_t row_pitch(int wfmt, uint32_t K) {
-    uint32_t b;
     switch (wfmt) {
-    case AMK_F32: b = 4 * K; break;
-    case AMK_BF16: b = 2 * K; break;
-    case AMK_INT8_PC: b = K + 2; break;              // int8: codes, then the row's fp16 scale
-    default: b = K / 2 + (K / 128) * 2; break;   // int4: group scales first, then nibbles
+    case AMK_F32: return 4 * K;
+    case AMK_BF16: return 2 * K;
+    case AMK_INT8_PC: return K;
+    default: return K / 2;   // int4: two codes per byte, low nibble first, biased by 8
     }
-    return (b + 15u) & ~15u;
 }
-// Rows are self-contained (scales travel inside their row), so a tile has no header and any
-// row can stream through the LDS ring on its own.
-AMK_HD inline uint32_t tile_header(int wfmt, uint32_t rows) {
-    (void)wfmt;
-    (void)rows;
-    return 0u;
+AMK_HD inline uint32_t row_scales(int wfmt, uint32_t K) {   // fp16 scales per row
+    return wfmt == AMK_INT8_PC ? 1u : wfmt == AMK_INT4_G128 ? K / 128 : 0u;
 }
+AMK_HD inline uint64_t tile_scale_off(int wfmt, uint32_t K, uint32_t rows) { return (uint64_t)rows * row_pitch(wfmt, K); }
 AMK_HD inline uint64_t tile_bytes(int wfmt, uint32_t K, uint32_t rows) {
-    return (uint64_t)tile_header(wfmt, rows) + (uint64_t)rows * row_pitch(wfmt, K);
+    return tile_scale_off(wfmt, K, rows) + (((uint64_t)rows * row_scales(wfmt, K) * 2 + 15) & ~15ull);
 }
-// int4 row: bytes [0, 2*K/128) hold the group scales (fp16), the nibbles start at this offset
-AMK_HD inline uint32_t int4_codes_off(uint32_t K) { return (K / 128) * 2; }
+// 1 KiB wave loads per row (16 B per lane; the last one may be partial)
+AMK_HD inline uint32_t row_loads(int wfmt, uint32_t K) { return (row_pitch(wfmt, K) + 1023u) / 1024u; }
 
 // Flag-carrying ("LL") buffers: one 8-byte word = 32-bit payload + 32-bit flag; the flag of a
 // word written in launch e is e+1 (never 0). bf16 activations pack 2 values per word; fp32
@@ -129,9 +132,6 @@ struct KParams {
     uint32_t* status;                // host-visible status word
     uint32_t* abort_flag;            // device word: set on watchdog timeout
     uint64_t watchdog_ticks;         // s_memrealtime ticks (100 MHz) before a spin-wait gives up
-    uint32_t ring_bytes;             // LDS ring size used
-    uint32_t loader_depth;
-    uint32_t prefetch_bytes;         // L2 prefetch distance ahead of the weight stream's LDS loads (0 = off)
     uint64_t* trace;                 // optional per-task timestamps (kTraceSlots per device task) or null
 };
 

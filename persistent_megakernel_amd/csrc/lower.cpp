@@ -300,6 +300,7 @@ bool check_plan(const amk_model_desc& d, const Lowered& out, std::string* msg) {
         if (m.mat == M_LM && d.tied_embeddings) return fail("tied model with an LM-head row");
         if (m.src_row >= rows || m.K != cols) return fail("repack row outside its source matrix");
         if (m.dst + row_pitch(d.wfmt, m.K) > total) return fail("repack row outside the weight stream");
+        if (m.sdst + 2ull * row_scales(d.wfmt, m.K) > total) return fail("repack row scales outside the weight stream");
     }
     const int n = out.n_cu;
     if ((int)out.dqueue_off.size() != n + 1 || (int)out.cu_stream_off.size() != n + 1 ||
@@ -314,7 +315,9 @@ bool check_plan(const amk_model_desc& d, const Lowered& out, std::string* msg) {
             if (t.tile_rows > (uint32_t)kRedRows) return fail("tile with more rows than the LDS row buffer");
             const uint32_t K = t.op == AMK_OP_OPROJ ? (uint32_t)qd : t.op == AMK_OP_DOWN ? (uint32_t)d.intermediate : (uint32_t)H;
             if (t.wofs + tile_bytes(d.wfmt, K, t.tile_rows) > len) return fail("tile outside its CU stream");
-            if (row_pitch(d.wfmt, K) > (uint32_t)kRingMaxBytes / 3) return fail("weight row larger than a third of the LDS ring");
+            if (t.wofs % 16) return fail("tile not 16-byte aligned in its CU stream");
+            if (tile_bytes(d.wfmt, K, t.tile_rows) - tile_scale_off(d.wfmt, K, t.tile_rows) > (uint64_t)kKvBytes)
+                return fail("tile whose scales do not fit the LDS scale buffer");
         }
     }
     return true;
@@ -425,15 +428,18 @@ amk_status finish(const amk_model_desc& d, const Shape& s, std::vector<GenTask>&
             dt.wofs = wofs[i];
             out.dtasks.push_back(dt);
             if (!dt.tile_rows) continue;
-            const uint32_t K = s.K_of(t.op), pitch = row_pitch(s.wfmt, K), hdr = tile_header(s.wfmt, dt.tile_rows);
+            const uint32_t K = s.K_of(t.op), pitch = row_pitch(s.wfmt, K);
             const uint64_t base = out.cu_stream_off[c] + wofs[i];
+            const uint64_t sbase = base + tile_scale_off(s.wfmt, K, dt.tile_rows);
+            const uint32_t nsc = row_scales(s.wfmt, K);
             for (uint32_t r = 0; r < dt.tile_rows; ++r) {
                 RowMap m;
                 tile_src(s, t, r, &m.mat, &m.src_row, d.tied_embeddings != 0);
                 // the LM head and the embedding are model-level matrices: table slot 0
                 m.layer = (m.mat == M_LM || m.mat == M_EMBED) ? 0u : t.layer;
                 m.K = K;
-                m.dst = base + hdr + (uint64_t)r * pitch;
+                m.dst = base + (uint64_t)r * pitch;
+                m.sdst = sbase + (uint64_t)r * nsc * 2;
                 out.rows.push_back(m);
             }
         }
@@ -527,7 +533,7 @@ amk_status lower_model(const amk_model_desc& d, const amk_schedule_config* cfg, 
         // attention (+ merge)
         std::vector<uint32_t> c_part(n_head_tasks);
         if (nc > 1) for (auto& c : c_part) c = newc();
-        std::vector<uint32_t> slot_in_xcd(8, 0);
+        std::vector<uint32_t> slot_in_xcd(8, 0), group_cu(n_head_tasks, 0);
         for (int m = 0; m < n_head_tasks; ++m) {
             const int h0 = m * heads_per_task;
             const int g = (int)((int64_t)h0 * nKV / nH);
@@ -546,13 +552,20 @@ amk_status lower_model(const amk_model_desc& d, const amk_schedule_config* cfg, 
                 if (c == nc - 1) T[id].waits.push_back({c_kv[g], UINT32_MAX});
                 T[id].sigs.push_back(nc == 1 ? c_att : c_part[m]);
             }
-            if (nc > 1)   // one merge per query head, next to the group's first chunk
-                for (int h = h0; h < h0 + heads_per_task; ++h) {
-                    uint32_t id = mk(AMK_OP_MERGE, l, h, 1, 0, nc, first_cu + (uint32_t)(h - h0));
+            group_cu[m] = first_cu;
+        }
+        // merges after every attention task of the layer: a CU's merge for one group must not
+        // sit in its queue ahead of its attention chunk for another group (that would chain the
+        // groups one after the other)
+        if (nc > 1)
+            for (int m = 0; m < n_head_tasks; ++m) {
+                const int h0 = m * heads_per_task;
+                for (int h = h0; h < h0 + heads_per_task; ++h) {   // one merge per query head
+                    uint32_t id = mk(AMK_OP_MERGE, l, h, 1, 0, nc, group_cu[m] + (uint32_t)(h - h0));
                     T[id].waits.push_back({c_part[m], UINT32_MAX});
                     T[id].sigs.push_back(c_att);
                 }
-        }
+            }
         // O projection
         const uint64_t uo = (uint64_t)s.H / vpw, to = ntasks(C.tasks_o, uo);
         for (uint64_t i = 0; i < to; ++i) {

@@ -15,7 +15,8 @@ enum Mat : uint32_t { M_EMBED = 0, M_LM = 1, M_WQ = 2, M_WK = 3, M_WV = 4, M_WO 
 // One row of a weight tile: which source row lands where in the stream.
 struct RowMap {
     uint32_t mat, layer, src_row, K;
-    uint64_t dst;        // byte offset of the row in the whole stream buffer
+    uint64_t dst;        // byte offset of the row's codes in the whole stream buffer
+    uint64_t sdst;       // byte offset of the row's fp16 scales (int formats; unused otherwise)
 };
 
 struct SchedHolder;

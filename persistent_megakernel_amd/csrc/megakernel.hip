@@ -4,27 +4,30 @@
 // queue of the static task DAG; cross-CU dependencies resolve only through monotone counters,
 // so the execution is a topological walk with no locks and no other signals (AutoMegaKernel
 // pages: page 1, author's note and "Deadlock-free by construction"; page 3, "How it works",
-// layer 0: one block per SM, scheduler loop wait -> dispatch -> signal, counter-based sync,
-// page-based on-chip scratchpad; page 1, "Why megakernels": activations stay on chip and the
-// next weights are fetched while the current ones compute).
+// layer 0: one block per SM, scheduler loop wait -> dispatch -> signal, counter-based sync;
+// page 1, "Why megakernels": activations stay on chip and the next weights are fetched while
+// the current ones compute).
 //
 // MI355X mapping:
-//  * Workgroup = 1024 threads. Wave 0 is a loader: it walks the same queue and streams every
-//    task's weight tile (and attention's KV blocks) into an LDS ring with LDS-DMA loads
-//    (global_load_lds_dwordx4, 1 KiB per instruction, up to ~40 KiB in flight), running ahead
-//    of the compute waves as far as the ring allows. Weights do not depend on activations, so
-//    they are prefetched while the compute waves still wait for their inputs.
-//  * Waves 1..15 compute: they read the task's input vector, run the fused prologue (RMSNorm),
-//    the GEMV rows out of the ring (fp32 accumulation, weights dequantised in registers), a
-//    wave reduction per row and the fused epilogue (RoPE + KV append, SwiGLU, residual,
-//    per-tile argmax).
+//  * Workgroup = 8 waves of 64 lanes, one per CU; all waves walk the queue together.
+//  * Weights are streamed by the waves that use them, straight into registers: wave w owns rows
+//    w, w + 8, ... of every GEMV tile and loads each row as 1 KiB wave loads (16 bytes per lane),
+//    kLoadSlots loads at a time. The first loads of the next task are issued as soon as the
+//    current task's rows are done (or, for tasks without weights, when they start), so the HBM
+//    latency of the next phase overlaps the wait for its inputs from other CUs. GEMV is
+//    HBM-bound: one multiply-add per weight element, no MFMA.
+//  * The input vector of a GEMV (after the fused RMSNorm) is staged once in LDS; each lane reads
+//    the slice matching its weight bytes. Row sums are reduced across the wave with DPP moves.
+//  * Attention stages the K and V rows of its positions in LDS with plain vector loads issued
+//    before it waits for q, then runs an online softmax with (query head x dimension group)
+//    lanes.
 //  * Counters are realised as flag-carrying words: every activation a task publishes is an
 //    8-byte word of 32-bit payload + 32-bit flag, written once per launch with flag = epoch+1
-//    through the device-coherent path (sc1). A consumer's wait on a counter is its read of the
-//    words the counter's producers wrote: it spins until every word it needs carries the
-//    current flag. Each flag is a per-producer monotone counter (it only grows across
-//    launches), thresholds are epoch-relative, and no reset launch is needed. The validator's
-//    rule V8 ensures every declared wait is observed this way.
+//    through the device-coherent path. A consumer's wait on a counter is its read of the words
+//    the counter's producers wrote: it spins until every word it needs carries the current
+//    flag. Each flag is a per-producer monotone counter (it only grows across launches),
+//    thresholds are epoch-relative, and no reset launch is needed. The validator's rule V8
+//    ensures every declared wait is observed this way.
 //  * Every spin-wait is bounded by a s_memrealtime watchdog; on expiry the workgroup raises a
 //    status word and every workgroup leaves its queue, so the launch always ends.
 #include <hip/hip_runtime.h>
@@ -38,24 +41,22 @@ namespace {
 
 typedef unsigned long long u64;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 #define DEV __device__ __forceinline__
 
 struct __attribute__((aligned(16))) Lds {
-    uint8_t ring[kRingMaxBytes];
     union {
         uint8_t hb[kHBytes];           // input vector: fp32 (fp32 activations) or bf16 bits
         float hf[kHBytes / 4];         // also: attention per-wave states, merge staging
     };
+    uint8_t kvb[kKvBytes];             // attention K then V rows of a round of positions; GEMV row scales
     float red[kRedRows];               // per-row GEMV results of the current task
     float att[kAttnLds / 4];           // attention q / current k, v; residual rows; reductions
-    uint32_t filled;                   // ring-stream bytes landed in LDS (monotone)
-    uint32_t released[kComputeWaves];  // per compute wave: ring-stream position it no longer needs
-    uint32_t bar;                      // compute-wave barrier counter (monotone)
+    DevTask tcache[kTaskCache];        // the first kTaskCache tasks of this CU's queue
+    uint32_t bar;                      // workgroup barrier counter (monotone)
     uint32_t abort_;                   // this workgroup gives up
     float fpart[2 * kComputeWaves];
     int32_t ipart[2 * kComputeWaves];
-    uint32_t pf_sink[64];              // destination of the loader's L2 prefetches (never read)
-    DevTask tcache[kTaskCache];        // the first kTaskCache tasks of this CU's queue
 };
 static_assert(sizeof(Lds) <= kLdsTotal, "LDS budget");
 
@@ -87,6 +88,21 @@ DEV float wave_max(float v) {
     for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
     return v;
 }
+// Sum over the 64 lanes with DPP moves: an inclusive scan inside each row of 16 lanes (row
+// shifts by 1, 2, 4, 8), then the row totals are carried by row broadcasts 15 and 31; the total
+// ends in lane 63 and is returned to every lane.
+DEV float wave_sum_dpp(float v) {
+#define AMK_DPP_ADD(ctrl, rmask) \
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl, rmask, 0xf, false))
+    AMK_DPP_ADD(0x111, 0xf);   // row_shr:1
+    AMK_DPP_ADD(0x112, 0xf);   // row_shr:2
+    AMK_DPP_ADD(0x114, 0xf);   // row_shr:4
+    AMK_DPP_ADD(0x118, 0xf);   // row_shr:8
+    AMK_DPP_ADD(0x142, 0xa);   // row_bcast:15 into rows 1 and 3
+    AMK_DPP_ADD(0x143, 0xc);   // row_bcast:31 into rows 2 and 3
+#undef AMK_DPP_ADD
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
 
 // flag-carrying words: device-coherent 8-byte loads and stores
 DEV u64 ll_load(const u64* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
@@ -94,40 +110,32 @@ DEV void ll_store(u64* p, uint32_t payload, uint32_t flag) {
     __hip_atomic_store(p, ((u64)flag << 32) | payload, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-DEV uint32_t lds_ld(const uint32_t* p) { return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP); }
-DEV void lds_st(uint32_t* p, uint32_t v) { __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP); }
-
-// one 1 KiB LDS-DMA load: lane i moves 16 bytes from gptr to LDS at m0 + 16 i. Written as
-// inline asm so that the compiler does not fence every later LDS access of the loader wave
-// behind it; completion is tracked with explicit vmcnt waits. The instruction has no VGPR
-// result, and its address operand is read at issue.
-DEV void dma16(const void* gptr, uint32_t lds_addr) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_addr)
-                 : "memory", "m0");
-}
-DEV void vm_wait0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-// L2 prefetch of 8 KiB: lane i touches the 128-byte line at gptr + 128 i with a 4-byte LDS-DMA
-// load into a sink (no VGPR result, so nothing in flight can clobber a register).
-DEV void prefetch_8k(const void* gptr, uint32_t sink_lds) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(sink_lds)
-                 : "memory", "m0");
-}
+// 16 bytes of a weight stream (read once per launch: non-temporal)
+DEV u32x4 wload(const uint8_t* p) { return __builtin_nontemporal_load((const u32x4*)p); }
+// keep the compiler from moving memory accesses across this point (prefetches stay early)
+DEV void compiler_fence() { asm volatile("" ::: "memory"); }
+// s_waitcnt operand: vector memory count 0, the other counters at their maximum (no wait)
+constexpr int kWaitVmem0 = 0x0f70;
 
 struct Ctx {
     const KParams* P;
     Lds* S;
     uint64_t deadline;
     int cu;
+    const uint8_t* wcu;   // this CU's weight stream
 };
 
-// task t of this CU's queue (starting at q0): from the LDS copy when it holds it
+// task t of this CU's queue (starting at q0): from the LDS copy when it holds it. The fields
+// are made wave-uniform so that everything derived from them lives in scalar registers.
 DEV DevTask task_at(const Ctx& c, uint32_t q0, uint32_t t) {
-    return t - q0 < (uint32_t)kTaskCache ? c.S->tcache[t - q0] : c.P->tasks[t];
-}
-
-DEV bool expired(const Ctx& c) {
-    if (rt() > c.deadline) return true;
-    return __hip_atomic_load(&c.S->abort_, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0;
+    const DevTask v = t - q0 < (uint32_t)kTaskCache ? c.S->tcache[t - q0] : c.P->tasks[t];
+    uint32_t w[sizeof(DevTask) / 4];
+    __builtin_memcpy(w, &v, sizeof(DevTask));
+#pragma unroll
+    for (int k = 0; k < (int)(sizeof(DevTask) / 4); ++k) w[k] = __builtin_amdgcn_readfirstlane(w[k]);
+    DevTask r;
+    __builtin_memcpy(&r, w, sizeof(DevTask));
+    return r;
 }
 
 DEV void raise_timeout(const Ctx& c) {
@@ -137,13 +145,11 @@ DEV void raise_timeout(const Ctx& c) {
 }
 
 // spin step of every wait: bounded by the watchdog and by the global abort flag. The global
-// flag is a device-coherent load (a memory round trip), so it is read only once a wait has
-// lasted about 100 us (counted in 64-spin steps of the realtime clock); another workgroup sets
-// it only after its own watchdog (far longer) expired.
+// flag is a device-coherent load (a memory round trip), so it is read only every 4096 spins;
+// another workgroup sets it only after its own watchdog (far longer) expired.
 DEV bool spin_ok(const Ctx& c, uint32_t& n) {
     if (((++n) & 63u) == 0) {
-        const uint64_t now = rt();
-        if (now > c.deadline) { raise_timeout(c); return false; }
+        if (rt() > c.deadline) { raise_timeout(c); return false; }
         if ((n & 0xfffu) == 0 &&
             __hip_atomic_load(c.P->abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
             __hip_atomic_store(&c.S->abort_, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -155,7 +161,7 @@ DEV bool spin_ok(const Ctx& c, uint32_t& n) {
     return true;
 }
 
-// barrier of the 15 compute waves (the loader wave never joins)
+// barrier of the workgroup's waves; watchdog-bounded like every wait
 DEV bool cbar(const Ctx& c, uint32_t& gen) {
     gen += kComputeWaves;
     bool ok = true;
@@ -171,7 +177,7 @@ DEV bool cbar(const Ctx& c, uint32_t& gen) {
     return __shfl(ok ? 1 : 0, 0, 64) != 0;
 }
 
-// ------------------------------------------------------------------ task geometry (shared by both roles)
+// ------------------------------------------------------------------ task geometry
 
 DEV uint32_t act_bytes(const KParams& P) { return P.act_f32 ? 4u : 2u; }
 DEV uint32_t kv_row_bytes(const KParams& P) { return (uint32_t)P.hd * act_bytes(P); }
@@ -181,7 +187,6 @@ DEV uint32_t K_of(const KParams& P, int op) {
 DEV bool is_gemv(int op) {
     return op == AMK_OP_QKV || op == AMK_OP_OPROJ || op == AMK_OP_GATEUP || op == AMK_OP_DOWN || op == AMK_OP_LM;
 }
-DEV uint32_t kb_round(uint64_t b) { return (uint32_t)((b + 1023) & ~1023ull); }
 
 // history positions [h0, h1) of attention chunk c of nc at position pos (the current position
 // pos itself belongs to the last chunk and comes from the flag-carrying words)
@@ -198,148 +203,196 @@ DEV const uint8_t* kv_ptr(const KParams& P, int layer, int kv, int g, uint32_t r
     return (const uint8_t*)P.kv + idx * act_bytes(P);
 }
 
-// Walk the ring segments of a task: fn(global pointer, bytes). GEMV: the weight tile. ATTN:
-// per block of kAttnBlock history positions, the K rows then the V rows.
-template <typename F>
-DEV void for_segments(const KParams& P, const DevTask& T, int cu, F&& fn) {
-    if (is_gemv(T.op)) {
-        const uint64_t bytes = tile_bytes(P.wfmt, K_of(P, T.op), T.tile_rows);
-        fn(P.wstream + P.cu_stream_off[cu] + T.wofs, bytes);
-    } else if (T.op == AMK_OP_ATTN) {
-        uint32_t h0, h1;
-        chunk_range(P.pos, T.arg[2], T.arg[3], h0, h1);
-        const int g = (int)((uint64_t)T.arg[0] * P.nKV / P.nH);
-        for (uint32_t p = h0; p < h1; p += kAttnBlock) {
-            const uint32_t np = min((uint32_t)kAttnBlock, h1 - p);
-            fn(kv_ptr(P, T.layer, 0, g, p), (uint64_t)np * kv_row_bytes(P));
-            fn(kv_ptr(P, T.layer, 1, g, p), (uint64_t)np * kv_row_bytes(P));
-        }
-    }
-}
+// ------------------------------------------------------------------ weight streaming
 
-// Ring-stream bytes a task occupies (what for_segments streams, each segment rounded to 1 KiB),
-// computed without touching global memory.
-DEV uint32_t task_foot(const KParams& P, const DevTask& T) {
-    if (is_gemv(T.op)) return kb_round(tile_bytes(P.wfmt, K_of(P, T.op), T.tile_rows));
-    if (T.op != AMK_OP_ATTN) return 0;
-    uint32_t h0, h1;
-    chunk_range(P.pos, T.arg[2], T.arg[3], h0, h1);
-    const uint32_t n = h1 - h0, nb = (n + kAttnBlock - 1) / kAttnBlock, rowb = kv_row_bytes(P);
-    if (!nb) return 0;
-    return (nb - 1) * 2 * kb_round((uint64_t)kAttnBlock * rowb) + 2 * kb_round((uint64_t)(n - (nb - 1) * kAttnBlock) * rowb);
-}
+// The loads of one wave for one GEMV tile, in order: for each of the wave's rows (w, w + 8, ...)
+// its row_loads() 1 KiB loads. A group is kLoadSlots consecutive loads; lane l's part of load
+// j of a row is bytes [1024 j + 16 l, + 16) of that row (past the row's end the lane re-reads
+// the row's first 16 bytes and ignores them). Buffer A holds the even groups, B the odd ones.
+// Inside a task every issue sends exactly kLoadSlots loads (slots past the wave's loads read a
+// fixed 16-byte dummy), so the compiler can count the loads in flight and wait for one buffer
+// only.
+struct Geo {
+    const uint8_t* w0;     // the wave's first row
+    uint32_t rstride;      // bytes between the wave's rows (kComputeWaves rows)
+    uint32_t pitch, nj;    // row bytes, loads per row
+    uint32_t nloads;       // loads of this wave: its rows times nj
+    uint32_t ng;           // groups
+};
 
-// ------------------------------------------------------------------ loader wave
-
-// smallest ring-stream position some compute wave still needs
-DEV uint32_t min_released(const Lds& S) {
-    uint32_t m = lds_ld(&S.released[0]);
-    for (int w = 1; w < kComputeWaves; ++w) {
-        const uint32_t r = lds_ld(&S.released[w]);
-        if ((int)(r - m) < 0) m = r;
-    }
-    return m;
-}
-
-constexpr uint32_t kLoadGroup = 8;   // 1 KiB loads issued back to back between bookkeeping
-constexpr uint32_t kMaxPrefetchPerGroup = 2;   // L2 prefetch instructions issued before one group
-
-// The loader wave: streams every segment of its queue into the ring, 1 KiB per LDS-DMA
-// instruction, in groups of kLoadGroup with one ring-space check and one publication per group.
-// At most DEPTH + kLoadGroup loads are in flight (the hardware counts up to 63). `filled` is
-// published DEPTH loads behind the issue point in steady state, and in full before the loader
-// blocks on ring space, so every landed byte a compute wave waits for is eventually published.
-template <int DEPTH>
-DEV void loader_run(const Ctx& c) {
-    static_assert(DEPTH + kLoadGroup + kMaxPrefetchPerGroup <= 63, "in-flight loads exceed the vmcnt range");
+DEV Geo geo_of(const Ctx& c, const DevTask& T, int cw) {
     const KParams& P = *c.P;
-    Lds& S = *c.S;
-    const int lane = lane_id();
-    const uint32_t ring = P.ring_bytes;
-    const uint32_t ring_lds = (uint32_t)(uintptr_t)S.ring;
-    uint32_t issued = 0, published = 0, consumed = 0;   // 1 KiB units issued/published; bytes consumed
-    uint32_t inflight = 0;                              // vector memory instructions possibly outstanding
-    uint32_t roff = 0;                                  // ring offset of the next 1 KiB
-    bool ok = true;
-    const uint32_t q0 = P.queue_off[c.cu], q1 = P.queue_off[c.cu + 1];
-    // the CU's weight stream is contiguous: it is touched prefetch_bytes ahead of the LDS loads
-    const uint8_t* wbase = P.wstream + P.cu_stream_off[c.cu];
-    const uint32_t wlen = (uint32_t)(P.cu_stream_off[c.cu + 1] - P.cu_stream_off[c.cu]);
-    const uint32_t sink = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)S.pf_sink);
-    uint32_t pf = 0;                                    // weight-stream bytes prefetched so far
-    for (uint32_t t = q0; t < q1 && ok; ++t) {
-        const DevTask T = task_at(c, q0, t);
-        uint64_t* tr = P.trace ? P.trace + (uint64_t)t * kTraceSlots : nullptr;
-        if (tr && lane == 0) tr[4] = rt();
-        for_segments(P, T, c.cu, [&](const uint8_t* g, uint64_t bytes) {
-            const uint32_t n_inst = (uint32_t)((bytes + 1023) / 1024);
-            const uint32_t tail = (uint32_t)(bytes - (uint64_t)(n_inst - 1) * 1024u);   // bytes in the last 1 KiB
-            const uint8_t* src = g + (uint32_t)lane * 16u;
-            const bool weights = g >= wbase && g < wbase + wlen;
-            const uint32_t wofs = weights ? (uint32_t)(g - wbase) : 0u;
-            for (uint32_t k = 0; k < n_inst && ok;) {
-                const uint32_t grp = min(kLoadGroup, n_inst - k);
-                if (weights && P.prefetch_bytes) {   // keep the L2 prefetch ahead of this group
-                    const uint32_t want = min(wofs + (k + grp) * 1024u + P.prefetch_bytes, wlen);
-                    for (uint32_t n = 0; pf < want && n < kMaxPrefetchPerGroup; ++n) {
-                        if (pf + (uint32_t)lane * 128u < wlen) prefetch_8k(wbase + pf + (uint32_t)lane * 128u, sink);
-                        pf += 8192u;
-                        ++inflight;
-                    }
-                }
-                const uint32_t need = (issued + grp) * 1024u;   // stream end after this group
-                if ((int)(need - (consumed + ring)) > 0) {
-                    consumed = min_released(S);
-                    if ((int)(need - (consumed + ring)) > 0) {
-                        // blocked: publish everything in flight, then wait for the compute waves
-                        vm_wait0();
-                        inflight = 0;
-                        published = issued;
-                        lds_st(&S.filled, published * 1024u);
-                        uint32_t n = 0;
-                        for (;;) {
-                            consumed = min_released(S);
-                            if ((int)(need - (consumed + ring)) <= 0) break;
-                            if (!spin_ok(c, n)) { ok = false; break; }
-                        }
-                        if (!ok) break;
-                    }
-                }
-                for (uint32_t j = 0; j < grp; ++j, ++k) {
-                    const uint32_t dst = __builtin_amdgcn_readfirstlane(ring_lds + roff);
-                    if (k + 1 < n_inst || (uint32_t)lane * 16u < tail) dma16(src + (uint64_t)k * 1024u, dst);
-                    roff += 1024u;
-                    if (roff == ring) roff = 0;
-                }
-                issued += grp;
-                inflight += grp;
-                if (inflight > (uint32_t)DEPTH) {
-                    // the DEPTH most recent instructions hold at most DEPTH of these 1 KiB loads:
-                    // everything issued before them has landed
-                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DEPTH) : "memory");
-                    inflight = DEPTH;
-                    if ((int)(issued - DEPTH - published) > 0) {
-                        published = issued - DEPTH;
-                        lds_st(&S.filled, published * 1024u);
-                    }
-                }
-            }
-        });
-        if (tr && lane == 0) tr[5] = rt();
-    }
-    vm_wait0();
-    lds_st(&S.filled, issued * 1024u);
+    Geo s;
+    const uint32_t K = K_of(P, T.op);
+    s.pitch = row_pitch(P.wfmt, K);
+    s.nj = row_loads(P.wfmt, K);
+    s.w0 = c.wcu + T.wofs + (uint64_t)cw * s.pitch;
+    s.rstride = (uint32_t)kComputeWaves * s.pitch;
+    const uint32_t nrows =
+        T.tile_rows > (uint32_t)cw ? (T.tile_rows - (uint32_t)cw + kComputeWaves - 1) / kComputeWaves : 0u;
+    s.nloads = nrows * s.nj;
+    s.ng = (s.nloads + kLoadSlots - 1) / kLoadSlots;
+    return s;
 }
 
-// ------------------------------------------------------------------ compute-side building blocks
+struct WBuf {
+    u32x4 w[kLoadSlots];
+};
 
-// Words each compute thread has in flight at once while gathering flag-carrying words. The
-// gather walks its words in chunks of this many, so its register use does not grow with the
-// vector length.
+// Issue group g of a wave's loads into b.
+DEV void issue_group(const Ctx& c, const Geo& s, uint32_t g, WBuf& b) {
+    const uint32_t lane = (uint32_t)lane_id();
+    const uint32_t f0 = g * kLoadSlots;
+    uint32_t i = f0 / s.nj, j = f0 - i * s.nj;
+#pragma unroll
+    for (int k = 0; k < kLoadSlots; ++k) {
+        const uint32_t off = 1024u * j + 16u * lane;
+        const uint8_t* p = f0 + (uint32_t)k < s.nloads ? s.w0 + (uint64_t)i * s.rstride + (off < s.pitch ? off : 0u)
+                                                       : (const uint8_t*)c.P->norms;
+        b.w[k] = wload(p);
+        if (++j == s.nj) { j = 0; ++i; }
+    }
+    compiler_fence();
+}
+
+// two bf16 values packed in a dword, as the operand type of the bf16 dot instruction (the
+// dword is taken by value: a bit cast straight from a vector element access lost the element)
+DEV bf16x2 as_bf2(uint32_t u) {
+    bf16x2 r;
+    __builtin_memcpy(&r, &u, 4);
+    return r;
+}
+
+// Dot product of lane l's 16 weight bytes of load j of a row with the matching slice of the
+// staged input. Weights are widened in registers: fp32 as is; bf16 pairs go through the bf16
+// dot instruction; int8 codes are converted to fp32 and their top halves (exactly the code as
+// bf16) packed in pairs for the same instruction; int4 codes are nibbles minus the bias 8, with
+// the lane's 32 codes (inside one 128-column group) scaled by the group's fp16 scale from LDS.
+// Products are exact in fp32; sums are fp32.
+template <int FMT>
+DEV float dot16(const Lds& S, u32x4 w, uint32_t j, uint32_t lane, uint32_t row, uint32_t K) {
+    const uint16_t* hb = (const uint16_t*)S.hb;
+    float acc = 0.f;
+    if constexpr (FMT == AMK_F32) {
+        const uint32_t c0 = 256u * j + 4u * lane;
+        const u32x4 hv = *(const u32x4*)(S.hf + c0);
+        acc += __uint_as_float(w.x) * __uint_as_float(hv.x);
+        acc += __uint_as_float(w.y) * __uint_as_float(hv.y);
+        acc += __uint_as_float(w.z) * __uint_as_float(hv.z);
+        acc += __uint_as_float(w.w) * __uint_as_float(hv.w);
+    } else if constexpr (FMT == AMK_BF16) {
+        const uint32_t c0 = 512u * j + 8u * lane;
+        const u32x4 hv = *(const u32x4*)(hb + c0);
+        const uint32_t a[4] = {w.x, w.y, w.z, w.w}, h[4] = {hv.x, hv.y, hv.z, hv.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(a[k]), as_bf2(h[k]), acc, false);
+    } else if constexpr (FMT == AMK_INT8_PC) {
+        const uint32_t c0 = 1024u * j + 16u * lane;
+        const u32x4 h0 = *(const u32x4*)(hb + c0), h1 = *(const u32x4*)(hb + c0 + 8);
+        const uint32_t hh[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+        const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const float f0 = (float)(int8_t)((a[k] >> (16 * p)) & 0xffu);
+                const float f1 = (float)(int8_t)((a[k] >> (16 * p + 8)) & 0xffu);
+                // bf16 pair (code 2m, code 2m+1): the high halves of the two fp32 values
+                const uint32_t wp = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+                acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(wp), as_bf2(hh[2 * k + p]), acc, false);
+            }
+    } else {   // int4 g128
+        const uint32_t c0 = 2048u * j + 32u * lane;
+        const float sc = h2f(((const uint16_t*)S.kvb)[row * (K / 128) + c0 / 128]);
+        const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+        float p = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const u32x4 hv = *(const u32x4*)(hb + c0 + 8 * k);
+            const uint32_t hh[4] = {hv.x, hv.y, hv.z, hv.w};
+#pragma unroll
+            for (int b = 0; b < 8; ++b) {
+                const uint32_t hw = hh[b >> 1];
+                p += (float)((int)((a[k] >> (4 * b)) & 0xfu) - 8) * bf2f((b & 1) ? (hw >> 16) : (hw & 0xffffu));
+            }
+        }
+        acc = sc * p;
+    }
+    return acc;
+}
+
+// Consume group g of the wave's loads from b: accumulate, and at each row's last load reduce
+// over the wave and write S.red[row] (times the row's fp16 scale for int8). `acc` carries a row
+// split across groups.
+template <int FMT>
+DEV void compute_group(const Lds& S_, const Geo& s, int cw, uint32_t K, uint32_t g, const WBuf& b, float& acc) {
+    Lds& S = const_cast<Lds&>(S_);
+    const uint32_t lane = (uint32_t)lane_id();
+    const uint32_t f0 = g * kLoadSlots;
+    uint32_t i = f0 / s.nj, j = f0 - i * s.nj;
+#pragma unroll
+    for (int k = 0; k < kLoadSlots; ++k) {
+        if (f0 + (uint32_t)k < s.nloads) {
+            const uint32_t row = (uint32_t)cw + kComputeWaves * i;
+            const float d = dot16<FMT>(S, b.w[k], j, lane, row, K);
+            acc += 1024u * j + 16u * lane < s.pitch ? d : 0.f;
+            if (j + 1 == s.nj) {
+                float sum = wave_sum_dpp(acc);
+                if constexpr (FMT == AMK_INT8_PC) sum *= h2f(((const uint16_t*)S.kvb)[row]);
+                if (lane == 0) S.red[row] = sum;
+                acc = 0.f;
+            }
+        }
+        if (++j == s.nj) { j = 0; ++i; }
+    }
+}
+
+// All groups of the wave's rows of task T, double-buffered: while one buffer is consumed the
+// other is in flight. On entry A holds group 0 and, with kAheadGroups == 2, B holds group 1
+// (issued ahead, and complete: the input staging waited for every load).
+template <int FMT>
+DEV void gemv_rows_fmt(const Ctx& c, const DevTask& T, int cw, WBuf& A, WBuf& B) {
+    const Geo s = geo_of(c, T, cw);
+    const uint32_t K = K_of(*c.P, T.op);
+    // nothing is in flight here; saying so lets the compiler count exactly from this point
+    __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+    if (kAheadGroups == 1 && s.ng > 1) issue_group(c, s, 1, B);
+    float acc = 0.f;
+    uint32_t g = 0;
+    for (; g + 2 < s.ng; g += 2) {
+        compute_group<FMT>(*c.S, s, cw, K, g, A, acc);
+        issue_group(c, s, g + 2, A);
+        compute_group<FMT>(*c.S, s, cw, K, g + 1, B, acc);
+        issue_group(c, s, g + 3, B);
+    }
+    if (g < s.ng) compute_group<FMT>(*c.S, s, cw, K, g, A, acc);
+    if (g + 1 < s.ng) compute_group<FMT>(*c.S, s, cw, K, g + 1, B, acc);
+}
+
+// Issue the first groups of task T's weights (the next task's, ahead of its inputs).
+DEV void prefetch_task(const Ctx& c, const DevTask& T, int cw, WBuf& A, WBuf& B) {
+    const Geo s = geo_of(c, T, cw);
+    if (s.ng > 0) issue_group(c, s, 0, A);
+    if (kAheadGroups == 2 && s.ng > 1) issue_group(c, s, 1, B);
+}
+
+DEV void gemv_rows(const Ctx& c, const DevTask& T, int cw, WBuf& A, WBuf& B) {
+    switch (c.P->wfmt) {
+    case AMK_F32: gemv_rows_fmt<AMK_F32>(c, T, cw, A, B); break;
+    case AMK_BF16: gemv_rows_fmt<AMK_BF16>(c, T, cw, A, B); break;
+    case AMK_INT8_PC: gemv_rows_fmt<AMK_INT8_PC>(c, T, cw, A, B); break;
+    default: gemv_rows_fmt<AMK_INT4_G128>(c, T, cw, A, B); break;
+    }
+}
+
+// ------------------------------------------------------------------ flag-carrying words
+
+// Words each thread has in flight at once while gathering flag-carrying words. The gather walks
+// its words in chunks of this many, so its register use does not grow with the vector length.
 constexpr int kGatherChunk = 4;
 
 // Wait until words [0, n) of a flag-carrying buffer all carry `flag`; hand each payload to fn.
-// Each compute thread polls words ctid + k * kComputeThreads, kGatherChunk of them at a time.
+// Each thread polls words tid + k * kComputeThreads, kGatherChunk of them at a time.
 template <typename F>
 DEV bool ll_gather(const Ctx& c, const u64* base, uint32_t n, int ctid, F&& fn) {
     const uint32_t flag = c.P->flag;
@@ -373,15 +426,6 @@ DEV bool ll_gather(const Ctx& c, const u64* base, uint32_t n, int ctid, F&& fn) 
     return true;
 }
 
-DEV bool wait_filled(const Ctx& c, uint32_t need) {
-    uint32_t n = 0;
-    while ((int)(lds_ld(&c.S->filled) - need) < 0)
-        if (!spin_ok(c, n)) return false;
-    return true;
-}
-
-DEV u32x4 ring16(const Lds& S, uint32_t off) { return *(const u32x4*)(S.ring + off); }
-
 DEV float rA(const KParams& P, float v) { return P.act_f32 ? v : bf2f(f2bf(v)); }
 // payload of a word -> activation value j (0/1 inside the word)
 DEV float word_val(const KParams& P, uint32_t payload, int j) {
@@ -398,14 +442,25 @@ DEV void hput(const KParams& P, Lds& S, uint32_t i, float v) {
 
 DEV u64* ll_layer(const KParams& P, const LLLayout& y, int layer) { return P.ll + (u64)layer * y.layer_words; }
 
+constexpr int kMaxGainsPerThread = kMaxHidden / kComputeThreads;
+
 // Stage the GEMV input of a task into S.hb (activation format), with RMSNorm when gains != 0.
-// Source: flag-carrying words (src) or, for layer 0, the embedding row of the input token.
+// Source: flag-carrying words (src) or, for layer 0, the embedding row of the input token. The
+// thread's norm gains are loaded before the wait so their latency overlaps it.
 DEV bool stage_input(const Ctx& c, int ctid, uint32_t& gen, const u64* src, const void* embed_row, uint32_t K,
                      const float* gains) {
     const KParams& P = *c.P;
     Lds& S = *c.S;
     const uint32_t vpw = P.act_f32 ? 1u : 2u;
     const uint32_t nw = K / vpw;
+    float gr[kMaxGainsPerThread];
+    if (gains) {
+#pragma unroll
+        for (int k = 0; k < kMaxGainsPerThread; ++k) {
+            const uint32_t i = (uint32_t)ctid + (uint32_t)k * kComputeThreads;
+            gr[k] = i < K ? gains[i] : 0.f;
+        }
+    }
     float ss = 0.f;
     // raw values go to the stage first (exact: they are activation-format values)
     if (src) {
@@ -435,138 +490,15 @@ DEV bool stage_input(const Ctx& c, int ctid, uint32_t& gen, const u64* src, cons
     float tot = 0.f;
     for (int w = 0; w < kComputeWaves; ++w) tot += S.fpart[w];
     const float r = 1.0f / __fsqrt_rn(tot / (float)K + P.eps);
-    for (uint32_t i = (uint32_t)ctid; i < K; i += kComputeThreads) {
-        float x = P.act_f32 ? S.hf[i] : bf2f(((uint16_t*)S.hb)[i]);
-        hput(P, S, i, rA(P, (x * r) * gains[i]));
+#pragma unroll
+    for (int k = 0; k < kMaxGainsPerThread; ++k) {
+        const uint32_t i = (uint32_t)ctid + (uint32_t)k * kComputeThreads;
+        if (i < K) {
+            const float x = P.act_f32 ? S.hf[i] : bf2f(((uint16_t*)S.hb)[i]);
+            hput(P, S, i, rA(P, (x * r) * gr[k]));
+        }
     }
     return cbar(c, gen);
-}
-
-DEV uint32_t wrap(uint32_t off, uint32_t ring) { return off >= ring ? off - ring : off; }
-
-// Partial dot products of two weight rows (ring offsets b0, b1) with the staged input vector
-// over this lane's 16-byte weight segments s = lane, lane + 64, ...; the input values of a
-// segment are read once for both rows. Weights are widened in registers: fp32 as is, bf16 by a
-// shift, int8 by a sign-extending byte conversion, int4 by nibble extraction minus the bias 8
-// with each 128-column group's partial sum scaled by its fp16 scale. Products are exact in fp32
-// (bf16 x bf16, int x bf16); sums are fp32.
-template <int FMT>
-DEV void dot2(const Lds& S, uint32_t b0, uint32_t b1, uint32_t K, uint32_t ring, int lane, float& acc0, float& acc1) {
-    const uint16_t* hb = (const uint16_t*)S.hb;
-    if constexpr (FMT == AMK_F32) {
-        for (uint32_t s = (uint32_t)lane; s < K / 4; s += 64) {
-            const u32x4 w0 = ring16(S, wrap(b0 + 16 * s, ring)), w1 = ring16(S, wrap(b1 + 16 * s, ring));
-            const u32x4 hv = *(const u32x4*)(S.hf + 4 * s);
-            const float h[4] = {__uint_as_float(hv.x), __uint_as_float(hv.y), __uint_as_float(hv.z), __uint_as_float(hv.w)};
-            const uint32_t a[4] = {w0.x, w0.y, w0.z, w0.w}, b[4] = {w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                acc0 += __uint_as_float(a[k]) * h[k];
-                acc1 += __uint_as_float(b[k]) * h[k];
-            }
-        }
-    } else if constexpr (FMT == AMK_BF16) {
-        for (uint32_t s = (uint32_t)lane; s < K / 8; s += 64) {
-            const u32x4 w0 = ring16(S, wrap(b0 + 16 * s, ring)), w1 = ring16(S, wrap(b1 + 16 * s, ring));
-            const u32x4 hv = *(const u32x4*)(hb + 8 * s);
-            const uint32_t hh[4] = {hv.x, hv.y, hv.z, hv.w}, a[4] = {w0.x, w0.y, w0.z, w0.w}, b[4] = {w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const float hl = bf2f(hh[k] & 0xffffu), hu = bf2f(hh[k] >> 16);
-                acc0 += bf2f(a[k] & 0xffffu) * hl;
-                acc0 += bf2f(a[k] >> 16) * hu;
-                acc1 += bf2f(b[k] & 0xffffu) * hl;
-                acc1 += bf2f(b[k] >> 16) * hu;
-            }
-        }
-    } else if constexpr (FMT == AMK_INT8_PC) {
-        for (uint32_t s = (uint32_t)lane; s < K / 16; s += 64) {
-            const u32x4 w0 = ring16(S, wrap(b0 + 16 * s, ring)), w1 = ring16(S, wrap(b1 + 16 * s, ring));
-            const u32x4 h0 = *(const u32x4*)(hb + 16 * s), h1 = *(const u32x4*)(hb + 16 * s + 8);
-            const uint32_t hh[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
-            const uint32_t a[4] = {w0.x, w0.y, w0.z, w0.w}, b[4] = {w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t hw = hh[(4 * k + j) >> 1];
-                    const float h = bf2f(((4 * k + j) & 1) ? (hw >> 16) : (hw & 0xffffu));
-                    acc0 += (float)(int8_t)((a[k] >> (8 * j)) & 0xffu) * h;
-                    acc1 += (float)(int8_t)((b[k] >> (8 * j)) & 0xffu) * h;
-                }
-        }
-    } else {   // int4 g128: row = [K/128 fp16 scales][K/2 bytes of nibbles, biased by 8]
-        const uint32_t coff = int4_codes_off(K);
-        for (uint32_t s = (uint32_t)lane; s < K / 32; s += 64) {
-            const u32x4 w0 = ring16(S, wrap(b0 + coff + 16 * s, ring)), w1 = ring16(S, wrap(b1 + coff + 16 * s, ring));
-            const float sc0 = h2f(*(const uint16_t*)(S.ring + wrap(b0 + 2 * (s / 4), ring)));
-            const float sc1 = h2f(*(const uint16_t*)(S.ring + wrap(b1 + 2 * (s / 4), ring)));
-            const uint32_t a[4] = {w0.x, w0.y, w0.z, w0.w}, b[4] = {w1.x, w1.y, w1.z, w1.w};
-            float p0 = 0.f, p1 = 0.f;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const u32x4 hv = *(const u32x4*)(hb + 32 * s + 8 * k);
-                const uint32_t hh[4] = {hv.x, hv.y, hv.z, hv.w};
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const uint32_t hw = hh[j >> 1];
-                    const float h = bf2f((j & 1) ? (hw >> 16) : (hw & 0xffffu));
-                    p0 += (float)((int)((a[k] >> (4 * j)) & 0xfu) - 8) * h;
-                    p1 += (float)((int)((b[k] >> (4 * j)) & 0xfu) - 8) * h;
-                }
-            }
-            acc0 += sc0 * p0;
-            acc1 += sc1 * p1;
-        }
-    }
-}
-
-// GEMV rows of one task out of the ring: S.red[r] = sum_k W[r][k] h[k] (times the row scale for
-// int8). Wave w takes the row pairs (2p, 2p+1), p = w, w + kComputeWaves, ...
-template <int FMT>
-DEV bool gemv_rows_fmt(const Ctx& c, int cw, uint32_t tile_pos, uint32_t rows, uint32_t K) {
-    const KParams& P = *c.P;
-    Lds& S = *c.S;
-    const int lane = lane_id();
-    const uint32_t ring = P.ring_bytes;
-    const uint32_t pitch = row_pitch(FMT, K);
-    const uint32_t end = tile_pos + kb_round(tile_bytes(FMT, K, rows));
-    const uint32_t pairs = (rows + 1) / 2;
-    // Advertise the first ring byte this wave still needs before waiting for any row: until
-    // it does, the loader cannot run more than one ring past the task start, and a wave whose
-    // first row lies beyond that would wait forever.
-    if (lane == 0) lds_st(&S.released[cw], (uint32_t)cw < pairs ? tile_pos + 2u * (uint32_t)cw * pitch : end);
-    for (uint32_t p = (uint32_t)cw; p < pairs; p += kComputeWaves) {
-        const uint32_t r0 = 2 * p;
-        const bool two = r0 + 1 < rows;
-        const uint32_t rpos = tile_pos + r0 * pitch;
-        if (!wait_filled(c, rpos + (two ? 2 : 1) * pitch)) return false;
-        const uint32_t b0 = rpos % ring, b1 = wrap(b0 + pitch, ring);
-        float acc0 = 0.f, acc1 = 0.f;
-        dot2<FMT>(S, b0, two ? b1 : b0, K, ring, lane, acc0, acc1);
-        acc0 = wave_sum(acc0);
-        acc1 = wave_sum(acc1);
-        if constexpr (FMT == AMK_INT8_PC) {
-            acc0 *= h2f(*(const uint16_t*)(S.ring + wrap(b0 + K, ring)));
-            acc1 *= h2f(*(const uint16_t*)(S.ring + wrap(b1 + K, ring)));
-        }
-        if (lane == 0) {
-            S.red[r0] = acc0;
-            if (two) S.red[r0 + 1] = acc1;
-            const uint32_t pn = p + kComputeWaves;
-            lds_st(&S.released[cw], pn < pairs ? tile_pos + 2u * pn * pitch : end);
-        }
-    }
-    return true;
-}
-
-DEV bool gemv_rows(const Ctx& c, int cw, uint32_t tile_pos, uint32_t rows, uint32_t K) {
-    switch (c.P->wfmt) {
-    case AMK_F32: return gemv_rows_fmt<AMK_F32>(c, cw, tile_pos, rows, K);
-    case AMK_BF16: return gemv_rows_fmt<AMK_BF16>(c, cw, tile_pos, rows, K);
-    case AMK_INT8_PC: return gemv_rows_fmt<AMK_INT8_PC>(c, cw, tile_pos, rows, K);
-    default: return gemv_rows_fmt<AMK_INT4_G128>(c, cw, tile_pos, rows, K);
-    }
 }
 
 // ------------------------------------------------------------------ the ops
@@ -575,23 +507,26 @@ struct TaskEnv {
     const Ctx* c;
     int ctid, cw;
     uint32_t* gen;
-    uint32_t tile_pos;   // ring-stream position of the task's first segment
     LLLayout y;
     int token;
     uint64_t* tr;        // this task's trace slots, or null
 };
 
-// timestamp slot k of the current task (first compute thread only)
+// timestamp slot k of the current task (first thread only)
 DEV void mark(const TaskEnv& e, int k) {
     if (e.tr && e.ctid == 0) e.tr[k] = rt();
 }
 
-DEV bool op_gemv(const TaskEnv& e, const DevTask& T) {
+// A GEMV task: wait for and stage its input vector (RMSNorm fused where the model has one), run
+// the tile's rows, then the op's epilogue: RoPE and the KV-cache append (QKV), the residual add
+// (O, down), SwiGLU (gate/up), the tile argmax and logits (LM head). On entry the first groups
+// of this task's weight loads are in A (and B), issued ahead.
+DEV bool op_gemv(const TaskEnv& e, const DevTask& T, WBuf& A, WBuf& B) {
     const Ctx& c = *e.c;
     const KParams& P = *c.P;
     Lds& S = *c.S;
     const int op = T.op, l = T.layer, ctid = e.ctid;
-    const uint32_t K = K_of(P, op), rows = T.tile_rows;
+    const uint32_t K = K_of(P, op);
     const uint32_t vpw = P.act_f32 ? 1u : 2u;
     const u64* src = nullptr;
     const void* emb = nullptr;
@@ -608,6 +543,14 @@ DEV bool op_gemv(const TaskEnv& e, const DevTask& T) {
     case AMK_OP_GATEUP: src = LLl + e.y.xo; gains = P.norms + ((uint64_t)l * 2 + 1) * P.H; break;
     case AMK_OP_DOWN: src = LLl + e.y.a; break;
     case AMK_OP_LM: src = ll_layer(P, e.y, P.L - 1) + e.y.xd; gains = P.norms + (uint64_t)P.L * 2 * P.H; break;
+    }
+    // quantised tiles: the row scales (int8) or group scales (int4) go to LDS. Any wait below
+    // waits for the weight loads already in flight too, so these loads cost no extra latency.
+    const uint32_t sc_chunks = (uint32_t)((tile_bytes(P.wfmt, K, T.tile_rows) - tile_scale_off(P.wfmt, K, T.tile_rows)) / 16);
+    if (sc_chunks) {
+        const uint8_t* sb = c.wcu + T.wofs + tile_scale_off(P.wfmt, K, T.tile_rows);
+        for (uint32_t q = (uint32_t)ctid; q < sc_chunks; q += kComputeThreads)
+            *(u32x4*)(S.kvb + 16 * q) = *(const u32x4*)(sb + 16ull * q);
     }
     // QKV: this thread's rotary cos/sin (quad ctid), loaded now so the load overlaps the input wait
     float rc0 = 1.f, rs0 = 0.f, rc1 = 1.f, rs1 = 0.f;
@@ -633,9 +576,10 @@ DEV bool op_gemv(const TaskEnv& e, const DevTask& T) {
                 return false;
         }
     }
-    if (!stage_input(c, ctid, *e.gen, src, emb, K, gains)) return false;
+    if (!stage_input(c, ctid, *e.gen, src, emb, K, gains)) return false;   // ends with a barrier
     mark(e, 1);
-    if (!gemv_rows(c, e.cw, e.tile_pos, rows, K)) return false;
+    gemv_rows(c, T, e.cw, A, B);
+    if (e.tr && ctid == 0) e.tr[4] = rt();
     if (!cbar(c, *e.gen)) return false;
     mark(e, 2);
     const uint32_t flag = P.flag;
@@ -645,7 +589,7 @@ DEV bool op_gemv(const TaskEnv& e, const DevTask& T) {
         const uint32_t nq = T.arg[1], per = (uint32_t)P.hd / 4, half = (uint32_t)P.hd / 2;
         const uint32_t qd = (uint32_t)(P.nH * P.hd), kd = (uint32_t)(P.nKV * P.hd);
         u64* out = (u64*)(LLl + e.y.qkv);
-        // one quad per thread (a task has at most kRedRows / 4 < kComputeThreads quads)
+        // one quad per thread (a task has at most kRedRows / 4 <= kComputeThreads quads)
         if ((uint32_t)ctid < nq) {
             const uint32_t k = (uint32_t)ctid;
             const uint32_t u = T.arg[0] + k, head = u / per, m = u % per;
@@ -653,9 +597,8 @@ DEV bool op_gemv(const TaskEnv& e, const DevTask& T) {
             float v0 = S.red[4 * k], v1 = S.red[4 * k + 1], v2 = S.red[4 * k + 2], v3 = S.red[4 * k + 3];
             const bool rot = base < qd + kd;
             if (rot) {
-                const float c0 = rc0, s0 = rs0, c1 = rc1, s1 = rs1;
-                const float a0 = v0 * c0 - v2 * s0, b0 = v2 * c0 + v0 * s0;
-                const float a1 = v1 * c1 - v3 * s1, b1 = v3 * c1 + v1 * s1;
+                const float a0 = v0 * rc0 - v2 * rs0, b0 = v2 * rc0 + v0 * rs0;
+                const float a1 = v1 * rc1 - v3 * rs1, b1 = v3 * rc1 + v1 * rs1;
                 v0 = a0; v2 = b0; v1 = a1; v3 = b1;
             }
             v0 = rA(P, v0); v1 = rA(P, v1); v2 = rA(P, v2); v3 = rA(P, v3);
@@ -702,7 +645,9 @@ DEV bool op_gemv(const TaskEnv& e, const DevTask& T) {
         u64* out = (u64*)(LLl + e.y.a) + j0 / vpw;
         for (uint32_t i = (uint32_t)ctid; i < n / vpw; i += kComputeThreads) {
             float v[2] = {0.f, 0.f};
-            for (uint32_t j = 0; j < vpw; ++j) {
+            #pragma unroll
+            for (uint32_t j = 0; j < 2; ++j) {
+                if (j >= vpw) break;
                 const float G = S.red[2 * (i * vpw + j)], U = S.red[2 * (i * vpw + j) + 1];
                 v[j] = rA(P, (G / (1.0f + expf(-G))) * U);
             }
@@ -758,10 +703,69 @@ constexpr int kAttF = kAttVc + 128;               // [kComputeWaves][kMaxAttnHea
 constexpr int kAttM = kAttF + kComputeWaves * kMaxAttnHeads;   // [kMaxAttnHeads] maxima
 static_assert(kAttM + kMaxAttnHeads <= kAttnLds / 4, "attention LDS map");
 constexpr int kAttMaxD = 8;                       // dims per lane: hd / lanes-per-head (the lowering keeps it <= 8)
+constexpr int kKvLoads = kKvBytes / 16 / kComputeThreads;   // 16-byte K/V loads per thread per round
 
-// One K or V element of ring row `roff` (activation format), as fp32.
-DEV float kv_at(const KParams& P, const Lds& S, uint32_t roff, uint32_t d) {
-    return P.act_f32 ? *(const float*)(S.ring + roff + 4 * d) : bf2f(*(const uint16_t*)(S.ring + roff + 2 * d));
+// This lane's D consecutive values [d0, d0 + D) of the staged K or V row at `p`, as fp32, read
+// with vector LDS loads (the slice is aligned to its own size: d0 is a multiple of D).
+DEV void kv_slice(const KParams& P, const uint8_t* p, uint32_t d0, uint32_t D, float (&v)[kAttMaxD]) {
+    if (P.act_f32) {
+        const float* f = (const float*)p + d0;
+        if (D >= 4) {
+            const u32x4 a = *(const u32x4*)f;
+            v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y); v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+            if (D == 8) {
+                const u32x4 b = *(const u32x4*)(f + 4);
+                v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y); v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+            }
+        } else if (D == 2) {
+            const float2 a = *(const float2*)f;
+            v[0] = a.x; v[1] = a.y;
+        } else {
+            v[0] = f[0];
+        }
+    } else {
+        const uint16_t* h = (const uint16_t*)p + d0;
+        if (D == 8) {
+            const u32x4 a = *(const u32x4*)h;
+            const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) { v[2 * k] = bf2f(w[k] & 0xffffu); v[2 * k + 1] = bf2f(w[k] >> 16); }
+        } else if (D == 4) {
+            const uint2 a = *(const uint2*)h;
+            v[0] = bf2f(a.x & 0xffffu); v[1] = bf2f(a.x >> 16); v[2] = bf2f(a.y & 0xffffu); v[3] = bf2f(a.y >> 16);
+        } else if (D == 2) {
+            const uint32_t a = *(const uint32_t*)h;
+            v[0] = bf2f(a & 0xffffu); v[1] = bf2f(a >> 16);
+        } else {
+            v[0] = bf2f(h[0]);
+        }
+    }
+}
+
+// Issue the loads of one round of history positions [a, a + n) of KV group g into registers:
+// the K rows, then the V rows, each block contiguous in the cache (16 bytes per load).
+DEV void kv_round_issue(const KParams& P, int l, int g, uint32_t a, uint32_t n, int ctid, u32x4 (&r)[kKvLoads]) {
+    const uint32_t blk = n * kv_row_bytes(P), chunks = 2 * blk / 16;
+    const uint8_t* kb = kv_ptr(P, l, 0, g, a);
+    const uint8_t* vb = kv_ptr(P, l, 1, g, a);
+#pragma unroll
+    for (int k = 0; k < kKvLoads; ++k) {
+        const uint32_t q = (uint32_t)ctid + (uint32_t)k * kComputeThreads;
+        if (q < chunks) {
+            const uint32_t off = 16 * q;
+            r[k] = off < blk ? *(const u32x4*)(kb + off) : *(const u32x4*)(vb + (off - blk));
+        }
+    }
+    compiler_fence();
+}
+// ... and store them to S.kvb: K rows at [0, n * row bytes), V rows after them
+DEV void kv_round_store(const KParams& P, Lds& S, uint32_t n, int ctid, const u32x4 (&r)[kKvLoads]) {
+    const uint32_t chunks = 2 * n * kv_row_bytes(P) / 16;
+#pragma unroll
+    for (int k = 0; k < kKvLoads; ++k) {
+        const uint32_t q = (uint32_t)ctid + (uint32_t)k * kComputeThreads;
+        if (q < chunks) *(u32x4*)(S.kvb + 16 * q) = r[k];
+    }
 }
 
 // Attention of query heads [h0, h0+nh) (one KV group g) over chunk ch of nc of the context
@@ -772,11 +776,11 @@ DEV float kv_at(const KParams& P, const Lds& S, uint32_t roff, uint32_t d) {
 // lanes (L = 64 / nh rounded to a power of two, at most hd), a lane owns D = hd / L
 // consecutive dims and keeps its q slice and its slice of the running output in registers. A
 // position's score is the lane-group sum of q.K over the group; softmax runs online (running
-// max m, running sum l, rescaled output o). Positions are dealt round robin to the compute
-// waves, so even a short chunk keeps every wave busy; the current position (last chunk only)
-// comes from the flag-carrying words, the history from the ring. At the end the per-wave
-// states (m, l, o) are combined with weights exp(m_w - M) computed once per (wave, head); a
-// single chunk writes the output row, a split context writes its (M, L, o) partial state.
+// max m, running sum l, rescaled output o). History positions are staged in LDS in rounds (the
+// first round's loads are issued before the wait for q) and dealt round robin to the waves; the
+// current position (last chunk only) comes from the flag-carrying words. At the end the
+// per-wave states (m, l, o) are combined with weights exp(m_w - M) computed once per (wave,
+// head); a single chunk writes the output row, a split context writes its (M, L, o) state.
 DEV bool op_attn(const TaskEnv& e, const DevTask& T) {
     const Ctx& c = *e.c;
     const KParams& P = *c.P;
@@ -791,6 +795,15 @@ DEV bool op_attn(const TaskEnv& e, const DevTask& T) {
     float* qs = S.att + kAttQ;
     float* kc = S.att + kAttKc;
     float* vc = S.att + kAttVc;
+    uint32_t p0, p1;
+    chunk_range(P.pos, ch, nc, p0, p1);
+    const uint32_t nhist = p1 - p0;
+    const uint32_t rowb = kv_row_bytes(P);
+    const uint32_t per_round = (uint32_t)kKvBytes / (2 * rowb);   // history positions per LDS round
+    // the first round's K/V loads go out before the wait for q
+    u32x4 kvr[kKvLoads];
+    uint32_t ra = p0, rn = min(per_round, nhist);
+    if (rn) kv_round_issue(P, l, g, ra, rn, ctid, kvr);
     // inputs: q of the task's heads; the current k, v of the group (last chunk only)
     if (!ll_gather(c, Lq + (uint64_t)h0 * hd / vpw, nh * hd / vpw, ctid, [&](uint32_t i, uint32_t pl) {
             for (uint32_t j = 0; j < vpw; ++j) qs[i * vpw + j] = word_val(P, pl, (int)j);
@@ -807,6 +820,7 @@ DEV bool op_attn(const TaskEnv& e, const DevTask& T) {
             }))
             return false;
     }
+    if (rn) kv_round_store(P, S, rn, ctid, kvr);
     if (!cbar(c, *e.gen)) return false;
     mark(e, 1);
     // lane layout
@@ -816,56 +830,53 @@ DEV bool op_attn(const TaskEnv& e, const DevTask& T) {
     const uint32_t hl = (uint32_t)lane / L, dg = (uint32_t)lane % L;
     const bool active = hl < nh;
     const uint32_t hq = active ? hl : 0;   // inactive lanes shadow head 0 and never store
-    float qr[kAttMaxD], o[kAttMaxD];
+    float qr[kAttMaxD], o[kAttMaxD], kv[kAttMaxD];
 #pragma unroll
     for (int k = 0; k < kAttMaxD; ++k) {
         qr[k] = (uint32_t)k < D ? qs[hq * hd + dg * D + k] : 0.f;
         o[k] = 0.f;
     }
     float m = -INFINITY, lsum = 0.f;
-    // positions of this task: history [p0, p1) from the ring (blocks of kAttnBlock: K then V
-    // segment), then the current position
-    uint32_t p0, p1;
-    chunk_range(P.pos, ch, nc, p0, p1);
-    const uint32_t nhist = p1 - p0, ntot = nhist + (cur ? 1u : 0u);
-    const uint32_t nb = (nhist + kAttnBlock - 1) / kAttnBlock;
-    const uint32_t rowb = kv_row_bytes(P), ring = P.ring_bytes;
-    const uint32_t full = 2 * kb_round((uint64_t)kAttnBlock * rowb);
-    const uint32_t tend = e.tile_pos + (nb ? (nb - 1) * full + 2 * kb_round((uint64_t)(nhist - (nb - 1) * kAttnBlock) * rowb) : 0);
     const float scale = P.attn_scale;
-    // advertise the first ring byte this wave needs (the block of its first position)
-    if (lane == 0) lds_st(&S.released[cw], (uint32_t)cw < nhist ? e.tile_pos + ((uint32_t)cw / kAttnBlock) * full : tend);
-    uint32_t have_blk = 0xffffffffu;
-    for (uint32_t i = (uint32_t)cw; i < ntot; i += kComputeWaves) {
-        uint32_t koff = 0, voff = 0;
-        const bool hist = i < nhist;
-        if (hist) {
-            const uint32_t b = i / kAttnBlock, r = i % kAttnBlock;
-            const uint32_t np = min((uint32_t)kAttnBlock, nhist - b * kAttnBlock);
-            const uint32_t kpos = e.tile_pos + b * full, vpos = kpos + kb_round((uint64_t)np * rowb);
-            if (b != have_blk) {
-                if (lane == 0) lds_st(&S.released[cw], kpos);
-                if (!wait_filled(c, vpos + np * rowb)) return false;
-                have_blk = b;
-            }
-            koff = wrap(kpos % ring + r * rowb, ring);
-            voff = wrap(vpos % ring + r * rowb, ring);
-        }
+    // one position: score, online-softmax update; krow/vrow are the staged rows, or null for
+    // the current position (k, v in S.att)
+    auto step = [&](const uint8_t* krow, const uint8_t* vrow) {
+        if (krow) kv_slice(P, krow, dg * D, D, kv);
+        else
+#pragma unroll
+            for (int k = 0; k < kAttMaxD; ++k) kv[k] = (uint32_t)k < D ? kc[dg * D + k] : 0.f;
         float sdot = 0.f;
 #pragma unroll
         for (int k = 0; k < kAttMaxD; ++k)
-            if ((uint32_t)k < D) sdot += qr[k] * (hist ? kv_at(P, S, koff, dg * D + k) : kc[dg * D + k]);
+            if ((uint32_t)k < D) sdot += qr[k] * kv[k];
         for (uint32_t off = L >> 1; off >= 1; off >>= 1) sdot += __shfl_xor(sdot, (int)off, 64);
         const float sc = sdot * scale;
         const float mn = fmaxf(m, sc);
         const float alpha = expf(m - mn), pw = expf(sc - mn);
         lsum = lsum * alpha + pw;
+        if (vrow) kv_slice(P, vrow, dg * D, D, kv);
+        else
+#pragma unroll
+            for (int k = 0; k < kAttMaxD; ++k) kv[k] = (uint32_t)k < D ? vc[dg * D + k] : 0.f;
 #pragma unroll
         for (int k = 0; k < kAttMaxD; ++k)
-            if ((uint32_t)k < D) o[k] = o[k] * alpha + pw * (hist ? kv_at(P, S, voff, dg * D + k) : vc[dg * D + k]);
+            if ((uint32_t)k < D) o[k] = o[k] * alpha + pw * kv[k];
         m = mn;
+    };
+    // history rounds
+    while (rn) {
+        for (uint32_t i = (uint32_t)cw; i < rn; i += kComputeWaves) step(S.kvb + i * rowb, S.kvb + (rn + i) * rowb);
+        const uint32_t na = ra + rn, nn = min(per_round, p1 - na);
+        if (!nn) break;
+        if (!cbar(c, *e.gen)) return false;   // every wave is done with this round's rows
+        kv_round_issue(P, l, g, na, nn, ctid, kvr);
+        kv_round_store(P, S, nn, ctid, kvr);
+        if (!cbar(c, *e.gen)) return false;
+        ra = na;
+        rn = nn;
     }
-    if (lane == 0) lds_st(&S.released[cw], tend);
+    // the current position: one wave
+    if (cur && (uint32_t)cw == nhist % kComputeWaves) step(nullptr, nullptr);
     // per-wave states -> LDS: hf[(cw * nh + h) * (hd + 2) + {0: m, 1: l, 2 + d: o}]
     const uint32_t st = hd + 2;
     if (active) {
@@ -892,7 +903,9 @@ DEV bool op_attn(const TaskEnv& e, const DevTask& T) {
         u64* out = ll_layer(P, e.y, l) + e.y.o + (uint64_t)h0 * hd / vpw;
         for (uint32_t i = (uint32_t)ctid; i < nh * hd / vpw; i += kComputeThreads) {
             float v[2] = {0.f, 0.f};
-            for (uint32_t j = 0; j < vpw; ++j) {
+            #pragma unroll
+            for (uint32_t j = 0; j < 2; ++j) {
+                if (j >= vpw) break;
                 const uint32_t t = i * vpw + j, h = t / hd, d = t % hd;
                 float os = 0.f, ls = 0.f;
                 for (int w = 0; w < kComputeWaves; ++w) {
@@ -960,7 +973,9 @@ DEV bool op_merge(const TaskEnv& e, const DevTask& T) {
     u64* out = ll_layer(P, e.y, l) + e.y.o + (uint64_t)h0 * hd / vpw;
     for (uint32_t i = (uint32_t)ctid; i < nh * hd / vpw; i += kComputeThreads) {
         float v[2] = {0.f, 0.f};
-        for (uint32_t j = 0; j < vpw; ++j) {
+        #pragma unroll
+        for (uint32_t j = 0; j < 2; ++j) {
+            if (j >= vpw) break;
             const uint32_t t = i * vpw + j, h = t / hd, d = t % hd;
             const float* base = S.hf + (uint64_t)h * nc * st;
             float os = 0.f;
@@ -972,6 +987,8 @@ DEV bool op_merge(const TaskEnv& e, const DevTask& T) {
     return true;
 }
 
+// The greedy token: the argmax over the LM tiles' (max, index) pairs, lowest index among equal
+// maxima; a tile that saw a NaN makes the token -1.
 DEV bool op_argmax(const TaskEnv& e, const DevTask& T) {
     const Ctx& c = *e.c;
     const KParams& P = *c.P;
@@ -1019,8 +1036,8 @@ DEV bool op_argmax(const TaskEnv& e, const DevTask& T) {
 DEV void compute_run(const Ctx& c) {
     const KParams& P = *c.P;
     Lds& S = *c.S;
-    const int ctid = (int)threadIdx.x - 64;
-    const int cw = ctid >> 6;
+    const int ctid = (int)threadIdx.x;
+    const int cw = __builtin_amdgcn_readfirstlane(ctid >> 6);
     uint32_t gen = 0;
     TaskEnv e;
     e.c = &c;
@@ -1034,23 +1051,34 @@ DEV void compute_run(const Ctx& c) {
         tok = 0;
     }
     e.token = tok;
-    uint32_t pos = 0;   // ring-stream position of the current task
+    WBuf A, B;
     const uint32_t q0 = P.queue_off[c.cu], q1 = P.queue_off[c.cu + 1];
+    // the first task's weights, if it has any
+    if (q0 < q1) {
+        const DevTask F = task_at(c, q0, q0);
+        if (is_gemv(F.op)) prefetch_task(c, F, cw, A, B);
+    }
     for (uint32_t t = q0; t < q1; ++t) {
         const DevTask T = task_at(c, q0, t);
-        e.tile_pos = pos;
+        const DevTask N = task_at(c, q0, t + 1 < q1 ? t + 1 : t);
+        const bool next_gemv = t + 1 < q1 && is_gemv(N.op);
         e.tr = P.trace ? P.trace + (uint64_t)t * kTraceSlots : nullptr;
         mark(e, 0);
         bool ok;
-        switch (T.op) {
-        case AMK_OP_ATTN: ok = op_attn(e, T); break;
-        case AMK_OP_MERGE: ok = op_merge(e, T); break;
-        case AMK_OP_ARGMAX: ok = op_argmax(e, T); break;
-        default: ok = op_gemv(e, T); break;
+        if (is_gemv(T.op)) {
+            ok = op_gemv(e, T, A, B);
+        } else {
+            switch (T.op) {
+            case AMK_OP_ATTN: ok = op_attn(e, T); break;
+            case AMK_OP_MERGE: ok = op_merge(e, T); break;
+            default: ok = op_argmax(e, T); break;
+            }
         }
-        pos += task_foot(P, T);
-        if (lane_id() == 0) lds_st(&S.released[cw], pos);
-        // all compute waves are done with this task's LDS data before the next task stages its input
+        if (e.tr && ctid == 0) e.tr[5] = rt();
+        // the task's outputs are out: start the next task's weights (behind those stores in the
+        // memory pipeline, so the outputs reach their consumers first)
+        if (ok && next_gemv) prefetch_task(c, N, cw, A, B);
+        // every wave is done with this task's LDS data before the next task stages its input
         if (!ok || !cbar(c, gen)) {
             __hip_atomic_store(&S.abort_, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             return;
@@ -1064,10 +1092,7 @@ DEV void compute_run(const Ctx& c) {
 extern "C" __global__ void __launch_bounds__(kThreads, 1) amk_megakernel(KParams P) {
     __shared__ Lds S;
     const int tid = threadIdx.x;
-    if (tid < kComputeWaves + 1) {
-        if (tid == 0) { S.filled = 0; S.bar = 0; S.abort_ = 0; }
-        if (tid < kComputeWaves) S.released[tid] = 0;
-    }
+    if (tid == 0) { S.bar = 0; S.abort_ = 0; }
     {   // copy the head of this CU's task queue to LDS (8 dwords per task)
         const uint32_t q0 = P.queue_off[blockIdx.x], q1 = P.queue_off[blockIdx.x + 1];
         const uint32_t n = min(q1 - q0, (uint32_t)kTaskCache) * (uint32_t)(sizeof(DevTask) / 4);
@@ -1081,20 +1106,8 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) amk_megakernel(KParams
     c.S = &S;
     c.cu = blockIdx.x;
     c.deadline = rt() + P.watchdog_ticks;
-    if (tid < 64) {
-        switch (P.loader_depth) {
-        case 8: loader_run<8>(c); break;
-        case 16: loader_run<16>(c); break;
-        case 24: loader_run<24>(c); break;
-        case 32: loader_run<32>(c); break;
-        case 48: loader_run<48>(c); break;
-        case 40: loader_run<40>(c); break;
-        case 52: loader_run<52>(c); break;
-        default: loader_run<48>(c); break;
-        }
-    } else {
-        compute_run(c);
-    }
+    c.wcu = P.wstream + P.cu_stream_off[blockIdx.x];
+    compute_run(c);
 }
 
 }  // namespace amk

@@ -73,27 +73,21 @@ __global__ void __launch_bounds__(256) k_repack(const RowMap* rows, uint32_t n_r
     } else if (wfmt == AMK_INT8_PC) {
         const uint16_t* s = (const uint16_t*)base + (uint64_t)m.src_row * K;
         const float sc = quant_scale(block_absmax(s, K, red), 127);
-        for (uint32_t k = threadIdx.x; k < pitch; k += blockDim.x) {
-            uint8_t v = 0;
-            if (k < K) v = (uint8_t)(int8_t)quant_code(bf2f(s[k]), sc, 127);
-            else if (k < K + 2) v = (uint8_t)(f2h_bits(sc) >> (8 * (k - K)));
-            dst[k] = v;
-        }
-    } else {
+        for (uint32_t k = threadIdx.x; k < pitch; k += blockDim.x) dst[k] = (uint8_t)(int8_t)quant_code(bf2f(s[k]), sc, 127);
+        if (threadIdx.x == 0) *(uint16_t*)(stream + m.sdst) = f2h_bits(sc);
+    } else {   // int4 g128: nibble pair (2k, 2k+1) -> byte k, low nibble first, codes biased by 8
         const uint16_t* s = (const uint16_t*)base + (uint64_t)m.src_row * K;
-        const uint32_t ng = K / 128, coff = int4_codes_off(K);
-        for (uint32_t b = 0; b < ng; ++b) {
+        for (uint32_t b = 0; b < K / 128; ++b) {
             const float sc = quant_scale(block_absmax(s + 128 * b, 128, red), 7);
-            if (threadIdx.x == 0) *(uint16_t*)(dst + 2 * b) = f2h_bits(sc);
-            if (threadIdx.x < 64) {   // 64 bytes: nibble pair (2k, 2k+1) -> byte k, low nibble first
+            if (threadIdx.x == 0) *(uint16_t*)(stream + m.sdst + 2 * b) = f2h_bits(sc);
+            if (threadIdx.x < 64) {
                 const uint32_t k = threadIdx.x;
                 const int q0 = quant_code(bf2f(s[128 * b + 2 * k]), sc, 7) + 8;
                 const int q1 = quant_code(bf2f(s[128 * b + 2 * k + 1]), sc, 7) + 8;
-                dst[coff + 64 * b + k] = (uint8_t)(q0 | (q1 << 4));
+                dst[64 * b + k] = (uint8_t)(q0 | (q1 << 4));
             }
             __syncthreads();
         }
-        for (uint32_t k = coff + K / 2 + threadIdx.x; k < pitch; k += blockDim.x) dst[k] = 0;
     }
 }
 

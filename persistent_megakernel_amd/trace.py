@@ -1,11 +1,11 @@
 """Per-task timestamp traces of the decode megakernel: where one launch spends its time.
 
 A trace row per task (queue order) holds six realtime-counter values (100 MHz): compute start,
-inputs observed, rows done, end, loader first issue, loader last issue (amk_set_trace). From
-them: per opcode the time spent waiting for inputs (producers on other CUs plus the staging
-prologue), computing out of LDS, and in the epilogue; per phase (opcode, layer) the moment the
-last CU finished, i.e. the critical path of the launch; and whether weight loads had been
-issued before the inputs arrived (prefetch ahead of the dependency).
+inputs observed, rows done, end, first wave's rows done (GEMV), outputs written (amk_set_trace).
+From them: per opcode the time spent waiting for inputs (producers on other CUs plus the
+staging prologue), computing, in the epilogue, the skew between the first wave and the whole
+workgroup at the end of the rows, and the closing barrier; per phase (opcode, layer) the moment
+the last CU finished, i.e. the critical path of the launch.
 
     python -m persistent_megakernel_amd.trace --workload tinyllama_int8 --pos 512
 """
@@ -37,12 +37,14 @@ def summarize(sched, trace) -> dict:
     for k, tid in enumerate(order):
         t = sched.tasks[tid]
         op, layer = t.opcode, t.args[0]
-        s, ready, done, end, l0, l1 = rel[k]
+        s, ready, done, end, w0, out = rel[k]
         d = by_op[OPNAMES.get(op, str(op))]
         d["wait"].append(ready - s)
         d["compute"].append(done - ready if op not in (A.AMK_OP_MERGE, A.AMK_OP_ARGMAX) else 0.0)
         d["epilogue"].append(end - (done if op not in (A.AMK_OP_MERGE, A.AMK_OP_ARGMAX) else ready))
-        d["loader_late"].append(max(0.0, l1 - ready))
+        if op in (A.AMK_OP_QKV, A.AMK_OP_OPROJ, A.AMK_OP_GATEUP, A.AMK_OP_DOWN, A.AMK_OP_LM):
+            d["wave_skew"].append(max(0.0, done - w0))
+        d["close"].append(max(0.0, end - out))
         p = phase[(op, layer)]
         p[0] = min(p[0], s)
         p[1] = max(p[1], ready)
@@ -72,7 +74,8 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = the workload's)")
     ap.add_argument("--phases", action="store_true", help="print every phase of the critical path")
-    ap.add_argument("--cfg", nargs="*", default=[], help="lowering knobs, e.g. loader_depth=56 attn_chunks=8")
+    ap.add_argument("--cfg", nargs="*", default=[], help="lowering knobs, e.g. attn_chunks=8 tasks_lm=256")
+    ap.add_argument("--raw", default=None, help="also save per-task records (op, layer, cu, 6 timestamps) to this .npz")
     args = ap.parse_args(argv)
     from . import schedule_config
     cfg = schedule_config(**{k: int(v) for k, v in (kv.split("=") for kv in args.cfg)}) if args.cfg else None
@@ -89,8 +92,15 @@ def main(argv=None) -> int:
     tok = int(I.prompt_tokens(shape, 1, stream=5)[0])
     run_steps(dec, [tok] * args.steps, args.pos, chain_from=1)
     torch.cuda.synchronize()
-    res = summarize(dec.schedule(), trace.cpu().numpy())
+    sched = dec.schedule()
+    res = summarize(sched, trace.cpu().numpy())
     res["cfg"] = args.cfg
+    if args.raw:
+        order = [t for q in sched.queues for t in q]
+        cu = [c for c, q in enumerate(sched.queues) for _ in q]
+        np.savez(args.raw, op=np.array([sched.tasks[t].opcode for t in order]),
+                 layer=np.array([sched.tasks[t].args[0] for t in order]), cu=np.array(cu),
+                 args=np.array([sched.tasks[t].args[1:] for t in order]), ts=trace.cpu().numpy())
     if not args.phases:
         res["phases"] = res["phases"][:12] + res["phases"][-4:]
     print(json.dumps(res, indent=1))

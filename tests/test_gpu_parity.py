@@ -109,11 +109,10 @@ def test_tiny_fp32_protocol(M):
 
 
 @pytest.mark.parametrize("cfg_kw", [dict(n_cu=1), dict(n_cu=7, cu_assign=1), dict(attn_chunks=3, attn_group_tasks=1),
-                                    dict(tasks_qkv=3, tasks_o=5, tasks_gateup=2, tasks_down=9, tasks_lm=4,
-                                         ring_kb=12, loader_depth=8)])
+                                    dict(tasks_qkv=3, tasks_o=5, tasks_gateup=2, tasks_down=9, tasks_lm=4)])
 def test_tiny_fp32_schedules(M, cfg_kw):
     """The same result under other valid lowerings: one CU, seven CUs round robin, split
-    context with a merge, uneven tiles with a 12 KiB ring."""
+    context with a merge, uneven tiles."""
     shape = I.SHAPES["tiny_fp32"].replace(n_generate=4)
     log(f"case tiny_fp32 schedule {cfg_kw}")
     r = _run(M, shape, I.make_weights(shape), I.prompt_tokens(shape), 4, cfg=M.schedule_config(**cfg_kw))
