@@ -150,7 +150,8 @@ typedef struct {
     int32_t n_cu;              /* queues = workgroups; 0 = the device's CU count (amk_lower: 256) */
     int32_t tasks_qkv, tasks_o, tasks_gateup, tasks_down, tasks_lm;   /* tasks per GEMV phase (0 = min(n_cu, units)) */
     int32_t attn_chunks;       /* context chunks per attention head group (0 = auto: 1 below 256 cache
-                                  rows, else enough chunks to give every CU one attention task) */
+                                  rows, else the least of: CUs per head group, cache rows / 32, and
+                                  the chunks whose merge states fit LDS) */
     int32_t attn_group_tasks;  /* 1: one attention task per KV group (up to 8 query heads), 2: one per
                                   query head, 0: auto (grouped whenever KV heads are shared) */
     int32_t cu_assign;         /* 0 = XCD-aware (unchunked attention of one KV group on one XCD; chunked

@@ -143,7 +143,7 @@ extern "C" amk_status amk_create(const amk_model_desc* desc, const amk_weights* 
     // ---- co-residency of one workgroup per CU
     int coop = 0;
     (void)hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
-    if (!coop || megakernel_blocks_per_cu() < 1) { delete c; return AMK_E_NOT_RESIDENT; }
+    if (!coop || megakernel_blocks_per_cu(desc->wfmt) < 1) { delete c; return AMK_E_NOT_RESIDENT; }
 
     // ---- device buffers
     const LLLayout y = ll_layout(d.hidden, d.n_layers, d.n_heads, d.n_kv_heads, d.head_dim, d.intermediate, d.act_f32,

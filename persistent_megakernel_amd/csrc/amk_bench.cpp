@@ -90,6 +90,7 @@ int copy_calibration(size_t mib) {
     for (int i = 0; i < 3; ++i) CK(hipMemcpy(b, a, n, hipMemcpyDeviceToDevice));
     CK(hipDeviceSynchronize());
     std::printf("{\"copy_bytes\": %zu, \"copies\": 3}\n", n);
+    std::fflush(stdout);
     CK(hipFree(a));
     CK(hipFree(b));
     return 0;
@@ -188,6 +189,7 @@ int main(int argc, char** argv) {
     std::printf("{\"workload\": \"%s\", \"steps\": %d, \"start_pos\": %d, \"us_per_token\": %.3f, "
                 "\"tokens_per_s\": %.1f, \"device_status\": %u}\n",
                 s->name, steps, pos0, 1e3 * ms / steps, 1e3 * steps / ms, status);
+    std::fflush(stdout);
     amk_destroy(ctx);
     CK(hipFree(tok));
     CK(hipFree(kv));

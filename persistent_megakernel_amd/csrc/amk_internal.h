@@ -35,8 +35,8 @@ constexpr int kTaskCache = 256;             // task descriptors of a CU's queue 
 #define AMK_AHEAD_GROUPS 1
 #endif
 constexpr int kLoadSlots = AMK_LOAD_SLOTS;  // 1 KiB (16 B per lane) weight loads per register buffer (2 buffers per wave)
-constexpr int kAheadGroups = AMK_AHEAD_GROUPS;   // groups of the next task's weights issued ahead (1 or 2)
-static_assert(kAheadGroups == 1 || kAheadGroups == 2, "prefetch depth");
+constexpr int kAheadGroups = AMK_AHEAD_GROUPS;   // groups of the next task's weights issued ahead (0, 1 or 2)
+static_assert(kAheadGroups >= 0 && kAheadGroups <= 2, "prefetch depth");
 constexpr int kAttnBlock = 64;              // positions per attention unit
 constexpr int kMaxAttnHeads = 8;            // query heads per attention task
 constexpr int kChunkedCtx = 256;            // caches at least this long get context-split attention by default

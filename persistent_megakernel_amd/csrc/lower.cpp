@@ -486,7 +486,7 @@ amk_status lower_model(const amk_model_desc& d, const amk_schedule_config* cfg, 
         nc = 1;
         if (d.max_ctx >= kChunkedCtx) {   // long caches: split the context so every CU streams a piece
             const int by_cu = std::max(1, n_cu / n_head_tasks);
-            const int by_ctx = std::max(1, d.max_ctx / 128);   // about 128 positions per chunk at full cache
+            const int by_ctx = std::max(1, d.max_ctx / 32);   // about 32 positions per chunk at full cache
             nc = std::max(1, std::min(std::min(by_cu, by_ctx), nc_max));
         }
     }

@@ -12,10 +12,10 @@
 //  * Workgroup = 8 waves of 64 lanes, one per CU; all waves walk the queue together.
 //  * Weights are streamed by the waves that use them, straight into registers: wave w owns rows
 //    w, w + 8, ... of every GEMV tile and loads each row as 1 KiB wave loads (16 bytes per lane),
-//    kLoadSlots loads at a time. The first loads of the next task are issued as soon as the
-//    current task's rows are done (or, for tasks without weights, when they start), so the HBM
-//    latency of the next phase overlaps the wait for its inputs from other CUs. GEMV is
-//    HBM-bound: one multiply-add per weight element, no MFMA.
+//    kLoadSlots loads per register buffer, two buffers. The first group of the next task's loads
+//    is issued as soon as the current task's outputs are out, so the HBM latency of the next
+//    phase overlaps the wait for its inputs from other CUs. GEMV is HBM-bound: one multiply-add
+//    per weight element, no MFMA.
 //  * The input vector of a GEMV (after the fused RMSNorm) is staged once in LDS; each lane reads
 //    the slice matching its weight bytes. Row sums are reduced across the wave with DPP moves.
 //  * Attention stages the K and V rows of its positions in LDS with plain vector loads issued
@@ -348,15 +348,16 @@ DEV void compute_group(const Lds& S_, const Geo& s, int cw, uint32_t K, uint32_t
 }
 
 // All groups of the wave's rows of task T, double-buffered: while one buffer is consumed the
-// other is in flight. On entry A holds group 0 and, with kAheadGroups == 2, B holds group 1
-// (issued ahead, and complete: the input staging waited for every load).
+// other is in flight. On entry A holds group 0 (kAheadGroups >= 1) and B group 1
+// (kAheadGroups == 2), issued ahead and complete: the input staging waited for every load.
 template <int FMT>
 DEV void gemv_rows_fmt(const Ctx& c, const DevTask& T, int cw, WBuf& A, WBuf& B) {
     const Geo s = geo_of(c, T, cw);
     const uint32_t K = K_of(*c.P, T.op);
     // nothing is in flight here; saying so lets the compiler count exactly from this point
     __builtin_amdgcn_s_waitcnt(kWaitVmem0);
-    if (kAheadGroups == 1 && s.ng > 1) issue_group(c, s, 1, B);
+    if (kAheadGroups == 0 && s.ng > 0) issue_group(c, s, 0, A);
+    if (kAheadGroups <= 1 && s.ng > 1) issue_group(c, s, 1, B);
     float acc = 0.f;
     uint32_t g = 0;
     for (; g + 2 < s.ng; g += 2) {
@@ -371,6 +372,7 @@ DEV void gemv_rows_fmt(const Ctx& c, const DevTask& T, int cw, WBuf& A, WBuf& B)
 
 // Issue the first groups of task T's weights (the next task's, ahead of its inputs).
 DEV void prefetch_task(const Ctx& c, const DevTask& T, int cw, WBuf& A, WBuf& B) {
+    if (kAheadGroups == 0) return;
     const Geo s = geo_of(c, T, cw);
     if (s.ng > 0) issue_group(c, s, 0, A);
     if (kAheadGroups == 2 && s.ng > 1) issue_group(c, s, 1, B);
@@ -442,6 +444,16 @@ DEV void hput(const KParams& P, Lds& S, uint32_t i, float v) {
 
 DEV u64* ll_layer(const KParams& P, const LLLayout& y, int layer) { return P.ll + (u64)layer * y.layer_words; }
 
+// The RMSNorm gains of a GEMV task's input (null for inputs without a norm).
+DEV const float* gains_of(const KParams& P, const DevTask& T) {
+    switch (T.op) {
+    case AMK_OP_QKV: return P.norms + (uint64_t)T.layer * 2 * P.H;
+    case AMK_OP_GATEUP: return P.norms + ((uint64_t)T.layer * 2 + 1) * P.H;
+    case AMK_OP_LM: return P.norms + (uint64_t)P.L * 2 * P.H;
+    default: return nullptr;
+    }
+}
+
 constexpr int kMaxGainsPerThread = kMaxHidden / kComputeThreads;
 
 // Stage the GEMV input of a task into S.hb (activation format), with RMSNorm when gains != 0.
@@ -483,7 +495,7 @@ DEV bool stage_input(const Ctx& c, int ctid, uint32_t& gen, const u64* src, cons
     }
     if (!gains) return cbar(c, gen);
     // RMSNorm: h_i = round_act(x_i * r * g_i), r = 1 / sqrt(mean(x^2) + eps)
-    ss = wave_sum(ss);
+    ss = wave_sum_dpp(ss);
     const int cw = ctid >> 6;
     if (lane_id() == 0) S.fpart[cw] = ss;
     if (!cbar(c, gen)) return false;
@@ -530,20 +542,19 @@ DEV bool op_gemv(const TaskEnv& e, const DevTask& T, WBuf& A, WBuf& B) {
     const uint32_t vpw = P.act_f32 ? 1u : 2u;
     const u64* src = nullptr;
     const void* emb = nullptr;
-    const float* gains = nullptr;
     const uint64_t esz = act_bytes(P);
     const u64* LLl = ll_layer(P, e.y, l);
     switch (op) {
     case AMK_OP_QKV:
         if (l == 0) emb = (const uint8_t*)P.embed + (uint64_t)e.token * P.H * esz;
         else src = ll_layer(P, e.y, l - 1) + e.y.xd;
-        gains = P.norms + (uint64_t)l * 2 * P.H;
         break;
     case AMK_OP_OPROJ: src = LLl + e.y.o; break;
-    case AMK_OP_GATEUP: src = LLl + e.y.xo; gains = P.norms + ((uint64_t)l * 2 + 1) * P.H; break;
+    case AMK_OP_GATEUP: src = LLl + e.y.xo; break;
     case AMK_OP_DOWN: src = LLl + e.y.a; break;
-    case AMK_OP_LM: src = ll_layer(P, e.y, P.L - 1) + e.y.xd; gains = P.norms + (uint64_t)P.L * 2 * P.H; break;
+    case AMK_OP_LM: src = ll_layer(P, e.y, P.L - 1) + e.y.xd; break;
     }
+
     // quantised tiles: the row scales (int8) or group scales (int4) go to LDS. Any wait below
     // waits for the weight loads already in flight too, so these loads cost no extra latency.
     const uint32_t sc_chunks = (uint32_t)((tile_bytes(P.wfmt, K, T.tile_rows) - tile_scale_off(P.wfmt, K, T.tile_rows)) / 16);
@@ -576,7 +587,7 @@ DEV bool op_gemv(const TaskEnv& e, const DevTask& T, WBuf& A, WBuf& B) {
                 return false;
         }
     }
-    if (!stage_input(c, ctid, *e.gen, src, emb, K, gains)) return false;   // ends with a barrier
+    if (!stage_input(c, ctid, *e.gen, src, emb, K, gains_of(P, T))) return false;   // ends with a barrier
     mark(e, 1);
     gemv_rows(c, T, e.cw, A, B);
     if (e.tr && ctid == 0) e.tr[4] = rt();
@@ -645,7 +656,7 @@ DEV bool op_gemv(const TaskEnv& e, const DevTask& T, WBuf& A, WBuf& B) {
         u64* out = (u64*)(LLl + e.y.a) + j0 / vpw;
         for (uint32_t i = (uint32_t)ctid; i < n / vpw; i += kComputeThreads) {
             float v[2] = {0.f, 0.f};
-            #pragma unroll
+#pragma unroll
             for (uint32_t j = 0; j < 2; ++j) {
                 if (j >= vpw) break;
                 const float G = S.red[2 * (i * vpw + j)], U = S.red[2 * (i * vpw + j) + 1];
@@ -703,7 +714,9 @@ constexpr int kAttF = kAttVc + 128;               // [kComputeWaves][kMaxAttnHea
 constexpr int kAttM = kAttF + kComputeWaves * kMaxAttnHeads;   // [kMaxAttnHeads] maxima
 static_assert(kAttM + kMaxAttnHeads <= kAttnLds / 4, "attention LDS map");
 constexpr int kAttMaxD = 8;                       // dims per lane: hd / lanes-per-head (the lowering keeps it <= 8)
-constexpr int kKvLoads = kKvBytes / 16 / kComputeThreads;   // 16-byte K/V loads per thread per round
+constexpr int kAttBatch = 4;                      // history positions a wave scores at once
+constexpr int kKvRound = kKvBytes;               // bytes of K and V rows staged per round
+constexpr int kKvLoads = kKvRound / 16 / kComputeThreads;   // 16-byte K/V loads per thread per round
 
 // This lane's D consecutive values [d0, d0 + D) of the staged K or V row at `p`, as fp32, read
 // with vector LDS loads (the slice is aligned to its own size: d0 is a multiple of D).
@@ -799,7 +812,7 @@ DEV bool op_attn(const TaskEnv& e, const DevTask& T) {
     chunk_range(P.pos, ch, nc, p0, p1);
     const uint32_t nhist = p1 - p0;
     const uint32_t rowb = kv_row_bytes(P);
-    const uint32_t per_round = (uint32_t)kKvBytes / (2 * rowb);   // history positions per LDS round
+    const uint32_t per_round = (uint32_t)kKvRound / (2 * rowb);   // history positions per LDS round
     // the first round's K/V loads go out before the wait for q
     u32x4 kvr[kKvLoads];
     uint32_t ra = p0, rn = min(per_round, nhist);
@@ -863,9 +876,51 @@ DEV bool op_attn(const TaskEnv& e, const DevTask& T) {
             if ((uint32_t)k < D) o[k] = o[k] * alpha + pw * kv[k];
         m = mn;
     };
-    // history rounds
+    // history rounds: each wave takes kAttBatch positions at a time (positions w, w + 8, ...), so
+    // the lane-group reductions of their scores overlap and the running state is rescaled once
+    // per batch
     while (rn) {
-        for (uint32_t i = (uint32_t)cw; i < rn; i += kComputeWaves) step(S.kvb + i * rowb, S.kvb + (rn + i) * rowb);
+        for (uint32_t i0 = (uint32_t)cw; i0 < rn; i0 += kComputeWaves * kAttBatch) {
+            float sc[kAttBatch];
+#pragma unroll
+            for (int u = 0; u < kAttBatch; ++u) {
+                const uint32_t i = i0 + (uint32_t)u * kComputeWaves;
+                float sdot = 0.f;
+                if (i < rn) {
+                    kv_slice(P, S.kvb + i * rowb, dg * D, D, kv);
+#pragma unroll
+                    for (int k = 0; k < kAttMaxD; ++k)
+                        if ((uint32_t)k < D) sdot += qr[k] * kv[k];
+                }
+                sc[u] = sdot;
+            }
+            for (uint32_t off = L >> 1; off >= 1; off >>= 1)
+#pragma unroll
+                for (int u = 0; u < kAttBatch; ++u) sc[u] += __shfl_xor(sc[u], (int)off, 64);
+            float mb = m;
+#pragma unroll
+            for (int u = 0; u < kAttBatch; ++u) {
+                sc[u] = i0 + (uint32_t)u * kComputeWaves < rn ? sc[u] * scale : -INFINITY;
+                mb = fmaxf(mb, sc[u]);
+            }
+            const float alpha = expf(m - mb);
+            lsum *= alpha;
+#pragma unroll
+            for (int k = 0; k < kAttMaxD; ++k) o[k] *= alpha;
+#pragma unroll
+            for (int u = 0; u < kAttBatch; ++u) {
+                const uint32_t i = i0 + (uint32_t)u * kComputeWaves;
+                if (i < rn) {
+                    const float pw = expf(sc[u] - mb);
+                    lsum += pw;
+                    kv_slice(P, S.kvb + (rn + i) * rowb, dg * D, D, kv);
+#pragma unroll
+                    for (int k = 0; k < kAttMaxD; ++k)
+                        if ((uint32_t)k < D) o[k] += pw * kv[k];
+                }
+            }
+            m = mb;
+        }
         const uint32_t na = ra + rn, nn = min(per_round, p1 - na);
         if (!nn) break;
         if (!cbar(c, *e.gen)) return false;   // every wave is done with this round's rows
@@ -903,7 +958,7 @@ DEV bool op_attn(const TaskEnv& e, const DevTask& T) {
         u64* out = ll_layer(P, e.y, l) + e.y.o + (uint64_t)h0 * hd / vpw;
         for (uint32_t i = (uint32_t)ctid; i < nh * hd / vpw; i += kComputeThreads) {
             float v[2] = {0.f, 0.f};
-            #pragma unroll
+#pragma unroll
             for (uint32_t j = 0; j < 2; ++j) {
                 if (j >= vpw) break;
                 const uint32_t t = i * vpw + j, h = t / hd, d = t % hd;
@@ -970,19 +1025,39 @@ DEV bool op_merge(const TaskEnv& e, const DevTask& T) {
         if (lane_id() == 0) Lh[h] = Ls;
     }
     if (!cbar(c, *e.gen)) return false;
+    // output words: G consecutive lanes share a word, each summing every G-th chunk, then the G
+    // partial sums are added across those lanes
     u64* out = ll_layer(P, e.y, l) + e.y.o + (uint64_t)h0 * hd / vpw;
-    for (uint32_t i = (uint32_t)ctid; i < nh * hd / vpw; i += kComputeThreads) {
+    const uint32_t nwords = nh * hd / vpw;
+    uint32_t G = 1;
+    while (2 * G <= nc && 2 * G <= 64 && nwords * 2 * G <= (uint32_t)kComputeThreads) G *= 2;
+    for (uint32_t w0 = 0; w0 < nwords; w0 += kComputeThreads / G) {
+        const uint32_t i = w0 + (uint32_t)ctid / G, k0 = (uint32_t)ctid % G;
         float v[2] = {0.f, 0.f};
-        #pragma unroll
-        for (uint32_t j = 0; j < 2; ++j) {
-            if (j >= vpw) break;
-            const uint32_t t = i * vpw + j, h = t / hd, d = t % hd;
-            const float* base = S.hf + (uint64_t)h * nc * st;
-            float os = 0.f;
-            for (uint32_t k = 0; k < nc; ++k) os += base[k * st] * base[k * st + 2 + d];
-            v[j] = rA(P, os / Lh[h]);
+        if (i < nwords) {
+#pragma unroll
+            for (uint32_t j = 0; j < 2; ++j) {
+                if (j >= vpw) break;
+                const uint32_t t = i * vpw + j, h = t / hd, d = t % hd;
+                const float* base = S.hf + (uint64_t)h * nc * st;
+                float os = 0.f;
+                for (uint32_t k = k0; k < nc; k += G) os += base[k * st] * base[k * st + 2 + d];
+                v[j] = os;
+            }
         }
-        ll_store(out + i, pack2(P, v[0], v[1]), P.flag);
+        for (uint32_t off = G >> 1; off >= 1; off >>= 1) {
+            v[0] += __shfl_xor(v[0], (int)off, 64);
+            v[1] += __shfl_xor(v[1], (int)off, 64);
+        }
+        if (i < nwords && k0 == 0) {
+            float r[2] = {0.f, 0.f};
+#pragma unroll
+            for (uint32_t j = 0; j < 2; ++j) {
+                if (j >= vpw) break;
+                r[j] = rA(P, v[j] / Lh[(i * vpw + j) / hd]);
+            }
+            ll_store(out + i, pack2(P, r[0], r[1]), P.flag);
+        }
     }
     return true;
 }
@@ -1053,7 +1128,7 @@ DEV void compute_run(const Ctx& c) {
     e.token = tok;
     WBuf A, B;
     const uint32_t q0 = P.queue_off[c.cu], q1 = P.queue_off[c.cu + 1];
-    // the first task's weights, if it has any
+    // the first task's gains and weights, if it has any
     if (q0 < q1) {
         const DevTask F = task_at(c, q0, q0);
         if (is_gemv(F.op)) prefetch_task(c, F, cw, A, B);
@@ -1087,10 +1162,15 @@ DEV void compute_run(const Ctx& c) {
     }
 }
 
-}  // namespace
-
-extern "C" __global__ void __launch_bounds__(kThreads, 1) amk_megakernel(KParams P) {
+// The kernel body for one weight format. The format (and with it the activation type: fp32
+// with fp32 weights, bf16 otherwise) is a compile-time constant, so each kernel carries only
+// its own code path.
+template <int FMT>
+DEV void megakernel_body(const KParams& Pin) {
     __shared__ Lds S;
+    KParams P = Pin;
+    P.wfmt = FMT;
+    P.act_f32 = FMT == AMK_F32 ? 1 : 0;
     const int tid = threadIdx.x;
     if (tid == 0) { S.bar = 0; S.abort_ = 0; }
     {   // copy the head of this CU's task queue to LDS (8 dwords per task)
@@ -1110,6 +1190,24 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) amk_megakernel(KParams
     compute_run(c);
 }
 
+}  // namespace
+
+extern "C" __global__ void __launch_bounds__(kThreads, 1) amk_megakernel_f32(KParams P) { megakernel_body<AMK_F32>(P); }
+extern "C" __global__ void __launch_bounds__(kThreads, 1) amk_megakernel_bf16(KParams P) { megakernel_body<AMK_BF16>(P); }
+extern "C" __global__ void __launch_bounds__(kThreads, 1) amk_megakernel_int8(KParams P) { megakernel_body<AMK_INT8_PC>(P); }
+extern "C" __global__ void __launch_bounds__(kThreads, 1) amk_megakernel_int4(KParams P) { megakernel_body<AMK_INT4_G128>(P); }
+
+namespace {
+const void* kernel_for(int wfmt) {
+    switch (wfmt) {
+    case AMK_F32: return (const void*)amk_megakernel_f32;
+    case AMK_BF16: return (const void*)amk_megakernel_bf16;
+    case AMK_INT8_PC: return (const void*)amk_megakernel_int8;
+    default: return (const void*)amk_megakernel_int4;
+    }
+}
+}  // namespace
+
 }  // namespace amk
 
 namespace amk {
@@ -1117,12 +1215,12 @@ namespace amk {
 hipError_t launch_megakernel(const KParams& p, int n_cu, hipStream_t st) {
     KParams local = p;
     void* args[] = {&local};
-    return hipLaunchCooperativeKernel((const void*)amk_megakernel, dim3(n_cu), dim3(kThreads), args, 0, st);
+    return hipLaunchCooperativeKernel(kernel_for(p.wfmt), dim3(n_cu), dim3(kThreads), args, 0, st);
 }
 
-int megakernel_blocks_per_cu() {
+int megakernel_blocks_per_cu(int wfmt) {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, (const void*)amk_megakernel, kThreads, 0) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel_for(wfmt), kThreads, 0) != hipSuccess) return 0;
     return nb;
 }
 

@@ -16,7 +16,7 @@ hipError_t launch_norms(const void* src, int wfmt, uint32_t n, float* dst, hipSt
 
 // The persistent kernel: one cooperative launch of n_cu workgroups of kThreads.
 hipError_t launch_megakernel(const KParams& p, int n_cu, hipStream_t st);
-// Workgroups of the megakernel that fit on one CU (0 = it cannot run).
-int megakernel_blocks_per_cu();
+// Workgroups of the megakernel for weight format wfmt that fit on one CU (0 = it cannot run).
+int megakernel_blocks_per_cu(int wfmt);
 
 }  // namespace amk
