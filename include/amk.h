@@ -222,7 +222,9 @@ amk_status amk_create(const amk_model_desc* desc, const amk_weights* weights, vo
  * A token outside [0, vocab) is replaced by 0 and flagged in the device status word. A
  * watchdog timeout in an earlier step (bounded spin-waits; only reachable with an invalid
  * schedule or broken hardware) is reported here as AMK_E_DEVICE_TIMEOUT without launching;
- * destroy and re-create the context to recover. */
+ * destroy and re-create the context to recover. A step that timed out still ends (its waits
+ * give up and the launch runs to completion), but its outputs and the cache row it appends
+ * at `pos` are unspecified. */
 amk_status amk_decode_step(amk_ctx* ctx, const int32_t* token_in, int32_t pos, int32_t* token_out,
                            float* logits, void* stream);
 

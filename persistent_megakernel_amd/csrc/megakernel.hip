@@ -53,7 +53,6 @@ struct __attribute__((aligned(16))) Lds {
     float red[kRedRows];               // per-row GEMV results of the current task
     float att[kAttnLds / 4];           // attention q / current k, v; residual rows; reductions
     DevTask tcache[kTaskCache];        // the first kTaskCache tasks of this CU's queue
-    uint32_t bar;                      // workgroup barrier counter (monotone)
     uint32_t abort_;                   // this workgroup gives up
     float fpart[2 * kComputeWaves];
     int32_t ipart[2 * kComputeWaves];
@@ -80,14 +79,6 @@ DEV float h2f(uint32_t h) {
     return (float)x;
 }
 
-DEV float wave_sum(float v) {
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
-}
-DEV float wave_max(float v) {
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
-}
 // Sum over the 64 lanes with DPP moves: an inclusive scan inside each row of 16 lanes (row
 // shifts by 1, 2, 4, 8), then the row totals are carried by row broadcasts 15 and 31; the total
 // ends in lane 63 and is returned to every lane.
@@ -101,6 +92,21 @@ DEV float wave_sum_dpp(float v) {
     AMK_DPP_ADD(0x142, 0xa);   // row_bcast:15 into rows 1 and 3
     AMK_DPP_ADD(0x143, 0xc);   // row_bcast:31 into rows 2 and 3
 #undef AMK_DPP_ADD
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// Maximum over the 64 lanes with the same DPP pattern as wave_sum_dpp.
+DEV float wave_max_dpp(float v) {
+#define AMK_DPP_MAX(ctrl, rmask) \
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, -INFINITY), \
+                                                                     __builtin_bit_cast(int, v), ctrl, rmask, 0xf, false)))
+    AMK_DPP_MAX(0x111, 0xf);
+    AMK_DPP_MAX(0x112, 0xf);
+    AMK_DPP_MAX(0x114, 0xf);
+    AMK_DPP_MAX(0x118, 0xf);
+    AMK_DPP_MAX(0x142, 0xa);
+    AMK_DPP_MAX(0x143, 0xc);
+#undef AMK_DPP_MAX
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
@@ -144,13 +150,14 @@ DEV void raise_timeout(const Ctx& c) {
     __hip_atomic_store(&c.P->status[0], kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-// spin step of every wait: bounded by the watchdog and by the global abort flag. The global
-// flag is a device-coherent load (a memory round trip), so it is read only every 4096 spins;
-// another workgroup sets it only after its own watchdog (far longer) expired.
+// spin step of every wait: bounded by the watchdog and by the global abort flag. The clock is
+// read on the first spin of a wait and every 16 spins after it; the global flag is a
+// device-coherent load (a memory round trip), so it is read only every 4096 spins (another
+// workgroup sets it only after its own watchdog, which is far longer, expired).
 DEV bool spin_ok(const Ctx& c, uint32_t& n) {
-    if (((++n) & 63u) == 0) {
+    if (((++n) & 15u) == 1) {
         if (rt() > c.deadline) { raise_timeout(c); return false; }
-        if ((n & 0xfffu) == 0 &&
+        if ((n & 0xfffu) == 1 &&
             __hip_atomic_load(c.P->abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
             __hip_atomic_store(&c.S->abort_, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             return false;
@@ -161,21 +168,11 @@ DEV bool spin_ok(const Ctx& c, uint32_t& n) {
     return true;
 }
 
-// barrier of the workgroup's waves; watchdog-bounded like every wait
-DEV bool cbar(const Ctx& c, uint32_t& gen) {
-    gen += kComputeWaves;
-    bool ok = true;
-    if (lane_id() == 0) {
-        __hip_atomic_fetch_add(&c.S->bar, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-        uint32_t n = 0;
-        while ((int)(__hip_atomic_load(&c.S->bar, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) - gen) < 0) {
-            if (!spin_ok(c, n)) { ok = false; break; }
-        }
-    }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    return __shfl(ok ? 1 : 0, 0, 64) != 0;
-}
+// Barrier of the workgroup's waves: the hardware barrier. It has no timeout, so the kernel keeps
+// one rule: every wave runs the same sequence of barriers whatever happens. Waits that give up
+// (watchdog, abort) just return; no wave leaves its task or its queue early, so a barrier never
+// waits for a wave that will not come.
+DEV void cbar() { __syncthreads(); }
 
 // ------------------------------------------------------------------ task geometry
 
@@ -459,7 +456,7 @@ constexpr int kMaxGainsPerThread = kMaxHidden / kComputeThreads;
 // Stage the GEMV input of a task into S.hb (activation format), with RMSNorm when gains != 0.
 // Source: flag-carrying words (src) or, for layer 0, the embedding row of the input token. The
 // thread's norm gains are loaded before the wait so their latency overlaps it.
-DEV bool stage_input(const Ctx& c, int ctid, uint32_t& gen, const u64* src, const void* embed_row, uint32_t K,
+DEV void stage_input(const Ctx& c, int ctid, const u64* src, const void* embed_row, uint32_t K,
                      const float* gains) {
     const KParams& P = *c.P;
     Lds& S = *c.S;
@@ -476,15 +473,14 @@ DEV bool stage_input(const Ctx& c, int ctid, uint32_t& gen, const u64* src, cons
     float ss = 0.f;
     // raw values go to the stage first (exact: they are activation-format values)
     if (src) {
-        if (!ll_gather(c, src, nw, ctid, [&](uint32_t i, uint32_t pl) {
+        (void)ll_gather(c, src, nw, ctid, [&](uint32_t i, uint32_t pl) {
                 for (uint32_t j = 0; j < vpw; ++j) {
                     float v = word_val(P, pl, (int)j);
                     ss += v * v;
                     if (P.act_f32) S.hf[i * vpw + j] = v;
                     else ((uint16_t*)S.hb)[i * vpw + j] = (uint16_t)(j ? (pl >> 16) : (pl & 0xffffu));
                 }
-            }))
-            return false;
+            });
     } else {
         for (uint32_t i = (uint32_t)ctid; i < K; i += kComputeThreads) {
             float v;
@@ -493,12 +489,15 @@ DEV bool stage_input(const Ctx& c, int ctid, uint32_t& gen, const u64* src, cons
             ss += v * v;
         }
     }
-    if (!gains) return cbar(c, gen);
+    if (!gains) {
+        cbar();
+        return;
+    }
     // RMSNorm: h_i = round_act(x_i * r * g_i), r = 1 / sqrt(mean(x^2) + eps)
     ss = wave_sum_dpp(ss);
     const int cw = ctid >> 6;
     if (lane_id() == 0) S.fpart[cw] = ss;
-    if (!cbar(c, gen)) return false;
+    cbar();
     float tot = 0.f;
     for (int w = 0; w < kComputeWaves; ++w) tot += S.fpart[w];
     const float r = 1.0f / __fsqrt_rn(tot / (float)K + P.eps);
@@ -510,7 +509,7 @@ DEV bool stage_input(const Ctx& c, int ctid, uint32_t& gen, const u64* src, cons
             hput(P, S, i, rA(P, (x * r) * gr[k]));
         }
     }
-    return cbar(c, gen);
+    cbar();
 }
 
 // ------------------------------------------------------------------ the ops
@@ -518,7 +517,6 @@ DEV bool stage_input(const Ctx& c, int ctid, uint32_t& gen, const u64* src, cons
 struct TaskEnv {
     const Ctx* c;
     int ctid, cw;
-    uint32_t* gen;
     LLLayout y;
     int token;
     uint64_t* tr;        // this task's trace slots, or null
@@ -533,7 +531,7 @@ DEV void mark(const TaskEnv& e, int k) {
 // the tile's rows, then the op's epilogue: RoPE and the KV-cache append (QKV), the residual add
 // (O, down), SwiGLU (gate/up), the tile argmax and logits (LM head). On entry the first groups
 // of this task's weight loads are in A (and B), issued ahead.
-DEV bool op_gemv(const TaskEnv& e, const DevTask& T, WBuf& A, WBuf& B) {
+DEV void op_gemv(const TaskEnv& e, const DevTask& T, WBuf& A, WBuf& B) {
     const Ctx& c = *e.c;
     const KParams& P = *c.P;
     Lds& S = *c.S;
@@ -581,17 +579,16 @@ DEV bool op_gemv(const TaskEnv& e, const DevTask& T, WBuf& A, WBuf& B) {
                 S.att[i] = P.act_f32 ? ((const float*)er)[r0 + i] : bf2f(((const uint16_t*)er)[r0 + i]);
         } else {
             const u64* rs = (op == AMK_OP_OPROJ ? ll_layer(P, e.y, l - 1) + e.y.xd : LLl + e.y.xo) + r0 / vpw;
-            if (!ll_gather(c, rs, n / vpw, ctid, [&](uint32_t i, uint32_t pl) {
+            (void)ll_gather(c, rs, n / vpw, ctid, [&](uint32_t i, uint32_t pl) {
                     for (uint32_t j = 0; j < vpw; ++j) S.att[i * vpw + j] = word_val(P, pl, (int)j);
-                }))
-                return false;
+                });
         }
     }
-    if (!stage_input(c, ctid, *e.gen, src, emb, K, gains_of(P, T))) return false;   // ends with a barrier
+    stage_input(c, ctid, src, emb, K, gains_of(P, T));   // ends with a barrier
     mark(e, 1);
     gemv_rows(c, T, e.cw, A, B);
     if (e.tr && ctid == 0) e.tr[4] = rt();
-    if (!cbar(c, *e.gen)) return false;
+    cbar();
     mark(e, 2);
     const uint32_t flag = P.flag;
     switch (op) {
@@ -684,7 +681,7 @@ DEV bool op_gemv(const TaskEnv& e, const DevTask& T, WBuf& A, WBuf& B) {
         }
         const int anynan = __any(nan);
         if (lane_id() == 0) { S.fpart[e.cw] = best; S.ipart[e.cw] = anynan ? -1 : bi; }
-        if (!cbar(c, *e.gen)) return false;
+        cbar();
         if (ctid == 0) {
             float b = S.fpart[0];
             int i0 = S.ipart[0];
@@ -702,7 +699,6 @@ DEV bool op_gemv(const TaskEnv& e, const DevTask& T, WBuf& A, WBuf& B) {
         break;
     }
     }
-    return true;
 }
 
 // LDS map of an attention task inside S.att (floats): q of the task's heads, the current k and v,
@@ -794,7 +790,7 @@ DEV void kv_round_store(const KParams& P, Lds& S, uint32_t n, int ctid, const u3
 // current position (last chunk only) comes from the flag-carrying words. At the end the
 // per-wave states (m, l, o) are combined with weights exp(m_w - M) computed once per (wave,
 // head); a single chunk writes the output row, a split context writes its (M, L, o) state.
-DEV bool op_attn(const TaskEnv& e, const DevTask& T) {
+DEV void op_attn(const TaskEnv& e, const DevTask& T) {
     const Ctx& c = *e.c;
     const KParams& P = *c.P;
     Lds& S = *c.S;
@@ -818,23 +814,20 @@ DEV bool op_attn(const TaskEnv& e, const DevTask& T) {
     uint32_t ra = p0, rn = min(per_round, nhist);
     if (rn) kv_round_issue(P, l, g, ra, rn, ctid, kvr);
     // inputs: q of the task's heads; the current k, v of the group (last chunk only)
-    if (!ll_gather(c, Lq + (uint64_t)h0 * hd / vpw, nh * hd / vpw, ctid, [&](uint32_t i, uint32_t pl) {
+    (void)ll_gather(c, Lq + (uint64_t)h0 * hd / vpw, nh * hd / vpw, ctid, [&](uint32_t i, uint32_t pl) {
             for (uint32_t j = 0; j < vpw; ++j) qs[i * vpw + j] = word_val(P, pl, (int)j);
-        }))
-        return false;
+        });
     if (cur) {
         const uint64_t kofs = ((uint64_t)P.nH + g) * hd / vpw, vofs = ((uint64_t)P.nH + P.nKV + g) * hd / vpw;
-        if (!ll_gather(c, Lq + kofs, hd / vpw, ctid, [&](uint32_t i, uint32_t pl) {
+        (void)ll_gather(c, Lq + kofs, hd / vpw, ctid, [&](uint32_t i, uint32_t pl) {
                 for (uint32_t j = 0; j < vpw; ++j) kc[i * vpw + j] = word_val(P, pl, (int)j);
-            }))
-            return false;
-        if (!ll_gather(c, Lq + vofs, hd / vpw, ctid, [&](uint32_t i, uint32_t pl) {
+            });
+        (void)ll_gather(c, Lq + vofs, hd / vpw, ctid, [&](uint32_t i, uint32_t pl) {
                 for (uint32_t j = 0; j < vpw; ++j) vc[i * vpw + j] = word_val(P, pl, (int)j);
-            }))
-            return false;
+            });
     }
     if (rn) kv_round_store(P, S, rn, ctid, kvr);
-    if (!cbar(c, *e.gen)) return false;
+    cbar();
     mark(e, 1);
     // lane layout
     uint32_t nhp = 1;
@@ -923,10 +916,10 @@ DEV bool op_attn(const TaskEnv& e, const DevTask& T) {
         }
         const uint32_t na = ra + rn, nn = min(per_round, p1 - na);
         if (!nn) break;
-        if (!cbar(c, *e.gen)) return false;   // every wave is done with this round's rows
+        cbar();   // every wave is done with this round's rows
         kv_round_issue(P, l, g, na, nn, ctid, kvr);
         kv_round_store(P, S, nn, ctid, kvr);
-        if (!cbar(c, *e.gen)) return false;
+        cbar();
         ra = na;
         rn = nn;
     }
@@ -941,7 +934,7 @@ DEV bool op_attn(const TaskEnv& e, const DevTask& T) {
         for (int k = 0; k < kAttMaxD; ++k)
             if ((uint32_t)k < D) w[2 + dg * D + k] = o[k];
     }
-    if (!cbar(c, *e.gen)) return false;
+    cbar();
     mark(e, 2);
     // combination weights, once per (wave, head)
     for (uint32_t t = (uint32_t)ctid; t < (uint32_t)kComputeWaves * nh; t += kComputeThreads) {
@@ -952,7 +945,7 @@ DEV bool op_attn(const TaskEnv& e, const DevTask& T) {
         S.att[kAttF + w * kMaxAttnHeads + h] = mw == -INFINITY ? 0.f : expf(mw - M);
         if (w == 0) S.att[kAttM + h] = M;
     }
-    if (!cbar(c, *e.gen)) return false;
+    cbar();
     const uint32_t flag = P.flag;
     if (nc == 1) {   // the output rows, rounded once
         u64* out = ll_layer(P, e.y, l) + e.y.o + (uint64_t)h0 * hd / vpw;
@@ -988,13 +981,12 @@ DEV bool op_attn(const TaskEnv& e, const DevTask& T) {
             ll_store(part + ((uint64_t)(h0 + h) * nc + ch) * st + k, __float_as_uint(v), flag);
         }
     }
-    return true;
 }
 
 // Merge of the context chunks of query heads [h0, h0+nh): o = sum_c exp(M_c - M) o_c divided by
 // sum_c exp(M_c - M) L_c, M = max_c M_c (the split-context form of the same softmax). The
 // weights are computed once per (head, chunk).
-DEV bool op_merge(const TaskEnv& e, const DevTask& T) {
+DEV void op_merge(const TaskEnv& e, const DevTask& T) {
     const Ctx& c = *e.c;
     const KParams& P = *c.P;
     Lds& S = *c.S;
@@ -1003,9 +995,8 @@ DEV bool op_merge(const TaskEnv& e, const DevTask& T) {
     const uint32_t hd = (uint32_t)P.hd, st = hd + 2;
     const uint32_t vpw = P.act_f32 ? 1u : 2u;
     const u64* part = ll_layer(P, e.y, l) + e.y.part + (uint64_t)h0 * nc * st;
-    if (!ll_gather(c, part, nh * nc * st, ctid, [&](uint32_t i, uint32_t pl) { S.hf[i] = __uint_as_float(pl); }))
-        return false;
-    if (!cbar(c, *e.gen)) return false;
+    (void)ll_gather(c, part, nh * nc * st, ctid, [&](uint32_t i, uint32_t pl) { S.hf[i] = __uint_as_float(pl); });
+    cbar();
     mark(e, 1);
     // per head: M, then the chunk weights f_c = exp(M_c - M) (stored over M_c) and L
     float* Lh = S.att;                       // [nh]
@@ -1013,7 +1004,7 @@ DEV bool op_merge(const TaskEnv& e, const DevTask& T) {
         float* base = S.hf + (uint64_t)h * nc * st;
         float M = -INFINITY;
         for (uint32_t k = (uint32_t)lane_id(); k < nc; k += 64) M = fmaxf(M, base[k * st]);
-        M = wave_max(M);
+        M = wave_max_dpp(M);
         float Ls = 0.f;
         for (uint32_t k = (uint32_t)lane_id(); k < nc; k += 64) {
             const float mk = base[k * st];
@@ -1021,10 +1012,10 @@ DEV bool op_merge(const TaskEnv& e, const DevTask& T) {
             Ls += f * base[k * st + 1];
             base[k * st] = f;
         }
-        Ls = wave_sum(Ls);
+        Ls = wave_sum_dpp(Ls);
         if (lane_id() == 0) Lh[h] = Ls;
     }
-    if (!cbar(c, *e.gen)) return false;
+    cbar();
     // output words: G consecutive lanes share a word, each summing every G-th chunk, then the G
     // partial sums are added across those lanes
     u64* out = ll_layer(P, e.y, l) + e.y.o + (uint64_t)h0 * hd / vpw;
@@ -1059,12 +1050,11 @@ DEV bool op_merge(const TaskEnv& e, const DevTask& T) {
             ll_store(out + i, pack2(P, r[0], r[1]), P.flag);
         }
     }
-    return true;
 }
 
 // The greedy token: the argmax over the LM tiles' (max, index) pairs, lowest index among equal
 // maxima; a tile that saw a NaN makes the token -1.
-DEV bool op_argmax(const TaskEnv& e, const DevTask& T) {
+DEV void op_argmax(const TaskEnv& e, const DevTask& T) {
     const Ctx& c = *e.c;
     const KParams& P = *c.P;
     Lds& S = *c.S;
@@ -1074,12 +1064,11 @@ DEV bool op_argmax(const TaskEnv& e, const DevTask& T) {
     int bi = 0x7fffffff;
     bool bad = false;
     // word 2t: value bits, word 2t+1: index (or -1 for a tile with NaN)
-    if (!ll_gather(c, P.ll + e.y.lmpart, 2 * nt, ctid, [&](uint32_t i, uint32_t pl) {
+    (void)ll_gather(c, P.ll + e.y.lmpart, 2 * nt, ctid, [&](uint32_t i, uint32_t pl) {
             if (i & 1) S.hf[i] = __int_as_float((int)pl);
             else S.hf[i] = __uint_as_float(pl);
-        }))
-        return false;
-    if (!cbar(c, *e.gen)) return false;
+        });
+    cbar();
     mark(e, 1);
     for (uint32_t t = (uint32_t)ctid; t < nt; t += kComputeThreads) {
         const float v = S.hf[2 * t];
@@ -1094,7 +1083,7 @@ DEV bool op_argmax(const TaskEnv& e, const DevTask& T) {
     }
     const int anybad = __any(bad);
     if (lane_id() == 0) { S.fpart[e.cw] = best; S.ipart[e.cw] = anybad ? -1 : bi; }
-    if (!cbar(c, *e.gen)) return false;
+    cbar();
     if (ctid == 0) {
         float b = S.fpart[0];
         int i0 = S.ipart[0];
@@ -1105,7 +1094,6 @@ DEV bool op_argmax(const TaskEnv& e, const DevTask& T) {
         }
         P.tok_out[0] = badn ? -1 : i0;
     }
-    return true;
 }
 
 DEV void compute_run(const Ctx& c) {
@@ -1113,12 +1101,10 @@ DEV void compute_run(const Ctx& c) {
     Lds& S = *c.S;
     const int ctid = (int)threadIdx.x;
     const int cw = __builtin_amdgcn_readfirstlane(ctid >> 6);
-    uint32_t gen = 0;
     TaskEnv e;
     e.c = &c;
     e.ctid = ctid;
     e.cw = cw;
-    e.gen = &gen;
     e.y = ll_layout(P.H, P.L, P.nH, P.nKV, P.hd, P.I, P.act_f32, P.nchunks, P.lm_tiles);
     int tok = P.tok_in[0];
     if (tok < 0 || tok >= P.V) {
@@ -1139,26 +1125,24 @@ DEV void compute_run(const Ctx& c) {
         const bool next_gemv = t + 1 < q1 && is_gemv(N.op);
         e.tr = P.trace ? P.trace + (uint64_t)t * kTraceSlots : nullptr;
         mark(e, 0);
-        bool ok;
+        // (after a timeout or an abort every wait returns at once, and the workgroup runs the rest
+        // of its queue without waiting, through the same barriers, so the launch ends)
         if (is_gemv(T.op)) {
-            ok = op_gemv(e, T, A, B);
+            op_gemv(e, T, A, B);
         } else {
             switch (T.op) {
-            case AMK_OP_ATTN: ok = op_attn(e, T); break;
-            case AMK_OP_MERGE: ok = op_merge(e, T); break;
-            default: ok = op_argmax(e, T); break;
+            case AMK_OP_ATTN: op_attn(e, T); break;
+            case AMK_OP_MERGE: op_merge(e, T); break;
+            default: op_argmax(e, T); break;
             }
         }
         if (e.tr && ctid == 0) e.tr[5] = rt();
+        // every wave is done with this task's LDS data before the next task stages its input
+        cbar();
+        mark(e, 3);
         // the task's outputs are out: start the next task's weights (behind those stores in the
         // memory pipeline, so the outputs reach their consumers first)
-        if (ok && next_gemv) prefetch_task(c, N, cw, A, B);
-        // every wave is done with this task's LDS data before the next task stages its input
-        if (!ok || !cbar(c, gen)) {
-            __hip_atomic_store(&S.abort_, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-            return;
-        }
-        mark(e, 3);
+        if (next_gemv) prefetch_task(c, N, cw, A, B);
     }
 }
 
@@ -1172,7 +1156,7 @@ DEV void megakernel_body(const KParams& Pin) {
     P.wfmt = FMT;
     P.act_f32 = FMT == AMK_F32 ? 1 : 0;
     const int tid = threadIdx.x;
-    if (tid == 0) { S.bar = 0; S.abort_ = 0; }
+    if (tid == 0) S.abort_ = 0;
     {   // copy the head of this CU's task queue to LDS (8 dwords per task)
         const uint32_t q0 = P.queue_off[blockIdx.x], q1 = P.queue_off[blockIdx.x + 1];
         const uint32_t n = min(q1 - q0, (uint32_t)kTaskCache) * (uint32_t)(sizeof(DevTask) / 4);
