@@ -191,12 +191,14 @@ void amk_schedule_free(amk_schedule* sched);
 typedef struct amk_ctx amk_ctx;
 
 /* Build a context on the current device: lower (or take `sched`), validate, check that one
- * 1024-thread workgroup per CU fits, quantise/repack the weights into library-owned device
- * memory, upload the task table and synchronise `stream`.
- *  desc      host; shape (AMK_E_UNSUPPORTED unless: head_dim in {16, 64, 128}; hidden, head
- *            counts and intermediate even; n_heads % n_kv_heads == 0; act_f32 == 1 only with
- *            AMK_F32; hidden and intermediate multiples of 128 for AMK_INT4_G128; vocab >= 2;
- *            hidden <= 8192; intermediate <= 16384).
+ * 512-thread workgroup per CU fits, quantise/repack the weights into library-owned device
+ * memory, upload the task table and synchronise `stream`. The device watchdog (how long any
+ * single wait inside a step may last before the step gives up) is 2000 ms, or the value in
+ * milliseconds of the environment variable AMK_WATCHDOG_MS when the context is created.
+ *  desc      host; shape (AMK_E_UNSUPPORTED unless: head_dim in {16, 64, 128}; hidden and
+ *            intermediate multiples of 16 (of 128 for AMK_INT4_G128, with n_heads * head_dim);
+ *            n_heads % n_kv_heads == 0; act_f32 == 1 exactly with AMK_F32; vocab >= 2;
+ *            hidden and n_heads * head_dim <= 8192; intermediate <= 16384).
  *  weights   host struct of device pointers, borrowed for this call only.
  *  kv_cache  device, caller-owned for the context's lifetime, layout
  *            [n_layers][2 (K, V)][n_kv_heads][max_ctx][head_dim] in the activation type

@@ -388,7 +388,7 @@ DEV void gemv_rows(const Ctx& c, const DevTask& T, int cw, WBuf& A, WBuf& B) {
 
 // Words each thread has in flight at once while gathering flag-carrying words. The gather walks
 // its words in chunks of this many, so its register use does not grow with the vector length.
-constexpr int kGatherChunk = 4;
+constexpr int kGatherChunk = 6;
 
 // Wait until words [0, n) of a flag-carrying buffer all carry `flag`; hand each payload to fn.
 // Each thread polls words tid + k * kComputeThreads, kGatherChunk of them at a time.
@@ -751,9 +751,14 @@ DEV void kv_slice(const KParams& P, const uint8_t* p, uint32_t d0, uint32_t D, f
     }
 }
 
+// The K/V loads of an attention round live in the two weight buffers (attention tasks stream
+// no weights): load k of a thread is A.w[k], then B.w[k - kLoadSlots].
+static_assert(kKvLoads <= 2 * kLoadSlots, "K/V round registers");
+DEV u32x4& kv_slot(WBuf& A, WBuf& B, int k) { return k < kLoadSlots ? A.w[k] : B.w[k - kLoadSlots]; }
+
 // Issue the loads of one round of history positions [a, a + n) of KV group g into registers:
 // the K rows, then the V rows, each block contiguous in the cache (16 bytes per load).
-DEV void kv_round_issue(const KParams& P, int l, int g, uint32_t a, uint32_t n, int ctid, u32x4 (&r)[kKvLoads]) {
+DEV void kv_round_issue(const KParams& P, int l, int g, uint32_t a, uint32_t n, int ctid, WBuf& A, WBuf& B) {
     const uint32_t blk = n * kv_row_bytes(P), chunks = 2 * blk / 16;
     const uint8_t* kb = kv_ptr(P, l, 0, g, a);
     const uint8_t* vb = kv_ptr(P, l, 1, g, a);
@@ -762,19 +767,37 @@ DEV void kv_round_issue(const KParams& P, int l, int g, uint32_t a, uint32_t n, 
         const uint32_t q = (uint32_t)ctid + (uint32_t)k * kComputeThreads;
         if (q < chunks) {
             const uint32_t off = 16 * q;
-            r[k] = off < blk ? *(const u32x4*)(kb + off) : *(const u32x4*)(vb + (off - blk));
+            kv_slot(A, B, k) = off < blk ? *(const u32x4*)(kb + off) : *(const u32x4*)(vb + (off - blk));
         }
     }
     compiler_fence();
 }
 // ... and store them to S.kvb: K rows at [0, n * row bytes), V rows after them
-DEV void kv_round_store(const KParams& P, Lds& S, uint32_t n, int ctid, const u32x4 (&r)[kKvLoads]) {
+DEV void kv_round_store(const KParams& P, Lds& S, uint32_t n, int ctid, WBuf& A, WBuf& B) {
     const uint32_t chunks = 2 * n * kv_row_bytes(P) / 16;
 #pragma unroll
     for (int k = 0; k < kKvLoads; ++k) {
         const uint32_t q = (uint32_t)ctid + (uint32_t)k * kComputeThreads;
-        if (q < chunks) *(u32x4*)(S.kvb + 16 * q) = r[k];
+        if (q < chunks) *(u32x4*)(S.kvb + 16 * q) = kv_slot(A, B, k);
     }
+}
+
+// The history positions of attention task T: chunk arg[2] of arg[3] of [0, pos), its KV group,
+// and the positions of its first LDS round.
+struct AttnSpan {
+    int l, g;
+    uint32_t p0, p1;     // history positions [p0, p1)
+    uint32_t per_round;  // positions per LDS round
+    uint32_t rn;         // positions of the first round
+};
+DEV AttnSpan attn_span(const KParams& P, const DevTask& T) {
+    AttnSpan a;
+    a.l = T.layer;
+    a.g = (int)((uint64_t)T.arg[0] * P.nKV / P.nH);
+    chunk_range(P.pos, T.arg[2], T.arg[3], a.p0, a.p1);
+    a.per_round = (uint32_t)kKvRound / (2 * kv_row_bytes(P));
+    a.rn = min(a.per_round, a.p1 - a.p0);
+    return a;
 }
 
 // Attention of query heads [h0, h0+nh) (one KV group g) over chunk ch of nc of the context
@@ -790,7 +813,7 @@ DEV void kv_round_store(const KParams& P, Lds& S, uint32_t n, int ctid, const u3
 // current position (last chunk only) comes from the flag-carrying words. At the end the
 // per-wave states (m, l, o) are combined with weights exp(m_w - M) computed once per (wave,
 // head); a single chunk writes the output row, a split context writes its (M, L, o) state.
-DEV void op_attn(const TaskEnv& e, const DevTask& T) {
+DEV void op_attn(const TaskEnv& e, const DevTask& T, WBuf& A, WBuf& B) {
     const Ctx& c = *e.c;
     const KParams& P = *c.P;
     Lds& S = *c.S;
@@ -804,15 +827,12 @@ DEV void op_attn(const TaskEnv& e, const DevTask& T) {
     float* qs = S.att + kAttQ;
     float* kc = S.att + kAttKc;
     float* vc = S.att + kAttVc;
-    uint32_t p0, p1;
-    chunk_range(P.pos, ch, nc, p0, p1);
-    const uint32_t nhist = p1 - p0;
+    const AttnSpan sp = attn_span(P, T);
+    const uint32_t p1 = sp.p1, nhist = sp.p1 - sp.p0, per_round = sp.per_round;
     const uint32_t rowb = kv_row_bytes(P);
-    const uint32_t per_round = (uint32_t)kKvRound / (2 * rowb);   // history positions per LDS round
     // the first round's K/V loads go out before the wait for q
-    u32x4 kvr[kKvLoads];
-    uint32_t ra = p0, rn = min(per_round, nhist);
-    if (rn) kv_round_issue(P, l, g, ra, rn, ctid, kvr);
+    uint32_t ra = sp.p0, rn = sp.rn;
+    if (rn) kv_round_issue(P, l, g, ra, rn, ctid, A, B);
     // inputs: q of the task's heads; the current k, v of the group (last chunk only)
     (void)ll_gather(c, Lq + (uint64_t)h0 * hd / vpw, nh * hd / vpw, ctid, [&](uint32_t i, uint32_t pl) {
             for (uint32_t j = 0; j < vpw; ++j) qs[i * vpw + j] = word_val(P, pl, (int)j);
@@ -826,7 +846,7 @@ DEV void op_attn(const TaskEnv& e, const DevTask& T) {
                 for (uint32_t j = 0; j < vpw; ++j) vc[i * vpw + j] = word_val(P, pl, (int)j);
             });
     }
-    if (rn) kv_round_store(P, S, rn, ctid, kvr);
+    if (rn) kv_round_store(P, S, rn, ctid, A, B);
     cbar();
     mark(e, 1);
     // lane layout
@@ -917,8 +937,8 @@ DEV void op_attn(const TaskEnv& e, const DevTask& T) {
         const uint32_t na = ra + rn, nn = min(per_round, p1 - na);
         if (!nn) break;
         cbar();   // every wave is done with this round's rows
-        kv_round_issue(P, l, g, na, nn, ctid, kvr);
-        kv_round_store(P, S, nn, ctid, kvr);
+        kv_round_issue(P, l, g, na, nn, ctid, A, B);
+        kv_round_store(P, S, nn, ctid, A, B);
         cbar();
         ra = na;
         rn = nn;
@@ -1114,10 +1134,11 @@ DEV void compute_run(const Ctx& c) {
     e.token = tok;
     WBuf A, B;
     const uint32_t q0 = P.queue_off[c.cu], q1 = P.queue_off[c.cu + 1];
-    // the first task's gains and weights, if it has any
+    // the first task's weights, if it has any
     if (q0 < q1) {
         const DevTask F = task_at(c, q0, q0);
         if (is_gemv(F.op)) prefetch_task(c, F, cw, A, B);
+
     }
     for (uint32_t t = q0; t < q1; ++t) {
         const DevTask T = task_at(c, q0, t);
@@ -1131,7 +1152,7 @@ DEV void compute_run(const Ctx& c) {
             op_gemv(e, T, A, B);
         } else {
             switch (T.op) {
-            case AMK_OP_ATTN: op_attn(e, T); break;
+            case AMK_OP_ATTN: op_attn(e, T, A, B); break;
             case AMK_OP_MERGE: op_merge(e, T); break;
             default: op_argmax(e, T); break;
             }
@@ -1143,6 +1164,7 @@ DEV void compute_run(const Ctx& c) {
         // the task's outputs are out: start the next task's weights (behind those stores in the
         // memory pipeline, so the outputs reach their consumers first)
         if (next_gemv) prefetch_task(c, N, cw, A, B);
+
     }
 }
 
