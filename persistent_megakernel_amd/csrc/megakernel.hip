@@ -132,11 +132,25 @@ struct Ctx {
 };
 
 // task t of this CU's queue (starting at q0): from the LDS copy when it holds it. The fields
-// are made wave-uniform so that everything derived from them lives in scalar registers.
+// are made wave-uniform so that everything derived from them lives in scalar registers. The
+// global path (queues longer than the copy) uses atomic loads so that the compiler cannot fold
+// the two paths into one generic (flat) load: a flat load also counts as a vector memory
+// access, and waiting for it would wait for every weight load the wave has in flight.
 DEV DevTask task_at(const Ctx& c, uint32_t q0, uint32_t t) {
-    const DevTask v = t - q0 < (uint32_t)kTaskCache ? c.S->tcache[t - q0] : c.P->tasks[t];
     uint32_t w[sizeof(DevTask) / 4];
-    __builtin_memcpy(w, &v, sizeof(DevTask));
+    if (t - q0 < (uint32_t)kTaskCache) {
+        __builtin_memcpy(w, &c.S->tcache[t - q0], sizeof(DevTask));
+    } else {
+        const u64* g = (const u64*)(c.P->tasks + t);
+#pragma unroll
+        for (int k = 0; k < (int)(sizeof(DevTask) / 8); ++k) {
+            const u64 v = __hip_atomic_load(g + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            w[2 * k] = (uint32_t)v;
+            w[2 * k + 1] = (uint32_t)(v >> 32);
+        }
+        // wait here, so that nothing past the join of the two paths waits for vector memory
+        __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+    }
 #pragma unroll
     for (int k = 0; k < (int)(sizeof(DevTask) / 4); ++k) w[k] = __builtin_amdgcn_readfirstlane(w[k]);
     DevTask r;
