@@ -39,7 +39,7 @@ WORKLOADS = {
 # counters measured for the default workload by rocprofv3 (--pmc FETCH_SIZE, then WRITE_SIZE),
 # scaled by the same counters on a device copy of known size; None until measured for the
 # current kernel
-TRAFFIC_BYTES_PER_LAUNCH = 1094707556
+TRAFFIC_BYTES_PER_LAUNCH = 1094407812
 
 
 def weight_bytes(shape) -> int:
