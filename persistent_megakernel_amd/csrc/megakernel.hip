@@ -827,7 +827,8 @@ DEV AttnSpan attn_span(const KParams& P, const DevTask& T) {
 // current position (last chunk only) comes from the flag-carrying words. At the end the
 // per-wave states (m, l, o) are combined with weights exp(m_w - M) computed once per (wave,
 // head); a single chunk writes the output row, a split context writes its (M, L, o) state.
-DEV void op_attn(const TaskEnv& e, const DevTask& T, WBuf& A, WBuf& B) {
+template <int DT>
+DEV void op_attn_d(const TaskEnv& e, const DevTask& T, WBuf& A, WBuf& B) {
     const Ctx& c = *e.c;
     const KParams& P = *c.P;
     Lds& S = *c.S;
@@ -863,10 +864,10 @@ DEV void op_attn(const TaskEnv& e, const DevTask& T, WBuf& A, WBuf& B) {
     if (rn) kv_round_store(P, S, rn, ctid, A, B);
     cbar();
     mark(e, 1);
-    // lane layout
-    uint32_t nhp = 1;
-    while (nhp < nh) nhp <<= 1;
-    const uint32_t L = min(64u / nhp, hd), D = hd / L;
+    // lane layout (D, the dims per lane, is the template parameter: every per-dim loop below is
+    // fixed at compile time)
+    constexpr uint32_t D = (uint32_t)DT;
+    const uint32_t L = hd / D;
     const uint32_t hl = (uint32_t)lane / L, dg = (uint32_t)lane % L;
     const bool active = hl < nh;
     const uint32_t hq = active ? hl : 0;   // inactive lanes shadow head 0 and never store
@@ -1014,6 +1015,21 @@ DEV void op_attn(const TaskEnv& e, const DevTask& T, WBuf& A, WBuf& B) {
             }
             ll_store(part + ((uint64_t)(h0 + h) * nc + ch) * st + k, __float_as_uint(v), flag);
         }
+    }
+}
+
+// Attention with the lane layout's dims per lane as a compile-time constant: a head owns
+// min(64 / nh rounded up to a power of two, hd) lanes, so D = hd / lanes is 1, 2, 4 or 8 (the
+// lowering keeps it <= 8).
+DEV void op_attn(const TaskEnv& e, const DevTask& T, WBuf& A, WBuf& B) {
+    const uint32_t nh = T.arg[1], hd = (uint32_t)e.c->P->hd;
+    uint32_t nhp = 1;
+    while (nhp < nh) nhp <<= 1;
+    switch (hd / min(64u / nhp, hd)) {
+    case 1: op_attn_d<1>(e, T, A, B); break;
+    case 2: op_attn_d<2>(e, T, A, B); break;
+    case 4: op_attn_d<4>(e, T, A, B); break;
+    default: op_attn_d<8>(e, T, A, B); break;
     }
 }
 
