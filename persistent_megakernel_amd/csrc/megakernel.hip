@@ -814,6 +814,9 @@ DEV AttnSpan attn_span(const KParams& P, const DevTask& T) {
     return a;
 }
 
+// The softmax exponentials here use the hardware base-2 exponential of x * log2(e) (a few ulp
+// in fp32, far inside the parity bounds): the library expf costs five times the instructions.
+//
 // Attention of query heads [h0, h0+nh) (one KV group g) over chunk ch of nc of the context
 // positions [0, pos]: the softmax-weighted sum of V rows with weights from q.K / sqrt(hd)
 // (page 3, "How it works", the attention instruction over the persistent KV cache).
@@ -893,7 +896,7 @@ DEV void op_attn_d(const TaskEnv& e, const DevTask& T, WBuf& A, WBuf& B) {
         for (uint32_t off = L >> 1; off >= 1; off >>= 1) sdot += __shfl_xor(sdot, (int)off, 64);
         const float sc = sdot * scale;
         const float mn = fmaxf(m, sc);
-        const float alpha = expf(m - mn), pw = expf(sc - mn);
+        const float alpha = __expf(m - mn), pw = __expf(sc - mn);
         lsum = lsum * alpha + pw;
         if (vrow) kv_slice(P, vrow, dg * D, D, kv);
         else
@@ -931,7 +934,7 @@ DEV void op_attn_d(const TaskEnv& e, const DevTask& T, WBuf& A, WBuf& B) {
                 sc[u] = i0 + (uint32_t)u * kComputeWaves < rn ? sc[u] * scale : -INFINITY;
                 mb = fmaxf(mb, sc[u]);
             }
-            const float alpha = expf(m - mb);
+            const float alpha = __expf(m - mb);
             lsum *= alpha;
 #pragma unroll
             for (int k = 0; k < kAttMaxD; ++k) o[k] *= alpha;
@@ -939,7 +942,7 @@ DEV void op_attn_d(const TaskEnv& e, const DevTask& T, WBuf& A, WBuf& B) {
             for (int u = 0; u < kAttBatch; ++u) {
                 const uint32_t i = i0 + (uint32_t)u * kComputeWaves;
                 if (i < rn) {
-                    const float pw = expf(sc[u] - mb);
+                    const float pw = __expf(sc[u] - mb);
                     lsum += pw;
                     kv_slice(P, S.kvb + (rn + i) * rowb, dg * D, D, kv);
 #pragma unroll
@@ -977,7 +980,7 @@ DEV void op_attn_d(const TaskEnv& e, const DevTask& T, WBuf& A, WBuf& B) {
         float M = -INFINITY;
         for (int v = 0; v < kComputeWaves; ++v) M = fmaxf(M, S.hf[((uint32_t)v * nh + h) * st]);
         const float mw = S.hf[(w * nh + h) * st];
-        S.att[kAttF + w * kMaxAttnHeads + h] = mw == -INFINITY ? 0.f : expf(mw - M);
+        S.att[kAttF + w * kMaxAttnHeads + h] = mw == -INFINITY ? 0.f : __expf(mw - M);
         if (w == 0) S.att[kAttM + h] = M;
     }
     cbar();
@@ -1058,7 +1061,7 @@ DEV void op_merge(const TaskEnv& e, const DevTask& T) {
         float Ls = 0.f;
         for (uint32_t k = (uint32_t)lane_id(); k < nc; k += 64) {
             const float mk = base[k * st];
-            const float f = mk == -INFINITY ? 0.f : expf(mk - M);
+            const float f = mk == -INFINITY ? 0.f : __expf(mk - M);
             Ls += f * base[k * st + 1];
             base[k * st] = f;
         }
