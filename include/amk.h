@@ -182,6 +182,53 @@ typedef struct {
  * leaves from it). Returns AMK_E_INVALID_ARG for null pointers or a wrong struct_size. */
 amk_status amk_validate(const amk_schedule* sched, amk_verdict* out);
 
+/* Run a schedule on the CPU under the kernel's synchronisation protocol and check it. Never
+ * touches a device. One host thread per queue walks its tasks in order: a task waits until
+ * every counter it waits on has reached its threshold, performs its pre accesses, increments
+ * its signalled counters, then performs its post (AMK_ACC_POST) accesses. A deadlock (every
+ * queue finished or blocked on a wait the counters cannot satisfy any more, at least one
+ * blocked) is detected exactly when it happens; each wait is also bounded by a watchdog, whose
+ * expiry is reported as a deadlock too (the device's timeout path). On either, every thread
+ * stops. A seeded random
+ * delay before each step varies the interleaving between runs. The declared accesses are
+ * checked with vector clocks:
+ *  - every queue carries a clock vector;
+ *  - a counter carries the join of its signallers' clocks;
+ *  - a wait that sees its threshold joins the counter's clock.
+ * Two accesses of different tasks to one element, one a write, race when neither is ordered
+ * before the other by queue order and waits. A wait joins every signaller seen so far, so a
+ * partial wait on a multi-producer counter can hide a race but never makes one up. Reads of
+ * elements nothing wrote before and no declared input covers are counted, and so are declared
+ * output elements nothing wrote and flag-carrying elements written by two tasks in one launch.
+ * Read-only regions are not tracked. The executor computes nothing; it checks the protocol.
+ *  sched  host; must pass the structural part of V0 (ids in range, every task in exactly one
+ *         queue exactly once), else AMK_E_INVALID_ARG. Borrowed for the call.
+ *  opts   host; seed, the largest delay in microseconds (0 = none), the watchdog in
+ *         milliseconds (0 = 2000), and the most shadow elements tracked (0 = 4M; regions past
+ *         the budget are not checked and their elements are counted in `unchecked`).
+ *  out    host; the outcome. */
+typedef struct {
+    uint32_t struct_size;      /* sizeof(amk_vm_opts) */
+    uint32_t seed;
+    uint32_t max_delay_us;
+    uint32_t watchdog_ms;
+    uint64_t max_elements;
+} amk_vm_opts;
+
+typedef struct {
+    int32_t completed;          /* every queue ran to its end (no deadlock) */
+    int32_t deadlocked;         /* no queue could move any more, or a wait outlived the watchdog */
+    uint32_t races;             /* conflicting element accesses found unordered */
+    uint32_t uncovered_reads;   /* read elements not written before and not declared inputs */
+    uint32_t unwritten_outputs; /* declared output elements nothing wrote (completed runs) */
+    int32_t task, other;        /* the task of the first problem found and its counterpart (or -1) */
+    uint64_t unchecked;         /* accessed elements of regions past the shadow budget */
+    uint32_t ll_rewrites;       /* flag-carrying elements written by a second task in the launch */
+    uint32_t pad;
+} amk_vm_result;
+
+amk_status amk_vm_run(const amk_schedule* sched, const amk_vm_opts* opts, amk_vm_result* out);
+
 /* Run the built-in lowering on the CPU (no device needed): model + config -> schedule. The
  * result is library-owned; free it with amk_schedule_free. AMK_E_UNSUPPORTED for shapes the
  * kernel does not implement (see amk_create). */

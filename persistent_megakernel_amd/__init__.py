@@ -22,7 +22,7 @@ from ._abi import (AMK_BF16, AMK_F32, AMK_INT4_G128, AMK_INT8_PC, AmkError, STAT
 
 __all__ = ["amk_validate", "amk_lower", "amk_create", "amk_decode_step", "amk_destroy",
            "amk_quantize", "amk_device_status", "amk_ctx_schedule", "amk_set_trace", "amk_version", "Decoder",
-           "model_desc", "schedule_config", "AmkError"]
+           "model_desc", "schedule_config", "AmkError", "amk_vm_run"]
 
 
 # ---------------------------------------------------------------- descriptors
@@ -141,6 +141,18 @@ def amk_validate(sched) -> A.amk_verdict:
     check("amk_validate", lib().amk_validate(C.byref(view), C.byref(out)))
     del keep
     return out
+
+
+def amk_vm_run(sched, seed: int = 0, max_delay_us: int = 0, watchdog_ms: int = 0, max_elements: int = 0) -> dict:
+    """Run a Python schedule on the CPU executor (amk_vm_run): the counter protocol on host
+    threads, checked with a happens-before race detector. Returns the outcome as a dict."""
+    cs = CSchedule(sched)
+    o = A.amk_vm_opts()
+    o.struct_size = C.sizeof(A.amk_vm_opts)
+    o.seed, o.max_delay_us, o.watchdog_ms, o.max_elements = seed, max_delay_us, watchdog_ms, max_elements
+    r = A.amk_vm_result()
+    check("amk_vm_run", lib().amk_vm_run(C.byref(cs.view), C.byref(o), C.byref(r)))
+    return {k: getattr(r, k) for k, _ in A.amk_vm_result._fields_}
 
 
 def amk_lower(desc: A.amk_model_desc, cfg: Optional[A.amk_schedule_config] = None):

@@ -91,6 +91,17 @@ class amk_schedule_config(C.Structure):
                 ("cu_assign", C.c_int32)]
 
 
+class amk_vm_opts(C.Structure):
+    _fields_ = [("struct_size", C.c_uint32), ("seed", C.c_uint32), ("max_delay_us", C.c_uint32),
+                ("watchdog_ms", C.c_uint32), ("max_elements", C.c_uint64)]
+
+
+class amk_vm_result(C.Structure):
+    _fields_ = [("completed", C.c_int32), ("deadlocked", C.c_int32), ("races", C.c_uint32),
+                ("uncovered_reads", C.c_uint32), ("unwritten_outputs", C.c_uint32), ("task", C.c_int32),
+                ("other", C.c_int32), ("unchecked", C.c_uint64), ("ll_rewrites", C.c_uint32), ("pad", C.c_uint32)]
+
+
 # every symbol include/amk.h declares, with (restype, argtypes)
 _P = C.c_void_p
 SIGNATURES = {
@@ -108,6 +119,7 @@ SIGNATURES = {
     "amk_destroy": (None, [_P]),
     "amk_quantize": (C.c_int, [C.c_int32, _P, C.c_int64, C.c_int64, _P, _P, _P]),
     "amk_version": (C.c_char_p, []),
+    "amk_vm_run": (C.c_int, [C.POINTER(amk_schedule), C.POINTER(amk_vm_opts), C.POINTER(amk_vm_result)]),
 }
 
 _lib = None

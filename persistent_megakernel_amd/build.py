@@ -19,7 +19,7 @@ BENCH = os.path.join(HERE, "amk_bench")
 ARCH = "gfx950"
 
 HIP_SOURCES = ["megakernel.hip", "prep.hip"]
-CPP_SOURCES = ["abi.cpp", "lower.cpp", "validate.cpp"]
+CPP_SOURCES = ["abi.cpp", "lower.cpp", "validate.cpp", "vm.cpp"]
 
 
 def _hipcc() -> str:
@@ -59,7 +59,7 @@ def build(verbose: bool = False) -> str:
             sys.stderr.write(o.stderr)
     objs = [j[j.index("-o") + 1] for j in jobs]
     tmp = LIB + ".tmp%d" % os.getpid()
-    _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs])
+    _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs, "-pthread"])
     os.replace(tmp, LIB)
     # the C-ABI benchmark driver (links the library, no device code of its own)
     tmp = BENCH + ".tmp%d" % os.getpid()
