@@ -197,3 +197,40 @@ def test_lowering_with_a_dropped_wait_is_caught_by_both_checkers(M):
         hits += any(r["races"] or r["uncovered_reads"] for r in rs)
         assert not any(r["deadlocked"] for r in rs)
     assert hits >= 4
+
+
+def _lowered_mutants(M, n, seed):
+    sc = M.amk_lower(M.model_desc(I.SHAPES["tiny_fp32"]), M.schedule_config(n_cu=16))
+    rng = random.Random(seed)
+    for _ in range(n):
+        s = sc.copy()
+        for _ in range(rng.randint(1, 2)):
+            S._mutate(s, rng)
+        yield s
+
+
+@pytest.mark.parametrize("n,seed", [(150, 1), pytest.param(1000, 2, marks=pytest.mark.slow)])
+def test_mutants_of_the_lowering_agree_with_the_validator(M, n, seed):
+    """Beyond brute-force sizes (149 tasks on 16 queues): mutants of the real lowering. Whatever
+    the validator accepts runs clean; whatever deadlocks or races, the validator rejected."""
+    counts = {"accepted": 0, "deadlock": 0, "race": 0, "refused": 0}
+    for s in _lowered_mutants(M, n, seed):
+        v = M.amk_validate(s)
+        try:
+            rs = _runs(M, s, n=2, delay=2)
+        except M.AmkError:
+            assert v.rule_mask & 1
+            counts["refused"] += 1
+            continue
+        for r in rs:
+            if v.accepted:
+                assert _clean(r), (hex(v.rule_mask), r)
+            if r["deadlocked"]:
+                # V1 (threshold), V3 or V4; or V0, after which nothing else is checked
+                assert v.rule_mask & 0b11011, hex(v.rule_mask)
+            if r["races"]:
+                assert not v.accepted
+        counts["accepted"] += v.accepted
+        counts["deadlock"] += any(r["deadlocked"] for r in rs)
+        counts["race"] += any(r["races"] for r in rs)
+    assert all(counts[k] > 0 for k in counts), counts
