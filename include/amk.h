@@ -277,6 +277,38 @@ amk_status amk_create(const amk_model_desc* desc, const amk_weights* weights, vo
 amk_status amk_decode_step(amk_ctx* ctx, const int32_t* token_in, int32_t pos, int32_t* token_out,
                            float* logits, void* stream);
 
+/* Prompt prefill: run `n_tokens` prompt tokens through the model in cooperative launches of up
+ * to 256 tokens each, instead of one decode launch per token (pages: page 3, "How it works",
+ * layer 1, GEMM tiles among the instruction kinds). The result is the one of n_tokens chained
+ * decode steps fed tokens[i] at position pos0 + i: cache rows [pos0, pos0 + n_tokens) are
+ * written, rows below pos0 are read, and token_out / logits are those of the step at the last
+ * position (the first generated token). The projections run as matrix-core GEMM tiles over the
+ * chunk's tokens; the schedule of each chunk size is lowered, validated (amk_validate) and
+ * uploaded on first use, and the first call allocates the chunk's activation buffers (about
+ * 256 x (3 x hidden + 2 x n_heads x head_dim + intermediate) activation values), so it is
+ * not capturable into a graph until every chunk size it uses has run once.
+ *  tokens     device int32[n_tokens]; a token outside [0, vocab) is replaced by 0 and flagged
+ *             in the device status word.
+ *  pos0       host int, 0 <= pos0 and pos0 + n_tokens <= max_ctx (else AMK_E_INVALID_ARG).
+ *  n_tokens   host int >= 1.
+ *  token_out  device int32[1]: greedy token after the last prompt token.
+ *  logits     device fp32[vocab] or NULL: the logits of the last prompt token.
+ *  stream     HIP stream; the call enqueues its launches and returns without synchronising.
+ * AMK_E_UNSUPPORTED when a weight row of the context's streams cannot be located (a user
+ * schedule that splits rows) or head_dim > 128; AMK_E_DEVICE_TIMEOUT as for amk_decode_step. */
+amk_status amk_prefill(amk_ctx* ctx, const int32_t* tokens, int32_t pos0, int32_t n_tokens, int32_t* token_out,
+                       float* logits, void* stream);
+
+/* The prefill schedule of one launch of n_tokens (1 .. 256) tokens for n_cu workgroups (0 =
+ * 256), in the schedule IR, for inspection with amk_validate / amk_vm_run on the CPU. Phase
+ * tasks over M-tiles of 64 tokens; every task of a phase waits on one counter signalled by all
+ * tasks of the previous phase. Accesses are declared in tile units over these regions: 0 the
+ * token ids (input), 1 the residual stream x, 2 the normalised rows h, 3 the rotated queries,
+ * 4 the attention output, 5 the SwiGLU output, 6 the LM tile results, 7 the logits (output),
+ * 8 the token out (output), 9 + layer the K and V rows of the chunk in that layer's cache.
+ * Caller frees with amk_schedule_free. */
+amk_status amk_lower_prefill(const amk_model_desc* desc, int32_t n_cu, int32_t n_tokens, amk_schedule** out);
+
 /* Device status word of the context (synchronises the context's last stream first):
  * 0 = fine; bit 0 = watchdog timeout; bit 1 = token out of range. */
 uint32_t amk_device_status(amk_ctx* ctx);

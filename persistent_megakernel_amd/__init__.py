@@ -22,7 +22,8 @@ from ._abi import (AMK_BF16, AMK_F32, AMK_INT4_G128, AMK_INT8_PC, AmkError, STAT
 
 __all__ = ["amk_validate", "amk_lower", "amk_create", "amk_decode_step", "amk_destroy",
            "amk_quantize", "amk_device_status", "amk_ctx_schedule", "amk_set_trace", "amk_version", "Decoder",
-           "model_desc", "schedule_config", "AmkError", "amk_vm_run"]
+           "model_desc", "schedule_config", "AmkError", "amk_vm_run",
+           "amk_prefill", "amk_lower_prefill"]
 
 
 # ---------------------------------------------------------------- descriptors
@@ -203,6 +204,27 @@ def amk_decode_step(ctx: int, token_in_ptr: int, pos: int, token_out_ptr: int, l
                                  C.c_void_p(logits_ptr or None), C.c_void_p(stream))
 
 
+def amk_prefill(ctx: int, tokens_ptr: int, pos0: int, n_tokens: int, token_out_ptr: int, logits_ptr: int = 0,
+                stream: int = 0) -> int:
+    """Enqueue the prefill launches of n_tokens prompt tokens; returns the amk_status."""
+    return lib().amk_prefill(C.c_void_p(ctx), C.c_void_p(tokens_ptr), int(pos0), int(n_tokens),
+                             C.c_void_p(token_out_ptr), C.c_void_p(logits_ptr or None), C.c_void_p(stream))
+
+
+def amk_lower_prefill(desc: A.amk_model_desc, n_cu: int, n_tokens: int, python: bool = True):
+    """The prefill schedule of one launch, as a Python schedule (python=True) or its verdict."""
+    p = C.POINTER(A.amk_schedule)()
+    check("amk_lower_prefill", lib().amk_lower_prefill(C.byref(desc), int(n_cu), int(n_tokens), C.byref(p)))
+    try:
+        if python:
+            return schedule_from_c(p)
+        out = A.amk_verdict()
+        check("amk_validate", lib().amk_validate(p, C.byref(out)))
+        return out
+    finally:
+        lib().amk_schedule_free(p)
+
+
 def amk_device_status(ctx: int) -> int:
     return int(lib().amk_device_status(C.c_void_p(ctx)))
 
@@ -298,6 +320,15 @@ class Decoder:
         rc = amk_decode_step(self.ctx, token_in.data_ptr(), pos, token_out.data_ptr(),
                              logits.data_ptr() if logits is not None else 0, st)
         check("amk_decode_step", rc)
+
+    def prefill(self, tokens, pos0: int, token_out, logits=None, stream=None) -> None:
+        """Prompt prefill (amk_prefill). tokens: device int32 [n]; token_out: device int32 (one
+        element used); logits: device fp32 [vocab] or None."""
+        torch = self.torch
+        st = (stream or torch.cuda.current_stream(self.device)).cuda_stream
+        rc = amk_prefill(self.ctx, tokens.data_ptr(), pos0, tokens.numel(), token_out.data_ptr(),
+                         logits.data_ptr() if logits is not None else 0, st)
+        check("amk_prefill", rc)
 
     def status(self) -> int:
         return amk_device_status(self.ctx)

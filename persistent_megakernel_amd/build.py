@@ -18,8 +18,8 @@ LIB = os.path.join(HERE, "libamk.so")
 BENCH = os.path.join(HERE, "amk_bench")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["megakernel.hip", "prep.hip"]
-CPP_SOURCES = ["abi.cpp", "lower.cpp", "validate.cpp", "vm.cpp"]
+HIP_SOURCES = ["megakernel.hip", "prep.hip", "prefill.hip"]
+CPP_SOURCES = ["abi.cpp", "lower.cpp", "lower_prefill.cpp", "validate.cpp", "vm.cpp"]
 
 
 def _hipcc() -> str:

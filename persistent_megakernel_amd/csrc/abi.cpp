@@ -13,6 +13,8 @@
 #include "amk.h"
 #include "amk_internal.h"
 #include "lower.h"
+#include "lower_prefill.h"
+#include "prefill.h"
 #include "prep.h"
 
 using namespace amk;
@@ -37,6 +39,24 @@ struct amk_ctx {
     hipStream_t last = nullptr;
     uint64_t* trace = nullptr;      // caller-owned, optional
     KParams base;
+    // prompt prefill
+    bool pf_rows_ok = false;        // every weight row has an address in the streams
+    RowAddr* d_rowtab = nullptr;
+    uint32_t tab_base[PM_N] = {}, tab_rows[PM_N] = {};
+    void* pf_x = nullptr;
+    void* pf_h = nullptr;
+    void* pf_q = nullptr;
+    void* pf_o = nullptr;
+    void* pf_a = nullptr;
+    uint32_t* pf_lmpart = nullptr;
+    struct PfVariant {
+        PfLowered L;
+        PfTask* d_tasks = nullptr;
+        uint32_t* d_qoff = nullptr;
+        uint32_t* d_ctr = nullptr;
+        uint32_t epoch = 0;
+    };
+    PfVariant* pf[kPfChunk / kPfMt + 1] = {};
 };
 
 namespace {
@@ -56,6 +76,21 @@ void logf(const char* what, const std::string& msg) {
 
 void free_ctx(amk_ctx* c) {
     if (!c) return;
+    for (auto*& v : c->pf) {
+        if (!v) continue;
+        (void)hipFree(v->d_tasks);
+        (void)hipFree(v->d_qoff);
+        (void)hipFree(v->d_ctr);
+        delete v;
+        v = nullptr;
+    }
+    (void)hipFree(c->d_rowtab);
+    (void)hipFree(c->pf_x);
+    (void)hipFree(c->pf_h);
+    (void)hipFree(c->pf_q);
+    (void)hipFree(c->pf_o);
+    (void)hipFree(c->pf_a);
+    (void)hipFree(c->pf_lmpart);
     (void)hipFree(c->d_wstream);
     (void)hipFree(c->d_tasks);
     (void)hipFree(c->d_qoff);
@@ -215,6 +250,46 @@ extern "C" amk_status amk_create(const amk_model_desc* desc, const amk_weights* 
         (void)hipFree(d_rows);
         (void)hipFree((void*)d_tab);
     }
+    // where every weight row landed, for the prefill (it reads the same streams)
+    {
+        const int L = d.n_layers, qd = d.n_heads * d.head_dim, kd = d.n_kv_heads * d.head_dim;
+        const uint32_t rows[PM_N] = {(uint32_t)qd, (uint32_t)kd, (uint32_t)kd, (uint32_t)d.hidden, (uint32_t)d.intermediate,
+                                     (uint32_t)d.intermediate, (uint32_t)d.hidden, (uint32_t)d.vocab};
+        uint64_t total = 0;
+        for (int m = 0; m < PM_N; ++m) {
+            c->tab_base[m] = (uint32_t)total;
+            c->tab_rows[m] = rows[m];
+            total += (uint64_t)rows[m] * (m == PM_LM ? 1 : L);
+        }
+        std::vector<RowAddr> tab(total, RowAddr{0, 0});
+        std::vector<uint8_t> seen(total, 0);
+        bool ok = total < (1ull << 32);
+        for (const RowMap& m : c->L.rows) {
+            int pm = -1;
+            switch (m.mat) {
+            case M_WQ: pm = PM_WQ; break;
+            case M_WK: pm = PM_WK; break;
+            case M_WV: pm = PM_WV; break;
+            case M_WO: pm = PM_WO; break;
+            case M_WG: pm = PM_WG; break;
+            case M_WU: pm = PM_WU; break;
+            case M_WD: pm = PM_WD; break;
+            case M_LM: pm = PM_LM; break;
+            case M_EMBED: pm = d.tied_embeddings ? PM_LM : -1; break;   // a tied LM head is the embedding
+            default: break;
+            }
+            if (pm < 0 || m.src_row >= rows[pm] || (pm != PM_LM && m.layer >= (uint32_t)L)) continue;
+            const uint64_t i = c->tab_base[pm] + (pm == PM_LM ? 0ull : (uint64_t)m.layer * rows[pm]) + m.src_row;
+            tab[i] = RowAddr{m.dst, m.sdst};
+            ++seen[i];
+        }
+        for (uint8_t v : seen) ok = ok && v == 1;
+        c->pf_rows_ok = ok;
+        if (ok) {
+            ck(upload(&c->d_rowtab, tab, stream));
+            ck(hipStreamSynchronize(stream));
+        }
+    }
     if (e != hipSuccess) { logf("create", hipGetErrorString(e)); free_ctx(c); return e == hipErrorOutOfMemory ? AMK_E_OOM : AMK_E_HIP; }
     c->L.rows.clear();
     c->L.rows.shrink_to_fit();
@@ -262,6 +337,114 @@ extern "C" amk_status amk_decode_step(amk_ctx* c, const int32_t* token_in, int32
     if (e != hipSuccess) { logf("decode_step", hipGetErrorString(e)); return AMK_E_HIP; }
     c->epoch++;
     c->last = st;
+    return AMK_OK;
+}
+
+namespace {
+
+// The prefill schedule for chunks of nm M-tiles: lowered, validated and uploaded on first use.
+amk_status pf_variant(amk_ctx* c, int nm, hipStream_t st, amk_ctx::PfVariant** out) {
+    if (c->pf[nm]) { *out = c->pf[nm]; return AMK_OK; }
+    auto* v = new amk_ctx::PfVariant();
+    std::string msg;
+    amk_status rs = lower_prefill(c->d, c->n_cu, nm * kPfMt, v->L, &msg);
+    if (rs != AMK_OK) { logf("prefill", msg); delete v; return rs; }
+    amk_verdict ver;
+    if (amk_validate(&v->L.sched->box.view, &ver) != AMK_OK || !ver.accepted) {
+        logf("prefill", "prefill schedule rejected by the validator");
+        delete v;
+        return AMK_E_REJECTED;
+    }
+    hipError_t e = hipSuccess;
+    auto ck = [&](hipError_t r) { if (e == hipSuccess) e = r; };
+    ck(upload(&v->d_tasks, v->L.dtasks, st));
+    ck(upload(&v->d_qoff, v->L.dqueue_off, st));
+    ck(hipMalloc((void**)&v->d_ctr, std::max<size_t>(1, v->L.n_counters) * sizeof(uint32_t)));
+    if (e == hipSuccess) ck(hipMemsetAsync(v->d_ctr, 0, std::max<size_t>(1, v->L.n_counters) * sizeof(uint32_t), st));
+    ck(hipStreamSynchronize(st));
+    if (e != hipSuccess) {
+        (void)hipFree(v->d_tasks);
+        (void)hipFree(v->d_qoff);
+        (void)hipFree(v->d_ctr);
+        delete v;
+        return e == hipErrorOutOfMemory ? AMK_E_OOM : AMK_E_HIP;
+    }
+    c->pf[nm] = v;
+    *out = v;
+    return AMK_OK;
+}
+
+amk_status pf_buffers(amk_ctx* c, int lm_tiles) {
+    if (c->pf_x) return AMK_OK;
+    const amk_model_desc& d = c->d;
+    const size_t esz = d.act_f32 ? 4 : 2, R = kPfChunk;
+    hipError_t e = hipSuccess;
+    auto ck = [&](hipError_t r) { if (e == hipSuccess) e = r; };
+    ck(hipMalloc(&c->pf_x, R * d.hidden * esz));
+    ck(hipMalloc(&c->pf_h, R * d.hidden * esz));
+    ck(hipMalloc(&c->pf_q, R * d.n_heads * d.head_dim * esz));
+    ck(hipMalloc(&c->pf_o, R * d.n_heads * d.head_dim * esz));
+    ck(hipMalloc(&c->pf_a, R * d.intermediate * esz));
+    ck(hipMalloc((void**)&c->pf_lmpart, 2 * sizeof(uint32_t) * (size_t)std::max(1, lm_tiles)));
+    if (e != hipSuccess) {
+        for (void** p : {&c->pf_x, &c->pf_h, &c->pf_q, &c->pf_o, &c->pf_a, (void**)&c->pf_lmpart}) { (void)hipFree(*p); *p = nullptr; }
+        return e == hipErrorOutOfMemory ? AMK_E_OOM : AMK_E_HIP;
+    }
+    return AMK_OK;
+}
+
+}  // namespace
+
+extern "C" amk_status amk_prefill(amk_ctx* c, const int32_t* tokens, int32_t pos0, int32_t n_tokens, int32_t* token_out,
+                                  float* logits, void* stream_v) {
+    if (!c || !tokens || !token_out || n_tokens <= 0 || pos0 < 0 || (int64_t)pos0 + n_tokens > c->d.max_ctx)
+        return AMK_E_INVALID_ARG;
+    if (__atomic_load_n(&c->h_status[0], __ATOMIC_ACQUIRE) & kStatusTimeout) return AMK_E_DEVICE_TIMEOUT;
+    if (!c->pf_rows_ok || c->d.head_dim > kPfMaxNt) return AMK_E_UNSUPPORTED;
+    if (prefill_blocks_per_cu(c->d.wfmt) < 1) return AMK_E_NOT_RESIDENT;
+    hipStream_t st = (hipStream_t)stream_v;
+    const amk_model_desc& d = c->d;
+    for (int32_t c0 = 0; c0 < n_tokens; c0 += kPfChunk) {
+        const int32_t T = std::min<int32_t>(kPfChunk, n_tokens - c0);
+        const int nm = (T + kPfMt - 1) / kPfMt;
+        amk_ctx::PfVariant* v = nullptr;
+        amk_status rs = pf_variant(c, nm, st, &v);
+        if (rs != AMK_OK) return rs;
+        rs = pf_buffers(c, v->L.lm_tiles);
+        if (rs != AMK_OK) return rs;
+        PfParams P;
+        std::memset(&P, 0, sizeof(P));
+        P.H = d.hidden; P.L = d.n_layers; P.nH = d.n_heads; P.nKV = d.n_kv_heads; P.hd = d.head_dim;
+        P.I = d.intermediate; P.V = d.vocab; P.max_ctx = d.max_ctx; P.wfmt = d.wfmt; P.act_f32 = d.act_f32;
+        P.eps = d.rms_eps;
+        P.attn_scale = c->base.attn_scale;
+        P.T = T;
+        P.pos0 = pos0 + c0;
+        P.do_lm = c0 + T == n_tokens;
+        P.tasks = v->d_tasks;
+        P.queue_off = v->d_qoff;
+        P.ctr = v->d_ctr;
+        P.epoch = v->epoch;
+        P.wstream = c->d_wstream;
+        P.rowtab = c->d_rowtab;
+        for (int m = 0; m < PM_N; ++m) { P.tab_base[m] = c->tab_base[m]; P.tab_rows[m] = c->tab_rows[m]; }
+        P.x = c->pf_x; P.h = c->pf_h; P.q = c->pf_q; P.o = c->pf_o; P.a = c->pf_a;
+        P.lmpart = c->pf_lmpart;
+        P.kv = c->base.kv;
+        P.embed = c->d_embed;
+        P.norms = c->d_norms;
+        P.rope = c->d_rope;
+        P.tokens = tokens + c0;
+        P.tok_out = token_out;
+        P.logits = logits;
+        P.status = c->d_status;
+        P.abort_flag = c->d_abort;
+        P.watchdog_ticks = c->base.watchdog_ticks;
+        hipError_t e = launch_prefill(P, c->n_cu, st);
+        if (e != hipSuccess) { logf("prefill", hipGetErrorString(e)); return AMK_E_HIP; }
+        v->epoch++;
+        c->last = st;
+    }
     return AMK_OK;
 }
 

@@ -1,0 +1,720 @@
+// The persistent prefill kernel for gfx950 (MI355X): T prompt tokens per cooperative launch.
+//
+// A workgroup per CU walks its queue of tile tasks (AutoMegaKernel pages: page 3, "How it
+// works", layer 0 wait -> dispatch -> signal, and layer 1, GEMM tiles among the instructions).
+// With T tokens at once the projections are matrix products, so they run on the matrix cores:
+//  * GEMM tile = up to 64 token rows x up to 128 output columns, 8 waves, each wave owning 16x16
+//    blocks of the tile. The K loop stages 256 (bf16) or 128 (fp32) input columns of the
+//    activations and of the weight rows in LDS per step, converting weight codes to the compute
+//    type on the way in (int8 and int4 codes are exact in bf16), and prefetches the next step
+//    into registers while the matrix cores work on the current one.
+//  * bf16 products use v_mfma_f32_16x16x32_bf16, fp32 products v_mfma_f32_16x16x4_f32. The
+//    matrix cores' fp32 accumulation is not correctly rounded (on this part one instruction's
+//    sum can be off by about one ulp of the sum of |products|, and the error grows with the
+//    length of a chain of accumulating instructions), so a chain covers at most 128 (bf16) or
+//    32 (fp32) input columns, from zero, and the partial sums are added to the total with
+//    ordinary round-to-nearest additions. Per-row int8 scales are applied to the finished sums
+//    and per-group int4 scales to each 128-column partial sum, as the formats define them.
+//  * Epilogues (RoPE and the K/V cache rows, residual adds, SwiGLU) run from an fp32 copy of the
+//    tile in LDS, so each output element is rounded once to the activation format.
+//  * Attention: one task per (query head, 64 queries); the K and V rows of 64 positions at a
+//    time are staged in LDS (K transposed) and shared by the task's queries; online softmax.
+//  * Weights are read where the decode path keeps them (its per-CU streams), through a table
+//    of row addresses, so a context holds one copy of every weight.
+//
+// Synchronisation: one counter per phase, signalled once by every task of the phase (release,
+// device scope, after every wave's stores are written back) and waited on by every task of the
+// next phase (the counter reaching producers x (launches so far + 1), then an acquire). Waits
+// are bounded by the same s_memrealtime watchdog as the decode kernel: on expiry the status
+// word is raised and every workgroup runs the rest of its queue without waiting, so the launch
+// always ends.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "amk_internal.h"
+#include "prefill.h"
+
+namespace amk {
+namespace {
+
+#define DEV __device__ __forceinline__
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+DEV uint64_t rt() { return __builtin_amdgcn_s_memrealtime(); }
+DEV int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+DEV float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN)
+DEV uint32_t f2bf(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+DEV float h2f(uint32_t h) {
+    _Float16 x;
+    uint16_t b = (uint16_t)h;
+    __builtin_memcpy(&x, &b, 2);
+    return (float)x;
+}
+DEV float wave_sum(float v) {
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+DEV float wave_max(float v) {
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// Activation access: fp32 or bf16 storage, fp32 values.
+template <int F32>
+DEV float act_ld(const void* p, uint64_t i) {
+    if (F32) return ((const float*)p)[i];
+    return bf2f(((const uint16_t*)p)[i]);
+}
+template <int F32>
+DEV void act_st(void* p, uint64_t i, float v) {
+    if (F32) ((float*)p)[i] = v;
+    else ((uint16_t*)p)[i] = (uint16_t)f2bf(v);
+}
+template <int F32>
+DEV float rnd(float v) { return F32 ? v : bf2f(f2bf(v)); }
+// A double rounded once to the activation format (nearest, ties to even): fp32 directly; bf16
+// by rounding the double's significand to 8 bits (below the fp32 normal range through fp32).
+template <int F32>
+DEV float rnd_d(double v) {
+    if (F32) return (float)v;
+    uint64_t u = (uint64_t)__double_as_longlong(v);
+    const uint32_t e = (uint32_t)(u >> 52) & 0x7ffu;
+    if (e == 0x7ffu || e < 1023u - 126u) return bf2f(f2bf((float)v));
+    u += (1ull << 44) - 1ull + ((u >> 45) & 1ull);
+    u &= ~((1ull << 45) - 1ull);
+    return (float)__longlong_as_double((long long)u);
+}
+DEV double wave_sum_d(double v) {
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+struct Shared {
+    uint32_t abort_;
+    uint32_t pad_[3];
+    double dpart[kPfWaves];
+    float part[2 * kPfWaves];
+    int32_t ipart[kPfWaves];
+    RowAddr rows[kPfMaxNt];          // B rows of the current GEMM tile
+    float scale[kPfMaxNt];           // their int8 scales
+};
+
+struct Ctx {
+    const PfParams* P;
+    Shared* S;
+    uint8_t* lds;                    // kPfLdsBytes of tile staging
+    uint64_t deadline;
+};
+
+DEV void raise_timeout(const Ctx& c) {
+    __hip_atomic_store(&c.S->abort_, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_store(c.P->abort_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&c.P->status[0], kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// Wait for every producer of the task's counter (thread 0 spins; the workgroup barrier then
+// releases the other waves). Bounded by the watchdog and the global abort flag.
+DEV void task_wait(const Ctx& c, const PfTask& T) {
+    if (T.wctr == kPfNone) return;
+    const PfParams& P = *c.P;
+    if (threadIdx.x == 0) {
+        const uint32_t target = T.wcnt * (P.epoch + 1u);
+        uint32_t n = 0;
+        while ((int32_t)(__hip_atomic_load(&P.ctr[T.wctr], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - target) < 0) {
+            if (__hip_atomic_load(&c.S->abort_, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) break;
+            if (((++n) & 15u) == 1) {
+                if (rt() > c.deadline) { raise_timeout(c); break; }
+                if ((n & 0xfffu) == 1 && __hip_atomic_load(P.abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+                    __hip_atomic_store(&c.S->abort_, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                    break;
+                }
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    __syncthreads();
+}
+
+// Publish the task's outputs: every wave's stores are written back at device scope, then one
+// increment of the task's counter.
+DEV void task_signal(const Ctx& c, const PfTask& T) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (T.sctr != kPfNone && threadIdx.x == 0)
+        __hip_atomic_fetch_add(&c.P->ctr[T.sctr], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ------------------------------------------------------------------ GEMM tile
+
+DEV const RowAddr& row_addr(const PfParams& P, uint32_t mat, uint32_t layer, uint32_t row) {
+    return P.rowtab[P.tab_base[mat] + layer * P.tab_rows[mat] + row];
+}
+
+// Bytes of one weight row segment of 16 bytes, in elements, per format.
+template <int FMT>
+constexpr int codes_per_seg() {
+    return FMT == AMK_F32 ? 4 : FMT == AMK_BF16 ? 8 : FMT == AMK_INT8_PC ? 16 : 32;
+}
+
+// C[mt x nt] = A[mt x K] * B[nt x K]^T for one tile. A: activation rows (row-major, lda
+// elements per row, rows >= mvalid read as zero). B: the rows in S.rows (nt of them). On return
+// the tile (int8 scales applied) is in LDS as fp32 [64][nt + 4], followed by a barrier.
+template <int FMT>
+DEV void gemm_tile(const Ctx& c, const void* A, uint32_t lda, uint32_t m0, uint32_t mvalid, uint32_t nt, uint32_t K) {
+    constexpr int F32 = FMT == AMK_F32;
+    constexpr int Kt = F32 ? kPfKt32 : kPfKt16;
+    constexpr int Pad = F32 ? kPfPad32 : kPfPad16;
+    constexpr int ES = F32 ? 4 : 2;                 // compute element bytes
+    constexpr int LD = Kt + Pad;                    // LDS row pitch (elements)
+    constexpr int EPS_A = 16 / ES;                  // activation elements per 16-byte segment
+    constexpr int SEGS_A = kPfMt * Kt / EPS_A / kPfThreads;   // per thread (4)
+    constexpr int CPS = codes_per_seg<FMT>();
+    constexpr int SPR = Kt / CPS;                   // weight segments per row per stage
+    constexpr int SEGS_B = kPfMaxNt * SPR / kPfThreads;       // per thread, at most
+    static_assert(SEGS_A * kPfThreads * EPS_A == kPfMt * Kt, "A staging");
+    const PfParams& P = *c.P;
+    Shared& S = *c.S;
+    uint8_t* Abuf = c.lds;
+    uint8_t* Bbuf = c.lds + kPfMt * LD * ES;
+    const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
+    const uint32_t nbn = nt / 16, nblk = 4 * nbn;   // 16x16 blocks (4 row blocks: rows past mvalid are zeros)
+    const uint32_t stages = (K + Kt - 1) / Kt;
+    const uint32_t segs_b = nt * SPR;
+
+    u32x4 ra[SEGS_A], rb[SEGS_B];
+    auto load = [&](uint32_t s) {
+        const uint32_t k0 = s * Kt;
+#pragma unroll
+        for (int i = 0; i < SEGS_A; ++i) {
+            const uint32_t g = (uint32_t)tid + (uint32_t)i * kPfThreads;
+            const uint32_t r = g / (Kt / EPS_A), col = (g % (Kt / EPS_A)) * EPS_A, k = k0 + col;
+            ra[i] = u32x4{0, 0, 0, 0};
+            if (r < mvalid && k < K) ra[i] = *(const u32x4*)((const uint8_t*)A + ((uint64_t)(m0 + r) * lda + k) * ES);
+        }
+#pragma unroll
+        for (int i = 0; i < SEGS_B; ++i) {
+            const uint32_t g = (uint32_t)tid + (uint32_t)i * kPfThreads;
+            const uint32_t r = g / SPR, k = k0 + (g % SPR) * CPS;
+            rb[i] = u32x4{0, 0, 0, 0};
+            if (g < segs_b && k < K) {
+                const uint64_t off = S.rows[r].codes + (FMT == AMK_F32 ? 4ull * k : FMT == AMK_BF16 ? 2ull * k
+                                                       : FMT == AMK_INT8_PC ? (uint64_t)k : (uint64_t)k / 2);
+                rb[i] = __builtin_nontemporal_load((const u32x4*)(P.wstream + off));
+            }
+        }
+    };
+    auto store = [&]() {
+#pragma unroll
+        for (int i = 0; i < SEGS_A; ++i) {
+            const uint32_t g = (uint32_t)tid + (uint32_t)i * kPfThreads;
+            const uint32_t r = g / (Kt / EPS_A), col = (g % (Kt / EPS_A)) * EPS_A;
+            *(u32x4*)(Abuf + (r * LD + col) * ES) = ra[i];
+        }
+#pragma unroll
+        for (int i = 0; i < SEGS_B; ++i) {
+            const uint32_t g = (uint32_t)tid + (uint32_t)i * kPfThreads;
+            if (g >= segs_b) continue;
+            const uint32_t r = g / SPR, col = (g % SPR) * CPS;
+            uint8_t* dst = Bbuf + (r * LD + col) * ES;
+            if (FMT == AMK_F32 || FMT == AMK_BF16) {
+                *(u32x4*)dst = rb[i];
+            } else if (FMT == AMK_INT8_PC) {
+                // 16 signed codes -> 16 bf16 (exact)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    u32x4 o;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t word = rb[i][2 * h + j / 2];
+                        const int b0 = (int)(int8_t)(word >> (16 * (j & 1)));
+                        const int b1 = (int)(int8_t)(word >> (16 * (j & 1) + 8));
+                        o[j] = (__float_as_uint((float)b0) >> 16) | (__float_as_uint((float)b1) & 0xffff0000u);
+                    }
+                    *(u32x4*)(dst + 16 * h) = o;
+                }
+            } else {
+                // 32 int4 codes (low nibble first, biased by 8) -> 32 bf16 (exact)
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    const uint32_t word = rb[i][h];
+                    u32x4 o;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int c0 = (int)((word >> (8 * j)) & 15u) - 8;
+                        const int c1 = (int)((word >> (8 * j + 4)) & 15u) - 8;
+                        o[j] = (__float_as_uint((float)c0) >> 16) | (__float_as_uint((float)c1) & 0xffff0000u);
+                    }
+                    *(u32x4*)(dst + 16 * h) = o;
+                }
+            }
+        }
+    };
+
+    f32x4 acc[4], part[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { acc[j] = f32x4{0.f, 0.f, 0.f, 0.f}; part[j] = acc[j]; }
+    const int q = lane & 15, kq = lane >> 4;
+
+    load(0);
+    for (uint32_t s = 0; s < stages; ++s) {
+        store();
+        __syncthreads();
+        if (s + 1 < stages) load(s + 1);   // in flight while the matrix cores work
+        const uint32_t kv = min((uint32_t)Kt, K - s * Kt);   // valid columns of this stage (multiple of 16)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t b = (uint32_t)w + 8u * (uint32_t)j;
+            if (b >= nblk) break;
+            const uint32_t bm = b / nbn, bn = b % nbn;
+            const uint8_t* arow = Abuf + (uint64_t)((bm * 16 + q) * LD) * ES;
+            const uint8_t* brow = Bbuf + (uint64_t)((bn * 16 + q) * LD) * ES;
+            if (F32) {
+                for (uint32_t k0 = 0; k0 < kv; k0 += 32) {
+                    part[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    for (uint32_t kk = k0; kk < k0 + 32 && kk < kv; kk += 4) {
+                        const float av = *(const float*)(arow + (kk + kq) * 4);
+                        const float bv = *(const float*)(brow + (kk + kq) * 4);
+                        part[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, part[j], 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[j][i] += part[j][i];
+                }
+            } else if (FMT == AMK_INT4_G128) {
+                // per 128-column group: partial sum, then scaled into the total
+                for (uint32_t g0 = 0; g0 < kv; g0 += 128) {
+                    part[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (uint32_t kk = 0; kk < 128; kk += 32) {
+                        const bf16x8 av = *(const bf16x8*)(arow + (g0 + kk + kq * 8) * 2);
+                        const bf16x8 bv = *(const bf16x8*)(brow + (g0 + kk + kq * 8) * 2);
+                        part[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, part[j], 0, 0, 0);
+                    }
+                    const uint32_t n = bn * 16 + (uint32_t)q, grp = (s * Kt + g0) / 128;
+                    const float sc = h2f(*(const uint16_t*)(P.wstream + S.rows[n].scales + 2ull * grp));
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[j][i] += sc * part[j][i];
+                }
+            } else {
+                for (uint32_t k0 = 0; k0 < kv; k0 += 128) {
+                    part[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    for (uint32_t kk = k0; kk < k0 + 128 && kk < kv; kk += 32) {
+                        const bf16x8 av = *(const bf16x8*)(arow + (kk + kq * 8) * 2);
+                        const bf16x8 bv = *(const bf16x8*)(brow + (kk + kq * 8) * 2);
+                        part[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, part[j], 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[j][i] += part[j][i];
+                }
+            }
+        }
+        __syncthreads();
+    }
+    // the tile to LDS, fp32 [64][nt + 4] (over the staging area, free after the last barrier)
+    float* C = (float*)c.lds;
+    const uint32_t ldc = nt + 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t b = (uint32_t)w + 8u * (uint32_t)j;
+        if (b >= nblk) break;
+        const uint32_t bm = b / nbn, bn = b % nbn, n = bn * 16 + (uint32_t)q;
+        const float sc = FMT == AMK_INT8_PC ? S.scale[n] : 1.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) C[(bm * 16 + (uint32_t)kq * 4 + (uint32_t)i) * ldc + n] = acc[j][i] * sc;
+    }
+    __syncthreads();
+}
+
+// Row addresses (and int8 scales) of the tile's B rows into LDS. rows(i) -> (matrix, row).
+template <int FMT, typename F>
+DEV void stage_rows(const Ctx& c, uint32_t nt, uint32_t layer, F&& rows) {
+    const PfParams& P = *c.P;
+    Shared& S = *c.S;
+    for (uint32_t i = threadIdx.x; i < nt; i += kPfThreads) {
+        uint32_t mat, r;
+        rows(i, mat, r);
+        const RowAddr a = row_addr(P, mat, mat == PM_LM ? 0 : layer, r);
+        S.rows[i] = a;
+        S.scale[i] = FMT == AMK_INT8_PC ? h2f(*(const uint16_t*)(P.wstream + a.scales)) : 1.f;
+    }
+    __syncthreads();
+}
+
+// rows of the task's M-tile that hold tokens of this launch
+DEV uint32_t rows_valid(const PfParams& P, const PfTask& T) {
+    return T.m0 < (uint32_t)P.T ? min(T.mt, (uint32_t)P.T - T.m0) : 0u;
+}
+
+DEV uint64_t kv_index(const PfParams& P, int layer, int isv, int g, uint32_t pos) {
+    return ((((uint64_t)layer * 2 + isv) * P.nKV + g) * P.max_ctx + pos) * P.hd;
+}
+
+template <int FMT>
+DEV void op_qkv(const Ctx& c, const PfTask& T) {
+    constexpr int F32 = FMT == AMK_F32;
+    const PfParams& P = *c.P;
+    const uint32_t l = T.layer, j = T.n0, hd = (uint32_t)P.hd, half = hd / 2;
+    const uint32_t nH = (uint32_t)P.nH, nKV = (uint32_t)P.nKV;
+    const uint32_t mvalid = rows_valid(P, T);
+    const uint32_t mat = j < nH ? PM_WQ : j < nH + nKV ? PM_WK : PM_WV;
+    const uint32_t head = j < nH ? j : j < nH + nKV ? j - nH : j - nH - nKV;
+    stage_rows<FMT>(c, hd, l, [&](uint32_t i, uint32_t& m, uint32_t& r) { m = mat; r = head * hd + i; });
+    gemm_tile<FMT>(c, P.h, (uint32_t)P.H, T.m0, mvalid, hd, (uint32_t)P.H);
+    const float* C = (const float*)c.lds;
+    const uint32_t ldc = hd + 4;
+    const uint32_t qd = nH * hd;
+    if (mat == PM_WV) {
+        for (uint32_t e = threadIdx.x; e < mvalid * hd; e += kPfThreads) {
+            const uint32_t m = e / hd, d = e % hd;
+            act_st<F32>(P.kv, kv_index(P, (int)l, 1, (int)head, (uint32_t)P.pos0 + T.m0 + m) + d, C[m * ldc + d]);
+        }
+        return;
+    }
+    for (uint32_t e = threadIdx.x; e < mvalid * half; e += kPfThreads) {
+        const uint32_t m = e / half, i = e % half, pos = (uint32_t)P.pos0 + T.m0 + m;
+        const float v0 = C[m * ldc + i], v2 = C[m * ldc + i + half];
+        const float cs = P.rope[((uint64_t)pos * half + i) * 2], sn = P.rope[((uint64_t)pos * half + i) * 2 + 1];
+        const float a = v0 * cs - v2 * sn, b = v2 * cs + v0 * sn;
+        if (mat == PM_WQ) {
+            const uint64_t base = (uint64_t)(T.m0 + m) * qd + head * hd;
+            act_st<F32>(P.q, base + i, a);
+            act_st<F32>(P.q, base + i + half, b);
+        } else {
+            const uint64_t base = kv_index(P, (int)l, 0, (int)head, pos);
+            act_st<F32>(P.kv, base + i, a);
+            act_st<F32>(P.kv, base + i + half, b);
+        }
+    }
+}
+
+// O or down projection + residual: x[m][n0 .. n0 + nn) += A[m] . W[n]
+template <int FMT>
+DEV void op_resid(const Ctx& c, const PfTask& T, bool down) {
+    constexpr int F32 = FMT == AMK_F32;
+    const PfParams& P = *c.P;
+    const uint32_t nn = T.nn, H = (uint32_t)P.H;
+    const uint32_t mvalid = rows_valid(P, T);
+    const uint32_t K = down ? (uint32_t)P.I : (uint32_t)(P.nH * P.hd);
+    stage_rows<FMT>(c, nn, T.layer, [&](uint32_t i, uint32_t& m, uint32_t& r) { m = down ? PM_WD : PM_WO; r = T.n0 + i; });
+    gemm_tile<FMT>(c, down ? P.a : P.o, K, T.m0, mvalid, nn, K);
+    const float* C = (const float*)c.lds;
+    const uint32_t ldc = nn + 4;
+    for (uint32_t e = threadIdx.x; e < mvalid * nn; e += kPfThreads) {
+        const uint32_t m = e / nn, n = e % nn;
+        const uint64_t xi = (uint64_t)(T.m0 + m) * H + T.n0 + n;
+        act_st<F32>(P.x, xi, act_ld<F32>(P.x, xi) + C[m * ldc + n]);
+    }
+}
+
+// gate/up for j in [n0, n0 + nn): B rows = nn gate rows then nn up rows; a = silu(g) * u
+template <int FMT>
+DEV void op_gateup(const Ctx& c, const PfTask& T) {
+    constexpr int F32 = FMT == AMK_F32;
+    const PfParams& P = *c.P;
+    const uint32_t nn = T.nn, I = (uint32_t)P.I;
+    const uint32_t mvalid = rows_valid(P, T);
+    stage_rows<FMT>(c, 2 * nn, T.layer, [&](uint32_t i, uint32_t& m, uint32_t& r) {
+        m = i < nn ? PM_WG : PM_WU;
+        r = T.n0 + (i < nn ? i : i - nn);
+    });
+    gemm_tile<FMT>(c, P.h, (uint32_t)P.H, T.m0, mvalid, 2 * nn, (uint32_t)P.H);
+    const float* C = (const float*)c.lds;
+    const uint32_t ldc = 2 * nn + 4;
+    for (uint32_t e = threadIdx.x; e < mvalid * nn; e += kPfThreads) {
+        const uint32_t m = e / nn, j = e % nn;
+        const float G = C[m * ldc + j], U = C[m * ldc + nn + j];
+        act_st<F32>(P.a, (uint64_t)(T.m0 + m) * I + T.n0 + j, (G / (1.0f + expf(-G))) * U);
+    }
+}
+
+// RMSNorm of rows [m0, m0 + mt): h = round(x * r * g). Layer 0's attention norm first copies
+// the token embeddings into x.
+template <int FMT>
+DEV void op_norm(const Ctx& c, const PfTask& T) {
+    constexpr int F32 = FMT == AMK_F32;
+    const PfParams& P = *c.P;
+    const uint32_t H = (uint32_t)P.H;
+    const uint32_t mend = min(T.m0 + T.mt, (uint32_t)P.T);
+    const float* g = P.norms + ((uint64_t)2 * T.layer + T.n0) * H;
+    const bool gather = T.layer == 0 && T.n0 == 0;
+    const int lane = lane_id(), w = threadIdx.x >> 6;
+    for (uint32_t m = T.m0 + (uint32_t)w; m < mend; m += kPfWaves) {
+        if (gather) {
+            int tok = P.tokens[m];
+            if (tok < 0 || tok >= P.V) {
+                if (lane == 0) __hip_atomic_store(&P.status[1], kStatusBadToken, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                tok = 0;
+            }
+            for (uint32_t k = (uint32_t)lane; k < H; k += 64)
+                act_st<F32>(P.x, (uint64_t)m * H + k, act_ld<F32>(P.embed, (uint64_t)tok * H + k));
+        }
+        // in double, as the norm is defined: the scale multiplies every element, so an error in
+        // it moves every value near a rounding boundary of the activation format at once
+        double ss = 0.0;
+        for (uint32_t k = (uint32_t)lane; k < H; k += 64) {
+            const double v = act_ld<F32>(P.x, (uint64_t)m * H + k);
+            ss += v * v;
+        }
+        ss = wave_sum_d(ss);
+        const double r = 1.0 / sqrt(ss / (double)H + (double)P.eps);
+        for (uint32_t k = (uint32_t)lane; k < H; k += 64)
+            act_st<F32>(P.h, (uint64_t)m * H + k, rnd_d<F32>(((double)act_ld<F32>(P.x, (uint64_t)m * H + k) * r) * (double)g[k]));
+    }
+}
+
+// Causal attention of queries [m0, m0 + mt) of query head n0 over cache rows [0, pos0 + m].
+template <int FMT>
+DEV void op_attn(const Ctx& c, const PfTask& T) {
+    constexpr int F32 = FMT == AMK_F32;
+    const PfParams& P = *c.P;
+    const uint32_t hd = (uint32_t)P.hd, h = T.n0, qd = (uint32_t)(P.nH * P.hd);
+    const int g = (int)((uint64_t)h * P.nKV / P.nH);
+    const uint32_t mvalid = rows_valid(P, T);
+    const int lane = lane_id(), w = threadIdx.x >> 6;
+    float* Qs = (float*)c.lds;                       // [64][hd]
+    float* KT = Qs + kPfMt * 128;                    // [hd][65]
+    float* Vs = KT + 128 * 65;                       // [64][hd + 4]
+    const uint32_t ldv = hd + 4;
+    for (uint32_t e = threadIdx.x; e < mvalid * hd; e += kPfThreads) {
+        const uint32_t m = e / hd, d = e % hd;
+        Qs[m * hd + d] = act_ld<F32>(P.q, (uint64_t)(T.m0 + m) * qd + h * hd + d);
+    }
+    if (mvalid == 0) return;
+    const uint32_t last = (uint32_t)P.pos0 + T.m0 + mvalid - 1;   // last position any query sees
+    const uint32_t nblocks = last / 64 + 1;
+    const float scale = P.attn_scale;
+    // per wave: queries w, w + 8, ... (at most 8); state in registers
+    float mrun[8], lrun[8], o0[8], o1[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { mrun[i] = -INFINITY; lrun[i] = 0.f; o0[i] = 0.f; o1[i] = 0.f; }
+    const uint64_t kbase = kv_index(P, (int)T.layer, 0, g, 0), vbase = kv_index(P, (int)T.layer, 1, g, 0);
+    for (uint32_t b = 0; b < nblocks; ++b) {
+        const uint32_t p0 = b * 64;
+        __syncthreads();   // the previous block is no longer read
+        // 16-byte segments of the K and V rows: consecutive threads take consecutive positions,
+        // so the transposed K stores go to consecutive LDS words
+        constexpr uint32_t EPS = F32 ? 4 : 8;
+        for (uint32_t e = threadIdx.x; e < 64 * (hd / EPS); e += kPfThreads) {
+            const uint32_t p = e % 64, d0 = (e / 64) * EPS, pos = p0 + p;
+            u32x4 ku = u32x4{0, 0, 0, 0}, vu = u32x4{0, 0, 0, 0};
+            if (pos <= last) {
+                const uint64_t es = F32 ? 4 : 2;
+                ku = *(const u32x4*)((const uint8_t*)P.kv + (kbase + (uint64_t)pos * hd + d0) * es);
+                vu = *(const u32x4*)((const uint8_t*)P.kv + (vbase + (uint64_t)pos * hd + d0) * es);
+            }
+#pragma unroll
+            for (uint32_t j = 0; j < EPS; ++j) {
+                const float kf = F32 ? __uint_as_float(ku[j]) : bf2f((ku[j / 2] >> (16 * (j % 2))) & 0xffffu);
+                const float vf = F32 ? __uint_as_float(vu[j]) : bf2f((vu[j / 2] >> (16 * (j % 2))) & 0xffffu);
+                KT[(d0 + j) * 65 + p] = kf;
+                Vs[p * ldv + d0 + j] = vf;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t m = (uint32_t)w + 8u * (uint32_t)i;
+            if (m >= mvalid) break;
+            const uint32_t qpos = (uint32_t)P.pos0 + T.m0 + m;
+            if (p0 > qpos) continue;
+            float s = 0.f;
+            for (uint32_t d = 0; d < hd; ++d) s += Qs[m * hd + d] * KT[d * 65 + lane];
+            s *= scale;
+            const bool ok = p0 + (uint32_t)lane <= qpos;
+            if (!ok) s = -INFINITY;
+            const float mnew = fmaxf(mrun[i], wave_max(s));
+            const float alpha = __expf(mrun[i] - mnew);
+            const float pw = ok ? __expf(s - mnew) : 0.f;
+            lrun[i] = lrun[i] * alpha + wave_sum(pw);
+            mrun[i] = mnew;
+            float a0 = o0[i] * alpha, a1 = o1[i] * alpha;
+            const uint32_t d0 = (uint32_t)lane % hd, d1 = (uint32_t)lane + 64;
+#pragma unroll 16
+            for (int p = 0; p < 64; ++p) {
+                const float wp = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pw), p));
+                a0 += wp * Vs[p * ldv + d0];
+                if (hd > 64) a1 += wp * Vs[p * ldv + (d1 < hd ? d1 : 0)];
+            }
+            o0[i] = a0;
+            o1[i] = a1;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t m = (uint32_t)w + 8u * (uint32_t)i;
+        if (m >= mvalid) break;
+        const uint64_t base = (uint64_t)(T.m0 + m) * qd + h * hd;
+        const float inv = 1.0f / lrun[i];
+        if ((uint32_t)lane < hd) act_st<F32>(P.o, base + lane, o0[i] * inv);
+        if (hd > 64 && (uint32_t)lane + 64 < hd) act_st<F32>(P.o, base + lane + 64, o1[i] * inv);
+    }
+}
+
+// Final RMSNorm of the last row, LM rows [n0, n0 + nn), tile argmax (lowest index among the
+// maxima; a NaN marks the tile).
+template <int FMT>
+DEV void op_lm(const Ctx& c, const PfTask& T) {
+    constexpr int F32 = FMT == AMK_F32;
+    const PfParams& P = *c.P;
+    Shared& S = *c.S;
+    const uint32_t H = (uint32_t)P.H;
+    const int lane = lane_id(), w = threadIdx.x >> 6;
+    float* hf = (float*)c.lds;   // [H]
+    const uint64_t xr = (uint64_t)(P.T - 1) * H;
+    double ss = 0.0;
+    for (uint32_t k = threadIdx.x; k < H; k += kPfThreads) {
+        const double v = act_ld<F32>(P.x, xr + k);
+        ss += v * v;
+    }
+    ss = wave_sum_d(ss);
+    if (lane == 0) S.dpart[w] = ss;
+    __syncthreads();
+    double tot = 0.0;
+    for (int i = 0; i < kPfWaves; ++i) tot += S.dpart[i];
+    const double r = 1.0 / sqrt(tot / (double)H + (double)P.eps);
+    const float* g = P.norms + (uint64_t)2 * P.L * H;
+    for (uint32_t k = threadIdx.x; k < H; k += kPfThreads)
+        hf[k] = rnd_d<F32>(((double)act_ld<F32>(P.x, xr + k) * r) * (double)g[k]);
+    __syncthreads();
+    constexpr int CPS = codes_per_seg<FMT>();
+    const uint32_t nseg = H / CPS;
+    float best = -INFINITY;
+    int bi = 0x7fffffff;
+    bool nan = false;
+    for (uint32_t v = T.n0 + (uint32_t)w; v < T.n0 + T.nn; v += kPfWaves) {
+        const RowAddr a = row_addr(P, PM_LM, 0, v);
+        const uint8_t* row = P.wstream + a.codes;
+        float acc = 0.f;
+        for (uint32_t sgi = (uint32_t)lane; sgi < nseg; sgi += 64) {
+            const u32x4 u = __builtin_nontemporal_load((const u32x4*)(row + 16ull * sgi));
+            const uint32_t k0 = sgi * CPS;
+            float part = 0.f;
+            if (FMT == AMK_F32) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) part += __uint_as_float(u[j]) * hf[k0 + j];
+            } else if (FMT == AMK_BF16) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    part += bf2f(u[j] & 0xffffu) * hf[k0 + 2 * j];
+                    part += bf2f(u[j] >> 16) * hf[k0 + 2 * j + 1];
+                }
+            } else if (FMT == AMK_INT8_PC) {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) part += (float)(int8_t)(u[j / 4] >> (8 * (j % 4))) * hf[k0 + j];
+            } else {
+#pragma unroll
+                for (int j = 0; j < 32; ++j) part += (float)((int)((u[j / 8] >> (4 * (j % 8))) & 15u) - 8) * hf[k0 + j];
+                part *= h2f(*(const uint16_t*)(P.wstream + a.scales + 2ull * (k0 / 128)));
+            }
+            acc += part;
+        }
+        acc = wave_sum(acc);
+        if (FMT == AMK_INT8_PC) acc *= h2f(*(const uint16_t*)(P.wstream + a.scales));
+        if (lane == 0 && P.logits) P.logits[v] = acc;
+        if (acc != acc) nan = true;
+        else if (acc > best || (acc == best && (int)v < bi)) { best = acc; bi = (int)v; }
+    }
+    if (lane == 0) { S.part[kPfWaves + w] = best; S.ipart[w] = nan ? -1 : bi; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float b = -INFINITY;
+        int i0 = 0x7fffffff;
+        bool bad = false;
+        for (int i = 0; i < kPfWaves; ++i) {
+            if (S.ipart[i] < 0) bad = true;
+            else if (S.part[kPfWaves + i] > b || (S.part[kPfWaves + i] == b && S.ipart[i] < i0)) { b = S.part[kPfWaves + i]; i0 = S.ipart[i]; }
+        }
+        P.lmpart[2 * T.mt] = __float_as_uint(b);
+        P.lmpart[2 * T.mt + 1] = bad ? 0xffffffffu : (uint32_t)i0;
+    }
+}
+
+DEV void op_argmax(const Ctx& c, const PfTask& T) {
+    const PfParams& P = *c.P;
+    if (threadIdx.x != 0) return;
+    float b = -INFINITY;
+    int i0 = 0x7fffffff;
+    bool bad = false;
+    for (uint32_t t = 0; t < T.mt; ++t) {
+        const float v = __uint_as_float(P.lmpart[2 * t]);
+        const int i = (int)P.lmpart[2 * t + 1];
+        if (i < 0) bad = true;
+        else if (v > b || (v == b && i < i0)) { b = v; i0 = i; }
+    }
+    P.tok_out[0] = bad ? -1 : i0;
+}
+
+template <int FMT>
+DEV void prefill_body(const PfParams& Pin) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kPfLdsBytes];
+    __shared__ Shared S;
+    const PfParams P = Pin;
+    if (threadIdx.x == 0) S.abort_ = 0;
+    __syncthreads();
+    Ctx c;
+    c.P = &P;
+    c.S = &S;
+    c.lds = lds;
+    c.deadline = rt() + P.watchdog_ticks;
+    const uint32_t q0 = P.queue_off[blockIdx.x], q1 = P.queue_off[blockIdx.x + 1];
+    for (uint32_t t = q0; t < q1; ++t) {
+        uint32_t wd[sizeof(PfTask) / 4];
+        __builtin_memcpy(wd, &P.tasks[t], sizeof(PfTask));
+#pragma unroll
+        for (int k = 0; k < (int)(sizeof(PfTask) / 4); ++k) wd[k] = __builtin_amdgcn_readfirstlane(wd[k]);
+        PfTask T;
+        __builtin_memcpy(&T, wd, sizeof(PfTask));
+        task_wait(c, T);
+        switch (T.op) {
+        case PF_NORM: op_norm<FMT>(c, T); break;
+        case PF_QKV: op_qkv<FMT>(c, T); break;
+        case PF_ATTN: op_attn<FMT>(c, T); break;
+        case PF_OPROJ: op_resid<FMT>(c, T, false); break;
+        case PF_GATEUP: op_gateup<FMT>(c, T); break;
+        case PF_DOWN: op_resid<FMT>(c, T, true); break;
+        case PF_LM: if (P.do_lm) op_lm<FMT>(c, T); break;
+        default: if (P.do_lm) op_argmax(c, T); break;
+        }
+        task_signal(c, T);
+    }
+}
+
+}  // namespace
+
+extern "C" __global__ void __launch_bounds__(kPfThreads, 1) amk_prefill_f32(PfParams P) { prefill_body<AMK_F32>(P); }
+extern "C" __global__ void __launch_bounds__(kPfThreads, 1) amk_prefill_bf16(PfParams P) { prefill_body<AMK_BF16>(P); }
+extern "C" __global__ void __launch_bounds__(kPfThreads, 1) amk_prefill_int8(PfParams P) { prefill_body<AMK_INT8_PC>(P); }
+extern "C" __global__ void __launch_bounds__(kPfThreads, 1) amk_prefill_int4(PfParams P) { prefill_body<AMK_INT4_G128>(P); }
+
+namespace {
+const void* pf_kernel_for(int wfmt) {
+    switch (wfmt) {
+    case AMK_F32: return (const void*)amk_prefill_f32;
+    case AMK_BF16: return (const void*)amk_prefill_bf16;
+    case AMK_INT8_PC: return (const void*)amk_prefill_int8;
+    default: return (const void*)amk_prefill_int4;
+    }
+}
+}  // namespace
+
+hipError_t launch_prefill(const PfParams& p, int n_cu, hipStream_t st) {
+    PfParams local = p;
+    void* args[] = {&local};
+    return hipLaunchCooperativeKernel(pf_kernel_for(p.wfmt), dim3(n_cu), dim3(kPfThreads), args, 0, st);
+}
+
+int prefill_blocks_per_cu(int wfmt) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, pf_kernel_for(wfmt), kPfThreads, 0) != hipSuccess) return 0;
+    return nb;
+}
+
+}  // namespace amk

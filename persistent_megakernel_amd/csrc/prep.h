@@ -19,4 +19,9 @@ hipError_t launch_megakernel(const KParams& p, int n_cu, hipStream_t st);
 // Workgroups of the megakernel for weight format wfmt that fit on one CU (0 = it cannot run).
 int megakernel_blocks_per_cu(int wfmt);
 
+// The prefill kernel: one cooperative launch of n_cu workgroups of kPfThreads.
+struct PfParams;
+hipError_t launch_prefill(const PfParams& p, int n_cu, hipStream_t st);
+int prefill_blocks_per_cu(int wfmt);
+
 }  // namespace amk

@@ -1,0 +1,90 @@
+"""The prefill lowering on the CPU: every workload's schedule is accepted by the validator at
+several chunk sizes, runs clean on the CPU executor, and a schedule with a wait removed is
+rejected; sizes outside one launch are refused."""
+import random
+
+import pytest
+
+import amk_inputs as I
+
+
+@pytest.fixture(scope="module")
+def M():
+    import persistent_megakernel_amd as M
+    M.lib()
+    return M
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "smollm2_135m_bf16", "tinyllama_int8"])
+@pytest.mark.parametrize("n", [1, 63, 64, 65, 256])
+def test_prefill_schedule_accepted(M, name, n):
+    v = M.amk_lower_prefill(M.model_desc(I.SHAPES[name]), 256, n, python=False)
+    assert v.accepted, (name, n, hex(v.rule_mask), v.task, v.region)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["llama7b_bf16", "llama3_8b_int4"])
+def test_prefill_schedule_accepted_large(M, name):
+    v = M.amk_lower_prefill(M.model_desc(I.SHAPES[name]), 256, 256, python=False)
+    assert v.accepted, (name, hex(v.rule_mask))
+
+
+@pytest.mark.parametrize("n_cu,n", [(1, 3), (7, 64), (16, 130), (256, 200)])
+def test_prefill_schedule_runs_clean_on_the_executor(M, n_cu, n):
+    s = M.amk_lower_prefill(M.model_desc(I.SHAPES["tiny_fp32"]), n_cu, n)
+    for seed in range(3):
+        r = M.amk_vm_run(s, seed=seed, max_delay_us=3, watchdog_ms=10000)
+        assert r["completed"] and not r["races"] and not r["uncovered_reads"] and not r["unwritten_outputs"], r
+
+
+def test_prefill_schedule_structure(M):
+    """Per layer seven phases, each waiting on all of the previous one; LM tiles and one argmax."""
+    sh = I.SHAPES["tiny_fp32"]
+    s = M.amk_lower_prefill(M.model_desc(sh), 16, 100)
+    ops = [t.opcode for t in s.tasks]
+    nm = 2
+    nqkv = sh.n_heads + 2 * sh.n_kv_heads
+    per_layer = nm * (2 + nqkv + sh.n_heads + 2 * (sh.hidden // 64) + sh.intermediate // 16)
+    n_lm = ops.count(7)
+    assert ops.count(8) == 1 and n_lm >= 1
+    assert len(ops) == sh.n_layers * per_layer + n_lm + 1
+    # every wait is a full wait on the counter of the phase before
+    producers = {}
+    for i, t in enumerate(s.tasks):
+        for c in t.signals:
+            producers[c] = producers.get(c, 0) + 1
+    for t in s.tasks:
+        for c, th in t.waits:
+            assert th == producers[c]
+
+
+def test_prefill_schedule_without_a_wait(M):
+    """Dropping a queue's first wait on a counter is rejected unless the queue order already
+    orders every access it guarded (e.g. the norm task of the same M-tile earlier in the same
+    queue); whatever the validator still accepts runs clean on the executor."""
+    s = M.amk_lower_prefill(M.model_desc(I.SHAPES["tiny_fp32"]), 8, 70)
+    first = []
+    for q in s.queues:
+        seen = set()
+        for i in q:
+            for c, _ in s.tasks[i].waits:
+                if c not in seen:
+                    first.append(i)
+                    seen.add(c)
+    rejected = 0
+    for i in first:
+        m = s.copy()
+        m.tasks[i].waits = []
+        if not M.amk_validate(m).accepted:
+            rejected += 1
+            continue
+        for seed in range(3):
+            r = M.amk_vm_run(m, seed=seed, max_delay_us=20, watchdog_ms=10000)
+            assert r["completed"] and not r["races"] and not r["uncovered_reads"], (i, r)
+    assert rejected >= 0.9 * len(first), (rejected, len(first))
+
+
+@pytest.mark.parametrize("n", [0, -1, 257])
+def test_prefill_sizes_outside_one_launch_are_refused(M, n):
+    with pytest.raises(M.AmkError):
+        M.amk_lower_prefill(M.model_desc(I.SHAPES["tiny_fp32"]), 256, n)
