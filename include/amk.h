@@ -285,7 +285,8 @@ amk_status amk_decode_step(amk_ctx* ctx, const int32_t* token_in, int32_t pos, i
  * position (the first generated token). The projections run as matrix-core GEMM tiles over the
  * chunk's tokens; the schedule of each chunk size is lowered, validated (amk_validate) and
  * uploaded on first use, and the first call allocates the chunk's activation buffers (about
- * 256 x (3 x hidden + 2 x n_heads x head_dim + intermediate) activation values), so it is
+ * 256 x (hidden + 2 x n_heads x head_dim + intermediate) activation values and a few doubles
+ * per row), so it is
  * not capturable into a graph until every chunk size it uses has run once.
  *  tokens     device int32[n_tokens]; a token outside [0, vocab) is replaced by 0 and flagged
  *             in the device status word.
@@ -303,7 +304,8 @@ amk_status amk_prefill(amk_ctx* ctx, const int32_t* tokens, int32_t pos0, int32_
  * 256), in the schedule IR, for inspection with amk_validate / amk_vm_run on the CPU. Phase
  * tasks over M-tiles of 64 tokens; every task of a phase waits on one counter signalled by all
  * tasks of the previous phase. Accesses are declared in tile units over these regions: 0 the
- * token ids (input), 1 the residual stream x, 2 the normalised rows h, 3 the rotated queries,
+ * token ids (input), 1 the residual stream x, 2 the per-row sums of squares of x by column tile
+ * (the RMSNorm inputs of the next GEMM, which fuses the norm), 3 the rotated queries,
  * 4 the attention output, 5 the SwiGLU output, 6 the LM tile results, 7 the logits (output),
  * 8 the token out (output), 9 + layer the K and V rows of the chunk in that layer's cache.
  * Caller frees with amk_schedule_free. */
@@ -329,6 +331,17 @@ const amk_schedule* amk_ctx_schedule(const amk_ctx* ctx);
  * `capacity` uint64 values, caller-owned, borrowed until disabled; capacity must be at least
  * 6 * n_tasks (else AMK_E_INVALID_ARG). trace = NULL disables (the default). */
 amk_status amk_set_trace(amk_ctx* ctx, uint64_t* trace, uint64_t capacity);
+
+/* Per-task timestamp trace of the prefill launches (the same attribution of time to tasks and
+ * to waits as amk_set_trace, for the prefill's tile tasks). When `trace` is non-NULL, every
+ * later prefill launch whose schedule has at most capacity / 4 tasks writes, for each task, 4
+ * uint64 values at trace[4 * k ...], k = the task's index in queue order of that launch's
+ * schedule (amk_lower_prefill with the context's CU count and 64 x ceil(tokens / 64) tokens
+ * gives the same schedule): [0] task start, [1] its wait satisfied, [2] its work done, [3]
+ * signalled; ticks of the 100 MHz realtime counter. Launches with more tasks record nothing.
+ * trace: device memory of `capacity` uint64 values, caller-owned, borrowed until disabled.
+ * trace = NULL disables (the default). */
+amk_status amk_set_prefill_trace(amk_ctx* ctx, uint64_t* trace, uint64_t capacity);
 
 /* Synchronise the last stream, free every library-owned buffer; never touches caller
  * buffers. NULL-safe. */

@@ -23,7 +23,7 @@ from ._abi import (AMK_BF16, AMK_F32, AMK_INT4_G128, AMK_INT8_PC, AmkError, STAT
 __all__ = ["amk_validate", "amk_lower", "amk_create", "amk_decode_step", "amk_destroy",
            "amk_quantize", "amk_device_status", "amk_ctx_schedule", "amk_set_trace", "amk_version", "Decoder",
            "model_desc", "schedule_config", "AmkError", "amk_vm_run",
-           "amk_prefill", "amk_lower_prefill"]
+           "amk_prefill", "amk_lower_prefill", "amk_set_prefill_trace"]
 
 
 # ---------------------------------------------------------------- descriptors
@@ -237,6 +237,11 @@ def amk_set_trace(ctx: int, trace_ptr: int, capacity: int) -> None:
     check("amk_set_trace", lib().amk_set_trace(C.c_void_p(ctx), C.c_void_p(trace_ptr or None), int(capacity)))
 
 
+def amk_set_prefill_trace(ctx: int, trace_ptr: int, capacity: int) -> None:
+    check("amk_set_prefill_trace", lib().amk_set_prefill_trace(C.c_void_p(ctx), C.c_void_p(trace_ptr or None),
+                                                               int(capacity)))
+
+
 def amk_destroy(ctx: Optional[int]) -> None:
     lib().amk_destroy(C.c_void_p(ctx) if ctx else None)
 
@@ -340,6 +345,14 @@ class Decoder:
         self.trace = self.torch.zeros((n, A.TRACE_SLOTS), dtype=self.torch.int64, device=self.device)
         amk_set_trace(self.ctx, self.trace.data_ptr(), self.trace.numel())
         return self.trace
+
+    def enable_prefill_trace(self, n_tokens: int, n_cu: int):
+        """Record per-task timestamps of later prefill launches of n_tokens (<= 256) tokens;
+        returns (device int64 tensor [n_tasks, 4], the launch's schedule)."""
+        sched = amk_lower_prefill(self.desc, n_cu, ((n_tokens + 63) // 64) * 64)
+        self.pf_trace = self.torch.zeros((len(sched.tasks), 4), dtype=self.torch.int64, device=self.device)
+        amk_set_prefill_trace(self.ctx, self.pf_trace.data_ptr(), self.pf_trace.numel())
+        return self.pf_trace, sched
 
     def schedule(self):
         return amk_ctx_schedule(self.ctx)

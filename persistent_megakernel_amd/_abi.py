@@ -121,6 +121,7 @@ SIGNATURES = {
     "amk_version": (C.c_char_p, []),
     "amk_vm_run": (C.c_int, [C.POINTER(amk_schedule), C.POINTER(amk_vm_opts), C.POINTER(amk_vm_result)]),
     "amk_prefill": (C.c_int, [_P, _P, C.c_int32, C.c_int32, _P, _P, _P]),
+    "amk_set_prefill_trace": (C.c_int, [_P, _P, C.c_uint64]),
     "amk_lower_prefill": (C.c_int, [C.POINTER(amk_model_desc), C.c_int32, C.c_int32,
                                     C.POINTER(C.POINTER(amk_schedule))]),
 }

@@ -44,11 +44,13 @@ struct amk_ctx {
     RowAddr* d_rowtab = nullptr;
     uint32_t tab_base[PM_N] = {}, tab_rows[PM_N] = {};
     void* pf_x = nullptr;
-    void* pf_h = nullptr;
+    double* pf_ssq = nullptr;
     void* pf_q = nullptr;
     void* pf_o = nullptr;
     void* pf_a = nullptr;
     uint32_t* pf_lmpart = nullptr;
+    uint64_t* pf_trace = nullptr;   // caller-owned, optional
+    uint64_t pf_trace_cap = 0;
     struct PfVariant {
         PfLowered L;
         PfTask* d_tasks = nullptr;
@@ -86,7 +88,7 @@ void free_ctx(amk_ctx* c) {
     }
     (void)hipFree(c->d_rowtab);
     (void)hipFree(c->pf_x);
-    (void)hipFree(c->pf_h);
+    (void)hipFree(c->pf_ssq);
     (void)hipFree(c->pf_q);
     (void)hipFree(c->pf_o);
     (void)hipFree(c->pf_a);
@@ -381,13 +383,13 @@ amk_status pf_buffers(amk_ctx* c, int lm_tiles) {
     hipError_t e = hipSuccess;
     auto ck = [&](hipError_t r) { if (e == hipSuccess) e = r; };
     ck(hipMalloc(&c->pf_x, R * d.hidden * esz));
-    ck(hipMalloc(&c->pf_h, R * d.hidden * esz));
+    ck(hipMalloc((void**)&c->pf_ssq, 2 * R * (size_t)(d.hidden / pf_nt_x(d.hidden)) * sizeof(double)));
     ck(hipMalloc(&c->pf_q, R * d.n_heads * d.head_dim * esz));
     ck(hipMalloc(&c->pf_o, R * d.n_heads * d.head_dim * esz));
     ck(hipMalloc(&c->pf_a, R * d.intermediate * esz));
     ck(hipMalloc((void**)&c->pf_lmpart, 2 * sizeof(uint32_t) * (size_t)std::max(1, lm_tiles)));
     if (e != hipSuccess) {
-        for (void** p : {&c->pf_x, &c->pf_h, &c->pf_q, &c->pf_o, &c->pf_a, (void**)&c->pf_lmpart}) { (void)hipFree(*p); *p = nullptr; }
+        for (void** p : {&c->pf_x, (void**)&c->pf_ssq, &c->pf_q, &c->pf_o, &c->pf_a, (void**)&c->pf_lmpart}) { (void)hipFree(*p); *p = nullptr; }
         return e == hipErrorOutOfMemory ? AMK_E_OOM : AMK_E_HIP;
     }
     return AMK_OK;
@@ -428,7 +430,7 @@ extern "C" amk_status amk_prefill(amk_ctx* c, const int32_t* tokens, int32_t pos
         P.wstream = c->d_wstream;
         P.rowtab = c->d_rowtab;
         for (int m = 0; m < PM_N; ++m) { P.tab_base[m] = c->tab_base[m]; P.tab_rows[m] = c->tab_rows[m]; }
-        P.x = c->pf_x; P.h = c->pf_h; P.q = c->pf_q; P.o = c->pf_o; P.a = c->pf_a;
+        P.x = c->pf_x; P.ssq = c->pf_ssq; P.q = c->pf_q; P.o = c->pf_o; P.a = c->pf_a;
         P.lmpart = c->pf_lmpart;
         P.kv = c->base.kv;
         P.embed = c->d_embed;
@@ -440,6 +442,7 @@ extern "C" amk_status amk_prefill(amk_ctx* c, const int32_t* tokens, int32_t pos
         P.status = c->d_status;
         P.abort_flag = c->d_abort;
         P.watchdog_ticks = c->base.watchdog_ticks;
+        P.trace = c->pf_trace && c->pf_trace_cap >= (uint64_t)kPfTraceSlots * v->L.dtasks.size() ? c->pf_trace : nullptr;
         hipError_t e = launch_prefill(P, c->n_cu, st);
         if (e != hipSuccess) { logf("prefill", hipGetErrorString(e)); return AMK_E_HIP; }
         v->epoch++;
@@ -461,6 +464,13 @@ extern "C" amk_status amk_set_trace(amk_ctx* c, uint64_t* trace, uint64_t capaci
     if (!c) return AMK_E_INVALID_ARG;
     if (trace && capacity < (uint64_t)kTraceSlots * c->L.dtasks.size()) return AMK_E_INVALID_ARG;
     c->trace = trace;
+    return AMK_OK;
+}
+
+extern "C" amk_status amk_set_prefill_trace(amk_ctx* c, uint64_t* trace, uint64_t capacity) {
+    if (!c || (trace && capacity == 0)) return AMK_E_INVALID_ARG;
+    c->pf_trace = trace;
+    c->pf_trace_cap = trace ? capacity : 0;
     return AMK_OK;
 }
 

@@ -3,16 +3,17 @@
 // check (AutoMegaKernel pages: page 2, "Statically verified schedule IR"; page 3, layer 2, the
 // lowering of a configuration to a tiled task DAG).
 //
-// Per layer: NORM (per M-tile) -> QKV (M-tile x fused head) -> ATTN (M-tile x query head) ->
-// O (M-tile x column tile) -> NORM -> gate/up (M-tile x j tile) -> down (M-tile x column tile);
-// then LM tiles over the vocabulary and one argmax. Every task of a phase waits for all tasks
-// of the previous phase through one counter. Tasks go to CUs round-robin, continuing from one
-// phase to the next.
+// EMBED (per M-tile), then per layer: QKV (M-tile x fused head; attention norm fused) -> ATTN
+// (M-tile x query head) -> O (M-tile x column tile) -> gate/up (M-tile x j tile; MLP norm fused)
+// -> down (M-tile x column tile); then LM tiles over the vocabulary and one argmax. Every task
+// of a phase waits for all tasks of the previous phase through one counter. Tasks go to CUs
+// round-robin, continuing from one phase to the next.
 //
 // Accesses are declared in tile units: a region's elements are (unit, row) pairs laid out
-// unit-major, so a tile's rows are one contiguous range. Buffers reused by every layer (x, h,
-// q, o, a) are one region each, so the validator also sees the hazards between layers; the K
-// and V rows of the chunk are one region per layer.
+// unit-major, so a tile's rows are one contiguous range. Buffers reused by every layer (x, the
+// per-tile sums of squares, q, o, a) are one region each, so the validator also sees the
+// hazards between layers; the K and V rows of the chunk are one region per layer. The sums of
+// squares have two halves (attention norm, MLP norm), each with a unit per column tile.
 #include "lower_prefill.h"
 
 #include <algorithm>
@@ -22,7 +23,7 @@ namespace amk {
 
 namespace {
 
-enum PReg : uint32_t { PR_TOK = 0, PR_X, PR_H, PR_Q, PR_O, PR_A, PR_LMPART, PR_LOGITS, PR_TOKOUT, PR_KV0 };
+enum PReg : uint32_t { PR_TOK = 0, PR_X, PR_SSQ, PR_Q, PR_O, PR_A, PR_LMPART, PR_LOGITS, PR_TOKOUT, PR_KV0 };
 
 struct PGen {
     PfTask t;
@@ -84,28 +85,35 @@ amk_status lower_prefill(const amk_model_desc& d, int n_cu, int n_tokens, PfLowe
     };
     const uint32_t R_KV = PR_KV0;   // + layer
     uint32_t pc = kPfNone, pn = 0;  // previous phase's counter and producer count
-    for (int l = 0; l < L; ++l) {
-        // attention-input NORM (layer 0: the embedding gather into x first)
-        uint32_t f = (uint32_t)G.size();
+    // sums of squares: half 0 feeds the attention norms, half 1 the MLP norms
+    auto ssq_units = [&](uint32_t id, uint32_t flags, int half, int mtile) {
+        const uint64_t m0 = (uint64_t)mtile * kPfMt, mv = rows_of(mtile);
+        for (int u = 0; u < nxt; ++u) {
+            const uint64_t b = ((uint64_t)half * nxt + u) * Tp + m0;
+            acc(id, PR_SSQ, flags, b, b + mv);
+        }
+    };
+    // token embeddings into x, with the first attention norm's sums of squares
+    {
+        const uint32_t f = (uint32_t)G.size();
         for (int i = 0; i < nm; ++i) {
-            uint32_t id = mk(PF_NORM, l, i, 0, 0, pc, pn);
+            uint32_t id = mk(PF_EMBED, 0, i, 0, 0, pc, pn);
             const uint64_t m0 = (uint64_t)i * kPfMt, mv = rows_of(i);
-            if (l == 0) {   // the task reads back only the rows it has just written itself
-                acc(id, PR_TOK, 0, m0, m0 + mv);
-                all_units(id, PR_X, AMK_ACC_WRITE, nxt, i);
-            } else {
-                all_units(id, PR_X, 0, nxt, i);
-            }
-            acc(id, PR_H, AMK_ACC_WRITE, m0, m0 + mv);
+            acc(id, PR_TOK, 0, m0, m0 + mv);
+            all_units(id, PR_X, AMK_ACC_WRITE, nxt, i);
+            ssq_units(id, AMK_ACC_WRITE, 0, i);
         }
         close(f, pc, pn);
-        // QKV
-        f = (uint32_t)G.size();
+    }
+    for (int l = 0; l < L; ++l) {
+        // QKV (the attention norm of its rows fused into its input)
+        uint32_t f = (uint32_t)G.size();
         for (int i = 0; i < nm; ++i)
             for (int j = 0; j < nqkv; ++j) {
                 uint32_t id = mk(PF_QKV, l, i, (uint32_t)j, (uint32_t)hd, pc, pn);
                 const uint64_t m0 = (uint64_t)i * kPfMt, mv = rows_of(i);
-                acc(id, PR_H, 0, m0, m0 + mv);
+                all_units(id, PR_X, 0, nxt, i);
+                ssq_units(id, 0, 0, i);
                 if (j < nH) acc(id, PR_Q, AMK_ACC_WRITE, j * Tp + m0, j * Tp + m0 + mv);
                 else {
                     const int kvsel = j < nH + nKV ? 0 : 1, g = j - nH - kvsel * nKV;
@@ -127,7 +135,7 @@ amk_status lower_prefill(const amk_model_desc& d, int n_cu, int n_tokens, PfLowe
                 acc(id, PR_O, AMK_ACC_WRITE, h * Tp + m0, h * Tp + m0 + mv);
             }
         close(f, pc, pn);
-        // O projection + residual
+        // O projection + residual (+ the MLP norm's sums of squares of its column tile)
         f = (uint32_t)G.size();
         for (int i = 0; i < nm; ++i)
             for (int t = 0; t < nxt; ++t) {
@@ -136,28 +144,22 @@ amk_status lower_prefill(const amk_model_desc& d, int n_cu, int n_tokens, PfLowe
                 all_units(id, PR_O, 0, nH, i);
                 acc(id, PR_X, 0, t * Tp + m0, t * Tp + m0 + mv);
                 acc(id, PR_X, AMK_ACC_WRITE, t * Tp + m0, t * Tp + m0 + mv);
+                const uint64_t b = ((uint64_t)nxt + t) * Tp + m0;
+                acc(id, PR_SSQ, AMK_ACC_WRITE, b, b + mv);
             }
         close(f, pc, pn);
-        // MLP-input NORM
-        f = (uint32_t)G.size();
-        for (int i = 0; i < nm; ++i) {
-            uint32_t id = mk(PF_NORM, l, i, 1, 0, pc, pn);
-            const uint64_t m0 = (uint64_t)i * kPfMt, mv = rows_of(i);
-            all_units(id, PR_X, 0, nxt, i);
-            acc(id, PR_H, AMK_ACC_WRITE, m0, m0 + mv);
-        }
-        close(f, pc, pn);
-        // gate/up + SwiGLU
+        // gate/up + SwiGLU (the MLP norm fused into its input)
         f = (uint32_t)G.size();
         for (int i = 0; i < nm; ++i)
             for (int t = 0; t < njt; ++t) {
                 uint32_t id = mk(PF_GATEUP, l, i, (uint32_t)(t * nj), (uint32_t)nj, pc, pn);
                 const uint64_t m0 = (uint64_t)i * kPfMt, mv = rows_of(i);
-                acc(id, PR_H, 0, m0, m0 + mv);
+                all_units(id, PR_X, 0, nxt, i);
+                ssq_units(id, 0, 1, i);
                 acc(id, PR_A, AMK_ACC_WRITE, t * Tp + m0, t * Tp + m0 + mv);
             }
         close(f, pc, pn);
-        // down + residual
+        // down + residual (+ the next attention norm's sums of squares of its column tile)
         f = (uint32_t)G.size();
         for (int i = 0; i < nm; ++i)
             for (int t = 0; t < nxt; ++t) {
@@ -166,6 +168,8 @@ amk_status lower_prefill(const amk_model_desc& d, int n_cu, int n_tokens, PfLowe
                 all_units(id, PR_A, 0, njt, i);
                 acc(id, PR_X, 0, t * Tp + m0, t * Tp + m0 + mv);
                 acc(id, PR_X, AMK_ACC_WRITE, t * Tp + m0, t * Tp + m0 + mv);
+                const uint64_t b = (uint64_t)t * Tp + m0;
+                acc(id, PR_SSQ, AMK_ACC_WRITE, b, b + mv);
             }
         close(f, pc, pn);
     }

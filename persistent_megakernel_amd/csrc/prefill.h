@@ -3,12 +3,15 @@
 //
 // A prefill launch runs T prompt tokens through the whole model at once (AutoMegaKernel pages:
 // page 3, "How it works", layer 1, where GEMM tiles are among the instruction kinds; page 2,
-// section 3, tiles as the scheduling unit). Per layer, the phases are:
-//   NORM (RMSNorm of T rows) -> QKV GEMM (+RoPE, K/V rows into the cache) -> causal attention
-//   -> O GEMM (+residual) -> NORM -> gate/up GEMM (+SwiGLU) -> down GEMM (+residual),
-// then the LM head on the last row and a greedy argmax. Every task of a phase waits until
-// all tasks of the previous phase have signalled one counter, so the same schedule IR,
-// validator and CPU executor cover it.
+// section 3, tiles as the scheduling unit). After one embedding phase, per layer:
+//   QKV GEMM (RMSNorm fused into its input; +RoPE, K/V rows into the cache) -> causal
+//   attention -> O GEMM (+residual) -> gate/up GEMM (RMSNorm fused; +SwiGLU) -> down GEMM
+//   (+residual),
+// then the LM head on the last row and a greedy argmax. The residual epilogues also leave, per
+// row and column tile, the sum of squares of the new x values, so the next GEMM finds each
+// row's norm scale without a phase of its own. Every task of a phase waits until all tasks of
+// the previous phase have signalled one counter, so the same schedule IR, validator and CPU
+// executor cover it.
 #pragma once
 #include <stdint.h>
 
@@ -23,7 +26,7 @@
 namespace amk {
 
 enum PfOp : uint16_t {
-    PF_NORM = 1,     // layer, m0, mt, n0 = 0 (attention input) or 1 (MLP input): RMSNorm of rows [m0, m0 + mt)
+    PF_EMBED = 1,    // m0, mt: token embeddings of rows [m0, m0 + mt) into x, and their sums of squares
     PF_QKV = 2,      // layer, m0, mt, n0 = fused head index (q heads, then k, then v): GEMM + RoPE + store
     PF_ATTN = 3,     // layer, m0, mt, n0 = query head: causal attention of queries [m0, m0 + mt)
     PF_OPROJ = 4,    // layer, m0, mt, n0, nn: O GEMM columns [n0, n0 + nn) + residual
@@ -67,7 +70,7 @@ constexpr int kPfPad16 = 8;      // LDS row padding (elements) of 16-bit operand
 constexpr int kPfPad32 = 4;      // of fp32 operand tiles
 constexpr int kPfChunk = 256;    // tokens per launch (longer prompts take several launches)
 constexpr int kPfLmRows = 512;   // most LM rows per task
-constexpr int kPfLdsBytes = 112 * 1024;
+constexpr int kPfLdsBytes = 132 * 1024;   // A and B stages (101,376 B) + the norm gains (up to 8192 fp32)
 
 struct PfParams {
     int32_t H, L, nH, nKV, hd, I, V, max_ctx, wfmt, act_f32;
@@ -87,7 +90,8 @@ struct PfParams {
     uint32_t tab_rows[PM_N];     // rows per layer of each matrix
     // activations of the chunk (activation type: fp32 or bf16), row-major [kPfChunk][...]
     void* x;                     // [.][H] residual stream
-    void* h;                     // [.][H] normalised input of the next GEMM
+    double* ssq;                 // [2][.][H / pf_nt_x(H)]: per row and column tile, the sum of squares of
+                                 // the row's x values there (0: next attention norm, 1: next MLP norm)
     void* q;                     // [.][nH * hd] rotated queries
     void* o;                     // [.][nH * hd] attention output
     void* a;                     // [.][I] SwiGLU output
@@ -104,7 +108,12 @@ struct PfParams {
     uint32_t* status;
     uint32_t* abort_flag;
     uint64_t watchdog_ticks;
+    uint64_t* trace;             // optional: kPfTraceSlots per task in queue order, or null
 };
+
+// Trace slots per prefill task (s_memrealtime ticks, 100 MHz): task start, inputs observed
+// (wait satisfied), work done, signalled.
+constexpr int kPfTraceSlots = 4;
 
 // GEMM column tile widths of a shape (host and device agree through these).
 PF_HD inline int pf_nt_x(int H) { return H % 64 == 0 ? 64 : H % 32 == 0 ? 32 : 16; }        // O and down

@@ -105,6 +105,7 @@ struct Shared {
     int32_t ipart[kPfWaves];
     RowAddr rows[kPfMaxNt];          // B rows of the current GEMM tile
     float scale[kPfMaxNt];           // their int8 scales
+    float rrow[kPfMt];               // norm scales of the tile's rows (GEMMs with a fused RMSNorm)
 };
 
 struct Ctx {
@@ -166,10 +167,15 @@ constexpr int codes_per_seg() {
 }
 
 // C[mt x nt] = A[mt x K] * B[nt x K]^T for one tile. A: activation rows (row-major, lda
-// elements per row, rows >= mvalid read as zero). B: the rows in S.rows (nt of them). On return
-// the tile (int8 scales applied) is in LDS as fp32 [64][nt + 4], followed by a barrier.
+// elements per row, rows >= mvalid read as zero). B: the rows in S.rows (nt of them). With
+// `gain` non-null the A rows are x rows and the GEMM's input is their RMSNorm: each row's scale
+// r = 1 / sqrt(sum of its squares / K + eps) comes from the row's per-tile sums of squares in
+// `ssq` ([row][nxt] doubles, summed in tile order, in double), and each element is staged as
+// round_act((x * r) * gain[k]). On return the tile (int8 scales applied) is in LDS as fp32
+// [64][nt + 4], followed by a barrier.
 template <int FMT>
-DEV void gemm_tile(const Ctx& c, const void* A, uint32_t lda, uint32_t m0, uint32_t mvalid, uint32_t nt, uint32_t K) {
+DEV void gemm_tile(const Ctx& c, const void* A, uint32_t lda, uint32_t m0, uint32_t mvalid, uint32_t nt, uint32_t K,
+                   const float* gain = nullptr, const double* ssq = nullptr) {
     constexpr int F32 = FMT == AMK_F32;
     constexpr int Kt = F32 ? kPfKt32 : kPfKt16;
     constexpr int Pad = F32 ? kPfPad32 : kPfPad16;
@@ -189,6 +195,24 @@ DEV void gemm_tile(const Ctx& c, const void* A, uint32_t lda, uint32_t m0, uint3
     const uint32_t nbn = nt / 16, nblk = 4 * nbn;   // 16x16 blocks (4 row blocks: rows past mvalid are zeros)
     const uint32_t stages = (K + Kt - 1) / Kt;
     const uint32_t segs_b = nt * SPR;
+    float* G = (float*)(c.lds + kPfMt * LD * ES + kPfMaxNt * LD * ES);   // the norm gains [K]
+    if (gain) {
+        for (uint32_t k = (uint32_t)tid; k < K; k += kPfThreads) G[k] = gain[k];
+        {   // eight threads per row: each sums the tiles t = j (mod 8), then a fixed xor tree
+            const uint32_t row = (uint32_t)tid >> 3, j = (uint32_t)tid & 7u;
+            const uint32_t nxt = (uint32_t)(P.H / pf_nt_x(P.H));
+            double ss = 0.0;
+            if (row < mvalid) {
+                const double* q = ssq + (uint64_t)(m0 + row) * nxt;
+                for (uint32_t t = j; t < nxt; t += 8) ss += q[t];
+            }
+            ss += __shfl_xor(ss, 1, 64);
+            ss += __shfl_xor(ss, 2, 64);
+            ss += __shfl_xor(ss, 4, 64);
+            if (j == 0) S.rrow[row] = row < mvalid ? (float)(1.0 / sqrt(ss / (double)K + (double)P.eps)) : 0.f;
+        }
+        __syncthreads();
+    }
 
     u32x4 ra[SEGS_A], rb[SEGS_B];
     auto load = [&](uint32_t s) {
@@ -212,12 +236,27 @@ DEV void gemm_tile(const Ctx& c, const void* A, uint32_t lda, uint32_t m0, uint3
             }
         }
     };
-    auto store = [&]() {
+    auto store = [&](uint32_t s) {
 #pragma unroll
         for (int i = 0; i < SEGS_A; ++i) {
             const uint32_t g = (uint32_t)tid + (uint32_t)i * kPfThreads;
-            const uint32_t r = g / (Kt / EPS_A), col = (g % (Kt / EPS_A)) * EPS_A;
-            *(u32x4*)(Abuf + (r * LD + col) * ES) = ra[i];
+            const uint32_t r = g / (Kt / EPS_A), col = (g % (Kt / EPS_A)) * EPS_A, k = s * Kt + col;
+            u32x4 v = ra[i];
+            if (gain && k < K) {   // RMSNorm on the way in: round_act((x * r) * g)
+                const float rr = S.rrow[r];
+                if (F32) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) v[j] = __float_as_uint((__uint_as_float(v[j]) * rr) * G[k + j]);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t lo = f2bf((bf2f(v[j] & 0xffffu) * rr) * G[k + 2 * j]);
+                        const uint32_t hi = f2bf((bf2f(v[j] >> 16) * rr) * G[k + 2 * j + 1]);
+                        v[j] = lo | (hi << 16);
+                    }
+                }
+            }
+            *(u32x4*)(Abuf + (r * LD + col) * ES) = v;
         }
 #pragma unroll
         for (int i = 0; i < SEGS_B; ++i) {
@@ -266,7 +305,7 @@ DEV void gemm_tile(const Ctx& c, const void* A, uint32_t lda, uint32_t m0, uint3
 
     load(0);
     for (uint32_t s = 0; s < stages; ++s) {
-        store();
+        store(s);
         __syncthreads();
         if (s + 1 < stages) load(s + 1);   // in flight while the matrix cores work
         const uint32_t kv = min((uint32_t)Kt, K - s * Kt);   // valid columns of this stage (multiple of 16)
@@ -367,7 +406,7 @@ DEV void op_qkv(const Ctx& c, const PfTask& T) {
     const uint32_t mat = j < nH ? PM_WQ : j < nH + nKV ? PM_WK : PM_WV;
     const uint32_t head = j < nH ? j : j < nH + nKV ? j - nH : j - nH - nKV;
     stage_rows<FMT>(c, hd, l, [&](uint32_t i, uint32_t& m, uint32_t& r) { m = mat; r = head * hd + i; });
-    gemm_tile<FMT>(c, P.h, (uint32_t)P.H, T.m0, mvalid, hd, (uint32_t)P.H);
+    gemm_tile<FMT>(c, P.x, (uint32_t)P.H, T.m0, mvalid, hd, (uint32_t)P.H, P.norms + (uint64_t)2 * l * P.H, P.ssq);
     const float* C = (const float*)c.lds;
     const uint32_t ldc = hd + 4;
     const uint32_t qd = nH * hd;
@@ -405,12 +444,25 @@ DEV void op_resid(const Ctx& c, const PfTask& T, bool down) {
     const uint32_t K = down ? (uint32_t)P.I : (uint32_t)(P.nH * P.hd);
     stage_rows<FMT>(c, nn, T.layer, [&](uint32_t i, uint32_t& m, uint32_t& r) { m = down ? PM_WD : PM_WO; r = T.n0 + i; });
     gemm_tile<FMT>(c, down ? P.a : P.o, K, T.m0, mvalid, nn, K);
-    const float* C = (const float*)c.lds;
+    float* C = (float*)c.lds;
     const uint32_t ldc = nn + 4;
     for (uint32_t e = threadIdx.x; e < mvalid * nn; e += kPfThreads) {
         const uint32_t m = e / nn, n = e % nn;
         const uint64_t xi = (uint64_t)(T.m0 + m) * H + T.n0 + n;
-        act_st<F32>(P.x, xi, act_ld<F32>(P.x, xi) + C[m * ldc + n]);
+        const float xn = rnd<F32>(act_ld<F32>(P.x, xi) + C[m * ldc + n]);
+        act_st<F32>(P.x, xi, xn);
+        C[m * ldc + n] = xn;
+    }
+    __syncthreads();
+    // per row, the sum of squares of the new x values of this column tile (in double), for the
+    // norm of the next GEMM (O: the MLP norm; down: the next layer's attention norm)
+    const uint32_t nxt = H / (uint32_t)pf_nt_x((int)H), tile = T.n0 / nn;
+    double* q = P.ssq + (down ? 0ull : (uint64_t)kPfChunk * nxt);
+    const int lane = lane_id(), w = threadIdx.x >> 6;
+    for (uint32_t m = (uint32_t)w; m < mvalid; m += kPfWaves) {
+        const double v = (uint32_t)lane < nn ? (double)C[m * ldc + lane] : 0.0;
+        const double ss = wave_sum_d(v * v);
+        if (lane == 0) q[(uint64_t)(T.m0 + m) * nxt + tile] = ss;
     }
 }
 
@@ -425,7 +477,8 @@ DEV void op_gateup(const Ctx& c, const PfTask& T) {
         m = i < nn ? PM_WG : PM_WU;
         r = T.n0 + (i < nn ? i : i - nn);
     });
-    gemm_tile<FMT>(c, P.h, (uint32_t)P.H, T.m0, mvalid, 2 * nn, (uint32_t)P.H);
+    gemm_tile<FMT>(c, P.x, (uint32_t)P.H, T.m0, mvalid, 2 * nn, (uint32_t)P.H, P.norms + ((uint64_t)2 * T.layer + 1) * P.H,
+                   P.ssq + (uint64_t)kPfChunk * (P.H / pf_nt_x(P.H)));
     const float* C = (const float*)c.lds;
     const uint32_t ldc = 2 * nn + 4;
     for (uint32_t e = threadIdx.x; e < mvalid * nn; e += kPfThreads) {
@@ -435,38 +488,43 @@ DEV void op_gateup(const Ctx& c, const PfTask& T) {
     }
 }
 
-// RMSNorm of rows [m0, m0 + mt): h = round(x * r * g). Layer 0's attention norm first copies
-// the token embeddings into x.
+// Layer 0's input: the token embeddings of rows [m0, m0 + mt) into x (exact copies), and per row
+// the sum of their squares (in double) for the first attention norm, as the tile-0 partial.
 template <int FMT>
-DEV void op_norm(const Ctx& c, const PfTask& T) {
+DEV void op_embed(const Ctx& c, const PfTask& T) {
     constexpr int F32 = FMT == AMK_F32;
+    constexpr uint32_t EPS = F32 ? 4 : 8;   // values per 16 bytes
     const PfParams& P = *c.P;
-    const uint32_t H = (uint32_t)P.H;
+    const uint32_t H = (uint32_t)P.H, nxt = H / (uint32_t)pf_nt_x(P.H);
     const uint32_t mend = min(T.m0 + T.mt, (uint32_t)P.T);
-    const float* g = P.norms + ((uint64_t)2 * T.layer + T.n0) * H;
-    const bool gather = T.layer == 0 && T.n0 == 0;
     const int lane = lane_id(), w = threadIdx.x >> 6;
+    const uint64_t rowb = (uint64_t)H * (F32 ? 4 : 2);
     for (uint32_t m = T.m0 + (uint32_t)w; m < mend; m += kPfWaves) {
-        if (gather) {
-            int tok = P.tokens[m];
-            if (tok < 0 || tok >= P.V) {
-                if (lane == 0) __hip_atomic_store(&P.status[1], kStatusBadToken, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-                tok = 0;
-            }
-            for (uint32_t k = (uint32_t)lane; k < H; k += 64)
-                act_st<F32>(P.x, (uint64_t)m * H + k, act_ld<F32>(P.embed, (uint64_t)tok * H + k));
+        int tok = P.tokens[m];
+        if (tok < 0 || tok >= P.V) {
+            if (lane == 0) __hip_atomic_store(&P.status[1], kStatusBadToken, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            tok = 0;
         }
-        // in double, as the norm is defined: the scale multiplies every element, so an error in
-        // it moves every value near a rounding boundary of the activation format at once
+        const uint8_t* src = (const uint8_t*)P.embed + (uint64_t)tok * rowb;
+        uint8_t* dst = (uint8_t*)P.x + (uint64_t)m * rowb;
         double ss = 0.0;
-        for (uint32_t k = (uint32_t)lane; k < H; k += 64) {
-            const double v = act_ld<F32>(P.x, (uint64_t)m * H + k);
-            ss += v * v;
+        for (uint32_t sg = (uint32_t)lane; sg < H / EPS; sg += 64) {
+            const u32x4 v = *(const u32x4*)(src + 16ull * sg);
+            *(u32x4*)(dst + 16ull * sg) = v;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (F32) {
+                    const double a = __uint_as_float(v[j]);
+                    ss += a * a;
+                } else {
+                    const double a = bf2f(v[j] & 0xffffu), b = bf2f(v[j] >> 16);
+                    ss += a * a + b * b;
+                }
+            }
         }
         ss = wave_sum_d(ss);
-        const double r = 1.0 / sqrt(ss / (double)H + (double)P.eps);
-        for (uint32_t k = (uint32_t)lane; k < H; k += 64)
-            act_st<F32>(P.h, (uint64_t)m * H + k, rnd_d<F32>(((double)act_ld<F32>(P.x, (uint64_t)m * H + k) * r) * (double)g[k]));
+        double* q = P.ssq + (uint64_t)m * nxt;
+        for (uint32_t t = (uint32_t)lane; t < nxt; t += 64) q[t] = t == 0 ? ss : 0.0;
     }
 }
 
@@ -555,6 +613,148 @@ DEV void op_attn(const Ctx& c, const PfTask& T) {
         const float inv = 1.0f / lrun[i];
         if ((uint32_t)lane < hd) act_st<F32>(P.o, base + lane, o0[i] * inv);
         if (hd > 64 && (uint32_t)lane + 64 < hd) act_st<F32>(P.o, base + lane + 64, o1[i] * inv);
+    }
+}
+
+// Causal attention on the matrix cores (16-bit activations, head_dim a multiple of 32): queries
+// [m0, m0 + mt) of query head n0. Wave w takes queries 16 (w % 4) .. +16 and, of every block of
+// 64 positions, the half 32 (w / 4) .. +32, with its own online-softmax state; the two halves
+// of each query are merged at the end. Scores: bf16 products of the stored (rounded) q and K
+// values on v_mfma_f32_16x16x32_bf16; probabilities stay fp32 and meet V (fp32 copies of the
+// stored values) on v_mfma_f32_16x16x4_f32, one short chain per block added to the running
+// output with round-to-nearest additions.
+template <int FMT>
+DEV void op_attn_mfma(const Ctx& c, const PfTask& T) {
+    const PfParams& P = *c.P;
+    const uint32_t hd = (uint32_t)P.hd, h = T.n0, qd = (uint32_t)(P.nH * P.hd);
+    const int g = (int)((uint64_t)h * P.nKV / P.nH);
+    const uint32_t mvalid = rows_valid(P, T);
+    if (mvalid == 0) return;
+    const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
+    const uint32_t bm = (uint32_t)w & 3u, half = (uint32_t)w >> 2;
+    const uint32_t LQ = hd + 8, LV = hd + 4, segs = hd / 8;
+    uint16_t* Qs = (uint16_t*)c.lds;                 // [64][LQ] bf16
+    uint16_t* Ks = Qs + kPfMt * LQ;                  // [64][LQ] bf16
+    float* Vs = (float*)(Ks + 64 * LQ);              // [64][LV] fp32
+    float* Pw = Vs + 64 * LV + (uint32_t)w * 16 * 33;   // this wave's probabilities [16][33]
+    const uint64_t kbase = kv_index(P, (int)T.layer, 0, g, 0), vbase = kv_index(P, (int)T.layer, 1, g, 0);
+    for (uint32_t e = (uint32_t)tid; e < kPfMt * segs; e += kPfThreads) {
+        const uint32_t q = e / segs, sg = e % segs;
+        u32x4 v = u32x4{0, 0, 0, 0};
+        if (q < mvalid) v = *(const u32x4*)((const uint16_t*)P.q + (uint64_t)(T.m0 + q) * qd + h * hd + sg * 8);
+        *(u32x4*)(Qs + q * LQ + sg * 8) = v;
+    }
+    const uint32_t qpos0 = (uint32_t)P.pos0 + T.m0;            // position of query row 0
+    const uint32_t last = qpos0 + mvalid - 1, nblocks = last / 64 + 1;
+    const uint32_t wq_last = min(16 * bm + 15, mvalid - 1);    // this wave's last query row
+    const bool wave_rows = 16 * bm < mvalid;
+    const float scale = P.attn_scale;
+    const uint32_t r4 = (uint32_t)(lane >> 4) * 4, col = (uint32_t)lane & 15u;
+    float mrun[4], lrun[4];
+    f32x4 O[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { mrun[i] = -INFINITY; lrun[i] = 0.f; }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) O[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint32_t nbd = hd / 16;
+    for (uint32_t b = 0; b < nblocks; ++b) {
+        const uint32_t p0 = b * 64;
+        __syncthreads();   // the previous block's K and V are no longer read
+        for (uint32_t e = (uint32_t)tid; e < 64 * segs; e += kPfThreads) {
+            const uint32_t p = e / segs, sg = e % segs, pos = p0 + p;
+            u32x4 kv = u32x4{0, 0, 0, 0}, vv = u32x4{0, 0, 0, 0};
+            if (pos <= last) {
+                kv = *(const u32x4*)((const uint16_t*)P.kv + kbase + (uint64_t)pos * hd + sg * 8);
+                vv = *(const u32x4*)((const uint16_t*)P.kv + vbase + (uint64_t)pos * hd + sg * 8);
+            }
+            *(u32x4*)(Ks + p * LQ + sg * 8) = kv;
+            float* vd = Vs + p * LV + sg * 8;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                vd[2 * j] = bf2f(vv[j] & 0xffffu);
+                vd[2 * j + 1] = bf2f(vv[j] >> 16);
+            }
+        }
+        __syncthreads();
+        const uint32_t pb = p0 + 32 * half;
+        if (!wave_rows || pb > qpos0 + wq_last) continue;   // no query of this wave sees these positions
+        f32x4 sc[2];
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            sc[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (uint32_t ks = 0; ks < hd; ks += 32) {
+                const bf16x8 a = *(const bf16x8*)(Qs + (16 * bm + col) * LQ + ks + (uint32_t)(lane >> 4) * 8);
+                const bf16x8 bb = *(const bf16x8*)(Ks + (32 * half + 16 * blk + col) * LQ + ks + (uint32_t)(lane >> 4) * 8);
+                sc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bb, sc[blk], 0, 0, 0);
+            }
+        }
+        float alpha[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t q = 16 * bm + r4 + (uint32_t)i, qpos = qpos0 + q;
+            float mx = -INFINITY;
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+                const uint32_t p = pb + 16 * (uint32_t)blk + col;
+                const bool ok = q < mvalid && p <= qpos;
+                sc[blk][i] = ok ? sc[blk][i] * scale : -INFINITY;
+                mx = fmaxf(mx, sc[blk][i]);
+            }
+            for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+            const float mnew = fmaxf(mrun[i], mx);
+            alpha[i] = mnew == -INFINITY ? 1.f : __expf(mrun[i] - mnew);
+            float sum = 0.f;
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+                const float pw = sc[blk][i] == -INFINITY ? 0.f : __expf(sc[blk][i] - mnew);
+                Pw[(r4 + (uint32_t)i) * 33 + 16 * (uint32_t)blk + col] = pw;
+                sum += pw;
+            }
+            for (int o = 1; o < 16; o <<= 1) sum += __shfl_xor(sum, o, 64);
+            lrun[i] = lrun[i] * alpha[i] + sum;
+            mrun[i] = mnew;
+        }
+        // O = O * alpha + P V (the 32 positions of this half-block, as one chain from zero)
+        for (uint32_t bd = 0; bd < nbd; ++bd) {
+            f32x4 part = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (uint32_t st = 0; st < 32; st += 4) {
+                const float a = Pw[col * 33 + st + (uint32_t)(lane >> 4)];
+                const float bv = Vs[(32 * half + st + (uint32_t)(lane >> 4)) * LV + 16 * bd + col];
+                part = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, part, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) O[bd][i] = O[bd][i] * alpha[i] + part[i];
+        }
+    }
+    // merge the two position halves of each query row block
+    __syncthreads();
+    float* Mb = (float*)Ks + bm * (16 * hd + 32);    // [16][hd] output, [16] maxima, [16] sums
+    if (half == 1) {
+        for (uint32_t bd = 0; bd < nbd; ++bd)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Mb[(r4 + (uint32_t)i) * hd + 16 * bd + col] = O[bd][i];
+        if (col == 0)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { Mb[16 * hd + r4 + (uint32_t)i] = mrun[i]; Mb[16 * hd + 16 + r4 + (uint32_t)i] = lrun[i]; }
+    }
+    __syncthreads();
+    if (half == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t q = 16 * bm + r4 + (uint32_t)i;
+            if (q >= mvalid) continue;
+            const float m2 = Mb[16 * hd + r4 + (uint32_t)i], l2 = Mb[16 * hd + 16 + r4 + (uint32_t)i];
+            const float M = fmaxf(mrun[i], m2);
+            const float a1 = mrun[i] == -INFINITY ? 0.f : __expf(mrun[i] - M);
+            const float a2 = m2 == -INFINITY ? 0.f : __expf(m2 - M);
+            const float inv = 1.0f / (lrun[i] * a1 + l2 * a2);
+            const uint64_t base = (uint64_t)(T.m0 + q) * qd + h * hd;
+            for (uint32_t bd = 0; bd < nbd; ++bd) {
+                const uint32_t d = 16 * bd + col;
+                act_st<0>(P.o, base + d, (O[bd][i] * a1 + Mb[(r4 + (uint32_t)i) * hd + d] * a2) * inv);
+            }
+        }
     }
 }
 
@@ -672,18 +872,26 @@ DEV void prefill_body(const PfParams& Pin) {
         for (int k = 0; k < (int)(sizeof(PfTask) / 4); ++k) wd[k] = __builtin_amdgcn_readfirstlane(wd[k]);
         PfTask T;
         __builtin_memcpy(&T, wd, sizeof(PfTask));
+        uint64_t* tr = P.trace ? P.trace + (uint64_t)t * kPfTraceSlots : nullptr;
+        if (tr && threadIdx.x == 0) tr[0] = rt();
         task_wait(c, T);
+        if (tr && threadIdx.x == 0) tr[1] = rt();
         switch (T.op) {
-        case PF_NORM: op_norm<FMT>(c, T); break;
+        case PF_EMBED: op_embed<FMT>(c, T); break;
         case PF_QKV: op_qkv<FMT>(c, T); break;
-        case PF_ATTN: op_attn<FMT>(c, T); break;
+        case PF_ATTN:
+            if (FMT != AMK_F32 && P.hd % 32 == 0) op_attn_mfma<FMT>(c, T);
+            else op_attn<FMT>(c, T);
+            break;
         case PF_OPROJ: op_resid<FMT>(c, T, false); break;
         case PF_GATEUP: op_gateup<FMT>(c, T); break;
         case PF_DOWN: op_resid<FMT>(c, T, true); break;
         case PF_LM: if (P.do_lm) op_lm<FMT>(c, T); break;
         default: if (P.do_lm) op_argmax(c, T); break;
         }
+        if (tr && threadIdx.x == 0) tr[2] = rt();
         task_signal(c, T);
+        if (tr && threadIdx.x == 0) tr[3] = rt();
     }
 }
 

@@ -38,16 +38,18 @@ def test_prefill_schedule_runs_clean_on_the_executor(M, n_cu, n):
 
 
 def test_prefill_schedule_structure(M):
-    """Per layer seven phases, each waiting on all of the previous one; LM tiles and one argmax."""
+    """One embedding phase, then five phases per layer (the norms fused into the GEMMs that
+    consume them), each waiting on all of the previous one; LM tiles and one argmax."""
     sh = I.SHAPES["tiny_fp32"]
     s = M.amk_lower_prefill(M.model_desc(sh), 16, 100)
     ops = [t.opcode for t in s.tasks]
     nm = 2
     nqkv = sh.n_heads + 2 * sh.n_kv_heads
-    per_layer = nm * (2 + nqkv + sh.n_heads + 2 * (sh.hidden // 64) + sh.intermediate // 16)
+    per_layer = nm * (nqkv + sh.n_heads + 2 * (sh.hidden // 64) + sh.intermediate // 16)
     n_lm = ops.count(7)
-    assert ops.count(8) == 1 and n_lm >= 1
-    assert len(ops) == sh.n_layers * per_layer + n_lm + 1
+    assert ops.count(8) == 1 and n_lm >= 1 and ops.count(1) == nm
+    assert len(ops) == nm + sh.n_layers * per_layer + n_lm + 1
+    assert len({c for t in s.tasks for c in t.signals}) == 1 + 5 * sh.n_layers + 1
     # every wait is a full wait on the counter of the phase before
     producers = {}
     for i, t in enumerate(s.tasks):
