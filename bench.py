@@ -9,8 +9,10 @@ fp16 scales, bf16 activations and KV cache, fp32 accumulation), random init, KV 
 
 Prints one JSON line: tokens/s and ms/step over the timed region, the roofline of the kernel
 (algorithmic HBM bytes per launch over the mean launch duration, both timed with HIP events on
-the launch stream, against the 8 TB/s HBM peak) and the CPU oracle timed on a bounded sample of
-the same workload.
+the launch stream, against the 8 TB/s HBM peak), the CPU oracle timed on a bounded sample of
+the same workload and, under "prefill", the prompt-prefill kernel on a 256-token prompt
+(prompt tokens/s, and algorithmic FLOPs over the launch duration against the bf16 matrix-core
+peak).
 """
 from __future__ import annotations
 
@@ -39,7 +41,9 @@ WORKLOADS = {
 # counters measured for the default workload by rocprofv3 (--pmc FETCH_SIZE, then WRITE_SIZE),
 # scaled by the same counters on a device copy of known size; None until measured for the
 # current kernel
-TRAFFIC_BYTES_PER_LAUNCH = 1094407812
+TRAFFIC_BYTES_PER_LAUNCH = 1094293439
+# the same for the prefill kernel on a 256-token prompt of the default workload
+PREFILL_TRAFFIC_BYTES_PER_LAUNCH = 3384578897
 
 
 def weight_bytes(shape) -> int:
@@ -70,6 +74,49 @@ def kv_bytes(shape, pos: int) -> int:
     act = 4 if shape.act_f32 else 2
     row = shape.n_layers * 2 * shape.n_kv_heads * shape.head_dim * act
     return row * pos + row
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def prefill_flops(shape, n_tokens: int, pos0: int = 0) -> int:
+    """Algorithmic FLOPs of one prefill of n_tokens tokens from pos0: every projection of every
+    token (2 per weight), causal attention (q.k and p.v, 2 x 2 x head_dim per query head and
+    visible position) and the LM head of the last token only."""
+    H, I_, L = shape.hidden, shape.intermediate, shape.n_layers
+    qd, kd = shape.q_dim, shape.kv_dim
+    per_tok = L * (qd * H + 2 * kd * H + H * qd + 3 * I_ * H)
+    vis = sum(pos0 + m + 1 for m in range(n_tokens))
+    attn = 4 * shape.n_heads * shape.head_dim * vis * L
+    return 2 * n_tokens * per_tok + attn + 2 * shape.vocab * H
+
+
+def prefill_leg(dec, shape, n_tokens: int = 256, reps: int = 10, traffic=None) -> dict:
+    """Prompt prefill (amk_prefill) of n_tokens synthetic tokens at position 0, timed with HIP
+    events around each launch on the launch stream; roofline against the bf16 matrix-core peak
+    (the projections run as bf16 MFMA GEMM tiles, int8 and int4 codes widened exactly)."""
+    import torch
+    import amk_inputs as I
+    toks = torch.tensor(I.prompt_tokens(shape, n_tokens, stream=7), dtype=torch.int32, device="cuda")
+    tout = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(3):   # the first call lowers, validates and uploads this chunk size's schedule
+        dec.prefill(toks, 0, tout)
+    torch.cuda.synchronize()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+    for r in range(reps):
+        marks[2 * r].record(stream)
+        dec.prefill(toks, 0, tout)
+        marks[2 * r + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = sum(marks[2 * r].elapsed_time(marks[2 * r + 1]) for r in range(reps)) / reps
+    fl = prefill_flops(shape, n_tokens)
+    tf = fl / (ms * 1e-3) / 1e12
+    return {"tokens": n_tokens, "launches": (n_tokens + 255) // 256, "value": round(n_tokens / (ms * 1e-3), 1),
+            "unit": "prompt tokens/s", "ms_per_prefill": round(ms, 4),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 5), "flops_per_launch": fl, "traffic": traffic},
+            "vs_decode": "one decode launch per prompt token at the timed decode rate"}
 
 
 def cpu_baseline(shape, w, pos0: int, budget_s: float = 12.0):
@@ -106,6 +153,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="tinyllama_int8", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prompt-prefill leg")
+    ap.add_argument("--prefill-tokens", type=int, default=256)
     ap.add_argument("--records", default=None, help="also append the JSON line to this file")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a device-to-device copy of this size (the traffic counters' calibration)")
@@ -164,6 +213,13 @@ def main() -> int:
     ev_ms = start.elapsed_time(stop)
     launch_ms = sum(marks[2 * k].elapsed_time(marks[2 * k + 1]) for k in range(K)) / K
     status = dec.status()
+    pf = None
+    if not args.no_prefill and not status:
+        print(f"[bench] prefill {args.prefill_tokens} tokens", file=sys.stderr, flush=True)
+        pf = prefill_leg(dec, shape, args.prefill_tokens,
+                         traffic=PREFILL_TRAFFIC_BYTES_PER_LAUNCH
+                         if args.workload == "tinyllama_int8" and args.prefill_tokens == 256 else None)
+        status = dec.status()
     dec.close()
     if status:
         print(json.dumps({"error": f"device status {status}"}))
@@ -191,6 +247,9 @@ def main() -> int:
         "us_per_launch": round(launch_ms * 1e3, 2),
         "wall_s_timed": round(wall, 4),
     }
+    if pf is not None:
+        pf["speedup_vs_decode_per_token"] = round(pf["value"] / rec["value"], 1)
+        rec["prefill"] = pf
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(base.replace(max_ctx=max(base.max_ctx, pos0 + 64)), w, pos0)

@@ -1,8 +1,9 @@
 // amk_bench: drive libamk.so through its C ABI alone (no Python, no torch): build a model of one
 // of the decode workloads' shapes with synthetic weights, then time back-to-back greedy decode
-// launches (the token chained on the device) with HIP events on the launch stream.
+// launches (the token chained on the device) with HIP events on the launch stream; or, with
+// prefill_tokens > 0, `steps` prompt prefills (amk_prefill) of that many tokens at position 0.
 //
-//   amk_bench [workload] [steps] [warmup] [start_pos] [cache_rows] [null_stream]
+//   amk_bench [workload] [steps] [warmup] [start_pos] [cache_rows] [null_stream] [prefill_tokens]
 //   amk_bench --copy MiB          (traffic-counter calibration: device-to-device copies)
 //   workloads: tiny_fp32 smollm2_135m_bf16 tinyllama_int8 llama7b_bf16 llama7b_int8 llama3_8b_int4
 //
@@ -112,6 +113,8 @@ int main(int argc, char** argv) {
     // optional: cache rows (0 = just enough for the run) and the launch stream (1 = the null stream)
     const int ctx_rows = argc > 5 ? std::atoi(argv[5]) : 0;
     const bool null_stream = argc > 6 && std::atoi(argv[6]) == 1;
+    const int prefill_tokens = argc > 7 ? std::atoi(argv[7]) : 0;
+    if (prefill_tokens < 0) return 2;
     const bool f32 = s->wfmt == AMK_F32;
     amk_model_desc d;
     std::memset(&d, 0, sizeof(d));
@@ -119,6 +122,7 @@ int main(int argc, char** argv) {
     d.hidden = s->H; d.n_layers = s->L; d.n_heads = s->nH; d.n_kv_heads = s->nKV; d.head_dim = s->hd;
     d.intermediate = s->I; d.vocab = s->V; d.tied_embeddings = s->tied;
     d.max_ctx = ctx_rows > pos0 + warmup + steps ? ctx_rows : pos0 + warmup + steps + 1;
+    if (d.max_ctx < prefill_tokens) d.max_ctx = prefill_tokens;
     d.rope_theta = s->theta; d.rms_eps = 1e-5f; d.wfmt = s->wfmt; d.act_f32 = s->act_f32;
 
     std::vector<void*> owned;
@@ -168,6 +172,36 @@ int main(int argc, char** argv) {
     }
     for (void* p : owned) CK(hipFree(p));   // the context keeps its own repacked copy
     owned.clear();
+
+    if (prefill_tokens > 0) {
+        std::vector<int32_t> ht(prefill_tokens);
+        for (int i = 0; i < prefill_tokens; ++i) ht[i] = (int32_t)(hash32((uint64_t)i + 4242) % (uint32_t)s->V);
+        int32_t* ptok = nullptr;
+        CK(hipMalloc(&ptok, sizeof(int32_t) * (prefill_tokens + 1)));
+        CK(hipMemcpy(ptok, ht.data(), sizeof(int32_t) * prefill_tokens, hipMemcpyHostToDevice));
+        for (int i = 0; i < warmup; ++i)
+            if (amk_prefill(ctx, ptok, 0, prefill_tokens, ptok + prefill_tokens, nullptr, st) != AMK_OK) return 1;
+        hipEvent_t a, b;
+        CK(hipEventCreate(&a));
+        CK(hipEventCreate(&b));
+        CK(hipEventRecord(a, st));
+        for (int i = 0; i < steps; ++i)
+            if (amk_prefill(ctx, ptok, 0, prefill_tokens, ptok + prefill_tokens, nullptr, st) != AMK_OK) return 1;
+        CK(hipEventRecord(b, st));
+        CK(hipEventSynchronize(b));
+        float ms = 0.f;
+        CK(hipEventElapsedTime(&ms, a, b));
+        const uint32_t status = amk_device_status(ctx);
+        std::printf("{\"workload\": \"%s\", \"prefill_tokens\": %d, \"prefills\": %d, \"us_per_prefill\": %.3f, "
+                    "\"prompt_tokens_per_s\": %.1f, \"device_status\": %u}\n",
+                    s->name, prefill_tokens, steps, 1e3 * ms / steps, 1e3 * steps * prefill_tokens / ms, status);
+        std::fflush(stdout);
+        amk_destroy(ctx);
+        CK(hipFree(ptok));
+        CK(hipFree(kv));
+        if (st) CK(hipStreamDestroy(st));
+        return status ? 1 : 0;
+    }
 
     int32_t* tok = nullptr;
     CK(hipMalloc(&tok, sizeof(int32_t) * (warmup + steps + 1)));
