@@ -45,7 +45,11 @@ amk_status lower_prefill(const amk_model_desc& d, int n_cu, int n_tokens, PfLowe
     const int nm = (n_tokens + kPfMt - 1) / kPfMt;
     const uint64_t Tp = (uint64_t)nm * kPfMt;
     const int ntx = pf_nt_x(H), nxt = H / ntx;          // O / down column tiles
-    const int nj = pf_nj(I), njt = I / nj;              // gate/up j tiles
+    // gate/up j tiles: 32 j (64 weight rows) per tile, or 64 j when that many tiles would take
+    // more than one round of the CUs (the tasks are latency-bound, so fewer rounds win)
+    int nj = pf_nj(I);
+    if (nj == 32 && I % 64 == 0 && (int64_t)nm * (I / 32) > n_cu) nj = 64;
+    const int njt = I / nj;
     const int nqkv = nH + 2 * nKV;
     const int lm_rows = std::min(kPfLmRows, std::max(1, (d.vocab + n_cu - 1) / n_cu));
     const int nlm = (d.vocab + lm_rows - 1) / lm_rows;

@@ -117,7 +117,7 @@ constexpr int kPfTraceSlots = 4;
 
 // GEMM column tile widths of a shape (host and device agree through these).
 PF_HD inline int pf_nt_x(int H) { return H % 64 == 0 ? 64 : H % 32 == 0 ? 32 : 16; }        // O and down
-PF_HD inline int pf_nj(int I) { return I % 32 == 0 ? 32 : 16; }                              // gate/up: j per tile
+PF_HD inline int pf_nj(int I) { return I % 32 == 0 ? 32 : 16; }                              // gate/up: j per tile (at least)
 PF_HD inline int pf_kt(int act_f32) { return act_f32 ? kPfKt32 : kPfKt16; }
 
 }  // namespace amk
