@@ -234,3 +234,28 @@ def test_full_depth_tinyllama_int8_prefill(M):
     assert r["err"] <= 0.25 and rms <= 0.05
     _assert_token(r, "tinyllama_int8 full depth")
     _close(r)
+
+
+def test_full_depth_tinyllama_int8_prefill_in_the_benchmarked_configuration(M):
+    """The prefill the benchmark times: TinyLlama-shaped int8 at full depth, a 256-token prompt
+    at position 0 in one launch (four M-tiles, 64-wide gate/up tiles). The oracle's 256 chained
+    steps decide the logits (full-depth bar); the K/V rows of the first layer, whose inputs are
+    exact, are checked at 16 sampled positions across the four M-tiles."""
+    shape = I.SHAPES["tinyllama_int8"]
+    n = 256
+    log(f"case prefill tinyllama_int8 full depth n={n} (benchmarked launch)")
+    r = _run(M, shape, n, max_ctx=1024, seed_stream=7, check_kv=False)
+    rms = float(np.sqrt(np.mean((r["glog"].astype(np.float64) - r["ref32"].astype(np.float64)) ** 2)))
+    worst = 0.0
+    for p in np.linspace(0, n - 1, 16).astype(int):
+        for kv in range(2):
+            for g in range(shape.n_kv_heads):
+                got = _kv_rows(r["dec"], 0, kv, g, int(p), 1)
+                want = r["ref"].get_kv(0, kv, g, int(p), 1).astype(np.float64)
+                assert np.all(np.abs(got - want) <= 2.0 ** -7 * np.abs(want) + 1e-3), (p, kv, g)
+                worst = max(worst, float(np.max(np.abs(got - want))))
+    log(f"tinyllama_int8 full depth n={n}: logits max abs err {r['err']:.3e}, rms {rms:.3e}, "
+        f"layer-0 kv worst {worst:.3e}, margin {r['margin']:.3e}")
+    assert r["err"] <= 0.25 and rms <= 0.05
+    _assert_token(r, "tinyllama_int8 full depth 256")
+    _close(r)
