@@ -45,10 +45,22 @@ amk_status lower_prefill(const amk_model_desc& d, int n_cu, int n_tokens, PfLowe
     const int nm = (n_tokens + kPfMt - 1) / kPfMt;
     const uint64_t Tp = (uint64_t)nm * kPfMt;
     const int ntx = pf_nt_x(H), nxt = H / ntx;          // O / down column tiles
-    // gate/up j tiles: 32 j (64 weight rows) per tile, or 64 j when that many tiles would take
-    // more than one round of the CUs (the tasks are latency-bound, so fewer rounds win)
+    // gate/up j tiles: 32 j (64 weight rows) per tile; when that many tiles would take more than
+    // one round of the CUs (the tasks are latency-bound, so fewer rounds win), the smallest width
+    // (a multiple of 8 that divides I) that fits one round, up to 64 j, or 128 j for int8 and int4
+    // weights (wide tiles: 256 weight rows staged 128 input columns at a time)
     int nj = pf_nj(I);
-    if (nj == 32 && I % 64 == 0 && (int64_t)nm * (I / 32) > n_cu) nj = 64;
+    if ((int64_t)nm * (I / nj) > n_cu) {
+        const bool wide = d.wfmt == AMK_INT8_PC || d.wfmt == AMK_INT4_G128;
+        const int max_nj = (wide ? kPfWideNt : kPfMaxNt) / 2;
+        const int want = (int)(((int64_t)nm * I + n_cu - 1) / n_cu);
+        int pick = 0;
+        for (int cand = (want + 7) / 8 * 8; cand <= max_nj && !pick; cand += 8)
+            if (I % cand == 0) pick = cand;
+        for (int cand = max_nj; cand > nj && !pick; cand -= 8)   // else the widest that divides I
+            if (I % cand == 0) pick = cand;
+        if (pick) nj = pick;
+    }
     const int njt = I / nj;
     const int nqkv = nH + 2 * nKV;
     const int lm_rows = std::min(kPfLmRows, std::max(1, (d.vocab + n_cu - 1) / n_cu));

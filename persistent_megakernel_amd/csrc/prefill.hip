@@ -103,8 +103,8 @@ struct Shared {
     double dpart[kPfWaves];
     float part[2 * kPfWaves];
     int32_t ipart[kPfWaves];
-    RowAddr rows[kPfMaxNt];          // B rows of the current GEMM tile
-    float scale[kPfMaxNt];           // their int8 scales
+    RowAddr rows[kPfWideNt];         // B rows of the current GEMM tile
+    float scale[kPfWideNt];          // their int8 scales
     float rrow[kPfMt];               // norm scales of the tile's rows (GEMMs with a fused RMSNorm)
 };
 
@@ -372,6 +372,210 @@ DEV void gemm_tile(const Ctx& c, const void* A, uint32_t lda, uint32_t m0, uint3
     __syncthreads();
 }
 
+// The same GEMM tile for gate/up tiles of more than kPfMaxNt weight rows (int8 and int4 weights):
+// 128 input columns per K stage, up to 256 rows, up to 8 blocks per wave.
+template <int FMT>
+DEV void gemm_tile_wide(const Ctx& c, const void* A, uint32_t lda, uint32_t m0, uint32_t mvalid, uint32_t nt, uint32_t K,
+                   const float* gain = nullptr, const double* ssq = nullptr) {
+    constexpr int F32 = FMT == AMK_F32;
+    static_assert(FMT == AMK_INT8_PC || FMT == AMK_INT4_G128, "wide tiles: 1- and 0.5-byte weights");
+    constexpr int Kt = kPfWideKt;
+    constexpr int JB = kPfWideNt / 16 * 4 / kPfWaves;   // 16x16 blocks per wave, at most
+    constexpr int Pad = F32 ? kPfPad32 : kPfPad16;
+    constexpr int ES = F32 ? 4 : 2;                 // compute element bytes
+    constexpr int LD = Kt + Pad;                    // LDS row pitch (elements)
+    constexpr int EPS_A = 16 / ES;                  // activation elements per 16-byte segment
+    constexpr int SEGS_A = kPfMt * Kt / EPS_A / kPfThreads;   // per thread (4)
+    constexpr int CPS = codes_per_seg<FMT>();
+    constexpr int SPR = Kt / CPS;                   // weight segments per row per stage
+    constexpr int SEGS_B = kPfWideNt * SPR / kPfThreads;      // per thread, at most
+    static_assert(kPfMt * LD * ES + kPfWideNt * LD * ES <= kPfGainOff, "stage layout below the gains");
+    static_assert(SEGS_A * kPfThreads * EPS_A == kPfMt * Kt, "A staging");
+    const PfParams& P = *c.P;
+    Shared& S = *c.S;
+    uint8_t* Abuf = c.lds;
+    uint8_t* Bbuf = c.lds + kPfMt * LD * ES;
+    const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
+    const uint32_t nbn = nt / 16, nblk = 4 * nbn;   // 16x16 blocks (4 row blocks: rows past mvalid are zeros)
+    const uint32_t stages = (K + Kt - 1) / Kt;
+    const uint32_t segs_b = nt * SPR;
+    float* G = (float*)(c.lds + kPfGainOff);   // the norm gains [K]
+    if (gain) {
+        for (uint32_t k = (uint32_t)tid; k < K; k += kPfThreads) G[k] = gain[k];
+        {   // eight threads per row: each sums the tiles t = j (mod 8), then a fixed xor tree
+            const uint32_t row = (uint32_t)tid >> 3, j = (uint32_t)tid & 7u;
+            const uint32_t nxt = (uint32_t)(P.H / pf_nt_x(P.H));
+            double ss = 0.0;
+            if (row < mvalid) {
+                const double* q = ssq + (uint64_t)(m0 + row) * nxt;
+                for (uint32_t t = j; t < nxt; t += 8) ss += q[t];
+            }
+            ss += __shfl_xor(ss, 1, 64);
+            ss += __shfl_xor(ss, 2, 64);
+            ss += __shfl_xor(ss, 4, 64);
+            if (j == 0) S.rrow[row] = row < mvalid ? (float)(1.0 / sqrt(ss / (double)K + (double)P.eps)) : 0.f;
+        }
+        __syncthreads();
+    }
+
+    u32x4 ra[SEGS_A], rb[SEGS_B];
+    auto load = [&](uint32_t s) {
+        const uint32_t k0 = s * Kt;
+#pragma unroll
+        for (int i = 0; i < SEGS_A; ++i) {
+            const uint32_t g = (uint32_t)tid + (uint32_t)i * kPfThreads;
+            const uint32_t r = g / (Kt / EPS_A), col = (g % (Kt / EPS_A)) * EPS_A, k = k0 + col;
+            ra[i] = u32x4{0, 0, 0, 0};
+            if (r < mvalid && k < K) ra[i] = *(const u32x4*)((const uint8_t*)A + ((uint64_t)(m0 + r) * lda + k) * ES);
+        }
+#pragma unroll
+        for (int i = 0; i < SEGS_B; ++i) {
+            const uint32_t g = (uint32_t)tid + (uint32_t)i * kPfThreads;
+            const uint32_t r = g / SPR, k = k0 + (g % SPR) * CPS;
+            rb[i] = u32x4{0, 0, 0, 0};
+            if (g < segs_b && k < K) {
+                const uint64_t off = S.rows[r].codes + (FMT == AMK_F32 ? 4ull * k : FMT == AMK_BF16 ? 2ull * k
+                                                       : FMT == AMK_INT8_PC ? (uint64_t)k : (uint64_t)k / 2);
+                rb[i] = __builtin_nontemporal_load((const u32x4*)(P.wstream + off));
+            }
+        }
+    };
+    auto store = [&](uint32_t s) {
+#pragma unroll
+        for (int i = 0; i < SEGS_A; ++i) {
+            const uint32_t g = (uint32_t)tid + (uint32_t)i * kPfThreads;
+            const uint32_t r = g / (Kt / EPS_A), col = (g % (Kt / EPS_A)) * EPS_A, k = s * Kt + col;
+            u32x4 v = ra[i];
+            if (gain && k < K) {   // RMSNorm on the way in: round_act((x * r) * g)
+                const float rr = S.rrow[r];
+                if (F32) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) v[j] = __float_as_uint((__uint_as_float(v[j]) * rr) * G[k + j]);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t lo = f2bf((bf2f(v[j] & 0xffffu) * rr) * G[k + 2 * j]);
+                        const uint32_t hi = f2bf((bf2f(v[j] >> 16) * rr) * G[k + 2 * j + 1]);
+                        v[j] = lo | (hi << 16);
+                    }
+                }
+            }
+            *(u32x4*)(Abuf + (r * LD + col) * ES) = v;
+        }
+#pragma unroll
+        for (int i = 0; i < SEGS_B; ++i) {
+            const uint32_t g = (uint32_t)tid + (uint32_t)i * kPfThreads;
+            if (g >= segs_b) continue;
+            const uint32_t r = g / SPR, col = (g % SPR) * CPS;
+            uint8_t* dst = Bbuf + (r * LD + col) * ES;
+            if (FMT == AMK_F32 || FMT == AMK_BF16) {
+                *(u32x4*)dst = rb[i];
+            } else if (FMT == AMK_INT8_PC) {
+                // 16 signed codes -> 16 bf16 (exact)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    u32x4 o;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t word = rb[i][2 * h + j / 2];
+                        const int b0 = (int)(int8_t)(word >> (16 * (j & 1)));
+                        const int b1 = (int)(int8_t)(word >> (16 * (j & 1) + 8));
+                        o[j] = (__float_as_uint((float)b0) >> 16) | (__float_as_uint((float)b1) & 0xffff0000u);
+                    }
+                    *(u32x4*)(dst + 16 * h) = o;
+                }
+            } else {
+                // 32 int4 codes (low nibble first, biased by 8) -> 32 bf16 (exact)
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    const uint32_t word = rb[i][h];
+                    u32x4 o;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int c0 = (int)((word >> (8 * j)) & 15u) - 8;
+                        const int c1 = (int)((word >> (8 * j + 4)) & 15u) - 8;
+                        o[j] = (__float_as_uint((float)c0) >> 16) | (__float_as_uint((float)c1) & 0xffff0000u);
+                    }
+                    *(u32x4*)(dst + 16 * h) = o;
+                }
+            }
+        }
+    };
+
+    f32x4 acc[JB];
+#pragma unroll
+    for (int j = 0; j < JB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int q = lane & 15, kq = lane >> 4;
+
+    load(0);
+    for (uint32_t s = 0; s < stages; ++s) {
+        store(s);
+        __syncthreads();
+        if (s + 1 < stages) load(s + 1);   // in flight while the matrix cores work
+        const uint32_t kv = min((uint32_t)Kt, K - s * Kt);   // valid columns of this stage (multiple of 16)
+#pragma unroll
+        for (int j = 0; j < JB; ++j) {
+            const uint32_t b = (uint32_t)w + 8u * (uint32_t)j;
+            if (b >= nblk) break;
+            const uint32_t bm = b / nbn, bn = b % nbn;
+            const uint8_t* arow = Abuf + (uint64_t)((bm * 16 + q) * LD) * ES;
+            const uint8_t* brow = Bbuf + (uint64_t)((bn * 16 + q) * LD) * ES;
+            if (F32) {
+                for (uint32_t k0 = 0; k0 < kv; k0 += 32) {
+                    f32x4 part = f32x4{0.f, 0.f, 0.f, 0.f};
+                    for (uint32_t kk = k0; kk < k0 + 32 && kk < kv; kk += 4) {
+                        const float av = *(const float*)(arow + (kk + kq) * 4);
+                        const float bv = *(const float*)(brow + (kk + kq) * 4);
+                        part = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, part, 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[j][i] += part[i];
+                }
+            } else if (FMT == AMK_INT4_G128) {
+                // per 128-column group: partial sum, then scaled into the total
+                for (uint32_t g0 = 0; g0 < kv; g0 += 128) {
+                    f32x4 part = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (uint32_t kk = 0; kk < 128; kk += 32) {
+                        const bf16x8 av = *(const bf16x8*)(arow + (g0 + kk + kq * 8) * 2);
+                        const bf16x8 bv = *(const bf16x8*)(brow + (g0 + kk + kq * 8) * 2);
+                        part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, part, 0, 0, 0);
+                    }
+                    const uint32_t n = bn * 16 + (uint32_t)q, grp = (s * Kt + g0) / 128;
+                    const float sc = h2f(*(const uint16_t*)(P.wstream + S.rows[n].scales + 2ull * grp));
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[j][i] += sc * part[i];
+                }
+            } else {
+                for (uint32_t k0 = 0; k0 < kv; k0 += 128) {
+                    f32x4 part = f32x4{0.f, 0.f, 0.f, 0.f};
+                    for (uint32_t kk = k0; kk < k0 + 128 && kk < kv; kk += 32) {
+                        const bf16x8 av = *(const bf16x8*)(arow + (kk + kq * 8) * 2);
+                        const bf16x8 bv = *(const bf16x8*)(brow + (kk + kq * 8) * 2);
+                        part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, part, 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[j][i] += part[i];
+                }
+            }
+        }
+        __syncthreads();
+    }
+    // the tile to LDS, fp32 [64][nt + 4] (over the staging area, free after the last barrier)
+    float* C = (float*)c.lds;
+    const uint32_t ldc = nt + 4;
+#pragma unroll
+    for (int j = 0; j < JB; ++j) {
+        const uint32_t b = (uint32_t)w + 8u * (uint32_t)j;
+        if (b >= nblk) break;
+        const uint32_t bm = b / nbn, bn = b % nbn, n = bn * 16 + (uint32_t)q;
+        const float sc = FMT == AMK_INT8_PC ? S.scale[n] : 1.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) C[(bm * 16 + (uint32_t)kq * 4 + (uint32_t)i) * ldc + n] = acc[j][i] * sc;
+    }
+    __syncthreads();
+}
+
 // Row addresses (and int8 scales) of the tile's B rows into LDS. rows(i) -> (matrix, row).
 template <int FMT, typename F>
 DEV void stage_rows(const Ctx& c, uint32_t nt, uint32_t layer, F&& rows) {
@@ -477,8 +681,17 @@ DEV void op_gateup(const Ctx& c, const PfTask& T) {
         m = i < nn ? PM_WG : PM_WU;
         r = T.n0 + (i < nn ? i : i - nn);
     });
-    gemm_tile<FMT>(c, P.x, (uint32_t)P.H, T.m0, mvalid, 2 * nn, (uint32_t)P.H, P.norms + ((uint64_t)2 * T.layer + 1) * P.H,
-                   P.ssq + (uint64_t)kPfChunk * (P.H / pf_nt_x(P.H)));
+    const float* gn = P.norms + ((uint64_t)2 * T.layer + 1) * P.H;
+    const double* sq = P.ssq + (uint64_t)kPfChunk * (P.H / pf_nt_x(P.H));
+    if constexpr (FMT == AMK_INT8_PC || FMT == AMK_INT4_G128) {
+        if (2 * nn > (uint32_t)kPfMaxNt) {
+            gemm_tile_wide<FMT>(c, P.x, (uint32_t)P.H, T.m0, mvalid, 2 * nn, (uint32_t)P.H, gn, sq);
+        } else {
+            gemm_tile<FMT>(c, P.x, (uint32_t)P.H, T.m0, mvalid, 2 * nn, (uint32_t)P.H, gn, sq);
+        }
+    } else {
+        gemm_tile<FMT>(c, P.x, (uint32_t)P.H, T.m0, mvalid, 2 * nn, (uint32_t)P.H, gn, sq);
+    }
     const float* C = (const float*)c.lds;
     const uint32_t ldc = 2 * nn + 4;
     for (uint32_t e = threadIdx.x; e < mvalid * nn; e += kPfThreads) {
