@@ -49,6 +49,7 @@ struct amk_ctx {
     void* pf_o = nullptr;
     void* pf_a = nullptr;
     uint32_t* pf_lmpart = nullptr;
+    float* pf_kpart = nullptr;      // K-split partial tiles: n_cu blocks of kPfMt x kPfMaxNt fp32
     uint64_t* pf_trace = nullptr;   // caller-owned, optional
     uint64_t pf_trace_cap = 0;
     struct PfVariant {
@@ -93,6 +94,7 @@ void free_ctx(amk_ctx* c) {
     (void)hipFree(c->pf_o);
     (void)hipFree(c->pf_a);
     (void)hipFree(c->pf_lmpart);
+    (void)hipFree(c->pf_kpart);
     (void)hipFree(c->d_wstream);
     (void)hipFree(c->d_tasks);
     (void)hipFree(c->d_qoff);
@@ -388,8 +390,12 @@ amk_status pf_buffers(amk_ctx* c, int lm_tiles) {
     ck(hipMalloc(&c->pf_o, R * d.n_heads * d.head_dim * esz));
     ck(hipMalloc(&c->pf_a, R * d.intermediate * esz));
     ck(hipMalloc((void**)&c->pf_lmpart, 2 * sizeof(uint32_t) * (size_t)std::max(1, lm_tiles)));
+    ck(hipMalloc((void**)&c->pf_kpart, (size_t)c->n_cu * kPfMt * kPfMaxNt * sizeof(float)));
     if (e != hipSuccess) {
-        for (void** p : {&c->pf_x, (void**)&c->pf_ssq, &c->pf_q, &c->pf_o, &c->pf_a, (void**)&c->pf_lmpart}) { (void)hipFree(*p); *p = nullptr; }
+        for (void** p : {&c->pf_x, (void**)&c->pf_ssq, &c->pf_q, &c->pf_o, &c->pf_a, (void**)&c->pf_lmpart, (void**)&c->pf_kpart}) {
+            (void)hipFree(*p);
+            *p = nullptr;
+        }
         return e == hipErrorOutOfMemory ? AMK_E_OOM : AMK_E_HIP;
     }
     return AMK_OK;
@@ -432,6 +438,7 @@ extern "C" amk_status amk_prefill(amk_ctx* c, const int32_t* tokens, int32_t pos
         for (int m = 0; m < PM_N; ++m) { P.tab_base[m] = c->tab_base[m]; P.tab_rows[m] = c->tab_rows[m]; }
         P.x = c->pf_x; P.ssq = c->pf_ssq; P.q = c->pf_q; P.o = c->pf_o; P.a = c->pf_a;
         P.lmpart = c->pf_lmpart;
+        P.kpart = c->pf_kpart;
         P.kv = c->base.kv;
         P.embed = c->d_embed;
         P.norms = c->d_norms;

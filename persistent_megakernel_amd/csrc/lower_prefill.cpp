@@ -23,7 +23,7 @@ namespace amk {
 
 namespace {
 
-enum PReg : uint32_t { PR_TOK = 0, PR_X, PR_SSQ, PR_Q, PR_O, PR_A, PR_LMPART, PR_LOGITS, PR_TOKOUT, PR_KV0 };
+enum PReg : uint32_t { PR_TOK = 0, PR_X, PR_SSQ, PR_Q, PR_O, PR_A, PR_LMPART, PR_LOGITS, PR_TOKOUT, PR_KPART, PR_KV0 };
 
 struct PGen {
     PfTask t;
@@ -68,7 +68,7 @@ amk_status lower_prefill(const amk_model_desc& d, int n_cu, int n_tokens, PfLowe
 
     std::vector<PGen> G;
     uint32_t nctr = 0, cursor = 0;
-    auto mk = [&](uint16_t op, int layer, int mtile, uint32_t n0, uint32_t nn, uint32_t wctr, uint32_t wcnt) {
+    auto mk = [&](uint8_t op, int layer, int mtile, uint32_t n0, uint32_t nn, uint32_t wctr, uint32_t wcnt) {
         PGen g;
         std::memset(&g.t, 0, sizeof(g.t));
         g.t.op = op;
@@ -108,6 +108,67 @@ amk_status lower_prefill(const amk_model_desc& d, int n_cu, int n_tokens, PfLowe
             const uint64_t b = ((uint64_t)half * nxt + u) * Tp + m0;
             acc(id, PR_SSQ, flags, b, b + mv);
         }
+    };
+    // O or down GEMM + residual (+ the sums of squares of its column tile, for the next norm:
+    // O feeds the MLP norm, down the next attention norm). When the phase has fewer tiles than
+    // CUs, each tile's K loop is split into up to kPfMaxSplit parts of whole K stages: the parts
+    // write fp32 partial tiles and signal the tile's own counter; one sum task per tile waits for
+    // them and does the residual epilogue, and the sum tasks close the phase.
+    const int kt = pf_kt(d.wfmt == AMK_F32);
+    auto resid_phase = [&](int l, bool down) {
+        const int K = down ? I : nH * hd;
+        const uint32_t in_reg = down ? PR_A : PR_O;
+        const int unit_w = down ? nj : hd;   // input columns per unit of the input region
+        const int half = down ? 0 : 1;
+        const int stages = (K + kt - 1) / kt, tiles = nm * nxt;
+        const int ns = std::max(1, std::min({kPfMaxSplit, n_cu / tiles, stages}));
+        auto epilogue = [&](uint32_t id, int i, int t) {
+            const uint64_t m0 = (uint64_t)i * kPfMt, mv = rows_of(i);
+            acc(id, PR_X, 0, t * Tp + m0, t * Tp + m0 + mv);
+            acc(id, PR_X, AMK_ACC_WRITE, t * Tp + m0, t * Tp + m0 + mv);
+            const uint64_t b = ((uint64_t)half * nxt + t) * Tp + m0;
+            acc(id, PR_SSQ, AMK_ACC_WRITE, b, b + mv);
+        };
+        auto part_block = [&](int s, int i, int t) { return ((uint64_t)(s * nm + i) * nxt + t) * kPfMt; };
+        const uint32_t f = (uint32_t)G.size();
+        if (ns == 1) {
+            for (int i = 0; i < nm; ++i)
+                for (int t = 0; t < nxt; ++t) {
+                    uint32_t id = mk(down ? PF_DOWN : PF_OPROJ, l, i, (uint32_t)(t * ntx), (uint32_t)ntx, pc, pn);
+                    all_units(id, in_reg, 0, down ? njt : nH, i);
+                    epilogue(id, i, t);
+                }
+            close(f, pc, pn);
+            return;
+        }
+        const uint32_t ctr0 = nctr;
+        nctr += (uint32_t)tiles;
+        for (int s = 0; s < ns; ++s) {
+            const int k0 = s * stages / ns * kt, k1 = std::min(K, (s + 1) * stages / ns * kt);
+            for (int i = 0; i < nm; ++i)
+                for (int t = 0; t < nxt; ++t) {
+                    uint32_t id = mk(down ? PF_DPART : PF_OPART, l, i, (uint32_t)(t * ntx), (uint32_t)ntx, pc, pn);
+                    G[id].t.ks = (uint8_t)(s << 4 | ns);
+                    G[id].t.sctr = ctr0 + (uint32_t)(i * nxt + t);
+                    const uint64_t m0 = (uint64_t)i * kPfMt, mv = rows_of(i);
+                    for (int u = k0 / unit_w; u < (k1 + unit_w - 1) / unit_w; ++u) acc(id, in_reg, 0, u * Tp + m0, u * Tp + m0 + mv);
+                    const uint64_t b = part_block(s, i, t);
+                    acc(id, PR_KPART, AMK_ACC_WRITE, b, b + mv);
+                }
+        }
+        const uint32_t fs = (uint32_t)G.size();
+        for (int i = 0; i < nm; ++i)
+            for (int t = 0; t < nxt; ++t) {
+                uint32_t id = mk(down ? PF_DSUM : PF_OSUM, l, i, (uint32_t)(t * ntx), (uint32_t)ntx, ctr0 + (uint32_t)(i * nxt + t),
+                                 (uint32_t)ns);
+                G[id].t.ks = (uint8_t)ns;
+                for (int s = 0; s < ns; ++s) {
+                    const uint64_t b = part_block(s, i, t);
+                    acc(id, PR_KPART, 0, b, b + rows_of(i));
+                }
+                epilogue(id, i, t);
+            }
+        close(fs, pc, pn);
     };
     // token embeddings into x, with the first attention norm's sums of squares
     {
@@ -151,19 +212,7 @@ amk_status lower_prefill(const amk_model_desc& d, int n_cu, int n_tokens, PfLowe
                 acc(id, PR_O, AMK_ACC_WRITE, h * Tp + m0, h * Tp + m0 + mv);
             }
         close(f, pc, pn);
-        // O projection + residual (+ the MLP norm's sums of squares of its column tile)
-        f = (uint32_t)G.size();
-        for (int i = 0; i < nm; ++i)
-            for (int t = 0; t < nxt; ++t) {
-                uint32_t id = mk(PF_OPROJ, l, i, (uint32_t)(t * ntx), (uint32_t)ntx, pc, pn);
-                const uint64_t m0 = (uint64_t)i * kPfMt, mv = rows_of(i);
-                all_units(id, PR_O, 0, nH, i);
-                acc(id, PR_X, 0, t * Tp + m0, t * Tp + m0 + mv);
-                acc(id, PR_X, AMK_ACC_WRITE, t * Tp + m0, t * Tp + m0 + mv);
-                const uint64_t b = ((uint64_t)nxt + t) * Tp + m0;
-                acc(id, PR_SSQ, AMK_ACC_WRITE, b, b + mv);
-            }
-        close(f, pc, pn);
+        resid_phase(l, false);
         // gate/up + SwiGLU (the MLP norm fused into its input)
         f = (uint32_t)G.size();
         for (int i = 0; i < nm; ++i)
@@ -175,19 +224,7 @@ amk_status lower_prefill(const amk_model_desc& d, int n_cu, int n_tokens, PfLowe
                 acc(id, PR_A, AMK_ACC_WRITE, t * Tp + m0, t * Tp + m0 + mv);
             }
         close(f, pc, pn);
-        // down + residual (+ the next attention norm's sums of squares of its column tile)
-        f = (uint32_t)G.size();
-        for (int i = 0; i < nm; ++i)
-            for (int t = 0; t < nxt; ++t) {
-                uint32_t id = mk(PF_DOWN, l, i, (uint32_t)(t * ntx), (uint32_t)ntx, pc, pn);
-                const uint64_t m0 = (uint64_t)i * kPfMt, mv = rows_of(i);
-                all_units(id, PR_A, 0, njt, i);
-                acc(id, PR_X, 0, t * Tp + m0, t * Tp + m0 + mv);
-                acc(id, PR_X, AMK_ACC_WRITE, t * Tp + m0, t * Tp + m0 + mv);
-                const uint64_t b = (uint64_t)t * Tp + m0;
-                acc(id, PR_SSQ, AMK_ACC_WRITE, b, b + mv);
-            }
-        close(f, pc, pn);
+        resid_phase(l, true);
     }
     // LM tiles on the last row, then the argmax
     uint32_t f = (uint32_t)G.size();

@@ -25,7 +25,7 @@
 
 namespace amk {
 
-enum PfOp : uint16_t {
+enum PfOp : uint8_t {
     PF_EMBED = 1,    // m0, mt: token embeddings of rows [m0, m0 + mt) into x, and their sums of squares
     PF_QKV = 2,      // layer, m0, mt, n0 = fused head index (q heads, then k, then v): GEMM + RoPE + store
     PF_ATTN = 3,     // layer, m0, mt, n0 = query head: causal attention of queries [m0, m0 + mt)
@@ -33,7 +33,14 @@ enum PfOp : uint16_t {
     PF_GATEUP = 5,   // layer, m0, mt, n0, nn: gate/up GEMM for j in [n0, n0 + nn) + SwiGLU
     PF_DOWN = 6,     // layer, m0, mt, n0, nn: down GEMM columns [n0, n0 + nn) + residual
     PF_LM = 7,       // n0, nn = vocabulary rows, mt = tile index: final RMSNorm of the last row + LM rows + tile argmax
-    PF_ARGMAX = 8    // mt = number of LM tiles: greedy token
+    PF_ARGMAX = 8,   // mt = number of LM tiles: greedy token
+    // O or down GEMM split along K (when a phase has fewer column tiles than CUs): the parts of
+    // one tile write fp32 partial tiles and signal the tile's own counter; one sum task per tile
+    // waits for them, adds them in split order and does the residual epilogue
+    PF_OPART = 9,    // layer, m0, mt, n0, nn, ks: partial O GEMM over split (ks >> 4) of (ks & 15)
+    PF_OSUM = 10,    // layer, m0, mt, n0, nn, ks & 15 = splits: sum of the partial tiles + residual
+    PF_DPART = 11,   // as PF_OPART for the down GEMM
+    PF_DSUM = 12     // as PF_OSUM for the down GEMM
 };
 
 constexpr uint32_t kPfNone = 0xffffffffu;
@@ -41,7 +48,9 @@ constexpr uint32_t kPfNone = 0xffffffffu;
 // Device task (32 bytes). One wait (a full wait: every producer of the counter) and at most
 // one signal per task.
 struct PfTask {
-    uint16_t op, layer;
+    uint8_t op;            // PfOp
+    uint8_t ks;            // K-split tasks: split index << 4 | number of splits (else 0)
+    uint16_t layer;
     uint32_t m0, mt;       // token rows [m0, m0 + mt) of the chunk
     uint32_t n0, nn;       // column / head / row range (per op)
     uint32_t wctr, wcnt;   // counter to wait on (kPfNone: none) and its producer count
@@ -75,6 +84,7 @@ constexpr int kPfPad16 = 8;      // LDS row padding (elements) of 16-bit operand
 constexpr int kPfPad32 = 4;      // of fp32 operand tiles
 constexpr int kPfChunk = 256;    // tokens per launch (longer prompts take several launches)
 constexpr int kPfLmRows = 512;   // most LM rows per task
+constexpr int kPfMaxSplit = 8;   // most K splits of an O or down tile
 constexpr int kPfLdsBytes = 132 * 1024;   // A and B stages (101,376 B) + the norm gains (up to 8192 fp32)
 
 struct PfParams {
@@ -101,6 +111,9 @@ struct PfParams {
     void* o;                     // [.][nH * hd] attention output
     void* a;                     // [.][I] SwiGLU output
     uint32_t* lmpart;            // [2 * LM tiles]: best value (fp32 bits), its index
+    float* kpart;                // K-split partial tiles: block ((split * M-tiles + M-tile) * column tiles
+                                 // + column tile) of kPfMt x (column tile width) fp32, row-major; at
+                                 // most n_cu blocks
     // model state
     void* kv;                    // [L][2][nKV][max_ctx][hd], activation type
     const void* embed;           // [V][H], activation type

@@ -145,10 +145,12 @@ DEV void task_wait(const Ctx& c, const PfTask& T) {
     __syncthreads();
 }
 
-// Publish the task's outputs: every wave's stores are written back at device scope, then one
-// increment of the task's counter.
+// Publish the task's outputs: every wave waits until its stores have reached the L2 of its XCD,
+// then one device-scope release by thread 0 (one write-back of that L2) and one increment of
+// the task's counter. (A release fence in every wave would write the L2 back once per wave: the
+// write-backs of all the CUs of an XCD queue at its L2, and cost 10 to 20 us per task.)
 DEV void task_signal(const Ctx& c, const PfTask& T) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (T.sctr != kPfNone && threadIdx.x == 0)
         __hip_atomic_fetch_add(&c.P->ctr[T.sctr], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
@@ -638,28 +640,49 @@ DEV void op_qkv(const Ctx& c, const PfTask& T) {
     }
 }
 
-// O or down projection + residual: x[m][n0 .. n0 + nn) += A[m] . W[n]
+// x += C (the GEMM tile in LDS, fp32 [mvalid][nn + 4]) over columns [n0, n0 + nn), rounded to
+// the activation type; then per row the sum of squares of the new x values of this column tile
+// (in double), for the norm of the next GEMM (O: the MLP norm; down: the next layer's attention
+// norm)
 template <int FMT>
-DEV void op_resid(const Ctx& c, const PfTask& T, bool down) {
+DEV void resid_epilogue(const Ctx& c, const PfTask& T, bool down, uint32_t mvalid) {
     constexpr int F32 = FMT == AMK_F32;
     const PfParams& P = *c.P;
     const uint32_t nn = T.nn, H = (uint32_t)P.H;
-    const uint32_t mvalid = rows_valid(P, T);
-    const uint32_t K = down ? (uint32_t)P.I : (uint32_t)(P.nH * P.hd);
-    stage_rows<FMT>(c, nn, T.layer, [&](uint32_t i, uint32_t& m, uint32_t& r) { m = down ? PM_WD : PM_WO; r = T.n0 + i; });
-    gemm_tile<FMT>(c, down ? P.a : P.o, K, T.m0, mvalid, nn, K);
     float* C = (float*)c.lds;
     const uint32_t ldc = nn + 4;
-    for (uint32_t e = threadIdx.x; e < mvalid * nn; e += kPfThreads) {
+    // eight consecutive columns per thread (nn is a multiple of 16): one vector load and one
+    // vector store of x, all in flight at once
+    for (uint32_t e = threadIdx.x * 8u; e < mvalid * nn; e += kPfThreads * 8u) {
         const uint32_t m = e / nn, n = e % nn;
         const uint64_t xi = (uint64_t)(T.m0 + m) * H + T.n0 + n;
-        const float xn = rnd<F32>(act_ld<F32>(P.x, xi) + C[m * ldc + n]);
-        act_st<F32>(P.x, xi, xn);
-        C[m * ldc + n] = xn;
+        float xv[8];
+        if (F32) {
+            const f32x4 lo = *(const f32x4*)((const float*)P.x + xi), hi = *(const f32x4*)((const float*)P.x + xi + 4);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) { xv[j] = lo[j]; xv[4 + j] = hi[j]; }
+        } else {
+            const u32x4 v = *(const u32x4*)((const uint16_t*)P.x + xi);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) { xv[2 * j] = bf2f(v[j] & 0xffffu); xv[2 * j + 1] = bf2f(v[j] >> 16); }
+        }
+        float* cr = C + m * ldc + n;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            xv[j] = rnd<F32>(xv[j] + cr[j]);
+            cr[j] = xv[j];
+        }
+        if (F32) {
+            *(f32x4*)((float*)P.x + xi) = f32x4{xv[0], xv[1], xv[2], xv[3]};
+            *(f32x4*)((float*)P.x + xi + 4) = f32x4{xv[4], xv[5], xv[6], xv[7]};
+        } else {
+            u32x4 v;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] = f2bf(xv[2 * j]) | (f2bf(xv[2 * j + 1]) << 16);
+            *(u32x4*)((uint16_t*)P.x + xi) = v;
+        }
     }
     __syncthreads();
-    // per row, the sum of squares of the new x values of this column tile (in double), for the
-    // norm of the next GEMM (O: the MLP norm; down: the next layer's attention norm)
     const uint32_t nxt = H / (uint32_t)pf_nt_x((int)H), tile = T.n0 / nn;
     double* q = P.ssq + (down ? 0ull : (uint64_t)kPfChunk * nxt);
     const int lane = lane_id(), w = threadIdx.x >> 6;
@@ -668,6 +691,80 @@ DEV void op_resid(const Ctx& c, const PfTask& T, bool down) {
         const double ss = wave_sum_d(v * v);
         if (lane == 0) q[(uint64_t)(T.m0 + m) * nxt + tile] = ss;
     }
+}
+
+// O or down projection + residual: x[m][n0 .. n0 + nn) += A[m] . W[n]
+template <int FMT>
+DEV void op_resid(const Ctx& c, const PfTask& T, bool down) {
+    const PfParams& P = *c.P;
+    const uint32_t nn = T.nn;
+    const uint32_t mvalid = rows_valid(P, T);
+    const uint32_t K = down ? (uint32_t)P.I : (uint32_t)(P.nH * P.hd);
+    stage_rows<FMT>(c, nn, T.layer, [&](uint32_t i, uint32_t& m, uint32_t& r) { m = down ? PM_WD : PM_WO; r = T.n0 + i; });
+    gemm_tile<FMT>(c, down ? P.a : P.o, K, T.m0, mvalid, nn, K);
+    resid_epilogue<FMT>(c, T, down, mvalid);
+}
+
+// Block of the K-split partial tile of split s of the task's tile (M-tile, column tile).
+DEV float* kpart_block(const PfParams& P, const PfTask& T, uint32_t s) {
+    const uint32_t nm = ((uint32_t)P.T + kPfMt - 1) / kPfMt, nxt = (uint32_t)P.H / T.nn;
+    return P.kpart + ((uint64_t)(s * nm + T.m0 / kPfMt) * nxt + T.n0 / T.nn) * kPfMt * T.nn;
+}
+
+// One K split of an O or down tile: whole K stages [s * stages / splits, (s + 1) * stages /
+// splits) through the same GEMM (weight rows and activations offset to the first column), the
+// fp32 partial tile to its block.
+template <int FMT>
+DEV void op_kpart(const Ctx& c, const PfTask& T, bool down) {
+    constexpr int F32 = FMT == AMK_F32;
+    constexpr int Kt = F32 ? kPfKt32 : kPfKt16;
+    constexpr int ES = F32 ? 4 : 2;
+    const PfParams& P = *c.P;
+    Shared& S = *c.S;
+    const uint32_t nn = T.nn, splits = T.ks & 15u, s = T.ks >> 4;
+    const uint32_t mvalid = rows_valid(P, T);
+    const uint32_t K = down ? (uint32_t)P.I : (uint32_t)(P.nH * P.hd);
+    const uint32_t stages = (K + Kt - 1) / Kt;
+    const uint32_t k0 = s * stages / splits * Kt, k1 = min(K, (s + 1) * stages / splits * Kt);
+    stage_rows<FMT>(c, nn, T.layer, [&](uint32_t i, uint32_t& m, uint32_t& r) { m = down ? PM_WD : PM_WO; r = T.n0 + i; });
+    for (uint32_t i = threadIdx.x; i < nn; i += kPfThreads) {   // the rows this thread staged
+        S.rows[i].codes += FMT == AMK_F32 ? 4ull * k0 : FMT == AMK_BF16 ? 2ull * k0 : FMT == AMK_INT8_PC ? (uint64_t)k0 : k0 / 2ull;
+        if (FMT == AMK_INT4_G128) S.rows[i].scales += 2ull * (k0 / 128u);
+    }
+    __syncthreads();
+    gemm_tile<FMT>(c, (const uint8_t*)(down ? P.a : P.o) + (uint64_t)k0 * ES, K, T.m0, mvalid, nn, k1 - k0);
+    const float* C = (const float*)c.lds;
+    float* dst = kpart_block(P, T, s);
+    for (uint32_t e = threadIdx.x * 4u; e < mvalid * nn; e += kPfThreads * 4u) {
+        const float* cr = C + (e / nn) * (nn + 4) + e % nn;
+        *(f32x4*)(dst + e) = f32x4{cr[0], cr[1], cr[2], cr[3]};
+    }
+}
+
+// The sum of an O or down tile's K splits, in split order, then the residual epilogue.
+template <int FMT>
+DEV void op_ksum(const Ctx& c, const PfTask& T, bool down) {
+    const PfParams& P = *c.P;
+    const uint32_t nn = T.nn, splits = T.ks & 15u;
+    const uint32_t mvalid = rows_valid(P, T);
+    float* C = (float*)c.lds;
+    // four consecutive elements per thread; every split's load is issued up front (splits past
+    // the last one re-read split 0 and are not added)
+    const float* b0 = kpart_block(P, T, 0);
+    const uint64_t split_stride = (uint64_t)(kpart_block(P, T, 1) - b0);
+    for (uint32_t e = threadIdx.x * 4u; e < mvalid * nn; e += kPfThreads * 4u) {
+        f32x4 v = *(const f32x4*)(b0 + e);
+#pragma unroll
+        for (uint32_t s = 1; s < (uint32_t)kPfMaxSplit; ++s) {
+            const f32x4 t = *(const f32x4*)(b0 + (s < splits ? s : 0u) * split_stride + e);
+            if (s < splits) v += t;
+        }
+        float* cr = C + (e / nn) * (nn + 4) + e % nn;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cr[j] = v[j];
+    }
+    __syncthreads();
+    resid_epilogue<FMT>(c, T, down, mvalid);
 }
 
 // gate/up for j in [n0, n0 + nn): B rows = nn gate rows then nn up rows; a = silu(g) * u
@@ -1099,6 +1196,10 @@ DEV void prefill_body(const PfParams& Pin) {
         case PF_OPROJ: op_resid<FMT>(c, T, false); break;
         case PF_GATEUP: op_gateup<FMT>(c, T); break;
         case PF_DOWN: op_resid<FMT>(c, T, true); break;
+        case PF_OPART: op_kpart<FMT>(c, T, false); break;
+        case PF_OSUM: op_ksum<FMT>(c, T, false); break;
+        case PF_DPART: op_kpart<FMT>(c, T, true); break;
+        case PF_DSUM: op_ksum<FMT>(c, T, true); break;
         case PF_LM: if (P.do_lm) op_lm<FMT>(c, T); break;
         default: if (P.do_lm) op_argmax(c, T); break;
         }

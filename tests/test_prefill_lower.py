@@ -37,20 +37,36 @@ def test_prefill_schedule_runs_clean_on_the_executor(M, n_cu, n):
         assert r["completed"] and not r["races"] and not r["uncovered_reads"] and not r["unwritten_outputs"], r
 
 
+def _splits(sh, K, nm, n_cu):
+    """K splits of an O or down tile: whole K stages over the CUs the phase's tiles leave idle."""
+    kt = 128 if sh.act_f32 else 256
+    tiles = nm * (sh.hidden // 64)
+    return max(1, min(8, n_cu // tiles, -(-K // kt)))
+
+
 def test_prefill_schedule_structure(M):
     """One embedding phase, then five phases per layer (the norms fused into the GEMMs that
-    consume them), each waiting on all of the previous one; LM tiles and one argmax."""
+    consume them), each waiting on all of the previous one; an O or down phase with fewer tiles
+    than CUs is split along K, its parts signalling one counter per tile that the tile's sum
+    task waits on; LM tiles and one argmax."""
     sh = I.SHAPES["tiny_fp32"]
-    s = M.amk_lower_prefill(M.model_desc(sh), 16, 100)
+    n_cu, nm = 16, 2
+    s = M.amk_lower_prefill(M.model_desc(sh), n_cu, 100)
     ops = [t.opcode for t in s.tasks]
-    nm = 2
     nqkv = sh.n_heads + 2 * sh.n_kv_heads
-    per_layer = nm * (nqkv + sh.n_heads + 2 * (sh.hidden // 64) + sh.intermediate // 16)
+    tiles = nm * (sh.hidden // 64)
+    so = _splits(sh, sh.n_heads * sh.head_dim, nm, n_cu)
+    sd = _splits(sh, sh.intermediate, nm, n_cu)
+    assert (so, sd) == (1, 2)
+    resid = lambda ns: tiles if ns == 1 else tiles * (ns + 1)
+    per_layer = nm * (nqkv + sh.n_heads + sh.intermediate // 16) + resid(so) + resid(sd)
     n_lm = ops.count(7)
     assert ops.count(8) == 1 and n_lm >= 1 and ops.count(1) == nm
     assert len(ops) == nm + sh.n_layers * per_layer + n_lm + 1
-    assert len({c for t in s.tasks for c in t.signals}) == 1 + 5 * sh.n_layers + 1
-    # every wait is a full wait on the counter of the phase before
+    assert ops.count(11) == sh.n_layers * tiles * sd and ops.count(12) == sh.n_layers * tiles
+    assert ops.count(6) == 0 and ops.count(4) == sh.n_layers * tiles
+    assert len({c for t in s.tasks for c in t.signals}) == 1 + (5 + tiles) * sh.n_layers + 1
+    # every wait is a full wait on its counter: the phase before, or a tile's K splits
     producers = {}
     for i, t in enumerate(s.tasks):
         for c in t.signals:
@@ -58,6 +74,24 @@ def test_prefill_schedule_structure(M):
     for t in s.tasks:
         for c, th in t.waits:
             assert th == producers[c]
+            if t.opcode == 12:
+                assert th == sd
+
+
+def test_prefill_k_split_of_the_benchmarked_shape(M):
+    """TinyLlama int8, 256 tokens on 256 CUs: 128 O and 128 down tiles, each split in two (one
+    round of the CUs); 64 tokens: in eight. Tiles past the split bound stay whole."""
+    sh = I.SHAPES["tinyllama_int8"]
+    for n, ns in ((256, 2), (64, 8)):
+        s = M.amk_lower_prefill(M.model_desc(sh), 256, n)
+        ops = [t.opcode for t in s.tasks]
+        tiles = (n // 64) * (sh.hidden // 64)
+        assert ops.count(9) == ops.count(11) == sh.n_layers * tiles * ns, n
+        assert ops.count(10) == ops.count(12) == sh.n_layers * tiles, n
+        assert ops.count(4) == ops.count(6) == 0
+    s = M.amk_lower_prefill(M.model_desc(sh), 64, 256)   # 128 tiles on 64 CUs: no split
+    ops = [t.opcode for t in s.tasks]
+    assert ops.count(4) == ops.count(6) == sh.n_layers * 128 and ops.count(9) == 0
 
 
 def test_prefill_schedule_without_a_wait(M):
