@@ -45,13 +45,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 DEV uint64_t rt() { return __builtin_amdgcn_s_memrealtime(); }
 DEV int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
 DEV float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
-// fp32 -> bf16 bits, round to nearest even (NaN stays NaN)
-DEV uint32_t f2bf(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
-}
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN): the hardware conversion
+// (v_cvt_pk_bf16_f32), one instruction where a bit-level rounding takes six
+DEV uint32_t f2bf(float f) { return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f); }
 DEV float h2f(uint32_t h) {
     _Float16 x;
     uint16_t b = (uint16_t)h;
