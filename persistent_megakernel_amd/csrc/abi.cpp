@@ -260,7 +260,7 @@ extern "C" amk_status amk_create(const amk_model_desc* desc, const amk_weights* 
         const uint32_t rows[PM_N] = {(uint32_t)qd, (uint32_t)kd, (uint32_t)kd, (uint32_t)d.hidden, (uint32_t)d.intermediate,
                                      (uint32_t)d.intermediate, (uint32_t)d.hidden, (uint32_t)d.vocab};
         uint64_t total = 0;
-        for (int m = 0; m < PM_N; ++m) {
+        for (int m = 0; m < (int)PM_N; ++m) {
             c->tab_base[m] = (uint32_t)total;
             c->tab_rows[m] = rows[m];
             total += (uint64_t)rows[m] * (m == PM_LM ? 1 : L);
@@ -435,7 +435,7 @@ extern "C" amk_status amk_prefill(amk_ctx* c, const int32_t* tokens, int32_t pos
         P.epoch = v->epoch;
         P.wstream = c->d_wstream;
         P.rowtab = c->d_rowtab;
-        for (int m = 0; m < PM_N; ++m) { P.tab_base[m] = c->tab_base[m]; P.tab_rows[m] = c->tab_rows[m]; }
+        for (int m = 0; m < (int)PM_N; ++m) { P.tab_base[m] = c->tab_base[m]; P.tab_rows[m] = c->tab_rows[m]; }
         P.x = c->pf_x; P.ssq = c->pf_ssq; P.q = c->pf_q; P.o = c->pf_o; P.a = c->pf_a;
         P.lmpart = c->pf_lmpart;
         P.kpart = c->pf_kpart;

@@ -598,6 +598,56 @@ DEV uint64_t kv_index(const PfParams& P, int layer, int isv, int g, uint32_t pos
     return ((((uint64_t)layer * 2 + isv) * P.nKV + g) * P.max_ctx + pos) * P.hd;
 }
 
+// First input column of K split s of `splits` (whole stages of Kt columns); s = splits gives K.
+DEV uint32_t ksplit_col(uint32_t K, uint32_t Kt, uint32_t s, uint32_t splits) {
+    return min(K, s * ((K + Kt - 1) / Kt) / splits * Kt);
+}
+
+// The weight rows of a GEMM task into LDS (their addresses, and int8 row scales). They do not
+// depend on the task's inputs, so this runs before the task's wait and its loads overlap it.
+// QKV: the fused head's hd rows; O, down and their K splits: rows [n0, n0 + nn), offset to the
+// split's first column; gate/up: nn gate rows, then the nn up rows.
+template <int FMT>
+DEV void stage_task_rows(const Ctx& c, const PfTask& T) {
+    const PfParams& P = *c.P;
+    Shared& S = *c.S;
+    switch (T.op) {
+    case PF_QKV: {
+        const uint32_t j = T.n0, hd = (uint32_t)P.hd, nH = (uint32_t)P.nH, nKV = (uint32_t)P.nKV;
+        const uint32_t mat = j < nH ? PM_WQ : j < nH + nKV ? PM_WK : PM_WV;
+        const uint32_t head = j < nH ? j : j < nH + nKV ? j - nH : j - nH - nKV;
+        stage_rows<FMT>(c, hd, T.layer, [&](uint32_t i, uint32_t& m, uint32_t& r) { m = mat; r = head * hd + i; });
+        break;
+    }
+    case PF_OPROJ:
+    case PF_DOWN:
+    case PF_OPART:
+    case PF_DPART: {
+        const bool down = T.op == PF_DOWN || T.op == PF_DPART;
+        stage_rows<FMT>(c, T.nn, T.layer, [&](uint32_t i, uint32_t& m, uint32_t& r) { m = down ? PM_WD : PM_WO; r = T.n0 + i; });
+        if (T.op == PF_OPART || T.op == PF_DPART) {
+            const uint32_t K = down ? (uint32_t)P.I : (uint32_t)(P.nH * P.hd);
+            const uint32_t k0 = ksplit_col(K, (uint32_t)pf_kt(FMT == AMK_F32), T.ks >> 4, T.ks & 15u);
+            for (uint32_t i = threadIdx.x; i < T.nn; i += kPfThreads) {   // the rows this thread staged
+                S.rows[i].codes += FMT == AMK_F32 ? 4ull * k0 : FMT == AMK_BF16 ? 2ull * k0 : FMT == AMK_INT8_PC ? (uint64_t)k0 : k0 / 2ull;
+                if (FMT == AMK_INT4_G128) S.rows[i].scales += 2ull * (k0 / 128u);
+            }
+            __syncthreads();
+        }
+        break;
+    }
+    case PF_GATEUP: {
+        const uint32_t nn = T.nn;
+        stage_rows<FMT>(c, 2 * nn, T.layer, [&](uint32_t i, uint32_t& m, uint32_t& r) {
+            m = i < nn ? PM_WG : PM_WU;
+            r = T.n0 + (i < nn ? i : i - nn);
+        });
+        break;
+    }
+    default: break;
+    }
+}
+
 template <int FMT>
 DEV void op_qkv(const Ctx& c, const PfTask& T) {
     constexpr int F32 = FMT == AMK_F32;
@@ -607,7 +657,6 @@ DEV void op_qkv(const Ctx& c, const PfTask& T) {
     const uint32_t mvalid = rows_valid(P, T);
     const uint32_t mat = j < nH ? PM_WQ : j < nH + nKV ? PM_WK : PM_WV;
     const uint32_t head = j < nH ? j : j < nH + nKV ? j - nH : j - nH - nKV;
-    stage_rows<FMT>(c, hd, l, [&](uint32_t i, uint32_t& m, uint32_t& r) { m = mat; r = head * hd + i; });
     gemm_tile<FMT>(c, P.x, (uint32_t)P.H, T.m0, mvalid, hd, (uint32_t)P.H, P.norms + (uint64_t)2 * l * P.H, P.ssq);
     const float* C = (const float*)c.lds;
     const uint32_t ldc = hd + 4;
@@ -696,7 +745,6 @@ DEV void op_resid(const Ctx& c, const PfTask& T, bool down) {
     const uint32_t nn = T.nn;
     const uint32_t mvalid = rows_valid(P, T);
     const uint32_t K = down ? (uint32_t)P.I : (uint32_t)(P.nH * P.hd);
-    stage_rows<FMT>(c, nn, T.layer, [&](uint32_t i, uint32_t& m, uint32_t& r) { m = down ? PM_WD : PM_WO; r = T.n0 + i; });
     gemm_tile<FMT>(c, down ? P.a : P.o, K, T.m0, mvalid, nn, K);
     resid_epilogue<FMT>(c, T, down, mvalid);
 }
@@ -708,26 +756,18 @@ DEV float* kpart_block(const PfParams& P, const PfTask& T, uint32_t s) {
 }
 
 // One K split of an O or down tile: whole K stages [s * stages / splits, (s + 1) * stages /
-// splits) through the same GEMM (weight rows and activations offset to the first column), the
-// fp32 partial tile to its block.
+// splits) through the same GEMM (weight rows, staged before the wait, and activations offset to
+// the first column), the fp32 partial tile to its block.
 template <int FMT>
 DEV void op_kpart(const Ctx& c, const PfTask& T, bool down) {
     constexpr int F32 = FMT == AMK_F32;
     constexpr int Kt = F32 ? kPfKt32 : kPfKt16;
     constexpr int ES = F32 ? 4 : 2;
     const PfParams& P = *c.P;
-    Shared& S = *c.S;
     const uint32_t nn = T.nn, splits = T.ks & 15u, s = T.ks >> 4;
     const uint32_t mvalid = rows_valid(P, T);
     const uint32_t K = down ? (uint32_t)P.I : (uint32_t)(P.nH * P.hd);
-    const uint32_t stages = (K + Kt - 1) / Kt;
-    const uint32_t k0 = s * stages / splits * Kt, k1 = min(K, (s + 1) * stages / splits * Kt);
-    stage_rows<FMT>(c, nn, T.layer, [&](uint32_t i, uint32_t& m, uint32_t& r) { m = down ? PM_WD : PM_WO; r = T.n0 + i; });
-    for (uint32_t i = threadIdx.x; i < nn; i += kPfThreads) {   // the rows this thread staged
-        S.rows[i].codes += FMT == AMK_F32 ? 4ull * k0 : FMT == AMK_BF16 ? 2ull * k0 : FMT == AMK_INT8_PC ? (uint64_t)k0 : k0 / 2ull;
-        if (FMT == AMK_INT4_G128) S.rows[i].scales += 2ull * (k0 / 128u);
-    }
-    __syncthreads();
+    const uint32_t k0 = ksplit_col(K, Kt, s, splits), k1 = ksplit_col(K, Kt, s + 1, splits);
     gemm_tile<FMT>(c, (const uint8_t*)(down ? P.a : P.o) + (uint64_t)k0 * ES, K, T.m0, mvalid, nn, k1 - k0);
     const float* C = (const float*)c.lds;
     float* dst = kpart_block(P, T, s);
@@ -770,10 +810,6 @@ DEV void op_gateup(const Ctx& c, const PfTask& T) {
     const PfParams& P = *c.P;
     const uint32_t nn = T.nn, I = (uint32_t)P.I;
     const uint32_t mvalid = rows_valid(P, T);
-    stage_rows<FMT>(c, 2 * nn, T.layer, [&](uint32_t i, uint32_t& m, uint32_t& r) {
-        m = i < nn ? PM_WG : PM_WU;
-        r = T.n0 + (i < nn ? i : i - nn);
-    });
     const float* gn = P.norms + ((uint64_t)2 * T.layer + 1) * P.H;
     const double* sq = P.ssq + (uint64_t)kPfChunk * (P.H / pf_nt_x(P.H));
     if constexpr (FMT == AMK_INT8_PC || FMT == AMK_INT4_G128) {
@@ -1180,6 +1216,7 @@ DEV void prefill_body(const PfParams& Pin) {
         __builtin_memcpy(&T, wd, sizeof(PfTask));
         uint64_t* tr = P.trace ? P.trace + (uint64_t)t * kPfTraceSlots : nullptr;
         if (tr && threadIdx.x == 0) tr[0] = rt();
+        stage_task_rows<FMT>(c, T);
         task_wait(c, T);
         if (tr && threadIdx.x == 0) tr[1] = rt();
         switch (T.op) {
