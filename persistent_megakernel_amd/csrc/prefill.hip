@@ -1131,38 +1131,58 @@ DEV void op_lm(const Ctx& c, const PfTask& T) {
     float best = -INFINITY;
     int bi = 0x7fffffff;
     bool nan = false;
-    for (uint32_t v = T.n0 + (uint32_t)w; v < T.n0 + T.nn; v += kPfWaves) {
-        const RowAddr a = row_addr(P, PM_LM, 0, v);
-        const uint8_t* row = P.wstream + a.codes;
-        float acc = 0.f;
-        for (uint32_t sgi = (uint32_t)lane; sgi < nseg; sgi += 64) {
-            const u32x4 u = __builtin_nontemporal_load((const u32x4*)(row + 16ull * sgi));
-            const uint32_t k0 = sgi * CPS;
-            float part = 0.f;
-            if (FMT == AMK_F32) {
+    // kLmRows rows per wave at a time, so that their loads are in flight together
+    constexpr uint32_t kLmRows = 4;
+    const uint32_t vend = T.n0 + T.nn;
+    for (uint32_t v0 = T.n0 + (uint32_t)w * kLmRows; v0 < vend; v0 += kPfWaves * kLmRows) {
+        const uint8_t* row[kLmRows];
+        uint64_t sc_off[kLmRows];
+        float acc[kLmRows];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) part += __uint_as_float(u[j]) * hf[k0 + j];
-            } else if (FMT == AMK_BF16) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    part += bf2f(u[j] & 0xffffu) * hf[k0 + 2 * j];
-                    part += bf2f(u[j] >> 16) * hf[k0 + 2 * j + 1];
-                }
-            } else if (FMT == AMK_INT8_PC) {
-#pragma unroll
-                for (int j = 0; j < 16; ++j) part += (float)(int8_t)(u[j / 4] >> (8 * (j % 4))) * hf[k0 + j];
-            } else {
-#pragma unroll
-                for (int j = 0; j < 32; ++j) part += (float)((int)((u[j / 8] >> (4 * (j % 8))) & 15u) - 8) * hf[k0 + j];
-                part *= h2f(*(const uint16_t*)(P.wstream + a.scales + 2ull * (k0 / 128)));
-            }
-            acc += part;
+        for (uint32_t r = 0; r < kLmRows; ++r) {
+            const RowAddr a = row_addr(P, PM_LM, 0, min(v0 + r, vend - 1));
+            row[r] = P.wstream + a.codes;
+            sc_off[r] = a.scales;
+            acc[r] = 0.f;
         }
-        acc = wave_sum(acc);
-        if (FMT == AMK_INT8_PC) acc *= h2f(*(const uint16_t*)(P.wstream + a.scales));
-        if (lane == 0 && P.logits) P.logits[v] = acc;
-        if (acc != acc) nan = true;
-        else if (acc > best || (acc == best && (int)v < bi)) { best = acc; bi = (int)v; }
+        for (uint32_t sgi = (uint32_t)lane; sgi < nseg; sgi += 64) {
+            u32x4 u[kLmRows];
+#pragma unroll
+            for (uint32_t r = 0; r < kLmRows; ++r) u[r] = __builtin_nontemporal_load((const u32x4*)(row[r] + 16ull * sgi));
+            const uint32_t k0 = sgi * CPS;
+#pragma unroll
+            for (uint32_t r = 0; r < kLmRows; ++r) {
+                float part = 0.f;
+                if (FMT == AMK_F32) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) part += __uint_as_float(u[r][j]) * hf[k0 + j];
+                } else if (FMT == AMK_BF16) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        part += bf2f(u[r][j] & 0xffffu) * hf[k0 + 2 * j];
+                        part += bf2f(u[r][j] >> 16) * hf[k0 + 2 * j + 1];
+                    }
+                } else if (FMT == AMK_INT8_PC) {
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) part += (float)(int8_t)(u[r][j / 4] >> (8 * (j % 4))) * hf[k0 + j];
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 32; ++j) part += (float)((int)((u[r][j / 8] >> (4 * (j % 8))) & 15u) - 8) * hf[k0 + j];
+                    part *= h2f(*(const uint16_t*)(P.wstream + sc_off[r] + 2ull * (k0 / 128)));
+                }
+                acc[r] += part;
+            }
+        }
+#pragma unroll
+        for (uint32_t r = 0; r < kLmRows; ++r) {
+            const uint32_t v = v0 + r;
+            float a = wave_sum(acc[r]);
+            if (v >= vend) continue;
+            if (FMT == AMK_INT8_PC) a *= h2f(*(const uint16_t*)(P.wstream + sc_off[r]));
+            if (lane == 0 && P.logits) P.logits[v] = a;
+            if (a != a) nan = true;
+            else if (a > best || (a == best && (int)v < bi)) { best = a; bi = (int)v; }
+        }
     }
     if (lane == 0) { S.part[kPfWaves + w] = best; S.ipart[w] = nan ? -1 : bi; }
     __syncthreads();
@@ -1180,18 +1200,28 @@ DEV void op_lm(const Ctx& c, const PfTask& T) {
 }
 
 DEV void op_argmax(const Ctx& c, const PfTask& T) {
+    // one wave: each lane takes every 64th LM tile, then a shuffle reduction; the largest value
+    // wins, ties to the smallest index; a tile that saw a NaN makes the token -1
     const PfParams& P = *c.P;
-    if (threadIdx.x != 0) return;
+    if (threadIdx.x >= 64) return;
+    const int lane = (int)threadIdx.x;
     float b = -INFINITY;
     int i0 = 0x7fffffff;
-    bool bad = false;
-    for (uint32_t t = 0; t < T.mt; ++t) {
+    int bad = 0;
+    for (uint32_t t = (uint32_t)lane; t < T.mt; t += 64) {
         const float v = __uint_as_float(P.lmpart[2 * t]);
         const int i = (int)P.lmpart[2 * t + 1];
-        if (i < 0) bad = true;
+        if (i < 0) bad = 1;
         else if (v > b || (v == b && i < i0)) { b = v; i0 = i; }
     }
-    P.tok_out[0] = bad ? -1 : i0;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float vb = __shfl_xor(b, o, 64);
+        const int vi = __shfl_xor(i0, o, 64);
+        bad |= __shfl_xor(bad, o, 64);
+        if (vb > b || (vb == b && vi < i0)) { b = vb; i0 = vi; }
+    }
+    if (lane == 0) P.tok_out[0] = bad ? -1 : i0;
 }
 
 template <int FMT>
