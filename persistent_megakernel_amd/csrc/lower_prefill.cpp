@@ -47,8 +47,8 @@ amk_status lower_prefill(const amk_model_desc& d, int n_cu, int n_tokens, PfLowe
     const int ntx = pf_nt_x(H), nxt = H / ntx;          // O / down column tiles
     // gate/up j tiles: 32 j (64 weight rows) per tile; when that many tiles would take more than
     // one round of the CUs (the tasks are latency-bound, so fewer rounds win), the smallest width
-    // (a multiple of 8 that divides I) that fits one round, up to 64 j, or 128 j for int8 and int4
-    // weights (wide tiles: 256 weight rows staged 128 input columns at a time)
+    // (a multiple of 8 that divides I) that fits one round, up to 64 j, or 96 j for int8 and int4
+    // weights (wide tiles: 192 weight rows staged 128 input columns at a time)
     int nj = pf_nj(I);
     if ((int64_t)nm * (I / nj) > n_cu) {
         const bool wide = d.wfmt == AMK_INT8_PC || d.wfmt == AMK_INT4_G128;

@@ -75,9 +75,9 @@ constexpr int kPfMt = 64;
 constexpr int kPfMaxNt = 128;
 constexpr int kPfKt16 = 256;
 constexpr int kPfKt32 = 128;
-// Wide tiles (int8 and int4 weights): up to 256 weight rows, staged 128 input columns at a time,
+// Wide tiles (int8 and int4 weights): up to 192 weight rows, staged 128 input columns at a time,
 // so that a phase with more tiles than CUs can take one round instead of two (gate/up).
-constexpr int kPfWideNt = 256;
+constexpr int kPfWideNt = 192;
 constexpr int kPfWideKt = 128;
 constexpr int kPfGainOff = 101376;   // LDS byte offset of the norm gains: after either stage layout
 constexpr int kPfPad16 = 8;      // LDS row padding (elements) of 16-bit operand tiles

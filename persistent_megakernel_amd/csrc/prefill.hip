@@ -307,14 +307,18 @@ DEV void gemm_tile(const Ctx& c, const void* A, uint32_t lda, uint32_t m0, uint3
         __syncthreads();
         if (s + 1 < stages) load(s + 1);   // in flight while the matrix cores work
         const uint32_t kv = min((uint32_t)Kt, K - s * Kt);   // valid columns of this stage (multiple of 16)
+        // blocks b = w + 8j are numbered column-major (row block b % 4, column block b / 4), so all
+        // of a wave's blocks share row block w % 4: the A fragments of a 128-column chunk are read
+        // from LDS once and serve each of its column blocks (int4: each chunk is one scale group)
+        const uint32_t bmw = (uint32_t)w & 3u;
+        if (F32) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t b = (uint32_t)w + 8u * (uint32_t)j;
-            if (b >= nblk) break;
-            const uint32_t bm = b / nbn, bn = b % nbn;
-            const uint8_t* arow = Abuf + (uint64_t)((bm * 16 + q) * LD) * ES;
-            const uint8_t* brow = Bbuf + (uint64_t)((bn * 16 + q) * LD) * ES;
-            if (F32) {
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t b = (uint32_t)w + 8u * (uint32_t)j;
+                if (b >= nblk) break;
+                const uint32_t bn = b / 4;
+                const uint8_t* arow = Abuf + (uint64_t)((bmw * 16 + q) * LD) * ES;
+                const uint8_t* brow = Bbuf + (uint64_t)((bn * 16 + q) * LD) * ES;
                 for (uint32_t k0 = 0; k0 < kv; k0 += 32) {
                     part[j] = f32x4{0.f, 0.f, 0.f, 0.f};
                     for (uint32_t kk = k0; kk < k0 + 32 && kk < kv; kk += 4) {
@@ -325,31 +329,36 @@ DEV void gemm_tile(const Ctx& c, const void* A, uint32_t lda, uint32_t m0, uint3
 #pragma unroll
                     for (int i = 0; i < 4; ++i) acc[j][i] += part[j][i];
                 }
-            } else if (FMT == AMK_INT4_G128) {
-                // per 128-column group: partial sum, then scaled into the total
-                for (uint32_t g0 = 0; g0 < kv; g0 += 128) {
-                    part[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        } else {
+            const uint8_t* arow = Abuf + (uint64_t)((bmw * 16 + q) * LD) * ES;
+            for (uint32_t k0 = 0; k0 < kv; k0 += 128) {
+                bf16x8 af[4];
 #pragma unroll
-                    for (uint32_t kk = 0; kk < 128; kk += 32) {
-                        const bf16x8 av = *(const bf16x8*)(arow + (g0 + kk + kq * 8) * 2);
-                        const bf16x8 bv = *(const bf16x8*)(brow + (g0 + kk + kq * 8) * 2);
-                        part[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, part[j], 0, 0, 0);
+                for (int t = 0; t < 4; ++t)
+                    if (k0 + 32u * t < kv) af[t] = *(const bf16x8*)(arow + (k0 + 32u * t + kq * 8) * 2);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t b = (uint32_t)w + 8u * (uint32_t)j;
+                    if (b >= nblk) break;
+                    const uint32_t bn = b / 4;
+                    const uint8_t* brow = Bbuf + (uint64_t)((bn * 16 + q) * LD) * ES;
+                    f32x4 pj = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        if (k0 + 32u * t < kv) {
+                            const bf16x8 bv = *(const bf16x8*)(brow + (k0 + 32u * t + kq * 8) * 2);
+                            pj = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[t], bv, pj, 0, 0, 0);
+                        }
+                    if (FMT == AMK_INT4_G128) {
+                        const uint32_t n = bn * 16 + (uint32_t)q, grp = (s * Kt + k0) / 128;
+                        const float sc = h2f(*(const uint16_t*)(P.wstream + S.rows[n].scales + 2ull * grp));
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc[j][i] += sc * pj[i];
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc[j][i] += pj[i];
                     }
-                    const uint32_t n = bn * 16 + (uint32_t)q, grp = (s * Kt + g0) / 128;
-                    const float sc = h2f(*(const uint16_t*)(P.wstream + S.rows[n].scales + 2ull * grp));
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[j][i] += sc * part[j][i];
-                }
-            } else {
-                for (uint32_t k0 = 0; k0 < kv; k0 += 128) {
-                    part[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    for (uint32_t kk = k0; kk < k0 + 128 && kk < kv; kk += 32) {
-                        const bf16x8 av = *(const bf16x8*)(arow + (kk + kq * 8) * 2);
-                        const bf16x8 bv = *(const bf16x8*)(brow + (kk + kq * 8) * 2);
-                        part[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, part[j], 0, 0, 0);
-                    }
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[j][i] += part[j][i];
                 }
             }
         }
@@ -362,7 +371,7 @@ DEV void gemm_tile(const Ctx& c, const void* A, uint32_t lda, uint32_t m0, uint3
     for (int j = 0; j < 4; ++j) {
         const uint32_t b = (uint32_t)w + 8u * (uint32_t)j;
         if (b >= nblk) break;
-        const uint32_t bm = b / nbn, bn = b % nbn, n = bn * 16 + (uint32_t)q;
+        const uint32_t bm = b % 4, bn = b / 4, n = bn * 16 + (uint32_t)q;
         const float sc = FMT == AMK_INT8_PC ? S.scale[n] : 1.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) C[(bm * 16 + (uint32_t)kq * 4 + (uint32_t)i) * ldc + n] = acc[j][i] * sc;
@@ -371,7 +380,7 @@ DEV void gemm_tile(const Ctx& c, const void* A, uint32_t lda, uint32_t m0, uint3
 }
 
 // The same GEMM tile for gate/up tiles of more than kPfMaxNt weight rows (int8 and int4 weights):
-// 128 input columns per K stage, up to 256 rows, up to 8 blocks per wave.
+// 128 input columns per K stage, up to 192 rows, up to 6 blocks per wave.
 template <int FMT>
 DEV void gemm_tile_wide(const Ctx& c, const void* A, uint32_t lda, uint32_t m0, uint32_t mvalid, uint32_t nt, uint32_t K,
                    const float* gain = nullptr, const double* ssq = nullptr) {
@@ -511,47 +520,35 @@ DEV void gemm_tile_wide(const Ctx& c, const void* A, uint32_t lda, uint32_t m0, 
         __syncthreads();
         if (s + 1 < stages) load(s + 1);   // in flight while the matrix cores work
         const uint32_t kv = min((uint32_t)Kt, K - s * Kt);   // valid columns of this stage (multiple of 16)
+        // blocks b = w + 8j are numbered column-major (row block b % 4, column block b / 4), so all
+        // of a wave's blocks share row block w % 4: the A fragments of a 128-column chunk are read
+        // from LDS once and serve each of its column blocks (int4: each chunk is one scale group)
+        const uint32_t bmw = (uint32_t)w & 3u;
+        const uint8_t* arow = Abuf + (uint64_t)((bmw * 16 + q) * LD) * ES;
+        for (uint32_t k0 = 0; k0 < kv; k0 += 128) {
+            bf16x8 af[4];
 #pragma unroll
-        for (int j = 0; j < JB; ++j) {
-            const uint32_t b = (uint32_t)w + 8u * (uint32_t)j;
-            if (b >= nblk) break;
-            const uint32_t bm = b / nbn, bn = b % nbn;
-            const uint8_t* arow = Abuf + (uint64_t)((bm * 16 + q) * LD) * ES;
-            const uint8_t* brow = Bbuf + (uint64_t)((bn * 16 + q) * LD) * ES;
-            if (F32) {
-                for (uint32_t k0 = 0; k0 < kv; k0 += 32) {
-                    f32x4 part = f32x4{0.f, 0.f, 0.f, 0.f};
-                    for (uint32_t kk = k0; kk < k0 + 32 && kk < kv; kk += 4) {
-                        const float av = *(const float*)(arow + (kk + kq) * 4);
-                        const float bv = *(const float*)(brow + (kk + kq) * 4);
-                        part = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, part, 0, 0, 0);
+            for (int t = 0; t < 4; ++t)
+                if (k0 + 32u * t < kv) af[t] = *(const bf16x8*)(arow + (k0 + 32u * t + kq * 8) * 2);
+#pragma unroll
+            for (int j = 0; j < JB; ++j) {
+                const uint32_t b = (uint32_t)w + 8u * (uint32_t)j;
+                if (b >= nblk) break;
+                const uint32_t bn = b / 4;
+                const uint8_t* brow = Bbuf + (uint64_t)((bn * 16 + q) * LD) * ES;
+                f32x4 part = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    if (k0 + 32u * t < kv) {
+                        const bf16x8 bv = *(const bf16x8*)(brow + (k0 + 32u * t + kq * 8) * 2);
+                        part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[t], bv, part, 0, 0, 0);
                     }
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[j][i] += part[i];
-                }
-            } else if (FMT == AMK_INT4_G128) {
-                // per 128-column group: partial sum, then scaled into the total
-                for (uint32_t g0 = 0; g0 < kv; g0 += 128) {
-                    f32x4 part = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (uint32_t kk = 0; kk < 128; kk += 32) {
-                        const bf16x8 av = *(const bf16x8*)(arow + (g0 + kk + kq * 8) * 2);
-                        const bf16x8 bv = *(const bf16x8*)(brow + (g0 + kk + kq * 8) * 2);
-                        part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, part, 0, 0, 0);
-                    }
-                    const uint32_t n = bn * 16 + (uint32_t)q, grp = (s * Kt + g0) / 128;
+                if (FMT == AMK_INT4_G128) {
+                    const uint32_t n = bn * 16 + (uint32_t)q, grp = (s * Kt + k0) / 128;
                     const float sc = h2f(*(const uint16_t*)(P.wstream + S.rows[n].scales + 2ull * grp));
 #pragma unroll
                     for (int i = 0; i < 4; ++i) acc[j][i] += sc * part[i];
-                }
-            } else {
-                for (uint32_t k0 = 0; k0 < kv; k0 += 128) {
-                    f32x4 part = f32x4{0.f, 0.f, 0.f, 0.f};
-                    for (uint32_t kk = k0; kk < k0 + 128 && kk < kv; kk += 32) {
-                        const bf16x8 av = *(const bf16x8*)(arow + (kk + kq * 8) * 2);
-                        const bf16x8 bv = *(const bf16x8*)(brow + (kk + kq * 8) * 2);
-                        part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, part, 0, 0, 0);
-                    }
+                } else {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) acc[j][i] += part[i];
                 }
@@ -566,7 +563,7 @@ DEV void gemm_tile_wide(const Ctx& c, const void* A, uint32_t lda, uint32_t m0, 
     for (int j = 0; j < JB; ++j) {
         const uint32_t b = (uint32_t)w + 8u * (uint32_t)j;
         if (b >= nblk) break;
-        const uint32_t bm = b / nbn, bn = b % nbn, n = bn * 16 + (uint32_t)q;
+        const uint32_t bm = b % 4, bn = b / 4, n = bn * 16 + (uint32_t)q;
         const float sc = FMT == AMK_INT8_PC ? S.scale[n] : 1.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) C[(bm * 16 + (uint32_t)kq * 4 + (uint32_t)i) * ldc + n] = acc[j][i] * sc;
