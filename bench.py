@@ -43,7 +43,7 @@ WORKLOADS = {
 # current kernel
 TRAFFIC_BYTES_PER_LAUNCH = 1094293439
 # the same for the prefill kernel on a 256-token prompt of the default workload
-PREFILL_TRAFFIC_BYTES_PER_LAUNCH = 2944159968
+PREFILL_TRAFFIC_BYTES_PER_LAUNCH = 2993278682
 
 
 def weight_bytes(shape) -> int:
