@@ -847,17 +847,25 @@ DEV void op_embed(const Ctx& c, const PfTask& T) {
         const uint8_t* src = (const uint8_t*)P.embed + (uint64_t)tok * rowb;
         uint8_t* dst = (uint8_t*)P.x + (uint64_t)m * rowb;
         double ss = 0.0;
-        for (uint32_t sg = (uint32_t)lane; sg < H / EPS; sg += 64) {
-            const u32x4 v = *(const u32x4*)(src + 16ull * sg);
-            *(u32x4*)(dst + 16ull * sg) = v;
+        // four 16-byte segments per lane at a time: their loads are issued before any store
+        for (uint32_t s0 = (uint32_t)lane; s0 < H / EPS; s0 += 4 * 64) {
+            u32x4 v[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (F32) {
-                    const double a = __uint_as_float(v[j]);
-                    ss += a * a;
-                } else {
-                    const double a = bf2f(v[j] & 0xffffu), b = bf2f(v[j] >> 16);
-                    ss += a * a + b * b;
+            for (uint32_t u = 0; u < 4; ++u)
+                if (s0 + 64 * u < H / EPS) v[u] = *(const u32x4*)(src + 16ull * (s0 + 64 * u));
+#pragma unroll
+            for (uint32_t u = 0; u < 4; ++u) {
+                if (s0 + 64 * u >= H / EPS) continue;
+                *(u32x4*)(dst + 16ull * (s0 + 64 * u)) = v[u];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (F32) {
+                        const double a = __uint_as_float(v[u][j]);
+                        ss += a * a;
+                    } else {
+                        const double a = bf2f(v[u][j] & 0xffffu), b = bf2f(v[u][j] >> 16);
+                        ss += a * a + b * b;
+                    }
                 }
             }
         }
