@@ -166,7 +166,8 @@ constexpr int codes_per_seg() {
 
 // C[mt x nt] = A[mt x K] * B[nt x K]^T for one tile. A: activation rows (row-major, lda
 // elements per row, rows >= mvalid read as zero). B: the rows in S.rows (nt of them). With
-// `gain` non-null the A rows are x rows and the GEMM's input is their RMSNorm: each row's scale
+// `gain` non-null the A rows are x rows and the GEMM's input is their RMSNorm (the gains, `gain`
+// [K], are already in LDS at kPfGainOff: the task staged them before its wait): each row's scale
 // r = 1 / sqrt(sum of its squares / K + eps) comes from the row's per-tile sums of squares in
 // `ssq` ([row][nxt] doubles, summed in tile order, in double), and each element is staged as
 // round_act((x * r) * gain[k]). On return the tile (int8 scales applied) is in LDS as fp32
@@ -193,9 +194,9 @@ DEV void gemm_tile(const Ctx& c, const void* A, uint32_t lda, uint32_t m0, uint3
     const uint32_t nbn = nt / 16, nblk = 4 * nbn;   // 16x16 blocks (4 row blocks: rows past mvalid are zeros)
     const uint32_t stages = (K + Kt - 1) / Kt;
     const uint32_t segs_b = nt * SPR;
-    float* G = (float*)(c.lds + kPfMt * LD * ES + kPfMaxNt * LD * ES);   // the norm gains [K]
+    static_assert(kPfMt * LD * ES + kPfMaxNt * LD * ES == kPfGainOff, "gains after the stages");
+    float* G = (float*)(c.lds + kPfGainOff);   // the norm gains [K], staged before the task's wait
     if (gain) {
-        for (uint32_t k = (uint32_t)tid; k < K; k += kPfThreads) G[k] = gain[k];
         {   // eight threads per row: each sums the tiles t = j (mod 8), then a fixed xor tree
             const uint32_t row = (uint32_t)tid >> 3, j = (uint32_t)tid & 7u;
             const uint32_t nxt = (uint32_t)(P.H / pf_nt_x(P.H));
@@ -406,9 +407,8 @@ DEV void gemm_tile_wide(const Ctx& c, const void* A, uint32_t lda, uint32_t m0, 
     const uint32_t nbn = nt / 16, nblk = 4 * nbn;   // 16x16 blocks (4 row blocks: rows past mvalid are zeros)
     const uint32_t stages = (K + Kt - 1) / Kt;
     const uint32_t segs_b = nt * SPR;
-    float* G = (float*)(c.lds + kPfGainOff);   // the norm gains [K]
+    float* G = (float*)(c.lds + kPfGainOff);   // the norm gains [K], staged before the task's wait
     if (gain) {
-        for (uint32_t k = (uint32_t)tid; k < K; k += kPfThreads) G[k] = gain[k];
         {   // eight threads per row: each sums the tiles t = j (mod 8), then a fixed xor tree
             const uint32_t row = (uint32_t)tid >> 3, j = (uint32_t)tid & 7u;
             const uint32_t nxt = (uint32_t)(P.H / pf_nt_x(P.H));
@@ -595,13 +595,21 @@ DEV uint64_t kv_index(const PfParams& P, int layer, int isv, int g, uint32_t pos
     return ((((uint64_t)layer * 2 + isv) * P.nKV + g) * P.max_ctx + pos) * P.hd;
 }
 
+// The H norm gains of a fused-norm GEMM to LDS (at kPfGainOff, where the GEMM tile reads them;
+// the barrier that ends the row staging publishes them).
+DEV void stage_gains(const Ctx& c, const float* gain) {
+    float* G = (float*)(c.lds + kPfGainOff);
+    for (uint32_t k = threadIdx.x; k < (uint32_t)c.P->H; k += kPfThreads) G[k] = gain[k];
+}
+
 // First input column of K split s of `splits` (whole stages of Kt columns); s = splits gives K.
 DEV uint32_t ksplit_col(uint32_t K, uint32_t Kt, uint32_t s, uint32_t splits) {
     return min(K, s * ((K + Kt - 1) / Kt) / splits * Kt);
 }
 
-// The weight rows of a GEMM task into LDS (their addresses, and int8 row scales). They do not
-// depend on the task's inputs, so this runs before the task's wait and its loads overlap it.
+// The weight rows of a GEMM task into LDS (their addresses, and int8 row scales), and for the
+// GEMMs with a fused norm its gains. They do not depend on the task's inputs, so this runs
+// before the task's wait and its loads overlap it.
 // QKV: the fused head's hd rows; O, down and their K splits: rows [n0, n0 + nn), offset to the
 // split's first column; gate/up: nn gate rows, then the nn up rows.
 template <int FMT>
@@ -613,6 +621,7 @@ DEV void stage_task_rows(const Ctx& c, const PfTask& T) {
         const uint32_t j = T.n0, hd = (uint32_t)P.hd, nH = (uint32_t)P.nH, nKV = (uint32_t)P.nKV;
         const uint32_t mat = j < nH ? PM_WQ : j < nH + nKV ? PM_WK : PM_WV;
         const uint32_t head = j < nH ? j : j < nH + nKV ? j - nH : j - nH - nKV;
+        stage_gains(c, P.norms + (uint64_t)2 * T.layer * P.H);
         stage_rows<FMT>(c, hd, T.layer, [&](uint32_t i, uint32_t& m, uint32_t& r) { m = mat; r = head * hd + i; });
         break;
     }
@@ -635,6 +644,7 @@ DEV void stage_task_rows(const Ctx& c, const PfTask& T) {
     }
     case PF_GATEUP: {
         const uint32_t nn = T.nn;
+        stage_gains(c, P.norms + ((uint64_t)2 * T.layer + 1) * P.H);
         stage_rows<FMT>(c, 2 * nn, T.layer, [&](uint32_t i, uint32_t& m, uint32_t& r) {
             m = i < nn ? PM_WG : PM_WU;
             r = T.n0 + (i < nn ? i : i - nn);
