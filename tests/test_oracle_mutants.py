@@ -28,6 +28,17 @@ MUTANTS = {
     "quant truncation": ("float n = nearbyintf(t);", "float n = truncf(t);"),
     "residual dropped": ("gemv(c, &c->wo[l], c->o, c->acc);\n        for (int i = 0; i < H; ++i) c->x[i] = orc_round(c->x[i] + c->acc[i], act);",
                          "gemv(c, &c->wo[l], c->o, c->acc);\n        for (int i = 0; i < H; ++i) c->x[i] = orc_round(c->acc[i], act);"),
+    "gate and up swapped": ("c->a[j] = orc_swiglu(c->g[j], c->u[j], act);", "c->a[j] = orc_swiglu(c->u[j], c->g[j], act);"),
+    "mlp norm uses attention gains": ("load_gains(c, c->mlp_norm[l], H, gain);", "load_gains(c, c->attn_norm[l], H, gain);"),
+    "mlp norm dropped": ("load_gains(c, c->mlp_norm[l], H, gain);\n        orc_rmsnorm(c->x, gain, H, d->rms_eps, act, c->h);",
+                         "load_gains(c, c->mlp_norm[l], H, gain);\n        for (int i = 0; i < H; ++i) c->h[i] = c->x[i];"),
+    "down residual dropped": ("gemv(c, &c->wd[l], c->a, c->acc);\n        for (int i = 0; i < H; ++i) c->x[i] = orc_round(c->x[i] + c->acc[i], act);",
+                              "gemv(c, &c->wd[l], c->a, c->acc);\n        for (int i = 0; i < H; ++i) c->x[i] = orc_round(c->acc[i], act);"),
+    "down reads the gate": ("gemv(c, &c->wd[l], c->a, c->acc);", "gemv(c, &c->wd[l], c->g, c->acc);"),
+    "attention norm uses mlp gains": ("load_gains(c, c->attn_norm[l], H, gain);", "load_gains(c, c->mlp_norm[l], H, gain);"),
+    "final norm dropped": ("load_gains(c, c->final_norm, H, gain);\n    orc_rmsnorm(c->x, gain, H, d->rms_eps, act, c->h);",
+                           "load_gains(c, c->final_norm, H, gain);\n    for (int i = 0; i < H; ++i) c->h[i] = c->x[i];"),
+    "value head for key": ("c->v[i] = orc_round(c->v[i], act);", "c->v[i] = orc_round(c->k[i], act);"),
     "swiglu sign": ("return orc_round(g / (1.0 + exp(-g)) * u, act_fmt);", "return orc_round(g / (1.0 + exp(g)) * u, act_fmt);"),
     "argmax last tie": ("if (best < 0 || v[i] > bv)", "if (best < 0 || v[i] >= bv)"),
     "ties away from zero": ("double r = nearbyint(scaled);", "double r = round(scaled);"),

@@ -311,6 +311,49 @@ def test_one_layer_closed_form_wiring():
     np.testing.assert_allclose(lg, final_logits(x1 + (h0 + h1) / 2), rtol=1e-6, atol=1e-7)
 
 
+def test_one_layer_mlp_closed_form_wiring():
+    """The MLP block alone, with every operand distinguishable: W_o = 0 (attention adds
+    nothing), attention-norm gains of 3 and MLP-norm gains g_m in {0.5, ..., 1.5}, so
+    RMSNorm(x) of the +-c embedding pattern is exactly +-g_m; W_g and W_u pick different
+    elements with different coefficients (G_j = alpha_j h[j mod H], U_j = beta_j h[(j+7) mod H]);
+    W_d sums a over j = i (mod H) times gamma. The expected logits come from numpy matmuls and
+    scipy's logistic: silu(G) = G * expit(G), a = fp32(silu(G) U), x' = fp32(x + W_d a).
+    Catches: the SiLU applied to the up projection, the MLP norm taking the attention gains or
+    being dropped, the down residual dropped, the SwiGLU product's operands crossed."""
+    shape = _wiring_shape()
+    H, Imid = shape.hidden, shape.intermediate
+    w = I.make_weights(shape)
+    L = w.layers[0]
+    L["wq"][:] = 0; L["wk"][:] = 0; L["wo"][:] = 0
+    L["attn_norm"][:] = 3.0
+    gm = (1.0 + 0.25 * (np.arange(H) % 5 - 2)).astype(np.float32)
+    L["mlp_norm"][:] = gm
+    j = np.arange(Imid)
+    alpha = (0.5 + 0.25 * (j % 7)).astype(np.float32)
+    beta = (-1.0 + 0.5 * (j % 5)).astype(np.float32)
+    beta[beta == 0] = 0.75                                        # every U_j non-zero
+    wg = np.zeros((Imid, H), np.float32); wg[j, j % H] = alpha
+    wu = np.zeros((Imid, H), np.float32); wu[j, (j + 7) % H] = beta
+    gamma = np.float32(0.375)
+    wd = np.zeros((H, Imid), np.float32); wd[j % H, j] = gamma
+    L["wg"][:] = wg; L["wu"][:] = wu; L["wd"][:] = wd
+    emb = np.stack([_ones_pattern(H, t) * (1 + t % 3) for t in range(shape.vocab)]).astype(np.float32)
+    w.embed = emb
+    m = _model(shape, w)
+    gf = w.final_norm.astype(np.float64)
+    for pos, t in enumerate((5, 11)):                             # c = 3 and c = 3: norm != identity
+        x = emb[t].astype(np.float64)
+        h = _ones_pattern(H, t) * gm.astype(np.float64)           # RMSNorm(+-c) * g_m, exact
+        G = wg.astype(np.float64) @ h
+        U = wu.astype(np.float64) @ h
+        a = (G * scipy.special.expit(G) * U).astype(np.float32).astype(np.float64)
+        x1 = (x + wd.astype(np.float64) @ a).astype(np.float32).astype(np.float64)
+        hn = ((x1 / np.sqrt(np.mean(x1 * x1))) * gf).astype(np.float32).astype(np.float64)
+        want = w.lm_head.astype(np.float64) @ hn
+        lg, _, _ = m.step(t, pos)
+        np.testing.assert_allclose(lg, want, rtol=1e-6, atol=1e-7)
+
+
 def test_one_layer_cache_rows_hold_each_steps_keys_and_values():
     """With W_k = W_v = I the cache row written at position p holds RoPE_p(h_p) and h_p."""
     shape = _wiring_shape()
