@@ -117,8 +117,9 @@ def _workers() -> int:
     return max(1, min(16, os.cpu_count() or 1))
 
 
-def _normal_f32(shape, std, mean, key) -> np.ndarray:
-    """N(mean, std^2) in fp32, drawn in 16M-element chunks with per-chunk seeds."""
+def _normal_f32(shape, std, mean, key, threads: bool = True) -> np.ndarray:
+    """N(mean, std^2) in fp32, drawn in 16M-element chunks with per-chunk seeds (on a thread
+    pool when `threads`; the values do not depend on it)."""
     n = int(np.prod(shape))
     out = np.empty(n, dtype=np.float32)
     chunks = [(c, min(_CHUNK, n - c * _CHUNK)) for c in range((n + _CHUNK - 1) // _CHUNK)]
@@ -132,8 +133,9 @@ def _normal_f32(shape, std, mean, key) -> np.ndarray:
         if mean:
             seg += np.float32(mean)
 
-    if len(chunks) == 1:
-        fill(chunks[0])
+    if len(chunks) == 1 or not threads:
+        for cl in chunks:
+            fill(cl)
     else:
         with ThreadPoolExecutor(_workers()) as ex:
             list(ex.map(fill, chunks))
@@ -159,15 +161,16 @@ def _master(shape: ModelShape, a32: np.ndarray) -> np.ndarray:
     return f32_to_bf16_bits(a32)
 
 
-def make_tensor(shape: ModelShape, name: str, layer: int = 0, seed: int | None = None) -> np.ndarray:
+def make_tensor(shape: ModelShape, name: str, layer: int = 0, seed: int | None = None,
+                threads: bool = True) -> np.ndarray:
     seed = shape.seed if seed is None else seed
     shp = shape.tensor_shape(name)
     if name in ("attn_norm", "mlp_norm", "final_norm"):
         tid = _TID.get(name, T_FINAL_NORM)
-        a = _normal_f32(shp, 0.02, 1.0, (seed, layer, tid))
+        a = _normal_f32(shp, 0.02, 1.0, (seed, layer, tid), threads)
     else:
         tid = {"embed": T_EMBED, "lm_head": T_LM_HEAD, **_TID}[name]
-        a = _normal_f32(shp, 0.02, 0.0, (seed, layer, tid))
+        a = _normal_f32(shp, 0.02, 0.0, (seed, layer, tid), threads)
     return _master(shape, a)
 
 
@@ -188,13 +191,18 @@ class Weights:
 
 
 def make_weights(shape: ModelShape, seed: int | None = None) -> Weights:
+    """Every tensor of the model, drawn on a thread pool (one tensor per job; each tensor's
+    draw depends only on its own seed key, so the result is the same for any pool size)."""
     seed = shape.seed if seed is None else seed
-    layers = [{n: make_tensor(shape, n, l, seed) for n in LAYER_TENSORS} for l in range(shape.n_layers)]
+    jobs = [(n, l) for l in range(shape.n_layers) for n in LAYER_TENSORS]
+    jobs += [("embed", 0), ("final_norm", 0)] + ([] if shape.tied else [("lm_head", 0)])
+    with ThreadPoolExecutor(_workers()) as ex:
+        out = dict(zip(jobs, ex.map(lambda j: make_tensor(shape, j[0], j[1], seed, threads=False), jobs)))
     return Weights(
-        embed=make_tensor(shape, "embed", 0, seed),
-        final_norm=make_tensor(shape, "final_norm", 0, seed),
-        lm_head=None if shape.tied else make_tensor(shape, "lm_head", 0, seed),
-        layers=layers,
+        embed=out[("embed", 0)],
+        final_norm=out[("final_norm", 0)],
+        lm_head=None if shape.tied else out[("lm_head", 0)],
+        layers=[{n: out[(n, l)] for n in LAYER_TENSORS} for l in range(shape.n_layers)],
     )
 
 

@@ -184,7 +184,8 @@ DEV void gemm_tile(const Ctx& c, const void* A, uint32_t lda, uint32_t m0, uint3
     constexpr int SEGS_A = kPfMt * Kt / EPS_A / kPfThreads;   // per thread (4)
     constexpr int CPS = codes_per_seg<FMT>();
     constexpr int SPR = Kt / CPS;                   // weight segments per row per stage
-    constexpr int SEGS_B = kPfMaxNt * SPR / kPfThreads;       // per thread, at most
+    constexpr int SEGS_B = (kPfMaxNt * SPR + kPfThreads - 1) / kPfThreads;   // per thread, at most
+    static_assert(SEGS_B * kPfThreads >= kPfMaxNt * SPR, "B staging covers every row");
     static_assert(SEGS_A * kPfThreads * EPS_A == kPfMt * Kt, "A staging");
     const PfParams& P = *c.P;
     Shared& S = *c.S;
@@ -396,7 +397,8 @@ DEV void gemm_tile_wide(const Ctx& c, const void* A, uint32_t lda, uint32_t m0, 
     constexpr int SEGS_A = kPfMt * Kt / EPS_A / kPfThreads;   // per thread (4)
     constexpr int CPS = codes_per_seg<FMT>();
     constexpr int SPR = Kt / CPS;                   // weight segments per row per stage
-    constexpr int SEGS_B = kPfWideNt * SPR / kPfThreads;      // per thread, at most
+    constexpr int SEGS_B = (kPfWideNt * SPR + kPfThreads - 1) / kPfThreads;   // per thread, at most
+    static_assert(SEGS_B * kPfThreads >= kPfWideNt * SPR, "B staging covers every row");
     static_assert(kPfMt * LD * ES + kPfWideNt * LD * ES <= kPfGainOff, "stage layout below the gains");
     static_assert(SEGS_A * kPfThreads * EPS_A == kPfMt * Kt, "A staging");
     const PfParams& P = *c.P;

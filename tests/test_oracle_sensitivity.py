@@ -36,3 +36,31 @@ def test_one_ulp_flip_moves_full_depth_logits():
     assert delta > 2e-2
     assert 3 * delta < FULL_DEPTH_ABS
 
+
+
+TWO_LAYER_ABS = 0.075   # same value as the prefill tests' two-layer bar: three one-ulp flips
+
+
+@pytest.mark.slow
+def test_one_ulp_flip_moves_two_layer_logits():
+    """The same effect two layers deep (the TinyLlama-shaped width, int8): one one-ulp change of
+    one input element moves the logits by more than 1e-2 and at most a third of the two-layer
+    bar, so 2e-2 is within a single rounding flip there, and three flips fit the bar."""
+    shape = I.SHAPES["tinyllama_int8"].replace(n_layers=2, max_ctx=16)
+    w = I.make_weights(shape)
+    tok = 1234
+    a = oracle.OracleModel(shape, w)
+    _, base, _ = a.step(tok, 0)
+    a.close()
+    deltas = []
+    for k in (5, 77, 1000, 2047):
+        emb = w.embed.copy()
+        emb[tok, k] = np.uint16(int(emb[tok, k]) + 1)
+        w2 = I.Weights(embed=emb, final_norm=w.final_norm, lm_head=w.lm_head, layers=w.layers)
+        b = oracle.OracleModel(shape, w2)
+        _, pert, _ = b.step(tok, 0)
+        b.close()
+        deltas.append(float(np.max(np.abs(pert.astype(np.float64) - base))))
+    print(f"two layers, one-ulp input flips: max abs logit changes {deltas}")
+    assert min(deltas) > 1e-2
+    assert 3 * max(deltas) <= TWO_LAYER_ABS
