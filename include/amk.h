@@ -277,6 +277,22 @@ amk_status amk_create(const amk_model_desc* desc, const amk_weights* weights, vo
 amk_status amk_decode_step(amk_ctx* ctx, const int32_t* token_in, int32_t pos, int32_t* token_out,
                            float* logits, void* stream);
 
+/* The decode step of amk_decode_step, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation): this call
+ * allocates nothing. The step's scratch memory (its flag-carrying activation words: every
+ * value one task publishes for another) lives in one static device array per GPU of
+ * AMK_STATIC_SCRATCH_BYTES (64 MiB), set up by the first amk_create on that GPU and held until
+ * the process ends. Every context on the GPU shares the array, and it keeps the last call's
+ * contents: each call writes its words with a flag value no earlier call on that GPU used, so
+ * nothing needs clearing between calls. Calls that overlap on one GPU (on two streams or from
+ * two host threads) race on the array and give unspecified results: serialise them.
+ * Arguments, effects and errors are those of amk_decode_step; in addition, a context whose step
+ * needs more flag-carrying words than the array holds is refused with AMK_E_INVALID_ARG
+ * (nothing launched; AMK_LOG=1 names the sizes). */
+#define AMK_STATIC_SCRATCH_BYTES (64ull << 20)
+amk_status amk_decode_step_static(amk_ctx* ctx, const int32_t* token_in, int32_t pos, int32_t* token_out,
+                                  float* logits, void* stream);
+
 /* Prompt prefill: run `n_tokens` prompt tokens through the model in cooperative launches of up
  * to 256 tokens each, instead of one decode launch per token (pages: page 3, "How it works",
  * layer 1, GEMM tiles among the instruction kinds). The result is the one of n_tokens chained

@@ -20,7 +20,7 @@ from . import _abi as A
 from ._abi import (AMK_BF16, AMK_F32, AMK_INT4_G128, AMK_INT8_PC, AmkError, STATUS_BAD_TOKEN,  # noqa: F401
                    STATUS_TIMEOUT, check, lib)
 
-__all__ = ["amk_validate", "amk_lower", "amk_create", "amk_decode_step", "amk_destroy",
+__all__ = ["amk_validate", "amk_lower", "amk_create", "amk_decode_step", "amk_decode_step_static", "amk_destroy",
            "amk_quantize", "amk_device_status", "amk_ctx_schedule", "amk_set_trace", "amk_version", "Decoder",
            "model_desc", "schedule_config", "AmkError", "amk_vm_run",
            "amk_prefill", "amk_lower_prefill", "amk_set_prefill_trace"]
@@ -202,6 +202,14 @@ def amk_decode_step(ctx: int, token_in_ptr: int, pos: int, token_out_ptr: int, l
     """Enqueue one decode launch; returns the amk_status (does not raise, for hot loops)."""
     return lib().amk_decode_step(C.c_void_p(ctx), C.c_void_p(token_in_ptr), int(pos), C.c_void_p(token_out_ptr),
                                  C.c_void_p(logits_ptr or None), C.c_void_p(stream))
+
+
+def amk_decode_step_static(ctx: int, token_in_ptr: int, pos: int, token_out_ptr: int, logits_ptr: int = 0,
+                           stream: int = 0) -> int:
+    """amk_decode_step with the step's flag-carrying words in the library's static per-device
+    array (allocates nothing); returns the amk_status."""
+    return lib().amk_decode_step_static(C.c_void_p(ctx), C.c_void_p(token_in_ptr), int(pos), C.c_void_p(token_out_ptr),
+                                        C.c_void_p(logits_ptr or None), C.c_void_p(stream))
 
 
 def amk_prefill(ctx: int, tokens_ptr: int, pos0: int, n_tokens: int, token_out_ptr: int, logits_ptr: int = 0,

@@ -113,6 +113,7 @@ SIGNATURES = {
                              C.POINTER(amk_schedule), C.POINTER(amk_schedule_config), _P,
                              C.POINTER(amk_verdict), C.POINTER(_P)]),
     "amk_decode_step": (C.c_int, [_P, _P, C.c_int32, _P, _P, _P]),
+    "amk_decode_step_static": (C.c_int, [_P, _P, C.c_int32, _P, _P, _P]),
     "amk_device_status": (C.c_uint32, [_P]),
     "amk_ctx_schedule": (C.POINTER(amk_schedule), [_P]),
     "amk_set_trace": (C.c_int, [_P, _P, C.c_uint64]),

@@ -36,6 +36,7 @@ struct amk_ctx {
     uint32_t* d_status = nullptr;   // device alias of h_status
     uint32_t* d_abort = nullptr;
     uint32_t epoch = 0;
+    uint64_t ll_words = 0;          // flag-carrying words one step uses
     hipStream_t last = nullptr;
     uint64_t* trace = nullptr;      // caller-owned, optional
     KParams base;
@@ -195,7 +196,10 @@ extern "C" amk_status amk_create(const amk_model_desc* desc, const amk_weights* 
     ck(upload(&c->d_tasks, c->L.dtasks, stream));
     ck(upload(&c->d_qoff, c->L.dqueue_off, stream));
     ck(upload(&c->d_cuoff, c->L.cu_stream_off, stream));
+    c->ll_words = y.total;
     ck(hipMalloc((void**)&c->d_ll, y.total * 8));
+    // the static flag-word array of amk_decode_step_static on this device (address, clear)
+    ck(scratch_setup(dev, stream));
     ck(hipMalloc(&c->d_embed, (size_t)d.vocab * d.hidden * esz));
     ck(hipMalloc((void**)&c->d_norms, (size_t)(2 * d.n_layers + 1) * d.hidden * sizeof(float)));
     ck(hipMalloc((void**)&c->d_abort, 64));
@@ -340,6 +344,35 @@ extern "C" amk_status amk_decode_step(amk_ctx* c, const int32_t* token_in, int32
     hipError_t e = launch_megakernel(P, c->n_cu, st);
     if (e != hipSuccess) { logf("decode_step", hipGetErrorString(e)); return AMK_E_HIP; }
     c->epoch++;
+    c->last = st;
+    return AMK_OK;
+}
+
+extern "C" amk_status amk_decode_step_static(amk_ctx* c, const int32_t* token_in, int32_t pos, int32_t* token_out,
+                                             float* logits, void* stream_v) {
+    if (!c || !token_in || !token_out) return AMK_E_INVALID_ARG;
+    if (pos < 0 || pos >= c->d.max_ctx) return AMK_E_INVALID_ARG;
+    if (c->ll_words > kScratchWords) {
+        logf("decode_step_static", "the step's flag-carrying words exceed the static array (" +
+                                       std::to_string(c->ll_words) + " > " + std::to_string(kScratchWords) + " words)");
+        return AMK_E_INVALID_ARG;
+    }
+    if (__atomic_load_n(&c->h_status[0], __ATOMIC_ACQUIRE) & kStatusTimeout) return AMK_E_DEVICE_TIMEOUT;
+    hipStream_t st = (hipStream_t)stream_v;
+    KParams P = c->base;
+    unsigned long long* words = nullptr;
+    uint32_t flag = 0;
+    hipError_t e = scratch_acquire(c->dev, st, &words, &flag);
+    if (e != hipSuccess) { logf("decode_step_static", hipGetErrorString(e)); return AMK_E_HIP; }
+    P.ll = words;
+    P.flag = flag;
+    P.tok_in = token_in;
+    P.tok_out = token_out;
+    P.logits = logits;
+    P.pos = pos;
+    P.trace = c->trace;
+    e = launch_megakernel(P, c->n_cu, st);
+    if (e != hipSuccess) { logf("decode_step_static", hipGetErrorString(e)); return AMK_E_HIP; }
     c->last = st;
     return AMK_OK;
 }

@@ -33,8 +33,16 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "amk_internal.h"
 #include "prep.h"
+
+// Flag-carrying words of the allocation-free decode entry point (amk_decode_step_static): one
+// array per device, shared by every context on that device, held until the process ends. In
+// host code this name is only a stand-in for the device symbol: every host-side use goes
+// through the address hipGetSymbolAddress returns for the current device (scratch_setup).
+static __device__ __align__(256) unsigned long long scratch[amk::kScratchWords];
 
 namespace amk {
 namespace {
@@ -1250,6 +1258,63 @@ const void* kernel_for(int wfmt) {
 }  // namespace amk
 
 namespace amk {
+
+namespace {
+
+// Per device: the device address of `scratch` and the epoch of the flags written into it.
+struct ScratchDev {
+    unsigned long long* ptr = nullptr;
+    uint32_t epoch = 0;        // launches so far since the last clear; the next flag is epoch + 1
+    bool ready = false;
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+ScratchDev g_scratch[kMaxDevices];
+
+__global__ void k_clear_words(unsigned long long* p, uint64_t n) {
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (uint64_t)gridDim.x * blockDim.x) p[i] = 0ull;
+}
+
+hipError_t clear_words(unsigned long long* p, uint64_t n, hipStream_t st) {
+    hipLaunchKernelGGL(k_clear_words, dim3(1024), dim3(256), 0, st, p, n);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t scratch_setup(int dev, hipStream_t st) {
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> g(g_scratch_mu);
+    ScratchDev& s = g_scratch[dev];
+    if (s.ready) return hipSuccess;
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    s.ptr = (unsigned long long*)p;
+    // flags start at 0, which no launch ever writes
+    e = clear_words(s.ptr, kScratchWords, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return e;
+    s.epoch = 0;
+    s.ready = true;
+    return hipSuccess;
+}
+
+hipError_t scratch_acquire(int dev, hipStream_t st, unsigned long long** ptr, uint32_t* flag) {
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> g(g_scratch_mu);
+    ScratchDev& s = g_scratch[dev];
+    if (!s.ready) return hipErrorNotInitialized;
+    if (s.epoch == 0xfffffffeu) {   // every flag value used: clear (a kernel on the caller's stream) and restart
+        hipError_t e = clear_words(s.ptr, kScratchWords, st);
+        if (e != hipSuccess) return e;
+        s.epoch = 0;
+    }
+    *ptr = s.ptr;
+    *flag = ++s.epoch;
+    return hipSuccess;
+}
 
 hipError_t launch_megakernel(const KParams& p, int n_cu, hipStream_t st) {
     KParams local = p;

@@ -18,6 +18,11 @@ hipError_t launch_norms(const void* src, int wfmt, uint32_t n, float* dst, hipSt
 hipError_t launch_megakernel(const KParams& p, int n_cu, hipStream_t st);
 // Workgroups of the megakernel for weight format wfmt that fit on one CU (0 = it cannot run).
 int megakernel_blocks_per_cu(int wfmt);
+// The static flag-word array of the allocation-free decode entry point, per device: set-up
+// (address lookup and clear; call once per device with that device current, allocation-free
+// afterwards), then, per launch, its device address and a fresh flag value.
+hipError_t scratch_setup(int dev, hipStream_t st);
+hipError_t scratch_acquire(int dev, hipStream_t st, unsigned long long** ptr, uint32_t* flag);
 
 // The prefill kernel: one cooperative launch of n_cu workgroups of kPfThreads.
 struct PfParams;
