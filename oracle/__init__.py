@@ -164,9 +164,10 @@ class OracleModel:
         self.shape = shape
         self.max_ctx = max_ctx or shape.max_ctx
         self.act_fmt = FMT_F32 if shape.act_f32 else FMT_BF16
+        # theta and eps as the model description carries them (fp32 values)
         d = _Desc(shape.hidden, shape.n_layers, shape.n_heads, shape.n_kv_heads, shape.head_dim,
                   shape.intermediate, shape.vocab, self.max_ctx, int(shape.tied), shape.wfmt,
-                  int(shape.act_f32), float(shape.rope_theta), float(shape.rms_eps))
+                  int(shape.act_f32), float(np.float32(shape.rope_theta)), float(np.float32(shape.rms_eps)))
         L = lib()
         self._h = L.orc_create(C.byref(d))
         if not self._h:

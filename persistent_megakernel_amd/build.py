@@ -1,7 +1,8 @@
 """Build libamk.so in-tree with hipcc for gfx950.
 
 Device sources (.hip) are compiled with packed fp32 arithmetic disabled (the hardware's
-packed fp32 forms are avoided on this target); host sources (.cpp) are plain C++17 built with g++.
+packed fp32 forms are avoided on this target) and without type-based alias analysis (the kernels
+reinterpret LDS bytes between widths); host sources (.cpp) are plain C++17 built with g++.
 """
 from __future__ import annotations
 
@@ -46,7 +47,7 @@ def build(verbose: bool = False) -> str:
     for s in HIP_SOURCES:
         obj = os.path.join(BUILD, s + ".o")
         jobs.append([hipcc, "-c", "-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-Wall",
-                     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-fno-strict-aliasing",
                      "-Wno-unused-function", "-Wno-unused-variable", *inc, "-o", obj, os.path.join(CSRC, s)])
     for s in CPP_SOURCES:   # host-only C++ (no device code): the system C++ compiler
         obj = os.path.join(BUILD, s + ".o")

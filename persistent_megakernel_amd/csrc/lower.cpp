@@ -64,10 +64,14 @@ amk_status check_desc(const amk_model_desc* d, std::string* msg) {
         return fail(AMK_E_UNSUPPORTED, "hidden and intermediate sizes must be multiples of 16 (16-byte weight segments)");
     if (d->act_f32 != (d->wfmt == AMK_F32 ? 1 : 0)) return fail(AMK_E_UNSUPPORTED, "fp32 activations go with fp32 weights only");
     const int64_t qd = (int64_t)d->n_heads * d->head_dim;
-    const int64_t kmax = d->act_f32 ? kHBytes / 4 : kHBytes / 2;
-    if (d->hidden > kMaxHidden || d->intermediate > kMaxInter || qd > kMaxHidden || d->hidden > kmax ||
-        d->intermediate > kmax || qd > kmax)
-        return fail(AMK_E_UNSUPPORTED, "dimension beyond the kernel's staging limits");
+    if (d->hidden > kMaxHidden || d->intermediate > kMaxInter || qd > kMaxHidden)
+        return fail(AMK_E_UNSUPPORTED, "dimension beyond the kernel's limits");
+    {   // every GEMV input fits the LDS stage (QKV, gate/up and the LM head carry their norm gains)
+        const uint64_t st = (uint64_t)stage_bytes(d->wfmt);
+        if (gemv_stage_need(d->wfmt, (uint32_t)d->hidden, true) > st || gemv_stage_need(d->wfmt, (uint32_t)qd, false) > st ||
+            gemv_stage_need(d->wfmt, (uint32_t)d->intermediate, false) > st)
+            return fail(AMK_E_UNSUPPORTED, "dimension beyond the kernel's LDS staging limits");
+    }
     if (d->wfmt == AMK_INT4_G128 && (d->hidden % 128 || d->intermediate % 128 || qd % 128))
         return fail(AMK_E_UNSUPPORTED, "int4 g128 needs input sizes that are multiples of 128");
     return AMK_OK;
@@ -192,7 +196,7 @@ bool derive_accesses(const Shape& s, const GenTask& t, uint64_t w_off, uint64_t 
         if (!nh || nh > (uint32_t)kMaxAttnHeads || nc != nchunks || c >= nc || h0 + nh > (uint32_t)s.nH) return false;
         const uint32_t g = (uint32_t)((uint64_t)h0 * s.nKV / s.nH);
         if ((uint64_t)(h0 + nh - 1) * s.nKV / s.nH != g) return false;   // one KV group per task
-        if ((uint64_t)kComputeWaves * nh * (s.hd + 2) > kStageFloats) return false;   // per-wave states in LDS
+        if (attn_stage_need(nh, (uint32_t)s.hd) > (uint64_t)stage_bytes(s.wfmt)) return false;   // per-wave states in LDS
         {   // dims per lane of the attention lane layout: hd / min(64 / nh rounded up to 2^k, hd) <= 8
             uint32_t nhp = 1;
             while (nhp < nh) nhp <<= 1;
@@ -213,7 +217,7 @@ bool derive_accesses(const Shape& s, const GenTask& t, uint64_t w_off, uint64_t 
     case AMK_OP_MERGE: {
         const uint32_t h0 = t.arg[0], nh = t.arg[1], nc = t.arg[3];
         if (!nh || nh > (uint32_t)kMaxAttnHeads || nc != nchunks || nc < 2 || h0 + nh > (uint32_t)s.nH) return false;
-        if ((uint64_t)nh * nc * (s.hd + 2) > kStageFloats) return false;   // chunk states staged in LDS
+        if (nh * merge_stage_need(nc, (uint32_t)s.hd) > (uint64_t)stage_bytes(s.wfmt)) return false;   // chunk states in LDS
         for (uint32_t h = h0; h < h0 + nh; ++h)
             add_acc(a, s.reg(l, L_PART), 0, (uint64_t)h * nc * (s.hd + 2), (uint64_t)(h + 1) * nc * (s.hd + 2));
         add_acc(a, s.reg(l, L_O), AMK_ACC_WRITE, (uint64_t)h0 * s.hd, (uint64_t)(h0 + nh) * s.hd);
@@ -262,7 +266,7 @@ bool derive_accesses(const Shape& s, const GenTask& t, uint64_t w_off, uint64_t 
         return true;
     }
     case AMK_OP_ARGMAX: {
-        if (t.arg[2] != lm_tiles || l != (uint32_t)s.L || 2ull * lm_tiles > kStageFloats) return false;
+        if (t.arg[2] != lm_tiles || l != (uint32_t)s.L || 8ull * lm_tiles > (uint64_t)stage_bytes(s.wfmt)) return false;
         add_acc(a, R_LMPART, 0, 0, 2ull * lm_tiles);
         add_acc(a, R_TOK_OUT, AMK_ACC_WRITE | AMK_ACC_POST, 0, 1);
         return true;
@@ -316,8 +320,6 @@ bool check_plan(const amk_model_desc& d, const Lowered& out, std::string* msg) {
             const uint32_t K = t.op == AMK_OP_OPROJ ? (uint32_t)qd : t.op == AMK_OP_DOWN ? (uint32_t)d.intermediate : (uint32_t)H;
             if (t.wofs + tile_bytes(d.wfmt, K, t.tile_rows) > len) return fail("tile outside its CU stream");
             if (t.wofs % 16) return fail("tile not 16-byte aligned in its CU stream");
-            if (tile_bytes(d.wfmt, K, t.tile_rows) - tile_scale_off(d.wfmt, K, t.tile_rows) > (uint64_t)kKvBytes)
-                return fail("tile whose scales do not fit the LDS scale buffer");
         }
     }
     return true;
@@ -473,14 +475,14 @@ amk_status lower_model(const amk_model_desc& d, const amk_schedule_config* cfg, 
             heads_per_task = h;
         }
     }
-    while (heads_per_task > 1 && (int64_t)kComputeWaves * heads_per_task * (s.hd + 2) > kStageFloats) {
+    while (heads_per_task > 1 && attn_stage_need((uint32_t)heads_per_task, (uint32_t)s.hd) > (uint64_t)stage_bytes(s.wfmt)) {
         int h = heads_per_task - 1;
         while (gsz % h) --h;
         heads_per_task = h;
     }
     const int n_head_tasks = nH / heads_per_task;
     // merges run one query head each: a head's chunk states must fit the LDS stage
-    const int nc_max = std::max(1, (int)(kStageFloats / (s.hd + 2)));
+    const int nc_max = std::max(1, (int)(stage_bytes(s.wfmt) / (8 * (s.hd + 2))));
     int nc = C.attn_chunks;
     if (nc <= 0) {
         nc = 1;

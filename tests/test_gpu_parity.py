@@ -154,6 +154,20 @@ def test_tiny_fp32_long_context_split(M):
     assert r["tf"] == r["gen"] and r["fr"] == r["gen"]
 
 
+def test_tiny_int4_odd_scale_groups(M):
+    """int4 g128 with an intermediate size of 384: three group scales per down-projection row,
+    so every other row's scales start in the middle of a dword; two layers over a prefilled
+    context, tiles of several rows per wave."""
+    shape = I.tiny_shape(hidden=256, n_layers=2, n_heads=4, n_kv_heads=2, head_dim=64, intermediate=384, vocab=300,
+                         wfmt=I.WF_INT4, act_f32=False, max_ctx=48, seed=22)
+    log("case tiny int4 K=384 down rows")
+    r = _run(M, shape, I.make_weights(shape), [7], 4, pos0=20, prefill=20)
+    log(f"tiny int4: max abs err {max(r['errs']):.3e}, min margin {min(r['margins']):.3e}")
+    assert max(r["errs"]) <= 2e-2
+    _check_ids(r["gen"], r["tf"], r["margins"], "tiny int4")
+    _check_ids(r["gen"], r["fr"], r["margins"], "tiny int4 free-running")
+
+
 # ------------------------------------------------------------------ depth-limited, full width
 
 DEPTH_CASES = [   # (workload, first position, prefilled cache rows)

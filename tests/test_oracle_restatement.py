@@ -106,13 +106,14 @@ class NumpyModel:
         self.V = np.zeros_like(self.K)
 
     def norm(self, x, g):
-        return self.rnd(x * (1.0 / np.sqrt(np.dot(x, x) / x.size + self.s.rms_eps)) * g)
+        eps = float(np.float32(self.s.rms_eps))   # the model description's fp32 value
+        return self.rnd(x * (1.0 / np.sqrt(np.dot(x, x) / x.size + eps)) * g)
 
     def rope(self, u, pos):
         """u: [heads, hd]; pair (i, i + hd/2) rotated by pos * theta^(-2i/hd)."""
         hd = self.s.head_dim
         i = np.arange(hd // 2, dtype=np.float64)
-        ang = pos * self.s.rope_theta ** (-(2.0 * i) / hd)
+        ang = pos * float(np.float32(self.s.rope_theta)) ** (-(2.0 * i) / hd)
         c, s = np.cos(ang), np.sin(ang)
         a, b = u[:, : hd // 2], u[:, hd // 2:]
         return np.concatenate([a * c - b * s, b * c + a * s], axis=1)
