@@ -197,7 +197,6 @@ extern "C" amk_status amk_create(const amk_model_desc* desc, const amk_weights* 
     hipError_t e = hipSuccess;
     auto ck = [&](hipError_t r) { if (e == hipSuccess) e = r; };
     ck(hipMalloc((void**)&c->d_wstream, wbytes ? wbytes : 256));
-    ck(upload(&c->d_tasks, c->L.dtasks, stream));
     ck(upload(&c->d_qoff, c->L.dqueue_off, stream));
     ck(upload(&c->d_cuoff, c->L.cu_stream_off, stream));
     c->ll_words = y.total;
@@ -248,6 +247,10 @@ extern "C" amk_status amk_create(const amk_model_desc* desc, const amk_weights* 
         for (size_t n = 0; n < nn; ++n)
             for (int i = 0; i < d.hidden; ++i) gmax[n] = std::max(gmax[n], std::fabs(norms[n * d.hidden + i]));
         ck(upload(&c->d_gmax, gmax, stream));
+        // each GEMV task's descriptor carries the bound of its own norm
+        for (DevTask& t : c->L.dtasks)
+            if (t.norm >= 0 && (size_t)t.norm < nn) t.gmax = gmax[(size_t)t.norm];
+        ck(upload(&c->d_tasks, c->L.dtasks, stream));
         ck(hipStreamSynchronize(stream));
     }
     // repack / quantise the weights into the per-CU streams

@@ -56,25 +56,54 @@ AMK_HD inline uint64_t gemv_stage_need(int wfmt, uint32_t K, bool norm) {
 AMK_HD inline uint64_t attn_stage_need(uint32_t nh, uint32_t hd) {
     return 8ull * ((uint64_t)nh * hd + 2ull * hd) + 8ull * kCompWaves * nh * (hd + 2) + (uint64_t)kCompWaves * 2048;
 }
-// Merge task stage: every chunk's state of one query head (fp64).
-AMK_HD inline uint64_t merge_stage_need(uint32_t nc, uint32_t hd) { return 8ull * nc * (hd + 2); }
+// Gathered flag words land in LDS in 1 KiB blocks of 128 words; one gather polls at most
+// kMaxGatherBlocks blocks.
+constexpr uint32_t kMaxGatherBlocks = 64;
+AMK_HD inline uint32_t gather_blocks(uint64_t words) { return (uint32_t)((words + 127) / 128); }
+// Attention task: the gathered q (and current k, v) words go past the attention stage.
+AMK_HD inline uint32_t attn_words_off(uint32_t nh, uint32_t hd) { return round_up_u((uint32_t)attn_stage_need(nh, hd), 1024u); }
+AMK_HD inline uint64_t attn_stage_total(uint32_t nh, uint32_t hd, uint32_t vpw) {
+    return attn_words_off(nh, hd) + 1024ull * (gather_blocks((uint64_t)nh * hd / vpw) + 2ull * gather_blocks(hd / vpw));
+}
+// Merge task: every chunk state of its heads gathered as words (two per fp64 value), then the
+// chunk weights of every head (fp64).
+AMK_HD inline uint64_t merge_state_words(uint32_t nh, uint32_t nc, uint32_t hd) { return 2ull * nh * nc * (hd + 2); }
+AMK_HD inline uint32_t merge_weights_off(uint32_t nh, uint32_t nc, uint32_t hd) {
+    return 1024u * gather_blocks(merge_state_words(nh, nc, hd));
+}
+AMK_HD inline uint64_t merge_stage_need(uint32_t nh, uint32_t nc, uint32_t hd) { return merge_weights_off(nh, nc, hd) + 8ull * nh * nc; }
+// Residual words of an O or down task (flag words as gathered, in the control area).
+constexpr uint32_t kResidWords = 512;
 
 // Limits the kernel supports (checked at create).
 constexpr int kMaxHidden = 8192;
 constexpr int kMaxInter = 16384;
+constexpr int kMaxCtx = 1 << 22;
+constexpr int kMaxChunks = 512;            // context chunks of one attention group
 // Flag-carrying words in the static per-device array of the allocation-free decode entry point
 // (64 MiB): a step whose layout needs more is refused.
 constexpr uint64_t kScratchWords = 8ull << 20;
 
-// Device task descriptor (32 bytes).
+// Device task descriptor (64 bytes): the task, and the geometry its kernels would otherwise
+// derive from the model shape on every task (set by the lowering, gmax by amk_create).
+constexpr uint32_t kNoWord = 0xffffffffu;   // src / aux: the embedding row instead of a flag-word buffer
 struct DevTask {
     uint16_t op;
     uint16_t layer;
     uint32_t arg[4];
     uint32_t tile_rows;      // rows in the weight tile (GEMV ops)
-    uint64_t wofs;           // byte offset of the tile inside this CU's weight stream
+    uint64_t wofs;           // GEMV: byte offset of the tile inside this CU's weight stream;
+                             // attention: byte offset in the cache of (layer, K rows, KV group, row 0)
+    uint32_t k;              // GEMV: input width K; attention and merge: cache row bytes
+    uint32_t pitch;          // GEMV: bytes per weight row; attention: cache rows per 1 KiB load
+    uint32_t nj;             // GEMV: 1 KiB loads per weight row; attention: bytes from the K rows to the V rows
+    int32_t norm;            // GEMV: index of the RMSNorm on its input (-1: none)
+    float gmax;              // GEMV: the largest |gain| of that norm
+    uint32_t src;            // flag-word offset of the task's input (kNoWord: the embedding row)
+    uint32_t dst;            // flag-word offset of the task's output
+    uint32_t aux;            // flag-word offset of the residual (O, down; kNoWord: the embedding row)
 };
-static_assert(sizeof(DevTask) == 32, "DevTask layout");
+static_assert(sizeof(DevTask) == 64, "DevTask layout");
 
 // Weight tile geometry for a GEMV with K inputs in format wfmt. A tile is its rows' codes, row
 // after row (row_pitch bytes each, a multiple of 16), then the scale block: int8 one fp16 scale

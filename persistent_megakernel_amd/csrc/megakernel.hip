@@ -70,9 +70,8 @@ constexpr int kWaitLgkm0 = 0xc07f;   // LDS / scalar loads done; vector memory u
 // ------------------------------------------------------------------ LDS
 
 struct Misc {
-    double ss;                        // sum of squares of the staged input
-    double maxabs;                    // largest |value| of the staged input
-    float resid[kRedRows];            // residual rows of O / down tasks (activation values)
+    double part[8][2];                // per wave: sum of squares and largest |value| of its staged input values
+    __attribute__((aligned(16))) u64 residw[kResidWords];   // residual rows of O / down tasks (flag words as gathered)
     uint64_t t_rows;                  // trace: compute wave 0's own rows done
 };
 static_assert(sizeof(Misc) <= kMiscBytes, "LDS control area");
@@ -165,6 +164,8 @@ DEV void bar() {
 struct Ctx {
     CKP* P;
     Lds L;
+    int pos;              // the step's position (read once)
+    double eps;           // the RMSNorm epsilon (read once)
     uint64_t deadline;
     int cu;
     const uint8_t* wcu;   // this CU's weight stream
@@ -183,22 +184,18 @@ DEV DevTask task_at(const Ctx& c, uint32_t t) {
 }
 
 DEV uint32_t act_bytes(CKP& P) { return P.act_f32 ? 4u : 2u; }
-DEV const u64* ll_layer(CKP& P, const LLLayout& y, int layer) { return P.ll + (u64)layer * y.layer_words; }
-
-// index of the norm a GEMV task's input carries (-1: none); gains at norms + idx * H
-DEV int norm_of(CKP& P, const DevTask& T) {
-    switch (T.op) {
-    case AMK_OP_QKV: return 2 * T.layer;
-    case AMK_OP_GATEUP: return 2 * T.layer + 1;
-    case AMK_OP_LM: return 2 * P.L;
-    default: return -1;
-    }
-}
 
 // Stage layout of a GEMV input: digit planes (or fp32 values) from offset 0, the raw input
 // values (activation format) over their start until the planes are written, the fp32 gains
-// after the planes.
-DEV uint32_t gains_off(CKP& P, uint32_t K) { return n_planes(P.wfmt) * plane_stride(P.wfmt, K); }
+// after the planes (n_planes(FMT) * plane_stride(FMT, K)).
+
+// The stage offset of a GEMV input's gathered words: over the plane area (the planes are written
+// only after every raw value is read), past the planes and gains for fp32 activations (8 bytes
+// a value, more than the fp32 plane).
+template <int FMT>
+DEV uint32_t raw_off(uint32_t K, bool norm) {
+    return FMT == AMK_F32 ? n_planes(FMT) * plane_stride(FMT, K) + (norm ? 4u * K : 0u) : 0u;
+}
 
 // Scale 2^S of the fixed-point input: |H| = |h| 2^S stays below 2^37 for every input value h
 // (bound: an upper bound of max |h|). Every thread computes it from the same two numbers.
@@ -214,65 +211,88 @@ DEV int fixed_shift(double bound) {
 template <int R>
 struct Ring {
     uint32_t slot;        // next slot to consume
+    uint32_t pending;     // slots consumed and not yet refilled: [slot - pending, slot)
     uint8_t* base;        // this wave's slot 0
-    // issue side
-    uint32_t t;           // next task whose loads are to be issued
-    TaskLoads tl;         // loads of the task being issued
-    LoadPos lp;
-    const uint8_t* dummy;
+    Cursor cur;           // issue side: the next load of the wave's sequence
+    const uint8_t* kv;    // the cache
 };
 
-// Issue the wave's next load into slot s (a dummy load once the queue has no more).
 DEV uint32_t uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 DEV uint64_t uni64(uint64_t v) { return ((uint64_t)uni((uint32_t)(v >> 32)) << 32) | uni((uint32_t)v); }
 
-// The iterator state is wave-uniform by construction; saying so keeps it in scalar registers
-// (and the descriptor loads on the scalar cache) whatever control flow surrounds the call.
-DEV void uniform_state(uint32_t& t, TaskLoads& tl, LoadPos& lp) {
-    t = uni(t);
-    tl.kind = uni(tl.kind); tl.n = uni(tl.n); tl.tile = uni64(tl.tile); tl.pitch = uni(tl.pitch); tl.nj = uni(tl.nj);
-    tl.m = uni(tl.m); tl.kofs = uni64(tl.kofs); tl.vofs = uni64(tl.vofs); tl.rowb = uni(tl.rowb); tl.rps = uni(tl.rps);
-    tl.nrows = uni(tl.nrows); tl.nbw = uni(tl.nbw);
-    lp.gi = uni(lp.gi); lp.gs = uni(lp.gs); lp.j = uni(lp.j); lp.gr = uni(lp.gr); lp.bi = uni(lp.bi); lp.half = uni(lp.half);
+// The cursor is wave-uniform by construction; saying so once per opened task keeps it in scalar
+// registers whatever control flow surrounds the issue.
+DEV void cursor_uniform(Cursor& c) {
+    c.t = uni(c.t); c.kind = uni(c.kind); c.left = uni(c.left); c.a = uni64(c.a); c.s1 = uni(c.s1); c.s2 = uni(c.s2);
+    c.n1 = uni(c.n1); c.n2 = uni(c.n2); c.x = uni(c.x); c.y = uni(c.y); c.gs = uni(c.gs); c.gi = uni(c.gi);
 }
 
+// Issue the wave's next load into the oldest free slot, opening queue entries below `limit`
+// as needed (deriving a task's geometry happens once per task; every other issue is a few
+// additions). Returns false, issuing nothing, when no entry below `limit` has a load left.
 template <int R>
-DEV void ring_issue(const Ctx& c, Ring<R>& r, uint32_t w, uint32_t s) {
-    CKP& P = *c.P;
-    uniform_state(r.t, r.tl, r.lp);
-    // the next load of the wave's sequence: wave-uniform state only
-    Load ld;
-    bool have = false;
-    for (;;) {
-        if (r.tl.kind && pos_next(r.tl, r.lp, w, &ld)) { have = true; break; }
-        if (r.t >= c.q1) { r.tl.kind = 0; break; }
-        const DevTask T = task_at(c, r.t++);
-        r.tl = task_loads(P, T, w);
-        pos_reset(r.tl, r.lp);
+DEV bool ring_issue(const Ctx& c, Ring<R>& r, uint32_t w, uint32_t limit) {
+    Cursor cu = r.cur;
+    while (cu.left == 0 && cu.t < limit) {
+        const uint32_t t = cu.t;
+        cursor_open(c, task_at(c, t), w, cu);
+        cu.t = t + 1;
+        cursor_uniform(cu);
     }
-    const uint8_t* src = r.dummy;
+    const bool have = cu.left != 0;
     if (have) {
-        const uint8_t* b = (r.tl.kind == 1 ? c.wcu : (const uint8_t*)P.kv) + ld.base;
-        src = b + load_lane_off(r.tl, ld, (uint32_t)lane_id());
+        const CLoad l = cursor_next(cu);
+        const uint8_t* src = (cu.kind == 1 ? c.wcu : r.kv) + l.base + cursor_lane_off(cu, l, (uint32_t)lane_id());
+        uint32_t s = r.slot + (uint32_t)R - r.pending;
+        if (s >= (uint32_t)R) s -= (uint32_t)R;
+        __builtin_amdgcn_global_load_lds((const void*)src, LDS3(r.base + s * 1024u), 16, 0, 0);
+        --r.pending;
     }
-    __builtin_amdgcn_global_load_lds((const void*)src, LDS3(r.base + s * 1024u), 16, 0, 0);
+    r.cur = cu;
+    return have;
+}
+
+// Refill the free slots with the wave's next loads from queue entries below `limit`.
+template <int R>
+DEV void ring_refill(const Ctx& c, Ring<R>& r, uint32_t w, uint32_t limit) {
+#pragma unroll 1
+    while (r.pending && ring_issue(c, r, w, limit)) {}
 }
 
 template <int R>
 DEV void ring_init(const Ctx& c, Ring<R>& r, uint32_t w) {
     r.base = c.L.ring + w * (uint32_t)R * 1024u;
     r.slot = 0;
-    r.t = c.q0;
-    r.tl.kind = 0;
-    r.dummy = c.P->wstream;   // any 16 readable bytes
-    for (uint32_t s = 0; s < (uint32_t)R; ++s) ring_issue(c, r, w, s);
+    r.pending = R;
+    r.cur.t = c.q0;
+    r.cur.kind = 0;
+    r.cur.left = 0;
+    r.kv = (const uint8_t*)c.P->kv;
+    ring_refill(c, r, w, c.q1);
 }
 
-// The next n (1..4) slots, after the loads that filled them have landed: with R loads in flight,
-// the oldest n are done once at most R - n are outstanding. The reads are one asm block that
-// waits for them itself, so the compiler neither reorders them nor waits for every ring load.
+// Wait until at most k of the wave's vector memory operations are outstanding (k < 16).
+DEV void wait_vm(uint32_t k) {
+    switch (k) {
+#define AMK_WAIT_CASE(K) case K: asm volatile("s_waitcnt vmcnt(" #K ")" ::: "memory"); break;
+    AMK_WAIT_CASE(0) AMK_WAIT_CASE(1) AMK_WAIT_CASE(2) AMK_WAIT_CASE(3) AMK_WAIT_CASE(4) AMK_WAIT_CASE(5)
+    AMK_WAIT_CASE(6) AMK_WAIT_CASE(7) AMK_WAIT_CASE(8) AMK_WAIT_CASE(9) AMK_WAIT_CASE(10) AMK_WAIT_CASE(11)
+    AMK_WAIT_CASE(12) AMK_WAIT_CASE(13) AMK_WAIT_CASE(14)
+#undef AMK_WAIT_CASE
+    default: break;
+    }
+}
+
+// The next n (1..4) slots, after the loads that filled them have landed. The wave's only vector
+// memory operations are its ring loads, issued and completed in slot order, R - pending of them
+// in flight: the oldest n are done once at most R - pending - n are outstanding (the slots hold
+// issued loads: every load of the task being consumed is issued before it is taken). The reads
+// are one asm block that waits for itself, so the compiler neither reorders them nor waits for
+// every ring load.
 template <int R>
 DEV void ring_take(Ring<R>& r, uint32_t n, u32x4 (&v)[4]) {
+    static_assert(R <= 15, "wait_vm covers counts below 15");
+    wait_vm((uint32_t)R - r.pending - n);
     const uint32_t lane16 = 16u * (uint32_t)lane_id();
     const uint32_t b = (uint32_t)(uintptr_t)LDS3(r.base);
     uint32_t a[4];
@@ -284,25 +304,26 @@ DEV void ring_take(Ring<R>& r, uint32_t n, u32x4 (&v)[4]) {
     }
     switch (n) {
     case 1:
-        asm volatile("s_waitcnt vmcnt(%1)\n\tds_read_b128 %0, %2\n\ts_waitcnt lgkmcnt(0)"
-                     : "=v"(v[0]) : "i"(R - 1), "v"(a[0]) : "memory");
+        asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v[0]) : "v"(a[0]) : "memory");
         break;
     case 2:
-        asm volatile("s_waitcnt vmcnt(%2)\n\tds_read_b128 %0, %3\n\tds_read_b128 %1, %4\n\ts_waitcnt lgkmcnt(0)"
-                     : "=&v"(v[0]), "=&v"(v[1]) : "i"(R - 2), "v"(a[0]), "v"(a[1]) : "memory");
+        asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&v"(v[0]), "=&v"(v[1]) : "v"(a[0]), "v"(a[1]) : "memory");
         break;
     case 3:
-        asm volatile("s_waitcnt vmcnt(%3)\n\tds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\t"
-                     "s_waitcnt lgkmcnt(0)"
-                     : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]) : "i"(R - 3), "v"(a[0]), "v"(a[1]), "v"(a[2]) : "memory");
+        asm volatile("ds_read_b128 %0, %3\n\tds_read_b128 %1, %4\n\tds_read_b128 %2, %5\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]) : "v"(a[0]), "v"(a[1]), "v"(a[2]) : "memory");
         break;
     default:
-        asm volatile("s_waitcnt vmcnt(%4)\n\tds_read_b128 %0, %5\n\tds_read_b128 %1, %6\n\tds_read_b128 %2, %7\n\t"
-                     "ds_read_b128 %3, %8\n\ts_waitcnt lgkmcnt(0)"
+        asm volatile("ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
+                     "s_waitcnt lgkmcnt(0)"
                      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
-                     : "i"(R - 4), "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]) : "memory");
+                     : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]) : "memory");
         break;
     }
+    r.slot += n;
+    if (r.slot >= (uint32_t)R) r.slot -= (uint32_t)R;
+    r.pending += n;
 }
 
 // LDS stores of the compute waves that the compiler would otherwise order after every ring
@@ -311,17 +332,11 @@ DEV void ring_take(Ring<R>& r, uint32_t n, u32x4 (&v)[4]) {
 DEV void lds_st128(void* p, u32x4 v) {
     asm volatile("ds_write_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"((uint32_t)(uintptr_t)LDS3(p)), "v"(v) : "memory");
 }
+DEV void lds_st32(void* p, uint32_t v) {
+    asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"((uint32_t)(uintptr_t)LDS3(p)), "v"(v) : "memory");
+}
 DEV void lds_st64(void* p, double v) {
     asm volatile("ds_write_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"((uint32_t)(uintptr_t)LDS3(p)), "v"(v) : "memory");
-}
-
-// The n slots just read are free: refill them with the next loads, in order.
-template <int R>
-DEV void ring_refill(const Ctx& c, Ring<R>& r, uint32_t w, uint32_t n) {
-    for (uint32_t k = 0; k < n; ++k) {
-        ring_issue(c, r, w, r.slot);
-        if (++r.slot == (uint32_t)R) r.slot = 0;
-    }
 }
 
 // ------------------------------------------------------------------ GEMV on the compute waves
@@ -365,11 +380,11 @@ DEV double int4_scale(const Ctx& c, const TaskLoads& t, uint32_t K, uint32_t til
 }
 
 template <int FMT, int R>
-DEV void gemv_compute(const Ctx& c, Ring<R>& ring, const DevTask& T, uint32_t w, int S) {
+DEV void gemv_compute(const Ctx& c, Ring<R>& ring, const DevTask& T, uint32_t t_idx, uint32_t w, int S) {
     CKP& P = *c.P;
-    const TaskLoads t = task_loads(P, T, w);
+    const TaskLoads t = task_loads(c, T, w);
     if (t.kind != 1) return;
-    const uint32_t K = gemv_K(P, T.op);
+    const uint32_t K = T.k;
     const uint32_t lane = (uint32_t)lane_id();
     const uint8_t* stage = c.L.stage;
     const uint32_t ps = plane_stride(FMT, K);
@@ -389,7 +404,7 @@ DEV void gemv_compute(const Ctx& c, Ring<R>& ring, const DevTask& T, uint32_t w,
                 for (int d = 0; d < 5; ++d) D[d] = *(const u32x4*)(stage + d * ps + c0);
                 u32x4 W[4];
                 ring_take(ring, gs, W);
-                ring_refill(c, ring, w, gs);
+                ring_refill(c, ring, w, t_idx + 1);
                 const bool valid = c0 < K;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -424,7 +439,7 @@ DEV void gemv_compute(const Ctx& c, Ring<R>& ring, const DevTask& T, uint32_t w,
                 for (int d = 0; d < 10; ++d) D[d] = *(const u32x4*)(stage + d * ps + c0b);
                 u32x4 W[4];
                 ring_take(ring, gs, W);
-                ring_refill(c, ring, w, gs);
+                ring_refill(c, ring, w, t_idx + 1);
                 const bool valid = c0b < t.pitch;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -465,7 +480,7 @@ DEV void gemv_compute(const Ctx& c, Ring<R>& ring, const DevTask& T, uint32_t w,
                 for (int k = 0; k < CPL; ++k) h[k] = (double)hp[k];
                 u32x4 W[4];
                 ring_take(ring, gs, W);
-                ring_refill(c, ring, w, gs);
+                ring_refill(c, ring, w, t_idx + 1);
                 const bool valid = c0 < K;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -598,12 +613,12 @@ DEV void row_slices4(const uint32_t (&row)[4], bool f32, uint32_t d0, double (&v
 // q.K / sqrt(hd) times V, online (running max m, running sum l, rescaled output o), in fp64
 // (page 3, "How it works", the attention instruction over the persistent KV cache).
 // Lanes are (query head, dimension group) pairs: a head owns L lanes, a lane D consecutive dims.
-template <int D, int R>
-DEV void attn_compute_d(const Ctx& c, Ring<R>& ring, const DevTask& T, uint32_t w) {
+template <int FMT, int D, int R = ring_slots(FMT)>
+DEV void attn_compute_d(const Ctx& c, Ring<R>& ring, const DevTask& T, uint32_t t_idx, uint32_t w) {
     CKP& P = *c.P;
-    const TaskLoads t = task_loads(P, T, w);
-    const uint32_t nh = T.arg[1], hd = (uint32_t)P.hd;
-    const bool f32 = P.act_f32 != 0;
+    const TaskLoads t = task_loads(c, T, w);
+    constexpr bool f32 = FMT == AMK_F32;
+    const uint32_t nh = T.arg[1], hd = T.k / (f32 ? 4u : 2u);
     const bool cur = T.arg[2] == T.arg[3] - 1;
     const AttnStage A = attn_stage(c.L, nh, hd);
     const uint32_t lane = (uint32_t)lane_id();
@@ -669,7 +684,7 @@ DEV void attn_compute_d(const Ctx& c, Ring<R>& ring, const DevTask& T, uint32_t 
         for (uint32_t bi = 0; bi < t.nbw; ++bi) {
             u32x4 W[4];
             ring_take(ring, 2, W);
-            ring_refill(c, ring, w, 2);
+            ring_refill(c, ring, w, t_idx + 1);
             lds_st128(cp + 16 * lane, W[0]);          // K rows of the block
             lds_st128(cp + 1024 + 16 * lane, W[1]);   // V rows
             const uint32_t b = w + kCompWaves * bi;
@@ -699,16 +714,16 @@ DEV void attn_compute_d(const Ctx& c, Ring<R>& ring, const DevTask& T, uint32_t 
     }
 }
 
-template <int R>
-DEV void attn_compute(const Ctx& c, Ring<R>& ring, const DevTask& T, uint32_t w) {
-    const uint32_t nh = T.arg[1], hd = (uint32_t)c.P->hd;
+template <int FMT, int R = ring_slots(FMT)>
+DEV void attn_compute(const Ctx& c, Ring<R>& ring, const DevTask& T, uint32_t t_idx, uint32_t w) {
+    const uint32_t nh = T.arg[1], hd = T.k / (FMT == AMK_F32 ? 4u : 2u);
     uint32_t nhp = 1;
     while (nhp < nh) nhp <<= 1;
     switch (hd / min(64u / nhp, hd)) {
-    case 1: attn_compute_d<1>(c, ring, T, w); break;
-    case 2: attn_compute_d<2>(c, ring, T, w); break;
-    case 4: attn_compute_d<4>(c, ring, T, w); break;
-    default: attn_compute_d<8>(c, ring, T, w); break;
+    case 1: attn_compute_d<FMT, 1>(c, ring, T, t_idx, w); break;
+    case 2: attn_compute_d<FMT, 2>(c, ring, T, t_idx, w); break;
+    case 4: attn_compute_d<FMT, 4>(c, ring, T, t_idx, w); break;
+    default: attn_compute_d<FMT, 8>(c, ring, T, t_idx, w); break;
     }
 }
 
@@ -722,38 +737,84 @@ DEV void attn_compute(const Ctx& c, Ring<R>& ring, const DevTask& T, uint32_t w)
 template <int FMT>
 DEV int stage_input(const Ctx& c, const DevTask& T, int tid) {
     CKP& P = *c.P;
-    const bool f32 = P.act_f32 != 0;
-    const uint32_t K = gemv_K(P, T.op);
-    const int ni = norm_of(P, T);
+    constexpr bool f32 = FMT == AMK_F32;
+    const uint32_t K = T.k;
+    const int ni = T.norm;
     constexpr int Q = FMT == AMK_INT4_G128 ? 8 : 4;
     constexpr int MAXU = (kMaxInter + 512 * Q - 1) / (512 * Q);   // units per thread: every column in one pass
     const uint32_t nunits = K / Q;
-    const double ss = c.L.misc->ss, maxabs = c.L.misc->maxabs;
-    // RMSNorm scale r = 1 / sqrt(mean(x^2) + eps)
-    const double r = ni >= 0 ? 1.0 / sqrt(ss / (double)K + P.eps) : 1.0;
-    const double bound = ni >= 0 ? maxabs * r * (double)*CONST4(float, P.gmax + ni) * 1.01 : maxabs;
-    const int S = fixed_shift(bound);
-    const float* gains = (const float*)(c.L.stage + gains_off(P, K));
+    const float* gains = (const float*)(c.L.stage + n_planes(FMT) * plane_stride(FMT, K));
     uint8_t* st = c.L.stage;
+    const uint8_t* raw = st + raw_off<FMT>(K, ni >= 0);   // the gathered words
     const uint32_t ps = plane_stride(FMT, K);
     float x[MAXU][Q];   // activation values: exact in fp32
+    // every unit's words (and gains) are read first, then converted: the LDS reads go out together
+    constexpr int WPU = f32 ? Q : Q / 2;   // gathered words per unit (8 bytes each)
+    u32x4 rw[MAXU][WPU / 2];
+    u32x4 gw[MAXU][Q / 4];
+    const uint32_t nu = (nunits + 511u) / 512u;   // unit rounds that hold any of the input (wave-uniform)
 #pragma unroll
     for (int u = 0; u < MAXU; ++u) {
+        if ((uint32_t)u >= nu) break;
+        const uint32_t unit = (uint32_t)tid + 512u * (uint32_t)u;
+        const uint32_t uc = unit < nunits ? unit : 0u;   // units past the input read unit 0 (unused)
+#pragma unroll
+        for (int k = 0; k < WPU / 2; ++k) rw[u][k] = *(const u32x4*)(raw + 8u * (uc * WPU) + 16u * k);
+#pragma unroll
+        for (int k = 0; k < Q / 4; ++k) gw[u][k] = ni >= 0 ? *(const u32x4*)(gains + uc * Q + 4u * k) : u32x4{0, 0, 0, 0};
+    }
+    // the raw values (exact in fp32) and this thread's part of their sum of squares and maximum
+    double ss = 0.0, mx = 0.0;
+#pragma unroll
+    for (int u = 0; u < MAXU; ++u) {
+        if ((uint32_t)u >= nu) break;
         const uint32_t unit = (uint32_t)tid + 512u * (uint32_t)u;
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
-            double v = 0.0;
-            if (unit < nunits) {
-                const uint32_t k = unit * Q + (uint32_t)q;
-                v = f32 ? (double)((const float*)st)[k] : bf2d(((const uint16_t*)st)[k]);
-                if (ni >= 0) v = round_act((v * r) * (double)gains[k], f32);
-            }
+            // value q of the unit: word q (fp32) or half q % 2 of word q / 2 (bf16); payloads sit in
+            // the words' low dwords (components x and z of each 16-byte read)
+            const u32x4 wv = rw[u][f32 ? q / 2 : q / 4];
+            const uint32_t pl = f32 ? ((q & 1) ? wv.z : wv.x) : (((q / 2) & 1) ? wv.z : wv.x);
+            const double v = unit < nunits ? (f32 ? (double)__uint_as_float(pl) : bf2d((pl >> (16u * (q & 1))) & 0xffffu)) : 0.0;
+            ss = fma(v, v, ss);
+            mx = fmax(mx, fabs(v));
             x[u][q] = (float)v;
         }
     }
-    bar();   // A1b: every raw value is read before any plane is written
+    ss = wave_sum_f64(ss);
+    mx = wave_max_f64(mx);
+    const uint32_t wv_ = (uint32_t)tid >> 6;
+    if ((tid & 63) == 0) {
+        lds_st64(&c.L.misc->part[wv_][0], ss);
+        lds_st64(&c.L.misc->part[wv_][1], mx);
+    }
+    bar();   // A1b: every raw value is read (planes may be written) and every wave's statistics are in
+    ss = 0.0;
+    mx = 0.0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {   // in wave order: every thread forms the same sums
+        ss += lds_ld64(&c.L.misc->part[k][0]);
+        mx = fmax(mx, lds_ld64(&c.L.misc->part[k][1]));
+    }
+    // RMSNorm scale r = 1 / sqrt(mean(x^2) + eps)
+    const double r = ni >= 0 ? 1.0 / sqrt(ss / (double)K + c.eps) : 1.0;
+    const double bound = ni >= 0 ? mx * r * (double)T.gmax * 1.01 : mx;
+    const int S = fixed_shift(bound);
+    if (ni >= 0) {
+#pragma unroll
+        for (int u = 0; u < MAXU; ++u) {
+            if ((uint32_t)u >= nu) break;
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                const u32x4 g4 = gw[u][q / 4];
+                const uint32_t gb = (q & 3) == 0 ? g4.x : (q & 3) == 1 ? g4.y : (q & 3) == 2 ? g4.z : g4.w;
+                x[u][q] = (float)round_act(((double)x[u][q] * r) * (double)__uint_as_float(gb), f32);
+            }
+        }
+    }
 #pragma unroll
     for (int u = 0; u < MAXU; ++u) {
+        if ((uint32_t)u >= nu) break;
         const uint32_t unit = (uint32_t)tid + 512u * (uint32_t)u;
         if (unit >= nunits) continue;
         const uint32_t k0 = unit * Q;
@@ -805,7 +866,6 @@ struct Io {
     const Ctx* c;
     uint32_t flag;
     bool abort_;
-    LLLayout y;
     int token;
     uint64_t* tr;
 };
@@ -835,124 +895,134 @@ DEV void mark(const Io& io, int k) {
     if (io.tr && lane_id() == 0) io.tr[k] = rt();
 }
 
-// Words each lane has in flight at once while gathering flag-carrying words.
-constexpr int kGather = 24;
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-constexpr int kCoherent = 16;   // buffer-load cache policy: device-coherent (the agent-scope load's)
+constexpr int kCoherent = 16;   // load cache policy: device-coherent (the agent-scope load's)
 
-// Wait until words [0, n) all carry the current flag; hand each payload to fn(i, payload).
-// Every lane polls words lane + 64 k, kGather of them at a time, all in flight together. The
-// loads are buffer loads off one descriptor with the lane's offset, so the addresses cost no
-// registers.
-template <typename F>
-DEV void gather(Io& io, const u64* base, uint32_t n, F&& fn) {
+// One range of flag-carrying words a gather polls: n words from src into LDS at dst (8 bytes a
+// word, in order; the LDS area is a whole number of 1 KiB blocks of 128 words).
+struct GSeg {
+    const u64* src;
+    uint32_t n;
+    uint8_t* dst;
+};
+
+// Wait until every word of up to three ranges carries the current flag, the words landing in
+// LDS. Each round fetches every incomplete 1 KiB block at once with device-coherent
+// memory-to-LDS loads (lane l: words 2l, 2l + 1 of the block; lanes past a range's end re-read
+// its first word), waits for them, and checks the flags in LDS; a block whose words all carry
+// the flag is done. At most kMaxGatherBlocks blocks in all (the lowering keeps every task's
+// inputs within it). The ranges are selected by value (no indexed array, so nothing goes to
+// private memory).
+DEV void gather(Io& io, uint32_t ns, GSeg g0, GSeg g1 = GSeg{nullptr, 0u, nullptr}, GSeg g2 = GSeg{nullptr, 0u, nullptr}) {
     const uint32_t lane = (uint32_t)lane_id();
     const uint32_t flag = io.flag;
-    for (uint32_t b0 = 0; b0 < n; b0 += 64u * kGather) {
-        const uint32_t nb = n - b0 < 64u * kGather ? n - b0 : 64u * kGather;
-        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)(base + b0), 0, (int)(nb * 8u), 0x00020000);
-        u32x2 w[kGather];
+    if (ns < 2) g1.n = 0;
+    if (ns < 3) g2.n = 0;
+    const uint32_t nb0 = gather_blocks(g0.n), nb1 = gather_blocks(g1.n), nb2 = gather_blocks(g2.n);
+    const uint32_t tot = nb0 + nb1 + nb2;
+    uint64_t mask = tot >= 64u ? ~0ull : ((1ull << tot) - 1ull);
+    uint32_t spins = 0;
+    // block b of the ranges: which range (by selection) and which block inside it
+#define AMK_LOCATE(b)                                                         \
+    const bool s0 = (b) < nb0, s1 = !s0 && (b) < nb0 + nb1;                   \
+    const u64* src = s0 ? g0.src : s1 ? g1.src : g2.src;                      \
+    const uint32_t n = s0 ? g0.n : s1 ? g1.n : g2.n;                          \
+    uint8_t* dst = s0 ? g0.dst : s1 ? g1.dst : g2.dst;                        \
+    const uint32_t blk = (b) - (s0 ? 0u : s1 ? nb0 : nb0 + nb1);              \
+    const uint32_t wi = blk * 128u + 2u * lane;
+    // First a light poll: eight sentinel words per block (every 16th word), 8 bytes each, until
+    // all carry the flag; only then are the blocks fetched whole (and any word still missing
+    // sends its block round again). The whole-block fetches of all CUs at once would otherwise
+    // load the fabric with repeated 1 KiB reads while the producers are still writing.
+    for (;;) {
+        bool ok = true;
 #pragma unroll
-        for (int k = 0; k < kGather; ++k) {
-            const uint32_t i = lane + 64u * (uint32_t)k;
-            w[k] = i < nb ? __builtin_amdgcn_raw_buffer_load_b64(rs, (int)(8u * i), 0, kCoherent) : u32x2{0u, flag};
+        for (uint32_t k = 0; k < 8; ++k) {
+            const uint32_t sx = lane + 64u * k;   // sentinel: block sx / 8, word 16 (sx % 8) + 15
+            const uint32_t b = sx / 8u < tot ? sx / 8u : 0u;
+            AMK_LOCATE(b)
+            (void)dst;
+            (void)wi;
+            uint32_t ws = blk * 128u + 16u * (sx % 8u) + 15u;
+            if (ws >= n) ws = n - 1u;
+            const u64 v = ll_load(src + ws);
+            ok &= sx / 8u >= tot || (uint32_t)(v >> 32) == flag;
         }
-        uint32_t spins = 0;
-        for (;;) {
-            bool done = true;
-#pragma unroll
-            for (int k = 0; k < kGather; ++k) done &= w[k].y == flag;
-            if (__builtin_amdgcn_ballot_w64(!done) == 0) break;
-            if (!spin_ok(io, spins)) break;
-#pragma unroll
-            for (int k = 0; k < kGather; ++k) {
-                const uint32_t i = lane + 64u * (uint32_t)k;
-                if (w[k].y != flag) w[k] = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)(8u * i), 0, kCoherent);
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < kGather; ++k) {
-            const uint32_t i = lane + 64u * (uint32_t)k;
-            if (i < nb) fn(b0 + i, w[k].x);
-        }
+        if (__builtin_amdgcn_ballot_w64(!ok) == 0 || !spin_ok(io, spins)) break;
     }
+    while (mask) {
+        for (uint64_t m = mask; m; m &= m - 1ull) {
+            const uint32_t b = (uint32_t)__builtin_ctzll(m);
+            AMK_LOCATE(b)
+            __builtin_amdgcn_global_load_lds((const void*)(src + (wi < n ? wi : 0u)), LDS3(dst + blk * 1024u), 16, 0, kCoherent);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        for (uint64_t m = mask; m; m &= m - 1ull) {
+            const uint32_t b = (uint32_t)__builtin_ctzll(m);
+            AMK_LOCATE(b)
+            (void)src;
+            const u32x4 v = *(const u32x4*)(dst + blk * 1024u + 16u * lane);
+            const bool ok = (wi >= n || v.y == flag) && (wi + 1u >= n || v.w == flag);
+            if (__builtin_amdgcn_ballot_w64(!ok) == 0) mask &= ~(1ull << b);
+        }
+        if (!mask || !spin_ok(io, spins)) break;
+    }
+#undef AMK_LOCATE
 }
 
-// payload of a word -> activation value j (0/1 inside the word)
-DEV double word_val(bool f32, uint32_t payload, int j) {
-    return f32 ? (double)__uint_as_float(payload) : bf2d(j ? (payload >> 16) : (payload & 0xffffu));
+// payload of gathered word i (an array of 8-byte words in LDS)
+DEV uint32_t wpl(const uint8_t* words, uint32_t i) { return *(const uint32_t*)(words + 8u * i); }
+// activation value k of a gathered vector (fp32: one value a word; bf16: two, low half first)
+DEV double wval(const uint8_t* words, uint32_t k, bool f32) {
+    return f32 ? (double)__uint_as_float(wpl(words, k)) : bf2d((wpl(words, k >> 1) >> (16u * (k & 1u))) & 0xffffu);
+}
+// fp64 value j of a gathered array of doubles (two words each, low half first)
+DEV double wdbl(const uint8_t* words, uint32_t j) {
+    return __longlong_as_double((long long)(((uint64_t)wpl(words, 2u * j + 1u) << 32) | wpl(words, 2u * j)));
 }
 
-// Gather a GEMV input of K activation values into the stage's raw area (activation format), with
-// its sum of squares and largest magnitude (fp64, into the control area). src null: the
-// embedding row of the input token.
-DEV void io_input(Io& io, const u64* src, uint32_t K) {
+// The input of a GEMV task (its words, or the embedding row as words) and, for O and down, its
+// residual rows, gathered together; then the input's sum of squares and largest magnitude
+// (fp64, into the control area).
+DEV void io_gemv_inputs(Io& io, const DevTask& T, uint32_t roff) {
     const Ctx& c = *io.c;
     CKP& P = *c.P;
     const bool f32 = P.act_f32 != 0;
     const uint32_t vpw = f32 ? 1u : 2u;
-    uint32_t* st = (uint32_t*)c.L.stage;   // one word's payload per 32 bits: the values in order
-    double ss = 0.0, mx = 0.0;
-    auto take = [&](uint32_t i, uint32_t pl) {
-        st[i] = pl;
-        for (uint32_t j = 0; j < vpw; ++j) {
-            const double v = word_val(f32, pl, (int)j);
-            ss = fma(v, v, ss);
-            mx = fmax(mx, fabs(v));
-        }
-    };
-    if (src) {
-        gather(io, src, K / vpw, take);
-    } else {
+    const uint32_t lane = (uint32_t)lane_id();
+    const uint32_t K = T.k, nw = K / vpw;
+    uint8_t* words = c.L.stage + roff;
+    const bool resid = T.op == AMK_OP_OPROJ || T.op == AMK_OP_DOWN;
+    const uint32_t r0 = T.arg[0], nr = T.arg[1] / vpw;
+    uint8_t* rw = (uint8_t*)c.L.misc->residw;
+    GSeg gi{nullptr, 0u, nullptr}, gr{nullptr, 0u, nullptr};
+    if (T.src != kNoWord) gi = GSeg{P.ll + T.src, nw, words};
+    else {   // layer 0's QKV: the embedding row of the input token
         const uint32_t* er = (const uint32_t*)((const uint8_t*)P.embed + (uint64_t)io.token * K * act_bytes(P));
-        for (uint32_t i = (uint32_t)lane_id(); i < K / vpw; i += 64u) take(i, er[i]);
+        for (uint32_t i = lane; i < nw; i += 64u) *(u64*)(words + 8u * i) = er[i];
     }
-    ss = wave_allsum_f64(ss);
-    mx = wave_max_f64(mx);
-    if (lane_id() == 0) { c.L.misc->ss = ss; c.L.misc->maxabs = mx; }
+    if (resid) {
+        if (T.aux != kNoWord) gr = GSeg{P.ll + T.aux + r0 / vpw, nr, rw};
+        else {   // layer 0's O projection: the residual is the embedding row
+            const uint32_t* er = (const uint32_t*)((const uint8_t*)P.embed + (uint64_t)io.token * P.H * act_bytes(P));
+            for (uint32_t i = lane; i < nr; i += 64u) *(u64*)(rw + 8u * i) = er[r0 / vpw + i];
+        }
+    }
+    // one gather for both (whichever of them come from flag words)
+    if (gi.n && gr.n) gather(io, 2, gi, gr);
+    else if (gi.n) gather(io, 1, gi);
+    else if (gr.n) gather(io, 1, gr);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the gains' loads too
 }
 
-// The norm gains of the input (fp32) after the planes of the stage.
-DEV void io_gains(const Io& io, int ni, uint32_t K) {
+// The norm gains of the input (fp32) after the planes of the stage, by memory-to-LDS loads that
+// are left in flight (the input gather waits for them with its own loads).
+DEV void io_gains(const Io& io, int ni, uint32_t K, uint32_t off) {
     const Ctx& c = *io.c;
     CKP& P = *c.P;
-    u32x4* g = (u32x4*)(c.L.stage + gains_off(P, K));
-    const u32x4* src = (const u32x4*)(P.norms + (uint64_t)ni * P.H);
-    for (uint32_t i = (uint32_t)lane_id(); i < K / 4; i += 64u) g[i] = src[i];
-}
-
-// Residual rows [r0, r0 + n) of an O or down task into the control area.
-DEV void io_resid(Io& io, const DevTask& T) {
-    const Ctx& c = *io.c;
-    CKP& P = *c.P;
-    const bool f32 = P.act_f32 != 0;
-    const uint32_t vpw = f32 ? 1u : 2u;
-    const uint32_t r0 = T.arg[0], n = T.arg[1];
-    float* out = c.L.misc->resid;
-    if (T.op == AMK_OP_OPROJ && T.layer == 0) {
-        const uint8_t* er = (const uint8_t*)P.embed + (uint64_t)io.token * P.H * act_bytes(P);
-        for (uint32_t i = (uint32_t)lane_id(); i < n; i += 64u)
-            out[i] = f32 ? ((const float*)er)[r0 + i] : (float)bf2d(((const uint16_t*)er)[r0 + i]);
-        return;
-    }
-    const u64* rs = (T.op == AMK_OP_OPROJ ? ll_layer(P, io.y, T.layer - 1) + io.y.xd : ll_layer(P, io.y, T.layer) + io.y.xo) +
-                    r0 / vpw;
-    gather(io, rs, n / vpw, [&](uint32_t i, uint32_t pl) {
-        for (uint32_t j = 0; j < vpw; ++j) out[i * vpw + j] = (float)word_val(f32, pl, (int)j);
-    });
-}
-
-// The GEMV task's input source (null: the embedding row).
-DEV const u64* io_src(const Io& io, const DevTask& T) {
-    CKP& P = *io.c->P;
-    const int l = T.layer;
-    switch (T.op) {
-    case AMK_OP_QKV: return l == 0 ? nullptr : ll_layer(P, io.y, l - 1) + io.y.xd;
-    case AMK_OP_OPROJ: return ll_layer(P, io.y, l) + io.y.o;
-    case AMK_OP_GATEUP: return ll_layer(P, io.y, l) + io.y.xo;
-    case AMK_OP_DOWN: return ll_layer(P, io.y, l) + io.y.a;
-    default: return ll_layer(P, io.y, P.L - 1) + io.y.xd;   // LM head
-    }
+    const uint8_t* src = (const uint8_t*)(P.norms + (uint64_t)ni * P.H);
+    const uint32_t lane16 = 16u * (uint32_t)lane_id(), nbytes = 4u * K;
+    for (uint32_t b = 0; b < nbytes; b += 1024u)
+        if (b + lane16 < nbytes) __builtin_amdgcn_global_load_lds((const void*)(src + b + lane16), LDS3(c.L.stage + off + b), 16, 0, 0);
 }
 
 DEV uint32_t pack2(bool f32, double a, double b) {
@@ -970,13 +1040,13 @@ DEV void io_gemv_epilogue(Io& io, const DevTask& T) {
     const uint32_t flag = io.flag;
     const int l = T.layer;
     const double* red = c.L.red;
-    const u64* LLl = ll_layer(P, io.y, l);
+    u64* const dst = P.ll + T.dst;
     switch (T.op) {
     case AMK_OP_QKV: {
         // rows come in quads (r, r+1, r+hd/2, r+hd/2+1) of one head of the fused [q; k; v]
         const uint32_t nq = T.arg[1], per = (uint32_t)P.hd / 4, half = (uint32_t)P.hd / 2;
         const uint32_t qd = (uint32_t)(P.nH * P.hd), kd = (uint32_t)(P.nKV * P.hd);
-        u64* out = (u64*)(LLl + io.y.qkv);
+        u64* out = dst;
         for (uint32_t k = lane; k < nq; k += 64u) {
             const uint32_t u = T.arg[0] + k, head = u / per, m = u % per;
             const uint32_t base = head * (uint32_t)P.hd;
@@ -1019,11 +1089,11 @@ DEV void io_gemv_epilogue(Io& io, const DevTask& T) {
     case AMK_OP_OPROJ:
     case AMK_OP_DOWN: {
         const uint32_t r0 = T.arg[0], n = T.arg[1];
-        u64* out = (u64*)(LLl + (T.op == AMK_OP_OPROJ ? io.y.xo : io.y.xd)) + r0 / vpw;
-        const float* rs = c.L.misc->resid;
+        u64* out = dst + r0 / vpw;
+        const uint8_t* rw = (const uint8_t*)c.L.misc->residw;
         for (uint32_t i = lane; i < n / vpw; i += 64u) {
-            const double a = (double)rs[i * vpw] + red[i * vpw];
-            const double b = vpw == 2 ? (double)rs[i * vpw + 1] + red[i * vpw + 1] : 0.0;
+            const double a = wval(rw, i * vpw, f32) + red[i * vpw];
+            const double b = vpw == 2 ? wval(rw, i * vpw + 1, f32) + red[i * vpw + 1] : 0.0;
             ll_store(out + i, pack2(f32, a, b), flag);
         }
         break;
@@ -1031,7 +1101,7 @@ DEV void io_gemv_epilogue(Io& io, const DevTask& T) {
     case AMK_OP_GATEUP: {
         // SwiGLU: silu(G) U = G / (1 + exp(-G)) * U
         const uint32_t j0 = T.arg[0], n = T.arg[1];
-        u64* out = (u64*)(LLl + io.y.a) + j0 / vpw;
+        u64* out = dst + j0 / vpw;
         for (uint32_t i = lane; i < n / vpw; i += 64u) {
             double v[2] = {0.0, 0.0};
             for (uint32_t j = 0; j < vpw; ++j) {
@@ -1061,7 +1131,7 @@ DEV void io_gemv_epilogue(Io& io, const DevTask& T) {
         }
         const bool anynan = __builtin_amdgcn_ballot_w64(nan) != 0;
         if (lane == 0) {
-            u64* out = P.ll + io.y.lmpart + 2ull * T.arg[2];
+            u64* out = dst + 2ull * T.arg[2];
             ll_store(out, __float_as_uint(anynan ? __uint_as_float(0x7fc00000u) : best), flag);
             ll_store(out + 1, (uint32_t)(anynan ? -1 : bi), flag);
         }
@@ -1070,126 +1140,148 @@ DEV void io_gemv_epilogue(Io& io, const DevTask& T) {
     }
 }
 
-// Attention: gather q of the task's heads (and the current k, v in the last chunk) into the
-// stage as fp64.
+// Attention: gather q of the task's heads (and the current k, v in the last chunk) as words past
+// the attention stage, then widen them into the stage as fp64.
 DEV void io_attn_inputs(Io& io, const DevTask& T) {
     const Ctx& c = *io.c;
     CKP& P = *c.P;
     const bool f32 = P.act_f32 != 0;
     const uint32_t vpw = f32 ? 1u : 2u;
     const uint32_t h0 = T.arg[0], nh = T.arg[1], hd = (uint32_t)P.hd;
-    const int g = (int)((uint64_t)h0 * P.nKV / P.nH);
+    const uint32_t lane = (uint32_t)lane_id();
+    const int g = (int)(h0 * (uint32_t)P.nKV / (uint32_t)P.nH);
     const AttnStage A = attn_stage(c.L, nh, hd);
-    const u64* Lq = ll_layer(P, io.y, T.layer) + io.y.qkv;
-    gather(io, Lq + (uint64_t)h0 * hd / vpw, nh * hd / vpw, [&](uint32_t i, uint32_t pl) {
-        for (uint32_t j = 0; j < vpw; ++j) A.q[i * vpw + j] = word_val(f32, pl, (int)j);
-    });
-    if (T.arg[2] == T.arg[3] - 1) {
-        const uint64_t kofs = ((uint64_t)P.nH + g) * hd / vpw, vofs = ((uint64_t)P.nH + P.nKV + g) * hd / vpw;
-        gather(io, Lq + kofs, hd / vpw, [&](uint32_t i, uint32_t pl) {
-            for (uint32_t j = 0; j < vpw; ++j) A.kc[i * vpw + j] = word_val(f32, pl, (int)j);
-        });
-        gather(io, Lq + vofs, hd / vpw, [&](uint32_t i, uint32_t pl) {
-            for (uint32_t j = 0; j < vpw; ++j) A.vc[i * vpw + j] = word_val(f32, pl, (int)j);
-        });
-    }
+    const u64* Lq = P.ll + T.src;
+    const bool cur = T.arg[2] == T.arg[3] - 1;
+    uint8_t* wq = c.L.stage + attn_words_off(nh, hd);
+    uint8_t* wk = wq + round_up_u(8u * nh * hd / vpw, 1024u);
+    uint8_t* wv = wk + round_up_u(8u * hd / vpw, 1024u);
+    gather(io, cur ? 3u : 1u, GSeg{Lq + (uint64_t)h0 * hd / vpw, nh * hd / vpw, wq},
+           GSeg{Lq + ((uint64_t)P.nH + g) * hd / vpw, hd / vpw, wk}, GSeg{Lq + ((uint64_t)P.nH + P.nKV + g) * hd / vpw, hd / vpw, wv});
+    for (uint32_t i = lane; i < nh * hd; i += 64u) A.q[i] = wval(wq, i, f32);
+    if (cur)
+        for (uint32_t i = lane; i < hd; i += 64u) {
+            A.kc[i] = wval(wk, i, f32);
+            A.vc[i] = wval(wv, i, f32);
+        }
 }
 
-// Attention epilogue: combine the compute waves' states (weights exp(m_w - M)); a single chunk
-// writes the output rows (rounded once), a split context writes its fp64 partial state
-// (M, L, o) per head, two words per value.
-DEV void io_attn_epilogue(Io& io, const DevTask& T) {
-    const Ctx& c = *io.c;
-    CKP& P = *c.P;
-    const bool f32 = P.act_f32 != 0;
-    const uint32_t vpw = f32 ? 1u : 2u;
-    const uint32_t h0 = T.arg[0], nh = T.arg[1], ch = T.arg[2], nc = T.arg[3], hd = (uint32_t)P.hd;
+// Attention epilogue, on every wave of the workgroup: combine the compute waves' states (weights
+// exp(m_w - M)) per (head, pair of dimensions), one pair a thread. A single chunk yields the
+// output words (rounded once); a split context yields its fp64 partial state (M, L, o) per head.
+// The results go to the row buffer in LDS; the I/O wave publishes them (attn_publish).
+// Thread tid: head tid / (hd / 2), dimensions 2 (tid mod hd / 2) and the next.
+DEV void attn_combine(const Ctx& c, const DevTask& T, uint32_t tid, bool f32) {
+    const uint32_t nh = T.arg[1], nc = T.arg[3], hd = T.k / (f32 ? 4u : 2u);
     const AttnStage A = attn_stage(c.L, nh, hd);
-    const uint32_t lane = (uint32_t)lane_id();
-    const uint32_t st = hd + 2;
-    const uint32_t flag = io.flag;
-    for (uint32_t h = 0; h < nh; ++h) {
-        double fw[kCompWaves];
-        double M = -INFINITY;
+    const uint32_t st = hd + 2, per = hd / 2;
+    if (tid >= nh * per) return;
+    const uint32_t h = tid / per, d = 2 * (tid % per);
+    double fw[kCompWaves];
+    double M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kCompWaves; ++w) M = fmax(M, A.st[(w * nh + h) * st]);
-        double Ls = 0.0;
+    for (int w = 0; w < kCompWaves; ++w) M = fmax(M, lds_ld64(A.st + (w * nh + h) * st));
+    double Ls = 0.0, o0 = 0.0, o1 = 0.0;
 #pragma unroll
-        for (int w = 0; w < kCompWaves; ++w) {
-            const double mw = A.st[(w * nh + h) * st];
-            fw[w] = mw == -INFINITY ? 0.0 : exp(mw - M);
-            Ls = fma(fw[w], A.st[(w * nh + h) * st + 1], Ls);
-        }
-        if (nc == 1) {
-            u64* out = (u64*)ll_layer(P, io.y, T.layer) + io.y.o + (uint64_t)(h0 + h) * hd / vpw;
-            for (uint32_t i = lane; i < hd / vpw; i += 64u) {
-                double v[2] = {0.0, 0.0};
-                for (uint32_t j = 0; j < vpw; ++j) {
-                    const uint32_t d = i * vpw + j;
-                    double os = 0.0;
-#pragma unroll
-                    for (int w = 0; w < kCompWaves; ++w) os = fma(fw[w], A.st[(w * nh + h) * st + 2 + d], os);
-                    v[j] = os / Ls;
-                }
-                ll_store(out + i, pack2(f32, v[0], v[1]), flag);
-            }
+    for (int w = 0; w < kCompWaves; ++w) {
+        const double* sw = A.st + (w * nh + h) * st;
+        const double mw = lds_ld64(sw);
+        fw[w] = mw == -INFINITY ? 0.0 : exp(mw - M);
+        Ls = fma(fw[w], lds_ld64(sw + 1), Ls);
+        o0 = fma(fw[w], lds_ld64(sw + 2 + d), o0);
+        o1 = fma(fw[w], lds_ld64(sw + 3 + d), o1);
+    }
+    if (nc == 1) {   // output payloads: one word per value pair (bf16) or per value (fp32)
+        uint32_t* out = (uint32_t*)c.L.red;
+        if (f32) {
+            lds_st32(out + h * hd + d, act_bits(o0 / Ls, true));
+            lds_st32(out + h * hd + d + 1, act_bits(o1 / Ls, true));
         } else {
-            u64* part = (u64*)ll_layer(P, io.y, T.layer) + io.y.part + 2ull * ((uint64_t)(h0 + h) * nc + ch) * st;
-            for (uint32_t k = lane; k < st; k += 64u) {
-                double v;
-                if (k == 0) {
-                    v = M;
-                } else if (k == 1) {
-                    v = Ls;
-                } else {
-                    v = 0.0;
-#pragma unroll
-                    for (int w = 0; w < kCompWaves; ++w) v = fma(fw[w], A.st[(w * nh + h) * st + k], v);
-                }
-                const uint64_t b = (uint64_t)__double_as_longlong(v);
-                ll_store(part + 2 * k, (uint32_t)b, flag);
-                ll_store(part + 2 * k + 1, (uint32_t)(b >> 32), flag);
-            }
+            lds_st32(out + (h * hd + d) / 2, act_bits(o0 / Ls, false) | (act_bits(o1 / Ls, false) << 16));
         }
+    } else {   // the partial state, fp64: [h][M, L, o...]
+        double* ps = c.L.red + h * st;
+        if (d == 0) { lds_st64(ps, M); lds_st64(ps + 1, Ls); }
+        lds_st64(ps + 2 + d, o0);
+        lds_st64(ps + 3 + d, o1);
     }
 }
 
-// Merge of the context chunks of query heads [h0, h0+nh): o = sum_c exp(M_c - M) o_c divided by
-// sum_c exp(M_c - M) L_c, M = max_c M_c (the split-context form of the same softmax), in fp64.
-DEV void io_merge(Io& io, const DevTask& T) {
+// The attention task's results from the row buffer to the flag words.
+DEV void attn_publish(Io& io, const DevTask& T) {
     const Ctx& c = *io.c;
     CKP& P = *c.P;
     const bool f32 = P.act_f32 != 0;
     const uint32_t vpw = f32 ? 1u : 2u;
-    const uint32_t h0 = T.arg[0], nh = T.arg[1], nc = T.arg[3], hd = (uint32_t)P.hd, st = hd + 2;
+    const uint32_t h0 = T.arg[0], nh = T.arg[1], ch = T.arg[2], nc = T.arg[3], hd = (uint32_t)P.hd, st = hd + 2;
     const uint32_t lane = (uint32_t)lane_id();
-    double* S = (double*)c.L.stage;   // [nc][st] of one head
-    for (uint32_t h = 0; h < nh; ++h) {
-        const u64* part = ll_layer(P, io.y, T.layer) + io.y.part + 2ull * (uint64_t)(h0 + h) * nc * st;
-        gather(io, part, 2 * nc * st, [&](uint32_t i, uint32_t pl) { ((uint32_t*)S)[i] = pl; });
-        double M = -INFINITY;
-        for (uint32_t k = lane; k < nc; k += 64u) M = fmax(M, S[k * st]);
-        M = wave_max_f64(M);
-        double Ls = 0.0;
-        for (uint32_t k = lane; k < nc; k += 64u) {
-            const double mk = S[k * st];
-            const double f = mk == -INFINITY ? 0.0 : exp(mk - M);
-            Ls = fma(f, S[k * st + 1], Ls);
-            S[k * st] = f;   // the chunk's weight, over its M
-        }
-        Ls = wave_allsum_f64(Ls);
-        u64* out = (u64*)ll_layer(P, io.y, T.layer) + io.y.o + (uint64_t)(h0 + h) * hd / vpw;
-        for (uint32_t i = lane; i < hd / vpw; i += 64u) {
-            double v[2] = {0.0, 0.0};
-            for (uint32_t j = 0; j < vpw; ++j) {
-                const uint32_t d = i * vpw + j;
-                double os = 0.0;
-                for (uint32_t k = 0; k < nc; ++k) os = fma(S[k * st], S[k * st + 2 + d], os);
-                v[j] = os / Ls;
-            }
-            ll_store(out + i, pack2(f32, v[0], v[1]), io.flag);
+    if (nc == 1) {
+        const uint32_t* src = (const uint32_t*)c.L.red;
+        u64* out = P.ll + T.dst + (uint64_t)h0 * hd / vpw;
+        for (uint32_t i = lane; i < nh * hd / vpw; i += 64u) ll_store(out + i, src[i], io.flag);
+    } else {
+        for (uint32_t h = 0; h < nh; ++h) {
+            u64* part = P.ll + T.dst + 2ull * ((uint64_t)(h0 + h) * nc + ch) * st;
+            const uint32_t* src = (const uint32_t*)(c.L.red + h * st);
+            for (uint32_t k = lane; k < 2 * st; k += 64u) ll_store(part + k, src[k], io.flag);
         }
     }
+}
+
+// Merge of the context chunks of query heads [h0, h0+nh), on every wave of the workgroup:
+// o = sum_c exp(M_c - M) o_c divided by sum_c exp(M_c - M) L_c, M = max_c M_c (the
+// split-context form of the same softmax), in fp64. The chunk states were gathered as words
+// (two per fp64 value). First the chunk weights, one (head, chunk) a thread, into LDS; a
+// barrier; then one (head, pair of dimensions) a thread, into the row buffer (published by the
+// I/O wave). Every wave runs the barrier.
+DEV void merge_compute(const Ctx& c, const DevTask& T, uint32_t tid, bool f32) {
+    const uint32_t nh = T.arg[1], nc = T.arg[3], hd = T.k / (f32 ? 4u : 2u), st = hd + 2, per = hd / 2;
+    const uint8_t* words = c.L.stage;
+    double* f = (double*)(c.L.stage + merge_weights_off(nh, nc, hd));   // [nh][nc]
+    for (uint32_t i = tid; i < nh * nc; i += 512u) {
+        const uint32_t h = i / nc, k = i % nc, hb = h * nc * st;
+        double M = -INFINITY;
+        for (uint32_t j = 0; j < nc; ++j) M = fmax(M, wdbl(words, hb + j * st));
+        const double mk = wdbl(words, hb + k * st);
+        lds_st64(f + i, mk == -INFINITY ? 0.0 : exp(mk - M));
+    }
+    bar();
+    if (tid < nh * per) {
+        const uint32_t h = tid / per, d = 2 * (tid % per), hb = h * nc * st;
+        double Ls = 0.0, o0 = 0.0, o1 = 0.0;
+        for (uint32_t k = 0; k < nc; ++k) {
+            const double fk = lds_ld64(f + h * nc + k);
+            Ls = fma(fk, wdbl(words, hb + k * st + 1), Ls);
+            o0 = fma(fk, wdbl(words, hb + k * st + 2 + d), o0);
+            o1 = fma(fk, wdbl(words, hb + k * st + 3 + d), o1);
+        }
+        uint32_t* out = (uint32_t*)c.L.red;
+        if (f32) {
+            lds_st32(out + h * hd + d, act_bits(o0 / Ls, true));
+            lds_st32(out + h * hd + d + 1, act_bits(o1 / Ls, true));
+        } else {
+            lds_st32(out + (h * hd + d) / 2, act_bits(o0 / Ls, false) | (act_bits(o1 / Ls, false) << 16));
+        }
+    }
+}
+
+// The merge's outputs from the row buffer to the flag words.
+DEV void merge_publish(Io& io, const DevTask& T) {
+    const Ctx& c = *io.c;
+    CKP& P = *c.P;
+    const uint32_t vpw = P.act_f32 ? 1u : 2u;
+    const uint32_t h0 = T.arg[0], nh = T.arg[1], hd = (uint32_t)P.hd;
+    const uint32_t* src = (const uint32_t*)c.L.red;
+    u64* out = P.ll + T.dst + (uint64_t)h0 * hd / vpw;
+    for (uint32_t i = (uint32_t)lane_id(); i < nh * hd / vpw; i += 64u) ll_store(out + i, src[i], io.flag);
+}
+
+// The merge's chunk states, gathered before the workgroup's barrier.
+DEV void io_merge_inputs(Io& io, const DevTask& T) {
+    const Ctx& c = *io.c;
+    CKP& P = *c.P;
+    const uint32_t h0 = T.arg[0], nh = T.arg[1], nc = T.arg[3], st = (uint32_t)P.hd + 2;
+    gather(io, 1, GSeg{P.ll + T.src + 2ull * (uint64_t)h0 * nc * st, 2u * nh * nc * st, c.L.stage});
 }
 
 // The greedy token: the argmax over the LM tiles' (max, index) pairs, lowest index among equal
@@ -1198,14 +1290,14 @@ DEV void io_argmax(Io& io, const DevTask& T) {
     const Ctx& c = *io.c;
     CKP& P = *c.P;
     const uint32_t nt = T.arg[2];
-    uint32_t* S = (uint32_t*)c.L.stage;
-    gather(io, P.ll + io.y.lmpart, 2 * nt, [&](uint32_t i, uint32_t pl) { S[i] = pl; });
+    uint8_t* words = c.L.stage;
+    gather(io, 1, GSeg{P.ll + T.src, 2u * nt, words});
     float best = -INFINITY;
     int bi = 0x7fffffff;
     bool bad = false;
     for (uint32_t t = (uint32_t)lane_id(); t < nt; t += 64u) {
-        const float v = __uint_as_float(S[2 * t]);
-        const int i = (int)S[2 * t + 1];
+        const float v = __uint_as_float(wpl(words, 2u * t));
+        const int i = (int)wpl(words, 2u * t + 1u);
         if (i < 0) bad = true;
         else if (v > best || (v == best && i < bi)) { best = v; bi = i; }
     }
@@ -1220,10 +1312,11 @@ DEV void io_argmax(Io& io, const DevTask& T) {
 
 // ------------------------------------------------------------------ the two roles
 
-// Per task, every wave runs four barriers: A1 (inputs staged by the I/O wave), A1b (inside the
-// GEMV staging, between its reads and its writes; a lone barrier for other tasks), A2 (planes
-// written), then the compute, and B (results in LDS); then the I/O wave writes the outputs while
-// the compute waves go on to the next task's A1.
+// Per task, every wave runs the same barriers: A1 (inputs gathered by the I/O wave), A1b (inside
+// the GEMV staging, between its reads and its writes; a lone barrier for other tasks), A2 (planes
+// written), then the compute (a merge has one more barrier inside), and B (results in LDS); an
+// attention task then combines the waves' states on every wave and has barrier C. The I/O wave
+// then writes the outputs while the compute waves go on to the next task's A1.
 template <int FMT>
 DEV void io_run(const Ctx& c0) {
     Io io;
@@ -1245,21 +1338,18 @@ DEV void io_run(const Ctx& c0) {
         asm volatile("" : "+s"(c.P));
         CKP& P = *c.P;
         io.c = &c;
-        io.y = ll_layout(P.H, P.L, P.nH, P.nKV, P.hd, P.I, P.act_f32, P.nchunks, P.lm_tiles);
         const DevTask T = task_at(c, t);
         io.tr = P.trace ? P.trace + (uint64_t)t * kTraceSlots : nullptr;
         mark(io, 0);
         const bool gemv = is_gemv_op(T.op);
         if (gemv) {
-            const uint32_t K = gemv_K(P, T.op);
-            const int ni = norm_of(P, T);
-            if (ni >= 0) io_gains(io, ni, K);
-            if (T.op == AMK_OP_OPROJ || T.op == AMK_OP_DOWN) io_resid(io, T);
-            io_input(io, io_src(io, T), K);
+            const uint32_t K = T.k;
+            if (T.norm >= 0) io_gains(io, T.norm, K, n_planes(FMT) * plane_stride(FMT, K));
+            io_gemv_inputs(io, T, raw_off<FMT>(K, T.norm >= 0));
         } else if (T.op == AMK_OP_ATTN) {
             io_attn_inputs(io, T);
         } else if (T.op == AMK_OP_MERGE) {
-            io_merge(io, T);
+            io_merge_inputs(io, T);
         } else {
             io_argmax(io, T);
         }
@@ -1268,11 +1358,17 @@ DEV void io_run(const Ctx& c0) {
         else bar();
         bar();                                   // A2
         mark(io, 1);
+        if (T.op == AMK_OP_MERGE) merge_compute(c, T, (uint32_t)tid, FMT == AMK_F32);
         bar();                                   // B
         mark(io, 2);
         if (io.tr && lane_id() == 0) io.tr[4] = c.L.misc->t_rows;
+        if (T.op == AMK_OP_ATTN) {
+            attn_combine(c, T, (uint32_t)tid, FMT == AMK_F32);
+            bar();                               // C: the combined results are in the row buffer
+        }
         if (gemv) io_gemv_epilogue(io, T);
-        else if (T.op == AMK_OP_ATTN) io_attn_epilogue(io, T);
+        else if (T.op == AMK_OP_ATTN) attn_publish(io, T);
+        else if (T.op == AMK_OP_MERGE) merge_publish(io, T);
         mark(io, 5);
         mark(io, 3);
     }
@@ -1295,10 +1391,19 @@ DEV void comp_run(const Ctx& c0, uint32_t w) {
         if (gemv) S = stage_input<FMT>(c, T, tid);
         else bar();
         bar();                                   // A2
-        if (gemv) gemv_compute<FMT, R>(c, ring, T, w, S);
-        else if (T.op == AMK_OP_ATTN) attn_compute<R>(c, ring, T, w);
+        if (gemv) gemv_compute<FMT, R>(c, ring, T, t, w, S);
+        else if (T.op == AMK_OP_ATTN) attn_compute<FMT>(c, ring, T, t, w);
+        else if (T.op == AMK_OP_MERGE) merge_compute(c, T, (uint32_t)tid, FMT == AMK_F32);
         if (w == 0 && P.trace && lane_id() == 0) c.L.misc->t_rows = rt();
         bar();                                   // B
+        if (T.op == AMK_OP_ATTN) {
+            attn_combine(c, T, (uint32_t)tid, FMT == AMK_F32);
+            bar();                               // C
+        }
+        // the lookahead: refill every free slot from the rest of the queue while the I/O wave
+        // writes this task's outputs and gathers the next inputs (a load issued into a busy
+        // memory system waits at issue; here that wait is off the task's critical path)
+        ring_refill(c, ring, w, c0.q1);
     }
     // every ring load has landed before the workgroup leaves
     __builtin_amdgcn_s_waitcnt(0);
@@ -1320,6 +1425,8 @@ DEV void megakernel_body() {
     c.cu = blockIdx.x;
     CKP& P = *c.P;
     c.deadline = rt() + P.watchdog_ticks;
+    c.pos = P.pos;
+    c.eps = P.eps;
     c.wcu = P.wstream + *CONST4(uint64_t, P.cu_stream_off + blockIdx.x);
     c.q0 = *CONST4(uint32_t, P.queue_off + blockIdx.x);
     c.q1 = *CONST4(uint32_t, P.queue_off + blockIdx.x + 1);

@@ -2,7 +2,10 @@
 // lowering of a model shape: every load of every compute wave of every CU stays inside that CU's
 // weight stream (GEMV) or inside the KV cache rows [0, pos) of its chunk's group (attention);
 // the loads of each task come in the order and number the consumer takes them; every byte of
-// every weight row a wave owns is loaded exactly once by the lane that consumes it.
+// every weight row a wave owns is loaded exactly once by the lane that consumes it; the issue
+// side's incremental cursor yields the same loads, lane by lane; and the ring protocol replayed
+// per wave (takes, refills from the current task, lookahead refills after it) always finds the
+// expected loads in the slots it takes.
 //
 //   ring_check H L nH nKV hd I V max_ctx wfmt pos [n_cu]     -> prints "ok <loads>" or a failure
 #include <cstdio>
@@ -86,6 +89,24 @@ int main(int argc, char** argv) {
                     ++n;
                 }
                 if (n != tl.n) return fail("load count of a task differs from what the consumer takes");
+                // the issue side's cursor yields the same loads, lane by lane
+                {
+                    Cursor cur;
+                    cursor_open(P, T, w, cur);
+                    if (cur.left != tl.n) return fail("cursor load count differs");
+                    if (tl.kind == 2 && tl.vofs - tl.kofs >= (1ull << 32)) return fail("K-to-V distance does not fit 32 bits");
+                    LoadPos rp;
+                    pos_reset(tl, rp);
+                    Load rl;
+                    while (cur.left) {
+                        if (!pos_next(tl, rp, w, &rl)) return fail("cursor yields more loads than the reference");
+                        const CLoad cl = cursor_next(cur);
+                        for (uint32_t lane = 0; lane < 64; ++lane)
+                            if (cl.base + cursor_lane_off(cur, cl, lane) != rl.base + load_lane_off(tl, rl, lane))
+                                return fail("cursor load differs from the reference sequence");
+                    }
+                    if (pos_next(tl, rp, w, &rl)) return fail("cursor yields fewer loads than the reference");
+                }
                 // the scale reads of the wave's rows (scalar dword loads): inside the tile's scale block
                 if (tl.kind == 1 && (d.wfmt == AMK_INT8_PC || d.wfmt == AMK_INT4_G128)) {
                     const uint32_t K = gemv_K(P, T.op);
@@ -123,6 +144,68 @@ int main(int argc, char** argv) {
                     if (covered != want) return fail("GEMV rows not covered exactly once");
                 }
                 total += n;
+            }
+        }
+    }
+    // The ring protocol of each compute wave, replayed: R slots; a task's compute takes its loads
+    // in consumer order (GEMV: per group of up to 4 rows, per chunk, the group's rows; attention:
+    // per block, K then V) and after each take refills only from its own queue entry; after the
+    // task, every free slot is refilled from the rest of the queue. Each take must find its slots
+    // holding issued loads (at least n of the R - pending in flight) and exactly the loads the
+    // consumer expects, in order.
+    const int R = ring_slots(d.wfmt);
+    for (int cu = 0; cu < Lw.n_cu; ++cu) {
+        for (uint32_t w = 0; w < (uint32_t)kCompWaves; ++w) {
+            const uint32_t q0 = Lw.dqueue_off[cu], q1 = Lw.dqueue_off[cu + 1];
+            std::vector<std::pair<uint32_t, uint32_t>> slot(R, {~0u, 0});   // (task, load index) held
+            uint32_t head = 0, pending = (uint32_t)R;
+            Cursor cur;
+            cur.t = q0; cur.kind = 0; cur.left = 0;
+            uint32_t cur_task = ~0u, cur_k = 0;   // the cursor's open task and its next load index
+            auto issue = [&](uint32_t limit) {
+                while (cur.left == 0 && cur.t < limit) {
+                    cursor_open(P, Lw.dtasks[cur.t], w, cur);
+                    cur_task = cur.t;
+                    cur_k = 0;
+                    cur.t++;
+                }
+                if (!cur.left) return false;
+                (void)cursor_next(cur);
+                const uint32_t sidx = (head + (uint32_t)R - pending) % (uint32_t)R;
+                slot[sidx] = {cur_task, cur_k++};
+                --pending;
+                return true;
+            };
+            auto refill = [&](uint32_t limit) { while (pending && issue(limit)) {} };
+            refill(q1);
+            for (uint32_t t = q0; t < q1; ++t) {
+                const DevTask& T = Lw.dtasks[t];
+                const TaskLoads tl = task_loads(P, T, w);
+                uint32_t k = 0;   // consumer's next load index in this task
+                auto take = [&](uint32_t n) -> bool {
+                    if ((uint32_t)R - pending < n) return false;
+                    for (uint32_t i = 0; i < n; ++i) {
+                        const auto& e = slot[(head + i) % (uint32_t)R];
+                        if (e.first != t || e.second != k + i) return false;
+                    }
+                    head = (head + n) % (uint32_t)R;
+                    pending += n;
+                    k += n;
+                    refill(t + 1);
+                    return true;
+                };
+                if (tl.kind == 1) {
+                    for (uint32_t gi = 0; 4 * gi < tl.m; ++gi) {
+                        const uint32_t gs = tl.m - 4 * gi < 4 ? tl.m - 4 * gi : 4;
+                        for (uint32_t j = 0; j < tl.nj; ++j)
+                            if (!take(gs)) return fail("ring take finds other loads than the GEMV expects");
+                    }
+                } else if (tl.kind == 2) {
+                    for (uint32_t bi = 0; bi < tl.nbw; ++bi)
+                        if (!take(2)) return fail("ring take finds other loads than the attention expects");
+                }
+                if (k != tl.n) return fail("consumer took another number of loads than the task has");
+                refill(q1);
             }
         }
     }
