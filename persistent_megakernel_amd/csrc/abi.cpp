@@ -31,9 +31,7 @@ struct amk_ctx {
     unsigned long long* d_ll = nullptr;
     void* d_embed = nullptr;
     float* d_norms = nullptr;
-    float* d_rope = nullptr;        // fp32 (cos, sin) table of the prefill
-    double* d_rope64 = nullptr;     // fp64 (cos, sin) table of the decode step
-    float* d_gmax = nullptr;        // largest |gain| of each norm
+    float* d_rope = nullptr;
     uint32_t* h_status = nullptr;   // host-mapped, written by the device
     uint32_t* d_status = nullptr;   // device alias of h_status
     uint32_t* d_abort = nullptr;
@@ -106,8 +104,6 @@ void free_ctx(amk_ctx* c) {
     (void)hipFree(c->d_embed);
     (void)hipFree(c->d_norms);
     (void)hipFree(c->d_rope);
-    (void)hipFree(c->d_rope64);
-    (void)hipFree(c->d_gmax);
     (void)hipFree(c->d_abort);
     if (c->h_status) (void)hipHostFree(c->h_status);
     delete c;
@@ -197,6 +193,7 @@ extern "C" amk_status amk_create(const amk_model_desc* desc, const amk_weights* 
     hipError_t e = hipSuccess;
     auto ck = [&](hipError_t r) { if (e == hipSuccess) e = r; };
     ck(hipMalloc((void**)&c->d_wstream, wbytes ? wbytes : 256));
+    ck(upload(&c->d_tasks, c->L.dtasks, stream));
     ck(upload(&c->d_qoff, c->L.dqueue_off, stream));
     ck(upload(&c->d_cuoff, c->L.cu_stream_off, stream));
     c->ll_words = y.total;
@@ -219,39 +216,19 @@ extern "C" amk_status amk_create(const amk_model_desc* desc, const amk_weights* 
         ck(launch_norms(w->mlp_norm[l], d.wfmt, d.hidden, c->d_norms + (size_t)(2 * l + 1) * d.hidden, stream));
     }
     ck(launch_norms(w->final_norm, d.wfmt, d.hidden, c->d_norms + (size_t)2 * d.n_layers * d.hidden, stream));
-    // RoPE tables: angle pos * theta^(-2i/hd), cos and sin evaluated in double; the decode step
-    // uses them in double, the prefill rounded to fp32
+    // RoPE table in fp32, angles evaluated in double: pos * theta^(-2i/hd)
     {
         const int half = d.head_dim / 2;
         std::vector<float> rope((size_t)d.max_ctx * half * 2);
-        std::vector<double> rope64((size_t)d.max_ctx * half * 2);
         for (int p = 0; p < d.max_ctx; ++p)
             for (int i = 0; i < half; ++i) {
-                const double inv = std::pow((double)d.rope_theta, -2.0 * (double)i / (double)d.head_dim);
+                const double inv = std::pow((double)d.rope_theta, -2.0 * i / d.head_dim);
                 const double a = (double)p * inv;
-                const size_t k = ((size_t)p * half + i) * 2;
-                rope64[k] = std::cos(a);
-                rope64[k + 1] = std::sin(a);
-                rope[k] = (float)rope64[k];
-                rope[k + 1] = (float)rope64[k + 1];
+                rope[((size_t)p * half + i) * 2] = (float)std::cos(a);
+                rope[((size_t)p * half + i) * 2 + 1] = (float)std::sin(a);
             }
         ck(upload(&c->d_rope, rope, stream));
-        ck(upload(&c->d_rope64, rope64, stream));
-        ck(hipStreamSynchronize(stream));   // the host vectors die here
-    }
-    // the largest |gain| of each norm (bounds the normalised input of the fixed-point GEMV)
-    {
-        const size_t nn = (size_t)2 * d.n_layers + 1;
-        std::vector<float> norms(nn * d.hidden), gmax(nn, 0.f);
-        ck(hipMemcpy(norms.data(), c->d_norms, norms.size() * sizeof(float), hipMemcpyDeviceToHost));
-        for (size_t n = 0; n < nn; ++n)
-            for (int i = 0; i < d.hidden; ++i) gmax[n] = std::max(gmax[n], std::fabs(norms[n * d.hidden + i]));
-        ck(upload(&c->d_gmax, gmax, stream));
-        // each GEMV task's descriptor carries the bound of its own norm
-        for (DevTask& t : c->L.dtasks)
-            if (t.norm >= 0 && (size_t)t.norm < nn) t.gmax = gmax[(size_t)t.norm];
-        ck(upload(&c->d_tasks, c->L.dtasks, stream));
-        ck(hipStreamSynchronize(stream));
+        ck(hipStreamSynchronize(stream));   // the host vector dies here
     }
     // repack / quantise the weights into the per-CU streams
     {
@@ -330,8 +307,8 @@ extern "C" amk_status amk_create(const amk_model_desc* desc, const amk_weights* 
     std::memset(&P, 0, sizeof(P));
     P.H = d.hidden; P.L = d.n_layers; P.nH = d.n_heads; P.nKV = d.n_kv_heads; P.hd = d.head_dim; P.I = d.intermediate;
     P.V = d.vocab; P.max_ctx = d.max_ctx; P.wfmt = d.wfmt; P.act_f32 = d.act_f32;
-    P.eps = (double)d.rms_eps;
-    P.attn_scale = 1.0 / std::sqrt((double)d.head_dim);
+    P.eps = d.rms_eps;
+    P.attn_scale = (float)(1.0 / std::sqrt((double)d.head_dim));
     P.nchunks = c->L.nchunks;
     P.lm_tiles = c->L.lm_tiles;
     P.tasks = c->d_tasks;
@@ -342,8 +319,7 @@ extern "C" amk_status amk_create(const amk_model_desc* desc, const amk_weights* 
     P.kv = kv_cache;
     P.embed = c->d_embed;
     P.norms = c->d_norms;
-    P.rope = c->d_rope64;
-    P.gmax = c->d_gmax;
+    P.rope = c->d_rope;
     P.status = c->d_status;
     P.abort_flag = c->d_abort;
     P.watchdog_ticks = watchdog_ticks();

@@ -13,97 +13,51 @@
 
 namespace amk {
 
-// Workgroup: one per CU, 8 waves. Waves 0..6 are compute waves: they stream the weight tiles
-// and attention K/V rows of their CU's queue through per-wave LDS rings (direct memory-to-LDS
-// loads, issued ahead across task boundaries) and do the dot products. Wave 7 is the I/O wave:
-// every other global access (polls of flag-carrying words, epilogue stores, gains, residual
-// rows, the embedding row) is its, so no poll ever waits behind a weight load.
+// Workgroup: one per CU, 8 waves, all of which walk the task queue. Every wave streams the
+// weight rows it owns straight into registers (no loader wave, no LDS staging of weights).
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
-constexpr int kCompWaves = 7;
-constexpr int kIoWave = 7;
+constexpr int kComputeWaves = kWaves;
+constexpr int kComputeThreads = kThreads;
 
-// LDS budget (bytes): the rings, the per-task row results (fp64), a small control area, and the
-// stage (the GEMV input as digit planes or fp32 values, or attention / merge state).
+// LDS budget (bytes): input-vector stage, attention K/V staging, row results, attention state,
+// task cache, control.
 constexpr int kLdsTotal = 160 * 1024;
-constexpr int kRedRows = 1024;              // row results per task (fp64)
-constexpr int kMiscBytes = 8 * 1024;        // statistics, residual rows, combination weights
+constexpr int kHBytes = 32 * 1024;          // input vector stage (fp32 up to 8192, or 16-bit up to 16384 values)
+constexpr int kKvBytes = 64 * 1024;         // attention: K and V rows of the positions being processed; int4 scales
+constexpr int kRedRows = 1024;              // row results per task
+constexpr int kAttnLds = 8 * 1024;          // attention: q, current k/v, combination weights; residual rows
+constexpr int kTaskCache = 256;             // task descriptors of a CU's queue kept in LDS (32 bytes each)
+#ifndef AMK_LOAD_SLOTS
+#define AMK_LOAD_SLOTS 6
+#endif
+#ifndef AMK_AHEAD_GROUPS
+#define AMK_AHEAD_GROUPS 1
+#endif
+constexpr int kLoadSlots = AMK_LOAD_SLOTS;  // 1 KiB (16 B per lane) weight loads per register buffer (2 buffers per wave)
+constexpr int kAheadGroups = AMK_AHEAD_GROUPS;   // groups of the next task's weights issued ahead (0, 1 or 2)
+static_assert(kAheadGroups >= 0 && kAheadGroups <= 2, "prefetch depth");
+constexpr int kAttnBlock = 64;              // positions per attention unit
 constexpr int kMaxAttnHeads = 8;            // query heads per attention task
 constexpr int kChunkedCtx = 256;            // caches at least this long get context-split attention by default
-// Ring slots (1 KiB loads) per compute wave: fewer for int4, whose digit planes are the largest.
-AMK_HD constexpr int ring_slots(int wfmt) { return wfmt == AMK_INT4_G128 ? 8 : 12; }
-AMK_HD constexpr int stage_bytes(int wfmt) {
-    return kLdsTotal - kCompWaves * ring_slots(wfmt) * 1024 - kRedRows * 8 - kMiscBytes;
-}
-AMK_HD constexpr uint32_t round_up_u(uint32_t x, uint32_t m) { return (x + m - 1) / m * m; }
-// Stage bytes a K-wide GEMV input needs. Quantised weights: the input in fixed point as signed
-// digit planes (int8: 5 byte planes of K bytes; int4: 10 nibble planes of K/2 bytes), padded to
-// whole 1 KiB chunks. fp32/bf16 weights: the input as fp32 values, padded to whole chunks.
-AMK_HD inline uint32_t plane_stride(int wfmt, uint32_t K) {
-    switch (wfmt) {
-    case AMK_F32: return 4 * round_up_u(K, 256);
-    case AMK_BF16: return 4 * round_up_u(K, 512);
-    case AMK_INT8_PC: return round_up_u(K, 1024);
-    default: return round_up_u(K / 2, 1024);
-    }
-}
-AMK_HD inline uint32_t n_planes(int wfmt) { return wfmt == AMK_INT8_PC ? 5u : wfmt == AMK_INT4_G128 ? 10u : 1u; }
-AMK_HD inline uint64_t gemv_stage_need(int wfmt, uint32_t K, bool norm) {
-    return (uint64_t)n_planes(wfmt) * plane_stride(wfmt, K) + (norm ? 4ull * K : 0ull);   // + fp32 gains
-}
-// Attention task stage: q and the current k, v (fp64), the per-wave states (m, l, o) in fp64,
-// and each compute wave's copy of its current K and V slots.
-AMK_HD inline uint64_t attn_stage_need(uint32_t nh, uint32_t hd) {
-    return 8ull * ((uint64_t)nh * hd + 2ull * hd) + 8ull * kCompWaves * nh * (hd + 2) + (uint64_t)kCompWaves * 2048;
-}
-// Gathered flag words land in LDS in 1 KiB blocks of 128 words; one gather polls at most
-// kMaxGatherBlocks blocks.
-constexpr uint32_t kMaxGatherBlocks = 64;
-AMK_HD inline uint32_t gather_blocks(uint64_t words) { return (uint32_t)((words + 127) / 128); }
-// Attention task: the gathered q (and current k, v) words go past the attention stage.
-AMK_HD inline uint32_t attn_words_off(uint32_t nh, uint32_t hd) { return round_up_u((uint32_t)attn_stage_need(nh, hd), 1024u); }
-AMK_HD inline uint64_t attn_stage_total(uint32_t nh, uint32_t hd, uint32_t vpw) {
-    return attn_words_off(nh, hd) + 1024ull * (gather_blocks((uint64_t)nh * hd / vpw) + 2ull * gather_blocks(hd / vpw));
-}
-// Merge task: every chunk state of its heads gathered as words (two per fp64 value), then the
-// chunk weights of every head (fp64).
-AMK_HD inline uint64_t merge_state_words(uint32_t nh, uint32_t nc, uint32_t hd) { return 2ull * nh * nc * (hd + 2); }
-AMK_HD inline uint32_t merge_weights_off(uint32_t nh, uint32_t nc, uint32_t hd) {
-    return 1024u * gather_blocks(merge_state_words(nh, nc, hd));
-}
-AMK_HD inline uint64_t merge_stage_need(uint32_t nh, uint32_t nc, uint32_t hd) { return merge_weights_off(nh, nc, hd) + 8ull * nh * nc; }
-// Residual words of an O or down task (flag words as gathered, in the control area).
-constexpr uint32_t kResidWords = 512;
-
-// Limits the kernel supports (checked at create).
-constexpr int kMaxHidden = 8192;
-constexpr int kMaxInter = 16384;
-constexpr int kMaxCtx = 1 << 22;
-constexpr int kMaxChunks = 512;            // context chunks of one attention group
+constexpr int64_t kStageFloats = kHBytes / 4;   // fp32 values the input-vector stage holds
 // Flag-carrying words in the static per-device array of the allocation-free decode entry point
 // (64 MiB): a step whose layout needs more is refused.
 constexpr uint64_t kScratchWords = 8ull << 20;
 
-// Device task descriptor (64 bytes): the task, and the geometry its kernels would otherwise
-// derive from the model shape on every task (set by the lowering, gmax by amk_create).
-constexpr uint32_t kNoWord = 0xffffffffu;   // src / aux: the embedding row instead of a flag-word buffer
+// Limits the kernel supports (checked at create).
+constexpr int kMaxHidden = 8192;
+constexpr int kMaxInter = 16384;
+
+// Device task descriptor (32 bytes).
 struct DevTask {
     uint16_t op;
     uint16_t layer;
     uint32_t arg[4];
     uint32_t tile_rows;      // rows in the weight tile (GEMV ops)
-    uint64_t wofs;           // GEMV: byte offset of the tile inside this CU's weight stream;
-                             // attention: byte offset in the cache of (layer, K rows, KV group, row 0)
-    uint32_t k;              // GEMV: input width K; attention and merge: cache row bytes
-    uint32_t pitch;          // GEMV: bytes per weight row; attention: cache rows per 1 KiB load
-    uint32_t nj;             // GEMV: 1 KiB loads per weight row; attention: bytes from the K rows to the V rows
-    int32_t norm;            // GEMV: index of the RMSNorm on its input (-1: none)
-    float gmax;              // GEMV: the largest |gain| of that norm
-    uint32_t src;            // flag-word offset of the task's input (kNoWord: the embedding row)
-    uint32_t dst;            // flag-word offset of the task's output
-    uint32_t aux;            // flag-word offset of the residual (O, down; kNoWord: the embedding row)
+    uint64_t wofs;           // byte offset of the tile inside this CU's weight stream
 };
-static_assert(sizeof(DevTask) == 64, "DevTask layout");
+static_assert(sizeof(DevTask) == 32, "DevTask layout");
 
 // Weight tile geometry for a GEMV with K inputs in format wfmt. A tile is its rows' codes, row
 // after row (row_pitch bytes each, a multiple of 16), then the scale block: int8 one fp16 scale
@@ -128,8 +82,7 @@ AMK_HD inline uint32_t row_loads(int wfmt, uint32_t K) { return (row_pitch(wfmt,
 
 // Flag-carrying ("LL") buffers: one 8-byte word = 32-bit payload + 32-bit flag; the flag of a
 // word written in launch e is e+1 (never 0). bf16 activations pack 2 values per word; fp32
-// activations hold one value per word; an attention partial state value (fp64) takes two words
-// (low half, high half).
+// activations and attention partial states hold one value per word.
 struct LLLayout {
     uint32_t vpw;            // activation values per word (2 bf16, 1 fp32)
     uint64_t qkv, part, o, xo, a, xd;   // word offsets inside one layer block
@@ -144,7 +97,7 @@ AMK_HD inline LLLayout ll_layout(int H, int L, int nH, int nKV, int hd, int I, i
     y.vpw = act_f32 ? 1 : 2;
     uint64_t off = 0;
     y.qkv = off; off += (uint64_t)(nH + 2 * nKV) * hd / y.vpw;
-    y.part = off; off += nchunks > 1 ? 2ull * nH * nchunks * (hd + 2) : 0;
+    y.part = off; off += nchunks > 1 ? (uint64_t)nH * nchunks * (hd + 2) : 0;
     y.o = off; off += (uint64_t)nH * hd / y.vpw;
     y.xo = off; off += (uint64_t)H / y.vpw;
     y.a = off; off += (uint64_t)I / y.vpw;
@@ -160,7 +113,7 @@ AMK_HD inline LLLayout ll_layout(int H, int L, int nH, int nKV, int hd, int I, i
 struct KParams {
     // shape
     int32_t H, L, nH, nKV, hd, I, V, max_ctx, wfmt, act_f32;
-    double eps, attn_scale;
+    float eps, attn_scale;
     int32_t nchunks, lm_tiles;
     // schedule
     const DevTask* tasks;
@@ -172,8 +125,7 @@ struct KParams {
     void* kv;                        // [L][2][nKV][max_ctx][hd], act type
     const void* embed;               // [V][H], act type
     const float* norms;              // [L][2][H] (attn, mlp) then [H] final, fp32
-    const double* rope;              // [max_ctx][hd/2][2] (cos, sin), fp64
-    const float* gmax;               // [2L + 1]: the largest |gain| of each norm
+    const float* rope;               // [max_ctx][hd/2][2] (cos, sin), fp32
     // step
     const int32_t* tok_in;
     int32_t* tok_out;

@@ -64,33 +64,12 @@ amk_status check_desc(const amk_model_desc* d, std::string* msg) {
         return fail(AMK_E_UNSUPPORTED, "hidden and intermediate sizes must be multiples of 16 (16-byte weight segments)");
     if (d->act_f32 != (d->wfmt == AMK_F32 ? 1 : 0)) return fail(AMK_E_UNSUPPORTED, "fp32 activations go with fp32 weights only");
     const int64_t qd = (int64_t)d->n_heads * d->head_dim;
-    if (d->hidden > kMaxHidden || d->intermediate > kMaxInter || qd > kMaxHidden)
-        return fail(AMK_E_UNSUPPORTED, "dimension beyond the kernel's limits");
-    {   // every GEMV input fits the LDS stage (QKV, gate/up and the LM head carry their norm gains)
-        const uint64_t st = (uint64_t)stage_bytes(d->wfmt);
-        if (gemv_stage_need(d->wfmt, (uint32_t)d->hidden, true) > st || gemv_stage_need(d->wfmt, (uint32_t)qd, false) > st ||
-            gemv_stage_need(d->wfmt, (uint32_t)d->intermediate, false) > st)
-            return fail(AMK_E_UNSUPPORTED, "dimension beyond the kernel's LDS staging limits");
-    }
-    {   // every GEMV input (plus O / down residual words) in one gather; fp32 inputs' words fit the stage
-        const uint32_t vpw = d->act_f32 ? 1u : 2u;
-        for (int64_t K : {(int64_t)d->hidden, (int64_t)d->intermediate, qd})
-            if (gather_blocks((uint64_t)K / vpw) + gather_blocks(kResidWords) > kMaxGatherBlocks)
-                return fail(AMK_E_UNSUPPORTED, "GEMV input beyond one gather");
-        if (d->act_f32) {
-            const uint64_t st = (uint64_t)stage_bytes(d->wfmt);
-            for (int64_t K : {(int64_t)d->hidden, (int64_t)d->intermediate, qd})
-                if ((uint64_t)n_planes(d->wfmt) * plane_stride(d->wfmt, (uint32_t)K) + 4ull * K + 1024ull * gather_blocks((uint64_t)K) > st)
-                    return fail(AMK_E_UNSUPPORTED, "fp32 GEMV input beyond the kernel's LDS staging limits");
-        }
-    }
+    const int64_t kmax = d->act_f32 ? kHBytes / 4 : kHBytes / 2;
+    if (d->hidden > kMaxHidden || d->intermediate > kMaxInter || qd > kMaxHidden || d->hidden > kmax ||
+        d->intermediate > kmax || qd > kmax)
+        return fail(AMK_E_UNSUPPORTED, "dimension beyond the kernel's staging limits");
     if (d->wfmt == AMK_INT4_G128 && (d->hidden % 128 || d->intermediate % 128 || qd % 128))
         return fail(AMK_E_UNSUPPORTED, "int4 g128 needs input sizes that are multiples of 128");
-    // positions and chunk indices multiply in 32 bits; one layer's K block of a KV group is less
-    // than 4 GiB from its V block
-    if (d->max_ctx > kMaxCtx) return fail(AMK_E_UNSUPPORTED, "max_ctx beyond the kernel's limit");
-    if ((uint64_t)d->n_kv_heads * (uint64_t)d->max_ctx * (uint64_t)d->head_dim * (d->act_f32 ? 4u : 2u) >= (1ull << 32))
-        return fail(AMK_E_UNSUPPORTED, "KV cache layer block of 4 GiB or more");
     return AMK_OK;
 }
 
@@ -213,8 +192,7 @@ bool derive_accesses(const Shape& s, const GenTask& t, uint64_t w_off, uint64_t 
         if (!nh || nh > (uint32_t)kMaxAttnHeads || nc != nchunks || c >= nc || h0 + nh > (uint32_t)s.nH) return false;
         const uint32_t g = (uint32_t)((uint64_t)h0 * s.nKV / s.nH);
         if ((uint64_t)(h0 + nh - 1) * s.nKV / s.nH != g) return false;   // one KV group per task
-        if (attn_stage_total(nh, (uint32_t)s.hd, (uint32_t)s.vpw) > (uint64_t)stage_bytes(s.wfmt)) return false;   // states and gathered words in LDS
-        if ((uint64_t)nh * (s.hd + 2) > (uint64_t)kRedRows) return false;   // the combined states fit the row buffer
+        if ((uint64_t)kComputeWaves * nh * (s.hd + 2) > kStageFloats) return false;   // per-wave states in LDS
         {   // dims per lane of the attention lane layout: hd / min(64 / nh rounded up to 2^k, hd) <= 8
             uint32_t nhp = 1;
             while (nhp < nh) nhp <<= 1;
@@ -235,8 +213,7 @@ bool derive_accesses(const Shape& s, const GenTask& t, uint64_t w_off, uint64_t 
     case AMK_OP_MERGE: {
         const uint32_t h0 = t.arg[0], nh = t.arg[1], nc = t.arg[3];
         if (!nh || nh > (uint32_t)kMaxAttnHeads || nc != nchunks || nc < 2 || h0 + nh > (uint32_t)s.nH) return false;
-        if (merge_stage_need(nh, nc, (uint32_t)s.hd) > (uint64_t)stage_bytes(s.wfmt)) return false;   // chunk states in LDS
-        if (gather_blocks(merge_state_words(nh, nc, (uint32_t)s.hd)) > kMaxGatherBlocks) return false;
+        if ((uint64_t)nh * nc * (s.hd + 2) > kStageFloats) return false;   // chunk states staged in LDS
         for (uint32_t h = h0; h < h0 + nh; ++h)
             add_acc(a, s.reg(l, L_PART), 0, (uint64_t)h * nc * (s.hd + 2), (uint64_t)(h + 1) * nc * (s.hd + 2));
         add_acc(a, s.reg(l, L_O), AMK_ACC_WRITE, (uint64_t)h0 * s.hd, (uint64_t)(h0 + nh) * s.hd);
@@ -245,7 +222,6 @@ bool derive_accesses(const Shape& s, const GenTask& t, uint64_t w_off, uint64_t 
     case AMK_OP_OPROJ: {
         const uint64_t r0 = t.arg[0], n = t.arg[1];
         if (!n || r0 + n > H || (r0 % s.vpw) || (n % s.vpw) || n > (uint64_t)kRedRows) return false;
-        if (n / s.vpw > kResidWords) return false;   // residual words in the control area
         add_acc(a, s.reg(l, L_O), 0, 0, qd);
         if (l == 0) {
             add_acc(a, R_TOK_IN, 0, 0, 1);
@@ -269,7 +245,6 @@ bool derive_accesses(const Shape& s, const GenTask& t, uint64_t w_off, uint64_t 
     case AMK_OP_DOWN: {
         const uint64_t r0 = t.arg[0], n = t.arg[1];
         if (!n || r0 + n > H || (r0 % s.vpw) || (n % s.vpw) || n > (uint64_t)kRedRows) return false;
-        if (n / s.vpw > kResidWords) return false;   // residual words in the control area
         add_acc(a, s.reg(l, L_A), 0, 0, (uint64_t)s.I);
         add_acc(a, s.reg(l, L_XO), 0, r0, r0 + n);
         add_acc(a, R_W, 0, w_off, w_off + w_bytes);
@@ -287,8 +262,7 @@ bool derive_accesses(const Shape& s, const GenTask& t, uint64_t w_off, uint64_t 
         return true;
     }
     case AMK_OP_ARGMAX: {
-        if (t.arg[2] != lm_tiles || l != (uint32_t)s.L || 16ull * lm_tiles > (uint64_t)stage_bytes(s.wfmt)) return false;
-        if (gather_blocks(2ull * lm_tiles) > kMaxGatherBlocks) return false;   // the tile pairs in one gather
+        if (t.arg[2] != lm_tiles || l != (uint32_t)s.L || 2ull * lm_tiles > kStageFloats) return false;
         add_acc(a, R_LMPART, 0, 0, 2ull * lm_tiles);
         add_acc(a, R_TOK_OUT, AMK_ACC_WRITE | AMK_ACC_POST, 0, 1);
         return true;
@@ -342,6 +316,8 @@ bool check_plan(const amk_model_desc& d, const Lowered& out, std::string* msg) {
             const uint32_t K = t.op == AMK_OP_OPROJ ? (uint32_t)qd : t.op == AMK_OP_DOWN ? (uint32_t)d.intermediate : (uint32_t)H;
             if (t.wofs + tile_bytes(d.wfmt, K, t.tile_rows) > len) return fail("tile outside its CU stream");
             if (t.wofs % 16) return fail("tile not 16-byte aligned in its CU stream");
+            if (tile_bytes(d.wfmt, K, t.tile_rows) - tile_scale_off(d.wfmt, K, t.tile_rows) > (uint64_t)kKvBytes)
+                return fail("tile whose scales do not fit the LDS scale buffer");
         }
     }
     return true;
@@ -350,79 +326,6 @@ bool check_plan(const amk_model_desc& d, const Lowered& out, std::string* msg) {
 namespace {
 
 // Shared back end: tasks with queues -> IR with accesses, device tables, stream layout.
-// The descriptor fields the kernel would otherwise derive per task: GEMV input width, row
-// pitch, loads per row and norm; attention cache offsets; the flag-word offsets of the task's
-// input, output and residual.
-void fill_geometry(const amk_model_desc& d, const Shape& s, const LLLayout& y, int lm_tiles, DevTask& dt) {
-    const uint32_t l = dt.layer, esz = s.act_f32 ? 4u : 2u;
-    auto ll = [&](uint32_t layer, uint64_t off) { return (uint32_t)(layer * y.layer_words + off); };
-    dt.norm = -1;
-    dt.gmax = 0.f;
-    dt.src = dt.dst = dt.aux = 0;
-    switch (dt.op) {
-    case AMK_OP_QKV: case AMK_OP_OPROJ: case AMK_OP_GATEUP: case AMK_OP_DOWN: case AMK_OP_LM: {
-        const uint32_t K = s.K_of(dt.op);
-        dt.k = K;
-        dt.pitch = row_pitch(s.wfmt, K);
-        dt.nj = row_loads(s.wfmt, K);
-        break;
-    }
-    case AMK_OP_MERGE:
-        dt.k = (uint32_t)s.hd * esz;   // cache row bytes (the head size, as for attention)
-        break;
-    case AMK_OP_ATTN: {
-        const uint32_t g = dt.arg[0] * (uint32_t)s.nKV / (uint32_t)s.nH;
-        const uint64_t blk = (uint64_t)d.max_ctx * s.hd * esz;   // one (layer, K or V, group) block
-        dt.wofs = ((uint64_t)l * 2 * s.nKV + g) * blk;
-        dt.k = (uint32_t)s.hd * esz;
-        dt.pitch = 1024u / dt.k;
-        dt.nj = (uint32_t)(s.nKV * blk);
-        break;
-    }
-    default: break;
-    }
-    switch (dt.op) {
-    case AMK_OP_QKV:
-        dt.norm = 2 * (int)l;
-        dt.src = l == 0 ? kNoWord : ll(l - 1, y.xd);
-        dt.dst = ll(l, y.qkv);
-        break;
-    case AMK_OP_ATTN:
-        dt.src = ll(l, y.qkv);
-        dt.dst = dt.arg[3] > 1 ? ll(l, y.part) : ll(l, y.o);
-        break;
-    case AMK_OP_MERGE:
-        dt.src = ll(l, y.part);
-        dt.dst = ll(l, y.o);
-        break;
-    case AMK_OP_OPROJ:
-        dt.src = ll(l, y.o);
-        dt.dst = ll(l, y.xo);
-        dt.aux = l == 0 ? kNoWord : ll(l - 1, y.xd);
-        break;
-    case AMK_OP_GATEUP:
-        dt.norm = 2 * (int)l + 1;
-        dt.src = ll(l, y.xo);
-        dt.dst = ll(l, y.a);
-        break;
-    case AMK_OP_DOWN:
-        dt.src = ll(l, y.a);
-        dt.dst = ll(l, y.xd);
-        dt.aux = ll(l, y.xo);
-        break;
-    case AMK_OP_LM:
-        dt.norm = 2 * s.L;
-        dt.src = ll((uint32_t)s.L - 1, y.xd);
-        dt.dst = (uint32_t)y.lmpart;
-        break;
-    case AMK_OP_ARGMAX:
-        dt.src = (uint32_t)y.lmpart;
-        break;
-    default: break;
-    }
-    (void)lm_tiles;
-}
-
 amk_status finish(const amk_model_desc& d, const Shape& s, std::vector<GenTask>& tasks, int n_cu, uint32_t n_counters,
                   int lm_tiles, Lowered& out, std::string* msg) {
     // producers per counter, then thresholds "all producers"
@@ -507,11 +410,6 @@ amk_status finish(const amk_model_desc& d, const Shape& s, std::vector<GenTask>&
     h->refresh();
 
     // device tables and repack plan
-    const LLLayout y = ll_layout(s.H, s.L, s.nH, s.nKV, s.hd, s.I, s.act_f32, s.nchunks, lm_tiles);
-    if (y.total >= kNoWord) {
-        if (msg) *msg = "flag-word buffer of 2^32 words or more";
-        return AMK_E_UNSUPPORTED;
-    }
     out.n_cu = n_cu;
     out.nchunks = s.nchunks;
     out.lm_tiles = lm_tiles;
@@ -528,7 +426,6 @@ amk_status finish(const amk_model_desc& d, const Shape& s, std::vector<GenTask>&
             for (int k = 0; k < 4; ++k) dt.arg[k] = t.arg[k];
             dt.tile_rows = tile_rows_of(s, t);
             dt.wofs = wofs[i];
-            fill_geometry(d, s, y, lm_tiles, dt);
             out.dtasks.push_back(dt);
             if (!dt.tile_rows) continue;
             const uint32_t K = s.K_of(t.op), pitch = row_pitch(s.wfmt, K);
@@ -576,23 +473,15 @@ amk_status lower_model(const amk_model_desc& d, const amk_schedule_config* cfg, 
             heads_per_task = h;
         }
     }
-    while (heads_per_task > 1 &&
-           attn_stage_total((uint32_t)heads_per_task, (uint32_t)s.hd, (uint32_t)s.vpw) > (uint64_t)stage_bytes(s.wfmt)) {
+    while (heads_per_task > 1 && (int64_t)kComputeWaves * heads_per_task * (s.hd + 2) > kStageFloats) {
         int h = heads_per_task - 1;
         while (gsz % h) --h;
         heads_per_task = h;
     }
     const int n_head_tasks = nH / heads_per_task;
     // merges run one query head each: a head's chunk states must fit the LDS stage
-    int nc_max = std::min(kMaxChunks, std::max(1, (int)(stage_bytes(s.wfmt) / (16 * (s.hd + 2)))));
-    while (nc_max > 1 && (merge_stage_need(1, (uint32_t)nc_max, (uint32_t)s.hd) > (uint64_t)stage_bytes(s.wfmt) ||
-                          gather_blocks(merge_state_words(1, (uint32_t)nc_max, (uint32_t)s.hd)) > kMaxGatherBlocks))
-        --nc_max;
+    const int nc_max = std::max(1, (int)(kStageFloats / (s.hd + 2)));
     int nc = C.attn_chunks;
-    if (nc > kMaxChunks) {
-        if (msg) *msg = "attn_chunks beyond the kernel's limit";
-        return AMK_E_UNSUPPORTED;
-    }
     if (nc <= 0) {
         nc = 1;
         if (d.max_ctx >= kChunkedCtx) {   // long caches: split the context so every CU streams a piece

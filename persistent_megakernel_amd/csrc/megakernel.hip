@@ -9,25 +9,18 @@
 // the current ones compute).
 //
 // MI355X mapping:
-//  * Workgroup = 8 waves of 64 lanes, one per CU, all walking the queue together through four
-//    workgroup barriers per task. Waves 0..6 are compute waves, wave 7 is the I/O wave.
-//  * Compute waves keep a ring of 1 KiB LDS slots each, fed by direct memory-to-LDS loads of
-//    the bytes their tasks need that do not depend on this step: weight tile rows and history
-//    K/V rows. A consumed slot is refilled at once with the next load of the wave's sequence,
-//    whatever task it belongs to, so the weights of the next phases stream in while the wave
-//    waits for this phase's inputs. Compute waves issue no other vector memory access, so the
-//    ring's order is the only thing their load counter tracks.
-//  * The I/O wave does every other global access: it polls the flag-carrying words a task waits
-//    for (all of them in flight at once), stages the embedding row, gains and residual rows,
-//    and stores every output. A poll never waits behind a weight load.
-//  * Exact arithmetic, so that every value rounded to the activation format rounds as in the
-//    exact definition: the GEMV input is written in fixed point (scale 2^S per input vector)
-//    as signed base-256 digits (int8 weights) or base-16 digits (int4 weights); the dot products
-//    of weight codes and digits are integer (v_dot4 / v_dot8) and exact, and each lane's digit
-//    sums combine exactly in fp64. fp32 and bf16 weights multiply the input in fp64. RMSNorm,
-//    RoPE (fp64 table), attention, softmax and SwiGLU are evaluated in fp64; values are rounded
-//    only where they are stored (activations, cache rows, fp32 logits). GEMV is HBM-bound (one
-//    multiply-add per weight element), so no MFMA.
+//  * Workgroup = 8 waves of 64 lanes, one per CU; all waves walk the queue together.
+//  * Weights are streamed by the waves that use them, straight into registers: wave w owns rows
+//    w, w + 8, ... of every GEMV tile and loads each row as 1 KiB wave loads (16 bytes per lane),
+//    kLoadSlots loads per register buffer, two buffers. The first group of the next task's loads
+//    is issued as soon as the current task's outputs are out, so the HBM latency of the next
+//    phase overlaps the wait for its inputs from other CUs. GEMV is HBM-bound: one multiply-add
+//    per weight element, no MFMA.
+//  * The input vector of a GEMV (after the fused RMSNorm) is staged once in LDS; each lane reads
+//    the slice matching its weight bytes. Row sums are reduced across the wave with DPP moves.
+//  * Attention stages the K and V rows of its positions in LDS with plain vector loads issued
+//    before it waits for q, then runs an online softmax with (query head x dimension group)
+//    lanes.
 //  * Counters are realised as flag-carrying words: every activation a task publishes is an
 //    8-byte word of 32-bit payload + 32-bit flag, written once per launch with flag = epoch+1
 //    through the device-coherent path. A consumer's wait on a counter is its read of the words
@@ -44,7 +37,6 @@
 
 #include "amk_internal.h"
 #include "prep.h"
-#include "ring_iter.h"
 
 // Flag-carrying words of the allocation-free decode entry point (amk_decode_step_static): one
 // array per device, shared by every context on that device, held until the process ends. In
@@ -57,91 +49,73 @@ namespace {
 
 typedef unsigned long long u64;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 #define DEV __device__ __forceinline__
-#define LDS3(p) ((__attribute__((address_space(3))) void*)(p))
-#define CONST4(T, p) ((const __attribute__((address_space(4))) T*)(p))
-// The kernel parameters, read in place from the kernel-argument segment through the scalar
-// cache (never copied to registers wholesale or to private memory).
-typedef const __attribute__((address_space(4))) KParams CKP;
 
-// s_waitcnt immediates (gfx9 layout: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
-constexpr int kWaitLgkm0 = 0xc07f;   // LDS / scalar loads done; vector memory untouched
-
-// ------------------------------------------------------------------ LDS
-
-struct Misc {
-    double part[8][2];                // per wave: sum of squares and largest |value| of its staged input values
-    __attribute__((aligned(16))) u64 residw[kResidWords];   // residual rows of O / down tasks (flag words as gathered)
-    uint64_t t_rows;                  // trace: compute wave 0's own rows done
+struct __attribute__((aligned(16))) Lds {
+    union {
+        uint8_t hb[kHBytes];           // input vector: fp32 (fp32 activations) or bf16 bits
+        float hf[kHBytes / 4];         // also: attention per-wave states, merge staging
+    };
+    uint8_t kvb[kKvBytes];             // attention K then V rows of a round of positions; GEMV row scales
+    float red[kRedRows];               // per-row GEMV results of the current task
+    float att[kAttnLds / 4];           // attention q / current k, v; residual rows; reductions
+    DevTask tcache[kTaskCache];        // the first kTaskCache tasks of this CU's queue
+    uint32_t abort_;                   // this workgroup gives up
+    float fpart[2 * kComputeWaves];
+    int32_t ipart[2 * kComputeWaves];
 };
-static_assert(sizeof(Misc) <= kMiscBytes, "LDS control area");
-
-struct Lds {
-    uint8_t* ring;                    // [kCompWaves][R][1024]
-    uint8_t* stage;
-    double* red;                      // [kRedRows]
-    Misc* misc;
-};
+static_assert(sizeof(Lds) <= kLdsTotal, "LDS budget");
 
 // ------------------------------------------------------------------ small helpers
 
 DEV uint64_t rt() { return __builtin_amdgcn_s_memrealtime(); }
 DEV int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
 
-DEV double bf2d(uint32_t b) { return (double)__uint_as_float(b << 16); }
+DEV float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN)
+DEV uint32_t f2bf(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+DEV float h2f(uint32_t h) {
+    _Float16 x;
+    uint16_t b = (uint16_t)h;
+    __builtin_memcpy(&x, &b, 2);
+    return (float)x;
+}
 
-// fp64 -> bf16 bits with one rounding (to nearest, ties to even), straight from the fp64 bits:
-// keep sign, exponent and the top 7 mantissa bits. Below bf16's smallest normal value the
-// conversion goes through fp32 (values that small are not produced by these models).
-DEV uint32_t d2bf(double d) {
-    uint64_t b = (uint64_t)__double_as_longlong(d);
-    const uint64_t a = b & 0x7fffffffffffffffull;
-    if (a > 0x7ff0000000000000ull) return 0x7fc0u;
-    if (a < 0x3810000000000000ull) {
-        uint32_t u = __float_as_uint((float)d);
-        u += 0x7fffu + ((u >> 16) & 1u);
-        return u >> 16;
-    }
-    b += 0xfffffffffffull + ((b >> 45) & 1ull);
-    b &= ~0x1fffffffffffull;
-    return __float_as_uint((float)__longlong_as_double((long long)b)) >> 16;   // exact, or inf past bf16's range
+// Sum over the 64 lanes with DPP moves: an inclusive scan inside each row of 16 lanes (row
+// shifts by 1, 2, 4, 8), then the row totals are carried by row broadcasts 15 and 31; the total
+// ends in lane 63 and is returned to every lane.
+DEV float wave_sum_dpp(float v) {
+#define AMK_DPP_ADD(ctrl, rmask) \
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl, rmask, 0xf, false))
+    AMK_DPP_ADD(0x111, 0xf);   // row_shr:1
+    AMK_DPP_ADD(0x112, 0xf);   // row_shr:2
+    AMK_DPP_ADD(0x114, 0xf);   // row_shr:4
+    AMK_DPP_ADD(0x118, 0xf);   // row_shr:8
+    AMK_DPP_ADD(0x142, 0xa);   // row_bcast:15 into rows 1 and 3
+    AMK_DPP_ADD(0x143, 0xc);   // row_bcast:31 into rows 2 and 3
+#undef AMK_DPP_ADD
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
-DEV uint32_t act_bits(double d, bool f32) { return f32 ? __float_as_uint((float)d) : d2bf(d); }
-DEV double round_act(double d, bool f32) { return f32 ? (double)(float)d : bf2d(d2bf(d)); }
 
-// fp64 sum over the 64 lanes (DPP row shifts, then row broadcasts; total read from lane 63)
-template <int CTRL, int RMASK>
-DEV double dpp_f64(double v) {
-    const uint64_t u = (uint64_t)__double_as_longlong(v);
-    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, RMASK, 0xf, false);
-    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, RMASK, 0xf, false);
-    return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
-}
-DEV double wave_sum_f64(double v) {
-    v += dpp_f64<0x111, 0xf>(v);   // row_shr:1
-    v += dpp_f64<0x112, 0xf>(v);   // row_shr:2
-    v += dpp_f64<0x114, 0xf>(v);   // row_shr:4
-    v += dpp_f64<0x118, 0xf>(v);   // row_shr:8
-    v += dpp_f64<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
-    v += dpp_f64<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
-    const uint64_t u = (uint64_t)__double_as_longlong(v);
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, 63);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), 63);
-    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
-}
-DEV double shfl_xor_f64(double v, int m) {
-    const uint64_t u = (uint64_t)__double_as_longlong(v);
-    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)u, m, 64);
-    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(u >> 32), m, 64);
-    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
-}
-DEV double wave_max_f64(double v) {
-    for (int m = 32; m >= 1; m >>= 1) v = fmax(v, shfl_xor_f64(v, m));
-    return v;
-}
-DEV double wave_allsum_f64(double v) {
-    for (int m = 32; m >= 1; m >>= 1) v += shfl_xor_f64(v, m);
-    return v;
+// Maximum over the 64 lanes with the same DPP pattern as wave_sum_dpp.
+DEV float wave_max_dpp(float v) {
+#define AMK_DPP_MAX(ctrl, rmask) \
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, -INFINITY), \
+                                                                     __builtin_bit_cast(int, v), ctrl, rmask, 0xf, false)))
+    AMK_DPP_MAX(0x111, 0xf);
+    AMK_DPP_MAX(0x112, 0xf);
+    AMK_DPP_MAX(0x114, 0xf);
+    AMK_DPP_MAX(0x118, 0xf);
+    AMK_DPP_MAX(0x142, 0xa);
+    AMK_DPP_MAX(0x143, 0xc);
+#undef AMK_DPP_MAX
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 // flag-carrying words: device-coherent 8-byte loads and stores
@@ -150,937 +124,536 @@ DEV void ll_store(u64* p, uint32_t payload, uint32_t flag) {
     __hip_atomic_store(p, ((u64)flag << 32) | payload, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Barrier of the workgroup's waves: LDS writes done, then the hardware barrier. It does not wait
-// for vector memory, so the compute waves' ring loads stay in flight across it. It has no
-// timeout, so every wave runs the same four barriers per task whatever happens: waits that give
-// up (watchdog, abort) just return and the wave carries on through its queue.
-DEV void bar() {
-    asm volatile("" ::: "memory");   // no LDS access moves across the barrier in compilation
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
+// 16 bytes of a weight stream (read once per launch: non-temporal)
+DEV u32x4 wload(const uint8_t* p) { return __builtin_nontemporal_load((const u32x4*)p); }
+// keep the compiler from moving memory accesses across this point (prefetches stay early)
+DEV void compiler_fence() { asm volatile("" ::: "memory"); }
+// s_waitcnt operand: vector memory count 0, the other counters at their maximum (no wait)
+constexpr int kWaitVmem0 = 0x0f70;
 
 struct Ctx {
-    CKP* P;
-    Lds L;
-    int pos;              // the step's position (read once)
-    double eps;           // the RMSNorm epsilon (read once)
+    const KParams* P;
+    Lds* S;
     uint64_t deadline;
     int cu;
     const uint8_t* wcu;   // this CU's weight stream
-    uint32_t q0, q1;      // this CU's queue
 };
 
-// task t of the queue, through the scalar cache (read-only during the launch)
-DEV DevTask task_at(const Ctx& c, uint32_t t) {
-    const __attribute__((address_space(4))) uint32_t* g = CONST4(uint32_t, c.P->tasks + t);
+// task t of this CU's queue (starting at q0): from the LDS copy when it holds it. The fields
+// are made wave-uniform so that everything derived from them lives in scalar registers. The
+// global path (queues longer than the copy) uses atomic loads so that the compiler cannot fold
+// the two paths into one generic (flat) load: a flat load also counts as a vector memory
+// access, and waiting for it would wait for every weight load the wave has in flight.
+DEV DevTask task_at(const Ctx& c, uint32_t q0, uint32_t t) {
     uint32_t w[sizeof(DevTask) / 4];
+    if (t - q0 < (uint32_t)kTaskCache) {
+        __builtin_memcpy(w, &c.S->tcache[t - q0], sizeof(DevTask));
+    } else {
+        const u64* g = (const u64*)(c.P->tasks + t);
 #pragma unroll
-    for (int k = 0; k < (int)(sizeof(DevTask) / 4); ++k) w[k] = __builtin_amdgcn_readfirstlane(g[k]);
+        for (int k = 0; k < (int)(sizeof(DevTask) / 8); ++k) {
+            const u64 v = __hip_atomic_load(g + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            w[2 * k] = (uint32_t)v;
+            w[2 * k + 1] = (uint32_t)(v >> 32);
+        }
+        // wait here, so that nothing past the join of the two paths waits for vector memory
+        __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+    }
+#pragma unroll
+    for (int k = 0; k < (int)(sizeof(DevTask) / 4); ++k) w[k] = __builtin_amdgcn_readfirstlane(w[k]);
     DevTask r;
     __builtin_memcpy(&r, w, sizeof(DevTask));
     return r;
 }
 
-DEV uint32_t act_bytes(CKP& P) { return P.act_f32 ? 4u : 2u; }
-
-// Stage layout of a GEMV input: digit planes (or fp32 values) from offset 0, the raw input
-// values (activation format) over their start until the planes are written, the fp32 gains
-// after the planes (n_planes(FMT) * plane_stride(FMT, K)).
-
-// The stage offset of a GEMV input's gathered words: over the plane area (the planes are written
-// only after every raw value is read), past the planes and gains for fp32 activations (8 bytes
-// a value, more than the fp32 plane).
-template <int FMT>
-DEV uint32_t raw_off(uint32_t K, bool norm) {
-    return FMT == AMK_F32 ? n_planes(FMT) * plane_stride(FMT, K) + (norm ? 4u * K : 0u) : 0u;
+DEV void raise_timeout(const Ctx& c) {
+    __hip_atomic_store(&c.S->abort_, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_store(c.P->abort_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&c.P->status[0], kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-// Scale 2^S of the fixed-point input: |H| = |h| 2^S stays below 2^37 for every input value h
-// (bound: an upper bound of max |h|). Every thread computes it from the same two numbers.
-DEV int fixed_shift(double bound) {
-    if (!(bound > 0.0)) return 0;
-    int e;
-    (void)frexp(bound, &e);   // bound < 2^e
-    return 37 - e;
-}
-
-// ------------------------------------------------------------------ the compute waves' ring
-
-template <int R>
-struct Ring {
-    uint32_t slot;        // next slot to consume
-    uint32_t pending;     // slots consumed and not yet refilled: [slot - pending, slot)
-    uint8_t* base;        // this wave's slot 0
-    Cursor cur;           // issue side: the next load of the wave's sequence
-    const uint8_t* kv;    // the cache
-};
-
-DEV uint32_t uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
-DEV uint64_t uni64(uint64_t v) { return ((uint64_t)uni((uint32_t)(v >> 32)) << 32) | uni((uint32_t)v); }
-
-// The cursor is wave-uniform by construction; saying so once per opened task keeps it in scalar
-// registers whatever control flow surrounds the issue.
-DEV void cursor_uniform(Cursor& c) {
-    c.t = uni(c.t); c.kind = uni(c.kind); c.left = uni(c.left); c.a = uni64(c.a); c.s1 = uni(c.s1); c.s2 = uni(c.s2);
-    c.n1 = uni(c.n1); c.n2 = uni(c.n2); c.x = uni(c.x); c.y = uni(c.y); c.gs = uni(c.gs); c.gi = uni(c.gi);
-}
-
-// Issue the wave's next load into the oldest free slot, opening queue entries below `limit`
-// as needed (deriving a task's geometry happens once per task; every other issue is a few
-// additions). Returns false, issuing nothing, when no entry below `limit` has a load left.
-template <int R>
-DEV bool ring_issue(const Ctx& c, Ring<R>& r, uint32_t w, uint32_t limit) {
-    Cursor cu = r.cur;
-    while (cu.left == 0 && cu.t < limit) {
-        const uint32_t t = cu.t;
-        cursor_open(c, task_at(c, t), w, cu);
-        cu.t = t + 1;
-        cursor_uniform(cu);
-    }
-    const bool have = cu.left != 0;
-    if (have) {
-        const CLoad l = cursor_next(cu);
-        const uint8_t* src = (cu.kind == 1 ? c.wcu : r.kv) + l.base + cursor_lane_off(cu, l, (uint32_t)lane_id());
-        uint32_t s = r.slot + (uint32_t)R - r.pending;
-        if (s >= (uint32_t)R) s -= (uint32_t)R;
-        __builtin_amdgcn_global_load_lds((const void*)src, LDS3(r.base + s * 1024u), 16, 0, 0);
-        --r.pending;
-    }
-    r.cur = cu;
-    return have;
-}
-
-// Refill the free slots with the wave's next loads from queue entries below `limit`.
-template <int R>
-DEV void ring_refill(const Ctx& c, Ring<R>& r, uint32_t w, uint32_t limit) {
-#pragma unroll 1
-    while (r.pending && ring_issue(c, r, w, limit)) {}
-}
-
-template <int R>
-DEV void ring_init(const Ctx& c, Ring<R>& r, uint32_t w) {
-    r.base = c.L.ring + w * (uint32_t)R * 1024u;
-    r.slot = 0;
-    r.pending = R;
-    r.cur.t = c.q0;
-    r.cur.kind = 0;
-    r.cur.left = 0;
-    r.kv = (const uint8_t*)c.P->kv;
-    ring_refill(c, r, w, c.q1);
-}
-
-// Wait until at most k of the wave's vector memory operations are outstanding (k < 16).
-DEV void wait_vm(uint32_t k) {
-    switch (k) {
-#define AMK_WAIT_CASE(K) case K: asm volatile("s_waitcnt vmcnt(" #K ")" ::: "memory"); break;
-    AMK_WAIT_CASE(0) AMK_WAIT_CASE(1) AMK_WAIT_CASE(2) AMK_WAIT_CASE(3) AMK_WAIT_CASE(4) AMK_WAIT_CASE(5)
-    AMK_WAIT_CASE(6) AMK_WAIT_CASE(7) AMK_WAIT_CASE(8) AMK_WAIT_CASE(9) AMK_WAIT_CASE(10) AMK_WAIT_CASE(11)
-    AMK_WAIT_CASE(12) AMK_WAIT_CASE(13) AMK_WAIT_CASE(14)
-#undef AMK_WAIT_CASE
-    default: break;
-    }
-}
-
-// The next n (1..4) slots, after the loads that filled them have landed. The wave's only vector
-// memory operations are its ring loads, issued and completed in slot order, R - pending of them
-// in flight: the oldest n are done once at most R - pending - n are outstanding (the slots hold
-// issued loads: every load of the task being consumed is issued before it is taken). The reads
-// are one asm block that waits for itself, so the compiler neither reorders them nor waits for
-// every ring load.
-template <int R>
-DEV void ring_take(Ring<R>& r, uint32_t n, u32x4 (&v)[4]) {
-    static_assert(R <= 15, "wait_vm covers counts below 15");
-    wait_vm((uint32_t)R - r.pending - n);
-    const uint32_t lane16 = 16u * (uint32_t)lane_id();
-    const uint32_t b = (uint32_t)(uintptr_t)LDS3(r.base);
-    uint32_t a[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        uint32_t s = r.slot + (uint32_t)k;
-        if (s >= (uint32_t)R) s -= (uint32_t)R;
-        a[k] = b + s * 1024u + lane16;
-    }
-    switch (n) {
-    case 1:
-        asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v[0]) : "v"(a[0]) : "memory");
-        break;
-    case 2:
-        asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
-                     : "=&v"(v[0]), "=&v"(v[1]) : "v"(a[0]), "v"(a[1]) : "memory");
-        break;
-    case 3:
-        asm volatile("ds_read_b128 %0, %3\n\tds_read_b128 %1, %4\n\tds_read_b128 %2, %5\n\ts_waitcnt lgkmcnt(0)"
-                     : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]) : "v"(a[0]), "v"(a[1]), "v"(a[2]) : "memory");
-        break;
-    default:
-        asm volatile("ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
-                     "s_waitcnt lgkmcnt(0)"
-                     : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
-                     : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]) : "memory");
-        break;
-    }
-    r.slot += n;
-    if (r.slot >= (uint32_t)R) r.slot -= (uint32_t)R;
-    r.pending += n;
-}
-
-// LDS stores of the compute waves that the compiler would otherwise order after every ring
-// load in flight (it cannot tell them apart from the ring's memory-to-LDS writes): written in
-// asm, each waiting for itself. Nothing else in the wave touches these bytes meanwhile.
-DEV void lds_st128(void* p, u32x4 v) {
-    asm volatile("ds_write_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"((uint32_t)(uintptr_t)LDS3(p)), "v"(v) : "memory");
-}
-DEV void lds_st32(void* p, uint32_t v) {
-    asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"((uint32_t)(uintptr_t)LDS3(p)), "v"(v) : "memory");
-}
-DEV void lds_st64(void* p, double v) {
-    asm volatile("ds_write_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"((uint32_t)(uintptr_t)LDS3(p)), "v"(v) : "memory");
-}
-
-// ------------------------------------------------------------------ GEMV on the compute waves
-
-// The exact value of one lane's digit sums: sum_d acc[d] * 2^(SHIFT d), every term and partial
-// sum an integer below 2^53 (exact in fp64).
-template <int ND, int SHIFT>
-DEV double digits_value(const int (&acc)[ND]) {
-    double v = (double)acc[ND - 1];
-#pragma unroll
-    for (int d = ND - 2; d >= 0; --d) v = fma(v, (double)(1 << SHIFT), (double)acc[d]);
-    return v;
-}
-
-DEV double half_bits(uint32_t h) {
-    _Float16 x;
-    const uint16_t b = (uint16_t)h;
-    __builtin_memcpy(&x, &b, 2);
-    return (double)(float)x;
-}
-
-// int4 group scale of this lane's 32 columns in chunk j of tile row `row` (K/128 fp16 scales
-// per row after the codes). The chunk's (up to) 16 scales come through the scalar cache as whole
-// dwords from the 4-byte boundary at or below the first one (a row's scales start mid-dword when
-// K/128 is odd); each lane then selects its own half, lane l taking scale l / 4 of the chunk.
-// Only dwords holding at least one of the chunk's scales are read.
-DEV double int4_scale(const Ctx& c, const TaskLoads& t, uint32_t K, uint32_t tile_rows, uint32_t row, uint32_t j) {
-    const uint64_t off = t.tile + (uint64_t)tile_rows * t.pitch + ((uint64_t)row * (K / 128) + 16ull * j) * 2;
-    const uint32_t a = (uint32_t)(off >> 1) & 1u;   // 1: the first scale is the high half of its dword
-    const __attribute__((address_space(4))) uint32_t* g = CONST4(uint32_t, c.wcu + (off & ~3ull));
-    const uint32_t ng = K / 128 - 16 * j;          // scales left in the row from this chunk on
-    const uint32_t nh = (ng < 16 ? ng : 16) + a;   // halves to cover from the dword boundary
-    const uint32_t h = (uint32_t)lane_id() / 4 + a;
-    uint32_t v = 0;
-#pragma unroll
-    for (int k = 0; k < 9; ++k) {
-        const uint32_t s = (uint32_t)(2 * k) < nh ? __builtin_amdgcn_readfirstlane(g[k]) : 0u;
-        v = (h >> 1) == (uint32_t)k ? s : v;
-    }
-    return half_bits((h & 1) ? v >> 16 : v & 0xffffu);
-}
-
-template <int FMT, int R>
-DEV void gemv_compute(const Ctx& c, Ring<R>& ring, const DevTask& T, uint32_t t_idx, uint32_t w, int S) {
-    CKP& P = *c.P;
-    const TaskLoads t = task_loads(c, T, w);
-    if (t.kind != 1) return;
-    const uint32_t K = T.k;
-    const uint32_t lane = (uint32_t)lane_id();
-    const uint8_t* stage = c.L.stage;
-    const uint32_t ps = plane_stride(FMT, K);
-    const double unscale = ldexp(1.0, -S);
-    for (uint32_t gi = 0; 4 * gi < t.m; ++gi) {
-        const uint32_t gs = t.m - 4 * gi < 4 ? t.m - 4 * gi : 4;
-        if constexpr (FMT == AMK_INT8_PC) {
-            int acc[4][5];
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int d = 0; d < 5; ++d) acc[r][d] = 0;
-            for (uint32_t j = 0; j < t.nj; ++j) {
-                const uint32_t c0 = 1024u * j + 16u * lane;
-                u32x4 D[5];
-#pragma unroll
-                for (int d = 0; d < 5; ++d) D[d] = *(const u32x4*)(stage + d * ps + c0);
-                u32x4 W[4];
-                ring_take(ring, gs, W);
-                ring_refill(c, ring, w, t_idx + 1);
-                const bool valid = c0 < K;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    if ((uint32_t)r >= gs) break;
-                    const u32x4 x = valid ? W[r] : u32x4{0, 0, 0, 0};
-#pragma unroll
-                    for (int d = 0; d < 5; ++d) {
-                        acc[r][d] = __builtin_amdgcn_sdot4((int)x.x, (int)D[d].x, acc[r][d], false);
-                        acc[r][d] = __builtin_amdgcn_sdot4((int)x.y, (int)D[d].y, acc[r][d], false);
-                        acc[r][d] = __builtin_amdgcn_sdot4((int)x.z, (int)D[d].z, acc[r][d], false);
-                        acc[r][d] = __builtin_amdgcn_sdot4((int)x.w, (int)D[d].w, acc[r][d], false);
-                    }
-                }
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                if ((uint32_t)r >= gs) break;
-                const uint32_t row = w + kCompWaves * (4 * gi + (uint32_t)r);
-                const double v = wave_sum_f64(digits_value<5, 8>(acc[r]));
-                // the row's fp16 scale, after the codes of the tile
-                const uint64_t so = t.tile + (uint64_t)T.tile_rows * t.pitch + 2ull * row;
-                const uint32_t wd = __builtin_amdgcn_readfirstlane(*CONST4(uint32_t, c.wcu + (so & ~3ull)));
-                const double sc = half_bits((so & 2) ? wd >> 16 : wd & 0xffffu);
-                if (lane == 0) lds_st64(c.L.red + row, (v * unscale) * sc);
-            }
-        } else if constexpr (FMT == AMK_INT4_G128) {
-            double y[4] = {0.0, 0.0, 0.0, 0.0};
-            for (uint32_t j = 0; j < t.nj; ++j) {
-                const uint32_t c0b = 1024u * j + 16u * lane;   // byte offset of the lane's 32 columns
-                u32x4 D[10];
-#pragma unroll
-                for (int d = 0; d < 10; ++d) D[d] = *(const u32x4*)(stage + d * ps + c0b);
-                u32x4 W[4];
-                ring_take(ring, gs, W);
-                ring_refill(c, ring, w, t_idx + 1);
-                const bool valid = c0b < t.pitch;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    if ((uint32_t)r >= gs) break;
-                    const uint32_t row = w + kCompWaves * (4 * gi + (uint32_t)r);
-                    // stored codes are q + 8 in each nibble; flipping bit 3 gives q as a signed nibble
-                    const uint32_t f = 0x88888888u;
-                    const u32x4 x = valid ? u32x4{W[r].x ^ f, W[r].y ^ f, W[r].z ^ f, W[r].w ^ f} : u32x4{0, 0, 0, 0};
-                    int acc[10];
-#pragma unroll
-                    for (int d = 0; d < 10; ++d) {
-                        int a = __builtin_amdgcn_sdot8((int)x.x, (int)D[d].x, 0, false);
-                        a = __builtin_amdgcn_sdot8((int)x.y, (int)D[d].y, a, false);
-                        a = __builtin_amdgcn_sdot8((int)x.z, (int)D[d].z, a, false);
-                        acc[d] = __builtin_amdgcn_sdot8((int)x.w, (int)D[d].w, a, false);
-                    }
-                    const double sc = int4_scale(c, t, K, T.tile_rows, row, j);
-                    y[r] = fma(digits_value<10, 4>(acc), valid ? sc : 0.0, y[r]);
-                }
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                if ((uint32_t)r >= gs) break;
-                const uint32_t row = w + kCompWaves * (4 * gi + (uint32_t)r);
-                const double v = wave_sum_f64(y[r]);
-                if (lane == 0) lds_st64(c.L.red + row, v * unscale);
-            }
-        } else {
-            // fp32 / bf16 weights: exact products with the fp32 input values, summed in fp64
-            constexpr int CPL = FMT == AMK_F32 ? 4 : 8;     // columns per lane per chunk
-            constexpr uint32_t CPC = FMT == AMK_F32 ? 256 : 512;   // columns per chunk
-            double y[4] = {0.0, 0.0, 0.0, 0.0};
-            for (uint32_t j = 0; j < t.nj; ++j) {
-                const uint32_t c0 = CPC * j + (uint32_t)CPL * lane;
-                double h[CPL];
-                const float* hp = (const float*)stage + c0;
-#pragma unroll
-                for (int k = 0; k < CPL; ++k) h[k] = (double)hp[k];
-                u32x4 W[4];
-                ring_take(ring, gs, W);
-                ring_refill(c, ring, w, t_idx + 1);
-                const bool valid = c0 < K;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    if ((uint32_t)r >= gs) break;
-                    const uint32_t wv[4] = {W[r].x, W[r].y, W[r].z, W[r].w};
-                    double a = 0.0;
-#pragma unroll
-                    for (int k = 0; k < CPL; ++k) {
-                        float wf;
-                        if constexpr (FMT == AMK_F32) wf = __uint_as_float(wv[k]);
-                        else wf = __uint_as_float((k & 1) ? (wv[k / 2] & 0xffff0000u) : (wv[k / 2] << 16));
-                        a = fma((double)wf, h[k], a);
-                    }
-                    y[r] += valid ? a : 0.0;
-                }
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                if ((uint32_t)r >= gs) break;
-                const uint32_t row = w + kCompWaves * (4 * gi + (uint32_t)r);
-                const double v = wave_sum_f64(y[r]);
-                if (lane == 0) lds_st64(c.L.red + row, v);
-            }
-        }
-    }
-}
-
-// ------------------------------------------------------------------ attention on the compute waves
-
-// Attention stage layout (from the stage start): q [nh][hd] and the current k, v [hd] (fp64), the
-// per-wave states [kCompWaves][nh][hd + 2] (fp64: m, l, o), then each compute wave's 2 KiB copy
-// of its current K and V slots.
-struct AttnStage {
-    double* q;
-    double* kc;
-    double* vc;
-    double* st;
-    uint8_t* kv;
-};
-DEV AttnStage attn_stage(const Lds& L, uint32_t nh, uint32_t hd) {
-    AttnStage a;
-    a.q = (double*)L.stage;
-    a.kc = a.q + nh * hd;
-    a.vc = a.kc + hd;
-    a.st = a.vc + hd;
-    a.kv = (uint8_t*)(a.st + kCompWaves * nh * (hd + 2));
-    return a;
-}
-
-// LDS loads of the compute waves that the compiler would otherwise order after every ring load
-// in flight (it cannot tell these bytes from the ring's): asm, each block waiting for itself.
-DEV uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)LDS3(p); }
-DEV double lds_ld64(const void* p) {
-    double v;
-    asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(p)) : "memory");
-    return v;
-}
-// NB (2, 4, 8 or 16) bytes at each of four LDS addresses, one wait for all four.
-template <int NB>
-DEV void lds_ld4(const uint32_t (&a)[4], u32x4 (&v)[4]) {
-    if constexpr (NB == 16) {
-        asm volatile("ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
-                     "s_waitcnt lgkmcnt(0)"
-                     : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]) : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]) : "memory");
-    } else {
-        uint2 x[4];
-        if constexpr (NB == 8) {
-            asm volatile("ds_read_b64 %0, %4\n\tds_read_b64 %1, %5\n\tds_read_b64 %2, %6\n\tds_read_b64 %3, %7\n\t"
-                         "s_waitcnt lgkmcnt(0)"
-                         : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]) : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]) : "memory");
-        } else {
-            uint32_t y[4];
-            if constexpr (NB == 4) {
-                asm volatile("ds_read_b32 %0, %4\n\tds_read_b32 %1, %5\n\tds_read_b32 %2, %6\n\tds_read_b32 %3, %7\n\t"
-                             "s_waitcnt lgkmcnt(0)"
-                             : "=&v"(y[0]), "=&v"(y[1]), "=&v"(y[2]), "=&v"(y[3]) : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]) : "memory");
-            } else {
-                asm volatile("ds_read_u16 %0, %4\n\tds_read_u16 %1, %5\n\tds_read_u16 %2, %6\n\tds_read_u16 %3, %7\n\t"
-                             "s_waitcnt lgkmcnt(0)"
-                             : "=&v"(y[0]), "=&v"(y[1]), "=&v"(y[2]), "=&v"(y[3]) : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]) : "memory");
-            }
-#pragma unroll
-            for (int k = 0; k < 4; ++k) x[k] = uint2{y[k], 0u};
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) v[k] = u32x4{x[k].x, x[k].y, 0u, 0u};
-    }
-}
-
-// This lane's D values [d0, d0 + D) of four staged K or V rows (LDS addresses of their first
-// element), as fp64.
-template <int D>
-DEV void row_slices4(const uint32_t (&row)[4], bool f32, uint32_t d0, double (&v)[4][D]) {
-    if (f32) {
-        constexpr int NB = D * 4 > 16 ? 16 : D * 4;
-        uint32_t a[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) a[u] = row[u] + 4 * d0;
-        u32x4 w[4];
-        lds_ld4<NB>(a, w);
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int k = 0; k < D && k < 4; ++k) v[u][k] = (double)__uint_as_float(w[u][k]);
-        if constexpr (D == 8) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) a[u] += 16;
-            lds_ld4<16>(a, w);
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-                for (int k = 0; k < 4; ++k) v[u][4 + k] = (double)__uint_as_float(w[u][k]);
-        }
-    } else {
-        constexpr int NB = D * 2;
-        uint32_t a[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) a[u] = row[u] + 2 * d0;
-        u32x4 w[4];
-        lds_ld4<NB>(a, w);
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int k = 0; k < D; ++k) v[u][k] = bf2d((k & 1) ? (w[u][k / 2] >> 16) : (w[u][k / 2] & 0xffffu));
-    }
-}
-
-// Attention of query heads [h0, h0 + nh) of one KV group over the wave's blocks of the chunk's
-// history rows (and, for compute wave 0 in the last chunk, the current position): softmax of
-// q.K / sqrt(hd) times V, online (running max m, running sum l, rescaled output o), in fp64
-// (page 3, "How it works", the attention instruction over the persistent KV cache).
-// Lanes are (query head, dimension group) pairs: a head owns L lanes, a lane D consecutive dims.
-template <int FMT, int D, int R = ring_slots(FMT)>
-DEV void attn_compute_d(const Ctx& c, Ring<R>& ring, const DevTask& T, uint32_t t_idx, uint32_t w) {
-    CKP& P = *c.P;
-    const TaskLoads t = task_loads(c, T, w);
-    constexpr bool f32 = FMT == AMK_F32;
-    const uint32_t nh = T.arg[1], hd = T.k / (f32 ? 4u : 2u);
-    const bool cur = T.arg[2] == T.arg[3] - 1;
-    const AttnStage A = attn_stage(c.L, nh, hd);
-    const uint32_t lane = (uint32_t)lane_id();
-    const uint32_t L = hd / (uint32_t)D;
-    const uint32_t hl = lane / L, dg = lane % L;
-    const bool active = hl < nh;
-    const uint32_t hq = active ? hl : 0;
-    double q[D], o[D];
-#pragma unroll
-    for (int k = 0; k < D; ++k) { q[k] = lds_ld64(A.q + hq * hd + dg * D + k); o[k] = 0.0; }
-    double m = -INFINITY, l = 0.0;
-    const double scale = P.attn_scale;
-    // one batch of up to 4 rows (nr of them) with their K and V slices: scores, then one rescale
-    // of the running state
-    auto batch = [&](const double (&kv)[4][D], const double (&vv)[4][D], uint32_t nr) {
-        double sc[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            double s = 0.0;
-#pragma unroll
-            for (int k = 0; k < D; ++k) s = fma(q[k], kv[u][k], s);
-            sc[u] = s;
-        }
-        for (uint32_t off = L >> 1; off >= 1; off >>= 1)
-#pragma unroll
-            for (int u = 0; u < 4; ++u) sc[u] += shfl_xor_f64(sc[u], (int)off);
-        double mb = m;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            sc[u] = (uint32_t)u < nr ? sc[u] * scale : -INFINITY;
-            mb = fmax(mb, sc[u]);
-        }
-        const double alpha = m == -INFINITY ? 0.0 : exp(m - mb);
-        l *= alpha;
-#pragma unroll
-        for (int k = 0; k < D; ++k) o[k] *= alpha;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if ((uint32_t)u >= nr) break;
-            const double p = exp(sc[u] - mb);
-            l += p;
-#pragma unroll
-            for (int k = 0; k < D; ++k) o[k] = fma(p, vv[u][k], o[k]);
-        }
-        m = mb;
-    };
-    if (cur && w == 0) {   // the current position, from the gathered k and v (fp64)
-        double kv[4][D], vv[4][D];
-#pragma unroll
-        for (int k = 0; k < D; ++k) {
-            kv[0][k] = lds_ld64(A.kc + dg * D + k);
-            vv[0][k] = lds_ld64(A.vc + dg * D + k);
-        }
-#pragma unroll
-        for (int u = 1; u < 4; ++u)
-#pragma unroll
-            for (int k = 0; k < D; ++k) { kv[u][k] = 0.0; vv[u][k] = 0.0; }
-        batch(kv, vv, 1);
-    }
-    if (t.kind == 2) {
-        uint8_t* cp = A.kv + w * 2048u;
-        const uint32_t cpa = lds_addr(cp);
-        for (uint32_t bi = 0; bi < t.nbw; ++bi) {
-            u32x4 W[4];
-            ring_take(ring, 2, W);
-            ring_refill(c, ring, w, t_idx + 1);
-            lds_st128(cp + 16 * lane, W[0]);          // K rows of the block
-            lds_st128(cp + 1024 + 16 * lane, W[1]);   // V rows
-            const uint32_t b = w + kCompWaves * bi;
-            const uint32_t row0 = b * t.rps;
-            const uint32_t nr = t.nrows - row0 < t.rps ? t.nrows - row0 : t.rps;
-            for (uint32_t r0 = 0; r0 < nr; r0 += 4) {
-                uint32_t ka[4], va[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const uint32_t rr = r0 + (uint32_t)u < nr ? r0 + (uint32_t)u : r0;
-                    ka[u] = cpa + rr * t.rowb;
-                    va[u] = cpa + 1024 + rr * t.rowb;
-                }
-                double kv[4][D], vv[4][D];
-                row_slices4<D>(ka, f32, dg * D, kv);
-                row_slices4<D>(va, f32, dg * D, vv);
-                batch(kv, vv, nr - r0 < 4 ? nr - r0 : 4);
-            }
-        }
-    }
-    // the wave's state: m, l, o per head
-    if (active) {
-        double* s = A.st + (w * nh + hl) * (hd + 2);
-        if (dg == 0) { lds_st64(s, m); lds_st64(s + 1, l); }
-#pragma unroll
-        for (int k = 0; k < D; ++k) lds_st64(s + 2 + dg * D + k, o[k]);
-    }
-}
-
-template <int FMT, int R = ring_slots(FMT)>
-DEV void attn_compute(const Ctx& c, Ring<R>& ring, const DevTask& T, uint32_t t_idx, uint32_t w) {
-    const uint32_t nh = T.arg[1], hd = T.k / (FMT == AMK_F32 ? 4u : 2u);
-    uint32_t nhp = 1;
-    while (nhp < nh) nhp <<= 1;
-    switch (hd / min(64u / nhp, hd)) {
-    case 1: attn_compute_d<FMT, 1>(c, ring, T, t_idx, w); break;
-    case 2: attn_compute_d<FMT, 2>(c, ring, T, t_idx, w); break;
-    case 4: attn_compute_d<FMT, 4>(c, ring, T, t_idx, w); break;
-    default: attn_compute_d<FMT, 8>(c, ring, T, t_idx, w); break;
-    }
-}
-
-// ------------------------------------------------------------------ staging (all waves)
-
-// Between the first two barriers of a GEMV task: the raw input and its statistics are in LDS.
-// Every thread takes units of Q consecutive columns (unit tid + 512 u): reads its raw values
-// (with the RMSNorm, rounded to the activation format as the step defines it), and after one
-// barrier writes their digit planes (or fp32 values) over the raw area. All raw values are read
-// before any plane is written. Returns S (input scale 2^S).
-template <int FMT>
-DEV int stage_input(const Ctx& c, const DevTask& T, int tid) {
-    CKP& P = *c.P;
-    constexpr bool f32 = FMT == AMK_F32;
-    const uint32_t K = T.k;
-    const int ni = T.norm;
-    constexpr int Q = FMT == AMK_INT4_G128 ? 8 : 4;
-    constexpr int MAXU = (kMaxInter + 512 * Q - 1) / (512 * Q);   // units per thread: every column in one pass
-    const uint32_t nunits = K / Q;
-    const float* gains = (const float*)(c.L.stage + n_planes(FMT) * plane_stride(FMT, K));
-    uint8_t* st = c.L.stage;
-    const uint8_t* raw = st + raw_off<FMT>(K, ni >= 0);   // the gathered words
-    const uint32_t ps = plane_stride(FMT, K);
-    float x[MAXU][Q];   // activation values: exact in fp32
-    // every unit's words (and gains) are read first, then converted: the LDS reads go out together
-    constexpr int WPU = f32 ? Q : Q / 2;   // gathered words per unit (8 bytes each)
-    u32x4 rw[MAXU][WPU / 2];
-    u32x4 gw[MAXU][Q / 4];
-    const uint32_t nu = (nunits + 511u) / 512u;   // unit rounds that hold any of the input (wave-uniform)
-#pragma unroll
-    for (int u = 0; u < MAXU; ++u) {
-        if ((uint32_t)u >= nu) break;
-        const uint32_t unit = (uint32_t)tid + 512u * (uint32_t)u;
-        const uint32_t uc = unit < nunits ? unit : 0u;   // units past the input read unit 0 (unused)
-#pragma unroll
-        for (int k = 0; k < WPU / 2; ++k) rw[u][k] = *(const u32x4*)(raw + 8u * (uc * WPU) + 16u * k);
-#pragma unroll
-        for (int k = 0; k < Q / 4; ++k) gw[u][k] = ni >= 0 ? *(const u32x4*)(gains + uc * Q + 4u * k) : u32x4{0, 0, 0, 0};
-    }
-    // the raw values (exact in fp32) and this thread's part of their sum of squares and maximum
-    double ss = 0.0, mx = 0.0;
-#pragma unroll
-    for (int u = 0; u < MAXU; ++u) {
-        if ((uint32_t)u >= nu) break;
-        const uint32_t unit = (uint32_t)tid + 512u * (uint32_t)u;
-#pragma unroll
-        for (int q = 0; q < Q; ++q) {
-            // value q of the unit: word q (fp32) or half q % 2 of word q / 2 (bf16); payloads sit in
-            // the words' low dwords (components x and z of each 16-byte read)
-            const u32x4 wv = rw[u][f32 ? q / 2 : q / 4];
-            const uint32_t pl = f32 ? ((q & 1) ? wv.z : wv.x) : (((q / 2) & 1) ? wv.z : wv.x);
-            const double v = unit < nunits ? (f32 ? (double)__uint_as_float(pl) : bf2d((pl >> (16u * (q & 1))) & 0xffffu)) : 0.0;
-            ss = fma(v, v, ss);
-            mx = fmax(mx, fabs(v));
-            x[u][q] = (float)v;
-        }
-    }
-    ss = wave_sum_f64(ss);
-    mx = wave_max_f64(mx);
-    const uint32_t wv_ = (uint32_t)tid >> 6;
-    if ((tid & 63) == 0) {
-        lds_st64(&c.L.misc->part[wv_][0], ss);
-        lds_st64(&c.L.misc->part[wv_][1], mx);
-    }
-    bar();   // A1b: every raw value is read (planes may be written) and every wave's statistics are in
-    ss = 0.0;
-    mx = 0.0;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {   // in wave order: every thread forms the same sums
-        ss += lds_ld64(&c.L.misc->part[k][0]);
-        mx = fmax(mx, lds_ld64(&c.L.misc->part[k][1]));
-    }
-    // RMSNorm scale r = 1 / sqrt(mean(x^2) + eps)
-    const double r = ni >= 0 ? 1.0 / sqrt(ss / (double)K + c.eps) : 1.0;
-    const double bound = ni >= 0 ? mx * r * (double)T.gmax * 1.01 : mx;
-    const int S = fixed_shift(bound);
-    if (ni >= 0) {
-#pragma unroll
-        for (int u = 0; u < MAXU; ++u) {
-            if ((uint32_t)u >= nu) break;
-#pragma unroll
-            for (int q = 0; q < Q; ++q) {
-                const u32x4 g4 = gw[u][q / 4];
-                const uint32_t gb = (q & 3) == 0 ? g4.x : (q & 3) == 1 ? g4.y : (q & 3) == 2 ? g4.z : g4.w;
-                x[u][q] = (float)round_act(((double)x[u][q] * r) * (double)__uint_as_float(gb), f32);
-            }
-        }
-    }
-#pragma unroll
-    for (int u = 0; u < MAXU; ++u) {
-        if ((uint32_t)u >= nu) break;
-        const uint32_t unit = (uint32_t)tid + 512u * (uint32_t)u;
-        if (unit >= nunits) continue;
-        const uint32_t k0 = unit * Q;
-        if constexpr (FMT == AMK_F32 || FMT == AMK_BF16) {
-            *(u32x4*)(st + 4 * k0) = u32x4{__float_as_uint(x[u][0]), __float_as_uint(x[u][1]), __float_as_uint(x[u][2]),
-                                          __float_as_uint(x[u][3])};
-        } else {
-            int64_t H[Q];
-#pragma unroll
-            for (int q = 0; q < Q; ++q) H[q] = (int64_t)rint(ldexp((double)x[u][q], S));
-            if constexpr (FMT == AMK_INT8_PC) {
-#pragma unroll
-                for (int d = 0; d < 5; ++d) {
-                    uint32_t word = 0;
-#pragma unroll
-                    for (int q = 0; q < Q; ++q) {
-                        const int64_t dig = (int64_t)(int8_t)(uint8_t)(H[q] & 0xff);   // in [-128, 127]
-                        H[q] = (H[q] - dig) >> 8;
-                        word |= ((uint32_t)dig & 0xffu) << (8 * q);
-                    }
-                    *(uint32_t*)(st + d * ps + k0) = word;
-                }
-            } else {
-#pragma unroll
-                for (int d = 0; d < 10; ++d) {
-                    uint32_t word = 0;
-#pragma unroll
-                    for (int q = 0; q < Q; ++q) {
-                        const int64_t dig = (int64_t)((H[q] & 0xf) ^ 8) - 8;   // in [-8, 7]
-                        H[q] = (H[q] - dig) >> 4;
-                        word |= ((uint32_t)dig & 0xfu) << (4 * q);
-                    }
-                    *(uint32_t*)(st + d * ps + k0 / 2) = word;
-                }
-            }
-        }
-    }
-    // fp inputs: zero the plane's padding to the chunk (the compute waves read whole chunks and
-    // multiply the padding by zero weights)
-    if constexpr (FMT == AMK_F32 || FMT == AMK_BF16) {
-        for (uint32_t k = K + (uint32_t)tid; k < ps / 4; k += 512u) ((float*)st)[k] = 0.f;
-    }
-    return S;
-}
-
-// ------------------------------------------------------------------ the I/O wave
-
-struct Io {
-    const Ctx* c;
-    uint32_t flag;
-    bool abort_;
-    int token;
-    uint64_t* tr;
-};
-
-DEV void raise_timeout(Io& io) {
-    io.abort_ = true;
-    __hip_atomic_store(io.c->P->abort_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&io.c->P->status[0], kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-}
-
-// spin step of every wait: bounded by the watchdog and by the global abort flag (read every
-// 4096 spins: another workgroup sets it only after its own watchdog expired)
-DEV bool spin_ok(Io& io, uint32_t& n) {
-    if (io.abort_) return false;
+// spin step of every wait: bounded by the watchdog and by the global abort flag. The clock is
+// read on the first spin of a wait and every 16 spins after it; the global flag is a
+// device-coherent load (a memory round trip), so it is read only every 4096 spins (another
+// workgroup sets it only after its own watchdog, which is far longer, expired).
+DEV bool spin_ok(const Ctx& c, uint32_t& n) {
     if (((++n) & 15u) == 1) {
-        if (rt() > io.c->deadline) { raise_timeout(io); return false; }
-        if ((n & 0xfffu) == 1 && __hip_atomic_load(io.c->P->abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-            io.abort_ = true;
+        if (rt() > c.deadline) { raise_timeout(c); return false; }
+        if ((n & 0xfffu) == 1 &&
+            __hip_atomic_load(c.P->abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+            __hip_atomic_store(&c.S->abort_, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             return false;
         }
     }
+    if (__hip_atomic_load(&c.S->abort_, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) return false;
     __builtin_amdgcn_s_sleep(1);
     return true;
 }
 
-DEV void mark(const Io& io, int k) {
-    if (io.tr && lane_id() == 0) io.tr[k] = rt();
+// Barrier of the workgroup's waves: the hardware barrier. It has no timeout, so the kernel keeps
+// one rule: every wave runs the same sequence of barriers whatever happens. Waits that give up
+// (watchdog, abort) just return; no wave leaves its task or its queue early, so a barrier never
+// waits for a wave that will not come.
+DEV void cbar() { __syncthreads(); }
+
+// ------------------------------------------------------------------ task geometry
+
+DEV uint32_t act_bytes(const KParams& P) { return P.act_f32 ? 4u : 2u; }
+DEV uint32_t kv_row_bytes(const KParams& P) { return (uint32_t)P.hd * act_bytes(P); }
+DEV uint32_t K_of(const KParams& P, int op) {
+    return op == AMK_OP_OPROJ ? (uint32_t)(P.nH * P.hd) : op == AMK_OP_DOWN ? (uint32_t)P.I : (uint32_t)P.H;
+}
+DEV bool is_gemv(int op) {
+    return op == AMK_OP_QKV || op == AMK_OP_OPROJ || op == AMK_OP_GATEUP || op == AMK_OP_DOWN || op == AMK_OP_LM;
 }
 
-constexpr int kCoherent = 16;   // load cache policy: device-coherent (the agent-scope load's)
+// history positions [h0, h1) of attention chunk c of nc at position pos (the current position
+// pos itself belongs to the last chunk and comes from the flag-carrying words)
+DEV void chunk_range(int pos, uint32_t c, uint32_t nc, uint32_t& h0, uint32_t& h1) {
+    const uint32_t n = (uint32_t)pos + 1;
+    h0 = (uint32_t)((uint64_t)n * c / nc);
+    h1 = (uint32_t)((uint64_t)n * (c + 1) / nc);
+    if (h1 > (uint32_t)pos) h1 = (uint32_t)pos;
+    if (h0 > h1) h0 = h1;
+}
 
-// One range of flag-carrying words a gather polls: n words from src into LDS at dst (8 bytes a
-// word, in order; the LDS area is a whole number of 1 KiB blocks of 128 words).
-struct GSeg {
-    const u64* src;
-    uint32_t n;
-    uint8_t* dst;
+DEV const uint8_t* kv_ptr(const KParams& P, int layer, int kv, int g, uint32_t row) {
+    const uint64_t idx = ((((uint64_t)layer * 2 + kv) * P.nKV + g) * P.max_ctx + row) * P.hd;
+    return (const uint8_t*)P.kv + idx * act_bytes(P);
+}
+
+// ------------------------------------------------------------------ weight streaming
+
+// The loads of one wave for one GEMV tile, in order: for each of the wave's rows (w, w + 8, ...)
+// its row_loads() 1 KiB loads. A group is kLoadSlots consecutive loads; lane l's part of load
+// j of a row is bytes [1024 j + 16 l, + 16) of that row (past the row's end the lane re-reads
+// the row's first 16 bytes and ignores them). Buffer A holds the even groups, B the odd ones.
+// Inside a task every issue sends exactly kLoadSlots loads (slots past the wave's loads read a
+// fixed 16-byte dummy), so the compiler can count the loads in flight and wait for one buffer
+// only.
+struct Geo {
+    const uint8_t* w0;     // the wave's first row
+    uint32_t rstride;      // bytes between the wave's rows (kComputeWaves rows)
+    uint32_t pitch, nj;    // row bytes, loads per row
+    uint32_t nloads;       // loads of this wave: its rows times nj
+    uint32_t ng;           // groups
 };
 
-// Wait until every word of up to three ranges carries the current flag, the words landing in
-// LDS. Each round fetches every incomplete 1 KiB block at once with device-coherent
-// memory-to-LDS loads (lane l: words 2l, 2l + 1 of the block; lanes past a range's end re-read
-// its first word), waits for them, and checks the flags in LDS; a block whose words all carry
-// the flag is done. At most kMaxGatherBlocks blocks in all (the lowering keeps every task's
-// inputs within it). The ranges are selected by value (no indexed array, so nothing goes to
-// private memory).
-DEV void gather(Io& io, uint32_t ns, GSeg g0, GSeg g1 = GSeg{nullptr, 0u, nullptr}, GSeg g2 = GSeg{nullptr, 0u, nullptr}) {
+DEV Geo geo_of(const Ctx& c, const DevTask& T, int cw) {
+    const KParams& P = *c.P;
+    Geo s;
+    const uint32_t K = K_of(P, T.op);
+    s.pitch = row_pitch(P.wfmt, K);
+    s.nj = row_loads(P.wfmt, K);
+    s.w0 = c.wcu + T.wofs + (uint64_t)cw * s.pitch;
+    s.rstride = (uint32_t)kComputeWaves * s.pitch;
+    const uint32_t nrows =
+        T.tile_rows > (uint32_t)cw ? (T.tile_rows - (uint32_t)cw + kComputeWaves - 1) / kComputeWaves : 0u;
+    s.nloads = nrows * s.nj;
+    s.ng = (s.nloads + kLoadSlots - 1) / kLoadSlots;
+    return s;
+}
+
+struct WBuf {
+    u32x4 w[kLoadSlots];
+};
+
+// Issue group g of a wave's loads into b.
+DEV void issue_group(const Ctx& c, const Geo& s, uint32_t g, WBuf& b) {
     const uint32_t lane = (uint32_t)lane_id();
-    const uint32_t flag = io.flag;
-    if (ns < 2) g1.n = 0;
-    if (ns < 3) g2.n = 0;
-    const uint32_t nb0 = gather_blocks(g0.n), nb1 = gather_blocks(g1.n), nb2 = gather_blocks(g2.n);
-    const uint32_t tot = nb0 + nb1 + nb2;
-    uint64_t mask = tot >= 64u ? ~0ull : ((1ull << tot) - 1ull);
-    uint32_t spins = 0;
-    // block b of the ranges: which range (by selection) and which block inside it
-#define AMK_LOCATE(b)                                                         \
-    const bool s0 = (b) < nb0, s1 = !s0 && (b) < nb0 + nb1;                   \
-    const u64* src = s0 ? g0.src : s1 ? g1.src : g2.src;                      \
-    const uint32_t n = s0 ? g0.n : s1 ? g1.n : g2.n;                          \
-    uint8_t* dst = s0 ? g0.dst : s1 ? g1.dst : g2.dst;                        \
-    const uint32_t blk = (b) - (s0 ? 0u : s1 ? nb0 : nb0 + nb1);              \
-    const uint32_t wi = blk * 128u + 2u * lane;
-    // First a light poll: eight sentinel words per block (every 16th word), 8 bytes each, until
-    // all carry the flag; only then are the blocks fetched whole (and any word still missing
-    // sends its block round again). The whole-block fetches of all CUs at once would otherwise
-    // load the fabric with repeated 1 KiB reads while the producers are still writing.
-    for (;;) {
-        bool ok = true;
+    const uint32_t f0 = g * kLoadSlots;
+    uint32_t i = f0 / s.nj, j = f0 - i * s.nj;
 #pragma unroll
-        for (uint32_t k = 0; k < 8; ++k) {
-            const uint32_t sx = lane + 64u * k;   // sentinel: block sx / 8, word 16 (sx % 8) + 15
-            const uint32_t b = sx / 8u < tot ? sx / 8u : 0u;
-            AMK_LOCATE(b)
-            (void)dst;
-            (void)wi;
-            uint32_t ws = blk * 128u + 16u * (sx % 8u) + 15u;
-            if (ws >= n) ws = n - 1u;
-            const u64 v = ll_load(src + ws);
-            ok &= sx / 8u >= tot || (uint32_t)(v >> 32) == flag;
-        }
-        if (__builtin_amdgcn_ballot_w64(!ok) == 0 || !spin_ok(io, spins)) break;
+    for (int k = 0; k < kLoadSlots; ++k) {
+        const uint32_t off = 1024u * j + 16u * lane;
+        const uint8_t* p = f0 + (uint32_t)k < s.nloads ? s.w0 + (uint64_t)i * s.rstride + (off < s.pitch ? off : 0u)
+                                                       : (const uint8_t*)c.P->norms;
+        b.w[k] = wload(p);
+        if (++j == s.nj) { j = 0; ++i; }
     }
-    while (mask) {
-        for (uint64_t m = mask; m; m &= m - 1ull) {
-            const uint32_t b = (uint32_t)__builtin_ctzll(m);
-            AMK_LOCATE(b)
-            __builtin_amdgcn_global_load_lds((const void*)(src + (wi < n ? wi : 0u)), LDS3(dst + blk * 1024u), 16, 0, kCoherent);
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        for (uint64_t m = mask; m; m &= m - 1ull) {
-            const uint32_t b = (uint32_t)__builtin_ctzll(m);
-            AMK_LOCATE(b)
-            (void)src;
-            const u32x4 v = *(const u32x4*)(dst + blk * 1024u + 16u * lane);
-            const bool ok = (wi >= n || v.y == flag) && (wi + 1u >= n || v.w == flag);
-            if (__builtin_amdgcn_ballot_w64(!ok) == 0) mask &= ~(1ull << b);
-        }
-        if (!mask || !spin_ok(io, spins)) break;
-    }
-#undef AMK_LOCATE
+    compiler_fence();
 }
 
-// payload of gathered word i (an array of 8-byte words in LDS)
-DEV uint32_t wpl(const uint8_t* words, uint32_t i) { return *(const uint32_t*)(words + 8u * i); }
-// activation value k of a gathered vector (fp32: one value a word; bf16: two, low half first)
-DEV double wval(const uint8_t* words, uint32_t k, bool f32) {
-    return f32 ? (double)__uint_as_float(wpl(words, k)) : bf2d((wpl(words, k >> 1) >> (16u * (k & 1u))) & 0xffffu);
-}
-// fp64 value j of a gathered array of doubles (two words each, low half first)
-DEV double wdbl(const uint8_t* words, uint32_t j) {
-    return __longlong_as_double((long long)(((uint64_t)wpl(words, 2u * j + 1u) << 32) | wpl(words, 2u * j)));
+// two bf16 values packed in a dword, as the operand type of the bf16 dot instruction (the
+// dword is taken by value: a bit cast straight from a vector element access lost the element)
+DEV bf16x2 as_bf2(uint32_t u) {
+    bf16x2 r;
+    __builtin_memcpy(&r, &u, 4);
+    return r;
 }
 
-// The input of a GEMV task (its words, or the embedding row as words) and, for O and down, its
-// residual rows, gathered together; then the input's sum of squares and largest magnitude
-// (fp64, into the control area).
-DEV void io_gemv_inputs(Io& io, const DevTask& T, uint32_t roff) {
-    const Ctx& c = *io.c;
-    CKP& P = *c.P;
-    const bool f32 = P.act_f32 != 0;
-    const uint32_t vpw = f32 ? 1u : 2u;
+// Dot product of lane l's 16 weight bytes of load j of a row with the matching slice of the
+// staged input. Weights are widened in registers: fp32 as is; bf16 pairs go through the bf16
+// dot instruction; int8 codes are converted to fp32 and their top halves (exactly the code as
+// bf16) packed in pairs for the same instruction; int4 codes are nibbles minus the bias 8, with
+// the lane's 32 codes (inside one 128-column group) scaled by the group's fp16 scale from LDS.
+// Products are exact in fp32; sums are fp32.
+template <int FMT>
+DEV float dot16(const Lds& S, u32x4 w, uint32_t j, uint32_t lane, uint32_t row, uint32_t K) {
+    const uint16_t* hb = (const uint16_t*)S.hb;
+    float acc = 0.f;
+    if constexpr (FMT == AMK_F32) {
+        const uint32_t c0 = 256u * j + 4u * lane;
+        const u32x4 hv = *(const u32x4*)(S.hf + c0);
+        acc += __uint_as_float(w.x) * __uint_as_float(hv.x);
+        acc += __uint_as_float(w.y) * __uint_as_float(hv.y);
+        acc += __uint_as_float(w.z) * __uint_as_float(hv.z);
+        acc += __uint_as_float(w.w) * __uint_as_float(hv.w);
+    } else if constexpr (FMT == AMK_BF16) {
+        const uint32_t c0 = 512u * j + 8u * lane;
+        const u32x4 hv = *(const u32x4*)(hb + c0);
+        const uint32_t a[4] = {w.x, w.y, w.z, w.w}, h[4] = {hv.x, hv.y, hv.z, hv.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(a[k]), as_bf2(h[k]), acc, false);
+    } else if constexpr (FMT == AMK_INT8_PC) {
+        const uint32_t c0 = 1024u * j + 16u * lane;
+        const u32x4 h0 = *(const u32x4*)(hb + c0), h1 = *(const u32x4*)(hb + c0 + 8);
+        const uint32_t hh[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+        const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const float f0 = (float)(int8_t)((a[k] >> (16 * p)) & 0xffu);
+                const float f1 = (float)(int8_t)((a[k] >> (16 * p + 8)) & 0xffu);
+                // bf16 pair (code 2m, code 2m+1): the high halves of the two fp32 values
+                const uint32_t wp = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+                acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(wp), as_bf2(hh[2 * k + p]), acc, false);
+            }
+    } else {   // int4 g128
+        const uint32_t c0 = 2048u * j + 32u * lane;
+        const float sc = h2f(((const uint16_t*)S.kvb)[row * (K / 128) + c0 / 128]);
+        const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+        float p = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const u32x4 hv = *(const u32x4*)(hb + c0 + 8 * k);
+            const uint32_t hh[4] = {hv.x, hv.y, hv.z, hv.w};
+#pragma unroll
+            for (int b = 0; b < 8; ++b) {
+                const uint32_t hw = hh[b >> 1];
+                p += (float)((int)((a[k] >> (4 * b)) & 0xfu) - 8) * bf2f((b & 1) ? (hw >> 16) : (hw & 0xffffu));
+            }
+        }
+        acc = sc * p;
+    }
+    return acc;
+}
+
+// Consume group g of the wave's loads from b: accumulate, and at each row's last load reduce
+// over the wave and write S.red[row] (times the row's fp16 scale for int8). `acc` carries a row
+// split across groups.
+template <int FMT>
+DEV void compute_group(const Lds& S_, const Geo& s, int cw, uint32_t K, uint32_t g, const WBuf& b, float& acc) {
+    Lds& S = const_cast<Lds&>(S_);
     const uint32_t lane = (uint32_t)lane_id();
-    const uint32_t K = T.k, nw = K / vpw;
-    uint8_t* words = c.L.stage + roff;
-    const bool resid = T.op == AMK_OP_OPROJ || T.op == AMK_OP_DOWN;
-    const uint32_t r0 = T.arg[0], nr = T.arg[1] / vpw;
-    uint8_t* rw = (uint8_t*)c.L.misc->residw;
-    GSeg gi{nullptr, 0u, nullptr}, gr{nullptr, 0u, nullptr};
-    if (T.src != kNoWord) gi = GSeg{P.ll + T.src, nw, words};
-    else {   // layer 0's QKV: the embedding row of the input token
-        const uint32_t* er = (const uint32_t*)((const uint8_t*)P.embed + (uint64_t)io.token * K * act_bytes(P));
-        for (uint32_t i = lane; i < nw; i += 64u) *(u64*)(words + 8u * i) = er[i];
+    const uint32_t f0 = g * kLoadSlots;
+    uint32_t i = f0 / s.nj, j = f0 - i * s.nj;
+#pragma unroll
+    for (int k = 0; k < kLoadSlots; ++k) {
+        if (f0 + (uint32_t)k < s.nloads) {
+            const uint32_t row = (uint32_t)cw + kComputeWaves * i;
+            const float d = dot16<FMT>(S, b.w[k], j, lane, row, K);
+            acc += 1024u * j + 16u * lane < s.pitch ? d : 0.f;
+            if (j + 1 == s.nj) {
+                float sum = wave_sum_dpp(acc);
+                if constexpr (FMT == AMK_INT8_PC) sum *= h2f(((const uint16_t*)S.kvb)[row]);
+                if (lane == 0) S.red[row] = sum;
+                acc = 0.f;
+            }
+        }
+        if (++j == s.nj) { j = 0; ++i; }
     }
-    if (resid) {
-        if (T.aux != kNoWord) gr = GSeg{P.ll + T.aux + r0 / vpw, nr, rw};
-        else {   // layer 0's O projection: the residual is the embedding row
-            const uint32_t* er = (const uint32_t*)((const uint8_t*)P.embed + (uint64_t)io.token * P.H * act_bytes(P));
-            for (uint32_t i = lane; i < nr; i += 64u) *(u64*)(rw + 8u * i) = er[r0 / vpw + i];
+}
+
+// All groups of the wave's rows of task T, double-buffered: while one buffer is consumed the
+// other is in flight. On entry A holds group 0 (kAheadGroups >= 1) and B group 1
+// (kAheadGroups == 2), issued ahead and complete: the input staging waited for every load.
+template <int FMT>
+DEV void gemv_rows_fmt(const Ctx& c, const DevTask& T, int cw, WBuf& A, WBuf& B) {
+    const Geo s = geo_of(c, T, cw);
+    const uint32_t K = K_of(*c.P, T.op);
+    // nothing is in flight here; saying so lets the compiler count exactly from this point
+    __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+    if (kAheadGroups == 0 && s.ng > 0) issue_group(c, s, 0, A);
+    if (kAheadGroups <= 1 && s.ng > 1) issue_group(c, s, 1, B);
+    float acc = 0.f;
+    uint32_t g = 0;
+    for (; g + 2 < s.ng; g += 2) {
+        compute_group<FMT>(*c.S, s, cw, K, g, A, acc);
+        issue_group(c, s, g + 2, A);
+        compute_group<FMT>(*c.S, s, cw, K, g + 1, B, acc);
+        issue_group(c, s, g + 3, B);
+    }
+    if (g < s.ng) compute_group<FMT>(*c.S, s, cw, K, g, A, acc);
+    if (g + 1 < s.ng) compute_group<FMT>(*c.S, s, cw, K, g + 1, B, acc);
+}
+
+// Issue the first groups of task T's weights (the next task's, ahead of its inputs).
+DEV void prefetch_task(const Ctx& c, const DevTask& T, int cw, WBuf& A, WBuf& B) {
+    if (kAheadGroups == 0) return;
+    const Geo s = geo_of(c, T, cw);
+    if (s.ng > 0) issue_group(c, s, 0, A);
+    if (kAheadGroups == 2 && s.ng > 1) issue_group(c, s, 1, B);
+}
+
+DEV void gemv_rows(const Ctx& c, const DevTask& T, int cw, WBuf& A, WBuf& B) {
+    switch (c.P->wfmt) {
+    case AMK_F32: gemv_rows_fmt<AMK_F32>(c, T, cw, A, B); break;
+    case AMK_BF16: gemv_rows_fmt<AMK_BF16>(c, T, cw, A, B); break;
+    case AMK_INT8_PC: gemv_rows_fmt<AMK_INT8_PC>(c, T, cw, A, B); break;
+    default: gemv_rows_fmt<AMK_INT4_G128>(c, T, cw, A, B); break;
+    }
+}
+
+// ------------------------------------------------------------------ flag-carrying words
+
+// Words each thread has in flight at once while gathering flag-carrying words. The gather walks
+// its words in chunks of this many, so its register use does not grow with the vector length.
+constexpr int kGatherChunk = 6;
+
+// Wait until words [0, n) of a flag-carrying buffer all carry `flag`; hand each payload to fn.
+// Each thread polls words tid + k * kComputeThreads, kGatherChunk of them at a time.
+template <typename F>
+DEV bool ll_gather(const Ctx& c, const u64* base, uint32_t n, int ctid, F&& fn) {
+    const uint32_t flag = c.P->flag;
+    const uint32_t step = (uint32_t)kGatherChunk * kComputeThreads;
+    for (uint32_t i0 = (uint32_t)ctid; i0 < n; i0 += step) {
+        u64 w[kGatherChunk];
+#pragma unroll
+        for (int k = 0; k < kGatherChunk; ++k) {
+            const uint32_t i = i0 + (uint32_t)k * kComputeThreads;
+            w[k] = i < n ? ll_load(base + i) : ((u64)flag << 32);
+        }
+        uint32_t spins = 0;
+        for (;;) {
+            bool done = true;
+#pragma unroll
+            for (int k = 0; k < kGatherChunk; ++k) done &= (uint32_t)(w[k] >> 32) == flag;
+            if (done) break;
+            if (!spin_ok(c, spins)) return false;
+#pragma unroll
+            for (int k = 0; k < kGatherChunk; ++k) {
+                const uint32_t i = i0 + (uint32_t)k * kComputeThreads;
+                if ((uint32_t)(w[k] >> 32) != flag) w[k] = ll_load(base + i);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kGatherChunk; ++k) {
+            const uint32_t i = i0 + (uint32_t)k * kComputeThreads;
+            if (i < n) fn(i, (uint32_t)w[k]);
         }
     }
-    // one gather for both (whichever of them come from flag words)
-    if (gi.n && gr.n) gather(io, 2, gi, gr);
-    else if (gi.n) gather(io, 1, gi);
-    else if (gr.n) gather(io, 1, gr);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the gains' loads too
+    return true;
 }
 
-// The norm gains of the input (fp32) after the planes of the stage, by memory-to-LDS loads that
-// are left in flight (the input gather waits for them with its own loads).
-DEV void io_gains(const Io& io, int ni, uint32_t K, uint32_t off) {
-    const Ctx& c = *io.c;
-    CKP& P = *c.P;
-    const uint8_t* src = (const uint8_t*)(P.norms + (uint64_t)ni * P.H);
-    const uint32_t lane16 = 16u * (uint32_t)lane_id(), nbytes = 4u * K;
-    for (uint32_t b = 0; b < nbytes; b += 1024u)
-        if (b + lane16 < nbytes) __builtin_amdgcn_global_load_lds((const void*)(src + b + lane16), LDS3(c.L.stage + off + b), 16, 0, 0);
+DEV float rA(const KParams& P, float v) { return P.act_f32 ? v : bf2f(f2bf(v)); }
+// payload of a word -> activation value j (0/1 inside the word)
+DEV float word_val(const KParams& P, uint32_t payload, int j) {
+    return P.act_f32 ? __uint_as_float(payload) : bf2f(j ? (payload >> 16) : (payload & 0xffffu));
+}
+DEV uint32_t pack2(const KParams& P, float a, float b) {
+    return P.act_f32 ? __float_as_uint(a) : (f2bf(a) | (f2bf(b) << 16));
+}
+// store the input-vector value i (already rounded to the activation format) into the stage
+DEV void hput(const KParams& P, Lds& S, uint32_t i, float v) {
+    if (P.act_f32) S.hf[i] = v;
+    else ((uint16_t*)S.hb)[i] = (uint16_t)f2bf(v);
 }
 
-DEV uint32_t pack2(bool f32, double a, double b) {
-    return f32 ? act_bits(a, true) : (act_bits(a, false) | (act_bits(b, false) << 16));
-}
+DEV u64* ll_layer(const KParams& P, const LLLayout& y, int layer) { return P.ll + (u64)layer * y.layer_words; }
 
-// The GEMV epilogue from the fp64 row results: RoPE and the KV-cache append (QKV), the residual
-// add (O, down), SwiGLU (gate/up), the fp32 logits and the tile argmax (LM head).
-DEV void io_gemv_epilogue(Io& io, const DevTask& T) {
-    const Ctx& c = *io.c;
-    CKP& P = *c.P;
-    const bool f32 = P.act_f32 != 0;
-    const uint32_t vpw = f32 ? 1u : 2u;
-    const uint32_t lane = (uint32_t)lane_id();
-    const uint32_t flag = io.flag;
-    const int l = T.layer;
-    const double* red = c.L.red;
-    u64* const dst = P.ll + T.dst;
+// The RMSNorm gains of a GEMV task's input (null for inputs without a norm).
+DEV const float* gains_of(const KParams& P, const DevTask& T) {
     switch (T.op) {
+    case AMK_OP_QKV: return P.norms + (uint64_t)T.layer * 2 * P.H;
+    case AMK_OP_GATEUP: return P.norms + ((uint64_t)T.layer * 2 + 1) * P.H;
+    case AMK_OP_LM: return P.norms + (uint64_t)P.L * 2 * P.H;
+    default: return nullptr;
+    }
+}
+
+constexpr int kMaxGainsPerThread = kMaxHidden / kComputeThreads;
+
+// Stage the GEMV input of a task into S.hb (activation format), with RMSNorm when gains != 0.
+// Source: flag-carrying words (src) or, for layer 0, the embedding row of the input token. The
+// thread's norm gains are loaded before the wait so their latency overlaps it.
+DEV void stage_input(const Ctx& c, int ctid, const u64* src, const void* embed_row, uint32_t K,
+                     const float* gains) {
+    const KParams& P = *c.P;
+    Lds& S = *c.S;
+    const uint32_t vpw = P.act_f32 ? 1u : 2u;
+    const uint32_t nw = K / vpw;
+    float gr[kMaxGainsPerThread];
+    if (gains) {
+#pragma unroll
+        for (int k = 0; k < kMaxGainsPerThread; ++k) {
+            const uint32_t i = (uint32_t)ctid + (uint32_t)k * kComputeThreads;
+            gr[k] = i < K ? gains[i] : 0.f;
+        }
+    }
+    float ss = 0.f;
+    // raw values go to the stage first (exact: they are activation-format values)
+    if (src) {
+        (void)ll_gather(c, src, nw, ctid, [&](uint32_t i, uint32_t pl) {
+                for (uint32_t j = 0; j < vpw; ++j) {
+                    float v = word_val(P, pl, (int)j);
+                    ss += v * v;
+                    if (P.act_f32) S.hf[i * vpw + j] = v;
+                    else ((uint16_t*)S.hb)[i * vpw + j] = (uint16_t)(j ? (pl >> 16) : (pl & 0xffffu));
+                }
+            });
+    } else {
+        for (uint32_t i = (uint32_t)ctid; i < K; i += kComputeThreads) {
+            float v;
+            if (P.act_f32) { v = ((const float*)embed_row)[i]; S.hf[i] = v; }
+            else { uint16_t b = ((const uint16_t*)embed_row)[i]; v = bf2f(b); ((uint16_t*)S.hb)[i] = b; }
+            ss += v * v;
+        }
+    }
+    if (!gains) {
+        cbar();
+        return;
+    }
+    // RMSNorm: h_i = round_act(x_i * r * g_i), r = 1 / sqrt(mean(x^2) + eps)
+    ss = wave_sum_dpp(ss);
+    const int cw = ctid >> 6;
+    if (lane_id() == 0) S.fpart[cw] = ss;
+    cbar();
+    float tot = 0.f;
+    for (int w = 0; w < kComputeWaves; ++w) tot += S.fpart[w];
+    const float r = 1.0f / __fsqrt_rn(tot / (float)K + P.eps);
+#pragma unroll
+    for (int k = 0; k < kMaxGainsPerThread; ++k) {
+        const uint32_t i = (uint32_t)ctid + (uint32_t)k * kComputeThreads;
+        if (i < K) {
+            const float x = P.act_f32 ? S.hf[i] : bf2f(((uint16_t*)S.hb)[i]);
+            hput(P, S, i, rA(P, (x * r) * gr[k]));
+        }
+    }
+    cbar();
+}
+
+// ------------------------------------------------------------------ the ops
+
+struct TaskEnv {
+    const Ctx* c;
+    int ctid, cw;
+    LLLayout y;
+    int token;
+    uint64_t* tr;        // this task's trace slots, or null
+};
+
+// timestamp slot k of the current task (first thread only)
+DEV void mark(const TaskEnv& e, int k) {
+    if (e.tr && e.ctid == 0) e.tr[k] = rt();
+}
+
+// A GEMV task: wait for and stage its input vector (RMSNorm fused where the model has one), run
+// the tile's rows, then the op's epilogue: RoPE and the KV-cache append (QKV), the residual add
+// (O, down), SwiGLU (gate/up), the tile argmax and logits (LM head). On entry the first groups
+// of this task's weight loads are in A (and B), issued ahead.
+DEV void op_gemv(const TaskEnv& e, const DevTask& T, WBuf& A, WBuf& B) {
+    const Ctx& c = *e.c;
+    const KParams& P = *c.P;
+    Lds& S = *c.S;
+    const int op = T.op, l = T.layer, ctid = e.ctid;
+    const uint32_t K = K_of(P, op);
+    const uint32_t vpw = P.act_f32 ? 1u : 2u;
+    const u64* src = nullptr;
+    const void* emb = nullptr;
+    const uint64_t esz = act_bytes(P);
+    const u64* LLl = ll_layer(P, e.y, l);
+    switch (op) {
+    case AMK_OP_QKV:
+        if (l == 0) emb = (const uint8_t*)P.embed + (uint64_t)e.token * P.H * esz;
+        else src = ll_layer(P, e.y, l - 1) + e.y.xd;
+        break;
+    case AMK_OP_OPROJ: src = LLl + e.y.o; break;
+    case AMK_OP_GATEUP: src = LLl + e.y.xo; break;
+    case AMK_OP_DOWN: src = LLl + e.y.a; break;
+    case AMK_OP_LM: src = ll_layer(P, e.y, P.L - 1) + e.y.xd; break;
+    }
+
+    // quantised tiles: the row scales (int8) or group scales (int4) go to LDS. Any wait below
+    // waits for the weight loads already in flight too, so these loads cost no extra latency.
+    const uint32_t sc_chunks = (uint32_t)((tile_bytes(P.wfmt, K, T.tile_rows) - tile_scale_off(P.wfmt, K, T.tile_rows)) / 16);
+    if (sc_chunks) {
+        const uint8_t* sb = c.wcu + T.wofs + tile_scale_off(P.wfmt, K, T.tile_rows);
+        for (uint32_t q = (uint32_t)ctid; q < sc_chunks; q += kComputeThreads)
+            *(u32x4*)(S.kvb + 16 * q) = *(const u32x4*)(sb + 16ull * q);
+    }
+    // QKV: this thread's rotary cos/sin (quad ctid), loaded now so the load overlaps the input wait
+    float rc0 = 1.f, rs0 = 0.f, rc1 = 1.f, rs1 = 0.f;
+    if (op == AMK_OP_QKV && (uint32_t)ctid < T.arg[1]) {
+        const uint32_t u = T.arg[0] + (uint32_t)ctid, per = (uint32_t)P.hd / 4;
+        if (u / per < (uint32_t)(P.nH + P.nKV)) {   // q and k heads rotate, v heads do not
+            const float4 cs = *(const float4*)(P.rope + ((uint64_t)P.pos * (P.hd / 2) + 2 * (u % per)) * 2);
+            rc0 = cs.x; rs0 = cs.y; rc1 = cs.z; rs1 = cs.w;
+        }
+    }
+    // residual rows (O and down): from the previous x (or the embedding row at layer 0)
+    if (op == AMK_OP_OPROJ || op == AMK_OP_DOWN) {
+        const uint32_t r0 = T.arg[0], n = T.arg[1];
+        if (op == AMK_OP_OPROJ && l == 0) {
+            const uint8_t* er = (const uint8_t*)P.embed + (uint64_t)e.token * P.H * esz;
+            for (uint32_t i = (uint32_t)ctid; i < n; i += kComputeThreads)
+                S.att[i] = P.act_f32 ? ((const float*)er)[r0 + i] : bf2f(((const uint16_t*)er)[r0 + i]);
+        } else {
+            const u64* rs = (op == AMK_OP_OPROJ ? ll_layer(P, e.y, l - 1) + e.y.xd : LLl + e.y.xo) + r0 / vpw;
+            (void)ll_gather(c, rs, n / vpw, ctid, [&](uint32_t i, uint32_t pl) {
+                    for (uint32_t j = 0; j < vpw; ++j) S.att[i * vpw + j] = word_val(P, pl, (int)j);
+                });
+        }
+    }
+    stage_input(c, ctid, src, emb, K, gains_of(P, T));   // ends with a barrier
+    mark(e, 1);
+    gemv_rows(c, T, e.cw, A, B);
+    if (e.tr && ctid == 0) e.tr[4] = rt();
+    cbar();
+    mark(e, 2);
+    const uint32_t flag = P.flag;
+    switch (op) {
     case AMK_OP_QKV: {
         // rows come in quads (r, r+1, r+hd/2, r+hd/2+1) of one head of the fused [q; k; v]
         const uint32_t nq = T.arg[1], per = (uint32_t)P.hd / 4, half = (uint32_t)P.hd / 2;
         const uint32_t qd = (uint32_t)(P.nH * P.hd), kd = (uint32_t)(P.nKV * P.hd);
-        u64* out = dst;
-        for (uint32_t k = lane; k < nq; k += 64u) {
+        u64* out = (u64*)(LLl + e.y.qkv);
+        // one quad per thread (a task has at most kRedRows / 4 <= kComputeThreads quads)
+        if ((uint32_t)ctid < nq) {
+            const uint32_t k = (uint32_t)ctid;
             const uint32_t u = T.arg[0] + k, head = u / per, m = u % per;
             const uint32_t base = head * (uint32_t)P.hd;
-            double v0 = red[4 * k], v1 = red[4 * k + 1], v2 = red[4 * k + 2], v3 = red[4 * k + 3];
-            if (base < qd + kd) {   // q and k heads rotate, v heads do not
-                const double* cs = P.rope + ((uint64_t)P.pos * half + 2 * m) * 2;
-                const double c0 = cs[0], s0 = cs[1], c1 = cs[2], s1 = cs[3];
-                const double a0 = v0 * c0 - v2 * s0, b0 = v2 * c0 + v0 * s0;
-                const double a1 = v1 * c1 - v3 * s1, b1 = v3 * c1 + v1 * s1;
+            float v0 = S.red[4 * k], v1 = S.red[4 * k + 1], v2 = S.red[4 * k + 2], v3 = S.red[4 * k + 3];
+            const bool rot = base < qd + kd;
+            if (rot) {
+                const float a0 = v0 * rc0 - v2 * rs0, b0 = v2 * rc0 + v0 * rs0;
+                const float a1 = v1 * rc1 - v3 * rs1, b1 = v3 * rc1 + v1 * rs1;
                 v0 = a0; v2 = b0; v1 = a1; v3 = b1;
             }
+            v0 = rA(P, v0); v1 = rA(P, v1); v2 = rA(P, v2); v3 = rA(P, v3);
             const uint32_t r0 = base + 2 * m, r2 = base + half + 2 * m;
-            if (f32) {
-                ll_store(out + r0, act_bits(v0, true), flag);
-                ll_store(out + r0 + 1, act_bits(v1, true), flag);
-                ll_store(out + r2, act_bits(v2, true), flag);
-                ll_store(out + r2 + 1, act_bits(v3, true), flag);
+            if (P.act_f32) {
+                ll_store(out + r0, __float_as_uint(v0), flag);
+                ll_store(out + r0 + 1, __float_as_uint(v1), flag);
+                ll_store(out + r2, __float_as_uint(v2), flag);
+                ll_store(out + r2 + 1, __float_as_uint(v3), flag);
             } else {
-                ll_store(out + r0 / 2, pack2(false, v0, v1), flag);
-                ll_store(out + r2 / 2, pack2(false, v2, v3), flag);
+                ll_store(out + r0 / 2, pack2(P, v0, v1), flag);
+                ll_store(out + r2 / 2, pack2(P, v2, v3), flag);
             }
             if (base >= qd) {   // k or v row: append to the cache at pos (after the signal)
                 const int isv = base >= qd + kd;
                 const int g = (int)((base - qd - (isv ? kd : 0)) / (uint32_t)P.hd);
-                uint8_t* row = (uint8_t*)P.kv + kv_off(P, l, isv, g, (uint32_t)P.pos);
+                uint8_t* row = (uint8_t*)kv_ptr(P, l, isv, g, (uint32_t)P.pos);
                 const uint32_t i0 = 2 * m, i2 = half + 2 * m;
-                if (f32) {
-                    uint32_t* f = (uint32_t*)row;
-                    f[i0] = act_bits(v0, true); f[i0 + 1] = act_bits(v1, true);
-                    f[i2] = act_bits(v2, true); f[i2 + 1] = act_bits(v3, true);
+                if (P.act_f32) {
+                    float* f = (float*)row;
+                    f[i0] = v0; f[i0 + 1] = v1; f[i2] = v2; f[i2 + 1] = v3;
                 } else {
                     uint32_t* h = (uint32_t*)row;
-                    h[i0 / 2] = pack2(false, v0, v1);
-                    h[i2 / 2] = pack2(false, v2, v3);
+                    h[i0 / 2] = pack2(P, v0, v1);
+                    h[i2 / 2] = pack2(P, v2, v3);
                 }
             }
         }
@@ -1089,38 +662,37 @@ DEV void io_gemv_epilogue(Io& io, const DevTask& T) {
     case AMK_OP_OPROJ:
     case AMK_OP_DOWN: {
         const uint32_t r0 = T.arg[0], n = T.arg[1];
-        u64* out = dst + r0 / vpw;
-        const uint8_t* rw = (const uint8_t*)c.L.misc->residw;
-        for (uint32_t i = lane; i < n / vpw; i += 64u) {
-            const double a = wval(rw, i * vpw, f32) + red[i * vpw];
-            const double b = vpw == 2 ? wval(rw, i * vpw + 1, f32) + red[i * vpw + 1] : 0.0;
-            ll_store(out + i, pack2(f32, a, b), flag);
+        u64* out = (u64*)(LLl + (op == AMK_OP_OPROJ ? e.y.xo : e.y.xd)) + r0 / vpw;
+        for (uint32_t i = (uint32_t)ctid; i < n / vpw; i += kComputeThreads) {
+            const float a = rA(P, S.att[i * vpw] + S.red[i * vpw]);
+            const float b = vpw == 2 ? rA(P, S.att[i * vpw + 1] + S.red[i * vpw + 1]) : 0.f;
+            ll_store(out + i, pack2(P, a, b), flag);
         }
         break;
     }
     case AMK_OP_GATEUP: {
-        // SwiGLU: silu(G) U = G / (1 + exp(-G)) * U
         const uint32_t j0 = T.arg[0], n = T.arg[1];
-        u64* out = dst + j0 / vpw;
-        for (uint32_t i = lane; i < n / vpw; i += 64u) {
-            double v[2] = {0.0, 0.0};
-            for (uint32_t j = 0; j < vpw; ++j) {
-                const double G = red[2 * (i * vpw + j)], U = red[2 * (i * vpw + j) + 1];
-                v[j] = (G / (1.0 + exp(-G))) * U;
+        u64* out = (u64*)(LLl + e.y.a) + j0 / vpw;
+        for (uint32_t i = (uint32_t)ctid; i < n / vpw; i += kComputeThreads) {
+            float v[2] = {0.f, 0.f};
+#pragma unroll
+            for (uint32_t j = 0; j < 2; ++j) {
+                if (j >= vpw) break;
+                const float G = S.red[2 * (i * vpw + j)], U = S.red[2 * (i * vpw + j) + 1];
+                v[j] = rA(P, (G / (1.0f + expf(-G))) * U);
             }
-            ll_store(out + i, pack2(f32, v[0], v[1]), flag);
+            ll_store(out + i, pack2(P, v[0], v[1]), flag);
         }
         break;
     }
     case AMK_OP_LM: {
-        // logits in fp32; tile argmax over them (lowest index among maxima; any NaN marks the tile)
+        // tile argmax (lowest index among maxima; any NaN marks the tile) and the logits
         const uint32_t v0 = T.arg[0], n = T.arg[1];
         float best = -INFINITY;
         int bi = 0x7fffffff;
         bool nan = false;
-        for (uint32_t i = lane; i < n; i += 64u) {
-            const float v = (float)red[i];
-            if (P.logits) P.logits[v0 + i] = v;
+        for (uint32_t i = (uint32_t)ctid; i < n; i += kComputeThreads) {
+            const float v = S.red[i];
             if (v != v) nan = true;
             else if (v > best || (v == best && (int)(v0 + i) < bi)) { best = v; bi = (int)(v0 + i); }
         }
@@ -1129,175 +701,439 @@ DEV void io_gemv_epilogue(Io& io, const DevTask& T) {
             const int oi = __shfl_xor(bi, o, 64);
             if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
         }
-        const bool anynan = __builtin_amdgcn_ballot_w64(nan) != 0;
-        if (lane == 0) {
-            u64* out = dst + 2ull * T.arg[2];
-            ll_store(out, __float_as_uint(anynan ? __uint_as_float(0x7fc00000u) : best), flag);
-            ll_store(out + 1, (uint32_t)(anynan ? -1 : bi), flag);
+        const int anynan = __any(nan);
+        if (lane_id() == 0) { S.fpart[e.cw] = best; S.ipart[e.cw] = anynan ? -1 : bi; }
+        cbar();
+        if (ctid == 0) {
+            float b = S.fpart[0];
+            int i0 = S.ipart[0];
+            bool badn = i0 < 0;
+            for (int w = 1; w < kComputeWaves; ++w) {
+                if (S.ipart[w] < 0) badn = true;
+                else if (S.fpart[w] > b || (S.fpart[w] == b && S.ipart[w] < i0)) { b = S.fpart[w]; i0 = S.ipart[w]; }
+            }
+            u64* out = P.ll + e.y.lmpart + 2ull * T.arg[2];
+            ll_store(out, __float_as_uint(badn ? __uint_as_float(0x7fc00000u) : b), flag);
+            ll_store(out + 1, (uint32_t)(badn ? -1 : i0), flag);
         }
+        if (P.logits)
+            for (uint32_t i = (uint32_t)ctid; i < n; i += kComputeThreads) P.logits[v0 + i] = S.red[i];
         break;
     }
     }
 }
 
-// Attention: gather q of the task's heads (and the current k, v in the last chunk) as words past
-// the attention stage, then widen them into the stage as fp64.
-DEV void io_attn_inputs(Io& io, const DevTask& T) {
-    const Ctx& c = *io.c;
-    CKP& P = *c.P;
-    const bool f32 = P.act_f32 != 0;
-    const uint32_t vpw = f32 ? 1u : 2u;
-    const uint32_t h0 = T.arg[0], nh = T.arg[1], hd = (uint32_t)P.hd;
-    const uint32_t lane = (uint32_t)lane_id();
-    const int g = (int)(h0 * (uint32_t)P.nKV / (uint32_t)P.nH);
-    const AttnStage A = attn_stage(c.L, nh, hd);
-    const u64* Lq = P.ll + T.src;
-    const bool cur = T.arg[2] == T.arg[3] - 1;
-    uint8_t* wq = c.L.stage + attn_words_off(nh, hd);
-    uint8_t* wk = wq + round_up_u(8u * nh * hd / vpw, 1024u);
-    uint8_t* wv = wk + round_up_u(8u * hd / vpw, 1024u);
-    gather(io, cur ? 3u : 1u, GSeg{Lq + (uint64_t)h0 * hd / vpw, nh * hd / vpw, wq},
-           GSeg{Lq + ((uint64_t)P.nH + g) * hd / vpw, hd / vpw, wk}, GSeg{Lq + ((uint64_t)P.nH + P.nKV + g) * hd / vpw, hd / vpw, wv});
-    for (uint32_t i = lane; i < nh * hd; i += 64u) A.q[i] = wval(wq, i, f32);
-    if (cur)
-        for (uint32_t i = lane; i < hd; i += 64u) {
-            A.kc[i] = wval(wk, i, f32);
-            A.vc[i] = wval(wv, i, f32);
-        }
-}
+// LDS map of an attention task inside S.att (floats): q of the task's heads, the current k and v,
+// the cross-wave combination weights, the per-head maxima.
+constexpr int kAttQ = 0;                          // [nh][hd], nh * hd <= 1024
+constexpr int kAttKc = kMaxAttnHeads * 128;       // [hd]
+constexpr int kAttVc = kAttKc + 128;              // [hd]
+constexpr int kAttF = kAttVc + 128;               // [kComputeWaves][kMaxAttnHeads] weights exp(m_w - M)
+constexpr int kAttM = kAttF + kComputeWaves * kMaxAttnHeads;   // [kMaxAttnHeads] maxima
+static_assert(kAttM + kMaxAttnHeads <= kAttnLds / 4, "attention LDS map");
+constexpr int kAttMaxD = 8;                       // dims per lane: hd / lanes-per-head (the lowering keeps it <= 8)
+constexpr int kAttBatch = 4;                      // history positions a wave scores at once
+constexpr int kKvRound = kKvBytes;               // bytes of K and V rows staged per round
+constexpr int kKvLoads = kKvRound / 16 / kComputeThreads;   // 16-byte K/V loads per thread per round
 
-// Attention epilogue, on every wave of the workgroup: combine the compute waves' states (weights
-// exp(m_w - M)) per (head, pair of dimensions), one pair a thread. A single chunk yields the
-// output words (rounded once); a split context yields its fp64 partial state (M, L, o) per head.
-// The results go to the row buffer in LDS; the I/O wave publishes them (attn_publish).
-// Thread tid: head tid / (hd / 2), dimensions 2 (tid mod hd / 2) and the next.
-DEV void attn_combine(const Ctx& c, const DevTask& T, uint32_t tid, bool f32) {
-    const uint32_t nh = T.arg[1], nc = T.arg[3], hd = T.k / (f32 ? 4u : 2u);
-    const AttnStage A = attn_stage(c.L, nh, hd);
-    const uint32_t st = hd + 2, per = hd / 2;
-    if (tid >= nh * per) return;
-    const uint32_t h = tid / per, d = 2 * (tid % per);
-    double fw[kCompWaves];
-    double M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kCompWaves; ++w) M = fmax(M, lds_ld64(A.st + (w * nh + h) * st));
-    double Ls = 0.0, o0 = 0.0, o1 = 0.0;
-#pragma unroll
-    for (int w = 0; w < kCompWaves; ++w) {
-        const double* sw = A.st + (w * nh + h) * st;
-        const double mw = lds_ld64(sw);
-        fw[w] = mw == -INFINITY ? 0.0 : exp(mw - M);
-        Ls = fma(fw[w], lds_ld64(sw + 1), Ls);
-        o0 = fma(fw[w], lds_ld64(sw + 2 + d), o0);
-        o1 = fma(fw[w], lds_ld64(sw + 3 + d), o1);
-    }
-    if (nc == 1) {   // output payloads: one word per value pair (bf16) or per value (fp32)
-        uint32_t* out = (uint32_t*)c.L.red;
-        if (f32) {
-            lds_st32(out + h * hd + d, act_bits(o0 / Ls, true));
-            lds_st32(out + h * hd + d + 1, act_bits(o1 / Ls, true));
+// This lane's D consecutive values [d0, d0 + D) of the staged K or V row at `p`, as fp32, read
+// with vector LDS loads (the slice is aligned to its own size: d0 is a multiple of D).
+DEV void kv_slice(const KParams& P, const uint8_t* p, uint32_t d0, uint32_t D, float (&v)[kAttMaxD]) {
+    if (P.act_f32) {
+        const float* f = (const float*)p + d0;
+        if (D >= 4) {
+            const u32x4 a = *(const u32x4*)f;
+            v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y); v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+            if (D == 8) {
+                const u32x4 b = *(const u32x4*)(f + 4);
+                v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y); v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+            }
+        } else if (D == 2) {
+            const float2 a = *(const float2*)f;
+            v[0] = a.x; v[1] = a.y;
         } else {
-            lds_st32(out + (h * hd + d) / 2, act_bits(o0 / Ls, false) | (act_bits(o1 / Ls, false) << 16));
+            v[0] = f[0];
         }
-    } else {   // the partial state, fp64: [h][M, L, o...]
-        double* ps = c.L.red + h * st;
-        if (d == 0) { lds_st64(ps, M); lds_st64(ps + 1, Ls); }
-        lds_st64(ps + 2 + d, o0);
-        lds_st64(ps + 3 + d, o1);
-    }
-}
-
-// The attention task's results from the row buffer to the flag words.
-DEV void attn_publish(Io& io, const DevTask& T) {
-    const Ctx& c = *io.c;
-    CKP& P = *c.P;
-    const bool f32 = P.act_f32 != 0;
-    const uint32_t vpw = f32 ? 1u : 2u;
-    const uint32_t h0 = T.arg[0], nh = T.arg[1], ch = T.arg[2], nc = T.arg[3], hd = (uint32_t)P.hd, st = hd + 2;
-    const uint32_t lane = (uint32_t)lane_id();
-    if (nc == 1) {
-        const uint32_t* src = (const uint32_t*)c.L.red;
-        u64* out = P.ll + T.dst + (uint64_t)h0 * hd / vpw;
-        for (uint32_t i = lane; i < nh * hd / vpw; i += 64u) ll_store(out + i, src[i], io.flag);
     } else {
-        for (uint32_t h = 0; h < nh; ++h) {
-            u64* part = P.ll + T.dst + 2ull * ((uint64_t)(h0 + h) * nc + ch) * st;
-            const uint32_t* src = (const uint32_t*)(c.L.red + h * st);
-            for (uint32_t k = lane; k < 2 * st; k += 64u) ll_store(part + k, src[k], io.flag);
-        }
-    }
-}
-
-// Merge of the context chunks of query heads [h0, h0+nh), on every wave of the workgroup:
-// o = sum_c exp(M_c - M) o_c divided by sum_c exp(M_c - M) L_c, M = max_c M_c (the
-// split-context form of the same softmax), in fp64. The chunk states were gathered as words
-// (two per fp64 value). First the chunk weights, one (head, chunk) a thread, into LDS; a
-// barrier; then one (head, pair of dimensions) a thread, into the row buffer (published by the
-// I/O wave). Every wave runs the barrier.
-DEV void merge_compute(const Ctx& c, const DevTask& T, uint32_t tid, bool f32) {
-    const uint32_t nh = T.arg[1], nc = T.arg[3], hd = T.k / (f32 ? 4u : 2u), st = hd + 2, per = hd / 2;
-    const uint8_t* words = c.L.stage;
-    double* f = (double*)(c.L.stage + merge_weights_off(nh, nc, hd));   // [nh][nc]
-    for (uint32_t i = tid; i < nh * nc; i += 512u) {
-        const uint32_t h = i / nc, k = i % nc, hb = h * nc * st;
-        double M = -INFINITY;
-        for (uint32_t j = 0; j < nc; ++j) M = fmax(M, wdbl(words, hb + j * st));
-        const double mk = wdbl(words, hb + k * st);
-        lds_st64(f + i, mk == -INFINITY ? 0.0 : exp(mk - M));
-    }
-    bar();
-    if (tid < nh * per) {
-        const uint32_t h = tid / per, d = 2 * (tid % per), hb = h * nc * st;
-        double Ls = 0.0, o0 = 0.0, o1 = 0.0;
-        for (uint32_t k = 0; k < nc; ++k) {
-            const double fk = lds_ld64(f + h * nc + k);
-            Ls = fma(fk, wdbl(words, hb + k * st + 1), Ls);
-            o0 = fma(fk, wdbl(words, hb + k * st + 2 + d), o0);
-            o1 = fma(fk, wdbl(words, hb + k * st + 3 + d), o1);
-        }
-        uint32_t* out = (uint32_t*)c.L.red;
-        if (f32) {
-            lds_st32(out + h * hd + d, act_bits(o0 / Ls, true));
-            lds_st32(out + h * hd + d + 1, act_bits(o1 / Ls, true));
+        const uint16_t* h = (const uint16_t*)p + d0;
+        if (D == 8) {
+            const u32x4 a = *(const u32x4*)h;
+            const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) { v[2 * k] = bf2f(w[k] & 0xffffu); v[2 * k + 1] = bf2f(w[k] >> 16); }
+        } else if (D == 4) {
+            const uint2 a = *(const uint2*)h;
+            v[0] = bf2f(a.x & 0xffffu); v[1] = bf2f(a.x >> 16); v[2] = bf2f(a.y & 0xffffu); v[3] = bf2f(a.y >> 16);
+        } else if (D == 2) {
+            const uint32_t a = *(const uint32_t*)h;
+            v[0] = bf2f(a & 0xffffu); v[1] = bf2f(a >> 16);
         } else {
-            lds_st32(out + (h * hd + d) / 2, act_bits(o0 / Ls, false) | (act_bits(o1 / Ls, false) << 16));
+            v[0] = bf2f(h[0]);
         }
     }
 }
 
-// The merge's outputs from the row buffer to the flag words.
-DEV void merge_publish(Io& io, const DevTask& T) {
-    const Ctx& c = *io.c;
-    CKP& P = *c.P;
-    const uint32_t vpw = P.act_f32 ? 1u : 2u;
-    const uint32_t h0 = T.arg[0], nh = T.arg[1], hd = (uint32_t)P.hd;
-    const uint32_t* src = (const uint32_t*)c.L.red;
-    u64* out = P.ll + T.dst + (uint64_t)h0 * hd / vpw;
-    for (uint32_t i = (uint32_t)lane_id(); i < nh * hd / vpw; i += 64u) ll_store(out + i, src[i], io.flag);
+// The K/V loads of an attention round live in the two weight buffers (attention tasks stream
+// no weights): load k of a thread is A.w[k], then B.w[k - kLoadSlots].
+static_assert(kKvLoads <= 2 * kLoadSlots, "K/V round registers");
+DEV u32x4& kv_slot(WBuf& A, WBuf& B, int k) { return k < kLoadSlots ? A.w[k] : B.w[k - kLoadSlots]; }
+
+// Issue the loads of one round of history positions [a, a + n) of KV group g into registers:
+// the K rows, then the V rows, each block contiguous in the cache (16 bytes per load).
+DEV void kv_round_issue(const KParams& P, int l, int g, uint32_t a, uint32_t n, int ctid, WBuf& A, WBuf& B) {
+    const uint32_t blk = n * kv_row_bytes(P), chunks = 2 * blk / 16;
+    const uint8_t* kb = kv_ptr(P, l, 0, g, a);
+    const uint8_t* vb = kv_ptr(P, l, 1, g, a);
+#pragma unroll
+    for (int k = 0; k < kKvLoads; ++k) {
+        const uint32_t q = (uint32_t)ctid + (uint32_t)k * kComputeThreads;
+        if (q < chunks) {
+            const uint32_t off = 16 * q;
+            kv_slot(A, B, k) = off < blk ? *(const u32x4*)(kb + off) : *(const u32x4*)(vb + (off - blk));
+        }
+    }
+    compiler_fence();
+}
+// ... and store them to S.kvb: K rows at [0, n * row bytes), V rows after them
+DEV void kv_round_store(const KParams& P, Lds& S, uint32_t n, int ctid, WBuf& A, WBuf& B) {
+    const uint32_t chunks = 2 * n * kv_row_bytes(P) / 16;
+#pragma unroll
+    for (int k = 0; k < kKvLoads; ++k) {
+        const uint32_t q = (uint32_t)ctid + (uint32_t)k * kComputeThreads;
+        if (q < chunks) *(u32x4*)(S.kvb + 16 * q) = kv_slot(A, B, k);
+    }
 }
 
-// The merge's chunk states, gathered before the workgroup's barrier.
-DEV void io_merge_inputs(Io& io, const DevTask& T) {
-    const Ctx& c = *io.c;
-    CKP& P = *c.P;
-    const uint32_t h0 = T.arg[0], nh = T.arg[1], nc = T.arg[3], st = (uint32_t)P.hd + 2;
-    gather(io, 1, GSeg{P.ll + T.src + 2ull * (uint64_t)h0 * nc * st, 2u * nh * nc * st, c.L.stage});
+// The history positions of attention task T: chunk arg[2] of arg[3] of [0, pos), its KV group,
+// and the positions of its first LDS round.
+struct AttnSpan {
+    int l, g;
+    uint32_t p0, p1;     // history positions [p0, p1)
+    uint32_t per_round;  // positions per LDS round
+    uint32_t rn;         // positions of the first round
+};
+DEV AttnSpan attn_span(const KParams& P, const DevTask& T) {
+    AttnSpan a;
+    a.l = T.layer;
+    a.g = (int)((uint64_t)T.arg[0] * P.nKV / P.nH);
+    chunk_range(P.pos, T.arg[2], T.arg[3], a.p0, a.p1);
+    a.per_round = (uint32_t)kKvRound / (2 * kv_row_bytes(P));
+    a.rn = min(a.per_round, a.p1 - a.p0);
+    return a;
+}
+
+// The softmax exponentials here use the hardware base-2 exponential of x * log2(e) (a few ulp
+// in fp32, far inside the parity bounds): the library expf costs five times the instructions.
+//
+// Attention of query heads [h0, h0+nh) (one KV group g) over chunk ch of nc of the context
+// positions [0, pos]: the softmax-weighted sum of V rows with weights from q.K / sqrt(hd)
+// (page 3, "How it works", the attention instruction over the persistent KV cache).
+//
+// Lane layout: the 64 lanes of a wave are (query head, dimension group) pairs: a head owns L
+// lanes (L = 64 / nh rounded to a power of two, at most hd), a lane owns D = hd / L
+// consecutive dims and keeps its q slice and its slice of the running output in registers. A
+// position's score is the lane-group sum of q.K over the group; softmax runs online (running
+// max m, running sum l, rescaled output o). History positions are staged in LDS in rounds (the
+// first round's loads are issued before the wait for q) and dealt round robin to the waves; the
+// current position (last chunk only) comes from the flag-carrying words. At the end the
+// per-wave states (m, l, o) are combined with weights exp(m_w - M) computed once per (wave,
+// head); a single chunk writes the output row, a split context writes its (M, L, o) state.
+template <int DT>
+DEV void op_attn_d(const TaskEnv& e, const DevTask& T, WBuf& A, WBuf& B) {
+    const Ctx& c = *e.c;
+    const KParams& P = *c.P;
+    Lds& S = *c.S;
+    const int l = T.layer, ctid = e.ctid, cw = e.cw, lane = lane_id();
+    const uint32_t h0 = T.arg[0], nh = T.arg[1], ch = T.arg[2], nc = T.arg[3];
+    const uint32_t hd = (uint32_t)P.hd;
+    const int g = (int)((uint64_t)h0 * P.nKV / P.nH);
+    const uint32_t vpw = P.act_f32 ? 1u : 2u;
+    const u64* Lq = ll_layer(P, e.y, l) + e.y.qkv;
+    const bool cur = ch == nc - 1;
+    float* qs = S.att + kAttQ;
+    float* kc = S.att + kAttKc;
+    float* vc = S.att + kAttVc;
+    const AttnSpan sp = attn_span(P, T);
+    const uint32_t p1 = sp.p1, nhist = sp.p1 - sp.p0, per_round = sp.per_round;
+    const uint32_t rowb = kv_row_bytes(P);
+    // the first round's K/V loads go out before the wait for q
+    uint32_t ra = sp.p0, rn = sp.rn;
+    if (rn) kv_round_issue(P, l, g, ra, rn, ctid, A, B);
+    // inputs: q of the task's heads; the current k, v of the group (last chunk only)
+    (void)ll_gather(c, Lq + (uint64_t)h0 * hd / vpw, nh * hd / vpw, ctid, [&](uint32_t i, uint32_t pl) {
+            for (uint32_t j = 0; j < vpw; ++j) qs[i * vpw + j] = word_val(P, pl, (int)j);
+        });
+    if (cur) {
+        const uint64_t kofs = ((uint64_t)P.nH + g) * hd / vpw, vofs = ((uint64_t)P.nH + P.nKV + g) * hd / vpw;
+        (void)ll_gather(c, Lq + kofs, hd / vpw, ctid, [&](uint32_t i, uint32_t pl) {
+                for (uint32_t j = 0; j < vpw; ++j) kc[i * vpw + j] = word_val(P, pl, (int)j);
+            });
+        (void)ll_gather(c, Lq + vofs, hd / vpw, ctid, [&](uint32_t i, uint32_t pl) {
+                for (uint32_t j = 0; j < vpw; ++j) vc[i * vpw + j] = word_val(P, pl, (int)j);
+            });
+    }
+    if (rn) kv_round_store(P, S, rn, ctid, A, B);
+    cbar();
+    mark(e, 1);
+    // lane layout (D, the dims per lane, is the template parameter: every per-dim loop below is
+    // fixed at compile time)
+    constexpr uint32_t D = (uint32_t)DT;
+    const uint32_t L = hd / D;
+    const uint32_t hl = (uint32_t)lane / L, dg = (uint32_t)lane % L;
+    const bool active = hl < nh;
+    const uint32_t hq = active ? hl : 0;   // inactive lanes shadow head 0 and never store
+    float qr[kAttMaxD], o[kAttMaxD], kv[kAttMaxD];
+#pragma unroll
+    for (int k = 0; k < kAttMaxD; ++k) {
+        qr[k] = (uint32_t)k < D ? qs[hq * hd + dg * D + k] : 0.f;
+        o[k] = 0.f;
+    }
+    float m = -INFINITY, lsum = 0.f;
+    const float scale = P.attn_scale;
+    // one position: score, online-softmax update; krow/vrow are the staged rows, or null for
+    // the current position (k, v in S.att)
+    auto step = [&](const uint8_t* krow, const uint8_t* vrow) {
+        if (krow) kv_slice(P, krow, dg * D, D, kv);
+        else
+#pragma unroll
+            for (int k = 0; k < kAttMaxD; ++k) kv[k] = (uint32_t)k < D ? kc[dg * D + k] : 0.f;
+        float sdot = 0.f;
+#pragma unroll
+        for (int k = 0; k < kAttMaxD; ++k)
+            if ((uint32_t)k < D) sdot += qr[k] * kv[k];
+        for (uint32_t off = L >> 1; off >= 1; off >>= 1) sdot += __shfl_xor(sdot, (int)off, 64);
+        const float sc = sdot * scale;
+        const float mn = fmaxf(m, sc);
+        const float alpha = __expf(m - mn), pw = __expf(sc - mn);
+        lsum = lsum * alpha + pw;
+        if (vrow) kv_slice(P, vrow, dg * D, D, kv);
+        else
+#pragma unroll
+            for (int k = 0; k < kAttMaxD; ++k) kv[k] = (uint32_t)k < D ? vc[dg * D + k] : 0.f;
+#pragma unroll
+        for (int k = 0; k < kAttMaxD; ++k)
+            if ((uint32_t)k < D) o[k] = o[k] * alpha + pw * kv[k];
+        m = mn;
+    };
+    // history rounds: each wave takes kAttBatch positions at a time (positions w, w + 8, ...), so
+    // the lane-group reductions of their scores overlap and the running state is rescaled once
+    // per batch
+    while (rn) {
+        for (uint32_t i0 = (uint32_t)cw; i0 < rn; i0 += kComputeWaves * kAttBatch) {
+            float sc[kAttBatch];
+#pragma unroll
+            for (int u = 0; u < kAttBatch; ++u) {
+                const uint32_t i = i0 + (uint32_t)u * kComputeWaves;
+                float sdot = 0.f;
+                if (i < rn) {
+                    kv_slice(P, S.kvb + i * rowb, dg * D, D, kv);
+#pragma unroll
+                    for (int k = 0; k < kAttMaxD; ++k)
+                        if ((uint32_t)k < D) sdot += qr[k] * kv[k];
+                }
+                sc[u] = sdot;
+            }
+            for (uint32_t off = L >> 1; off >= 1; off >>= 1)
+#pragma unroll
+                for (int u = 0; u < kAttBatch; ++u) sc[u] += __shfl_xor(sc[u], (int)off, 64);
+            float mb = m;
+#pragma unroll
+            for (int u = 0; u < kAttBatch; ++u) {
+                sc[u] = i0 + (uint32_t)u * kComputeWaves < rn ? sc[u] * scale : -INFINITY;
+                mb = fmaxf(mb, sc[u]);
+            }
+            const float alpha = __expf(m - mb);
+            lsum *= alpha;
+#pragma unroll
+            for (int k = 0; k < kAttMaxD; ++k) o[k] *= alpha;
+#pragma unroll
+            for (int u = 0; u < kAttBatch; ++u) {
+                const uint32_t i = i0 + (uint32_t)u * kComputeWaves;
+                if (i < rn) {
+                    const float pw = __expf(sc[u] - mb);
+                    lsum += pw;
+                    kv_slice(P, S.kvb + (rn + i) * rowb, dg * D, D, kv);
+#pragma unroll
+                    for (int k = 0; k < kAttMaxD; ++k)
+                        if ((uint32_t)k < D) o[k] += pw * kv[k];
+                }
+            }
+            m = mb;
+        }
+        const uint32_t na = ra + rn, nn = min(per_round, p1 - na);
+        if (!nn) break;
+        cbar();   // every wave is done with this round's rows
+        kv_round_issue(P, l, g, na, nn, ctid, A, B);
+        kv_round_store(P, S, nn, ctid, A, B);
+        cbar();
+        ra = na;
+        rn = nn;
+    }
+    // the current position: one wave
+    if (cur && (uint32_t)cw == nhist % kComputeWaves) step(nullptr, nullptr);
+    // per-wave states -> LDS: hf[(cw * nh + h) * (hd + 2) + {0: m, 1: l, 2 + d: o}]
+    const uint32_t st = hd + 2;
+    if (active) {
+        float* w = S.hf + ((uint32_t)cw * nh + hl) * st;
+        if (dg == 0) { w[0] = m; w[1] = lsum; }
+#pragma unroll
+        for (int k = 0; k < kAttMaxD; ++k)
+            if ((uint32_t)k < D) w[2 + dg * D + k] = o[k];
+    }
+    cbar();
+    mark(e, 2);
+    // combination weights, once per (wave, head)
+    for (uint32_t t = (uint32_t)ctid; t < (uint32_t)kComputeWaves * nh; t += kComputeThreads) {
+        const uint32_t w = t / nh, h = t % nh;
+        float M = -INFINITY;
+        for (int v = 0; v < kComputeWaves; ++v) M = fmaxf(M, S.hf[((uint32_t)v * nh + h) * st]);
+        const float mw = S.hf[(w * nh + h) * st];
+        S.att[kAttF + w * kMaxAttnHeads + h] = mw == -INFINITY ? 0.f : __expf(mw - M);
+        if (w == 0) S.att[kAttM + h] = M;
+    }
+    cbar();
+    const uint32_t flag = P.flag;
+    if (nc == 1) {   // the output rows, rounded once
+        u64* out = ll_layer(P, e.y, l) + e.y.o + (uint64_t)h0 * hd / vpw;
+        for (uint32_t i = (uint32_t)ctid; i < nh * hd / vpw; i += kComputeThreads) {
+            float v[2] = {0.f, 0.f};
+#pragma unroll
+            for (uint32_t j = 0; j < 2; ++j) {
+                if (j >= vpw) break;
+                const uint32_t t = i * vpw + j, h = t / hd, d = t % hd;
+                float os = 0.f, ls = 0.f;
+                for (int w = 0; w < kComputeWaves; ++w) {
+                    const float f = S.att[kAttF + w * kMaxAttnHeads + h];
+                    const float* ws = S.hf + ((uint32_t)w * nh + h) * st;
+                    ls += f * ws[1];
+                    os += f * ws[2 + d];
+                }
+                v[j] = rA(P, os / ls);
+            }
+            ll_store(out + i, pack2(P, v[0], v[1]), flag);
+        }
+    } else {   // partial state (M, L, o[hd]) per head, one fp32 per word
+        u64* part = ll_layer(P, e.y, l) + e.y.part;
+        for (uint32_t t = (uint32_t)ctid; t < nh * st; t += kComputeThreads) {
+            const uint32_t h = t / st, k = t % st;
+            float v;
+            if (k == 0) {
+                v = S.att[kAttM + h];
+            } else {
+                v = 0.f;
+                for (int w = 0; w < kComputeWaves; ++w)
+                    v += S.att[kAttF + w * kMaxAttnHeads + h] * S.hf[((uint32_t)w * nh + h) * st + k];
+            }
+            ll_store(part + ((uint64_t)(h0 + h) * nc + ch) * st + k, __float_as_uint(v), flag);
+        }
+    }
+}
+
+// Attention with the lane layout's dims per lane as a compile-time constant: a head owns
+// min(64 / nh rounded up to a power of two, hd) lanes, so D = hd / lanes is 1, 2, 4 or 8 (the
+// lowering keeps it <= 8).
+DEV void op_attn(const TaskEnv& e, const DevTask& T, WBuf& A, WBuf& B) {
+    const uint32_t nh = T.arg[1], hd = (uint32_t)e.c->P->hd;
+    uint32_t nhp = 1;
+    while (nhp < nh) nhp <<= 1;
+    switch (hd / min(64u / nhp, hd)) {
+    case 1: op_attn_d<1>(e, T, A, B); break;
+    case 2: op_attn_d<2>(e, T, A, B); break;
+    case 4: op_attn_d<4>(e, T, A, B); break;
+    default: op_attn_d<8>(e, T, A, B); break;
+    }
+}
+
+// Merge of the context chunks of query heads [h0, h0+nh): o = sum_c exp(M_c - M) o_c divided by
+// sum_c exp(M_c - M) L_c, M = max_c M_c (the split-context form of the same softmax). The
+// weights are computed once per (head, chunk).
+DEV void op_merge(const TaskEnv& e, const DevTask& T) {
+    const Ctx& c = *e.c;
+    const KParams& P = *c.P;
+    Lds& S = *c.S;
+    const int l = T.layer, ctid = e.ctid;
+    const uint32_t h0 = T.arg[0], nh = T.arg[1], nc = T.arg[3];
+    const uint32_t hd = (uint32_t)P.hd, st = hd + 2;
+    const uint32_t vpw = P.act_f32 ? 1u : 2u;
+    const u64* part = ll_layer(P, e.y, l) + e.y.part + (uint64_t)h0 * nc * st;
+    (void)ll_gather(c, part, nh * nc * st, ctid, [&](uint32_t i, uint32_t pl) { S.hf[i] = __uint_as_float(pl); });
+    cbar();
+    mark(e, 1);
+    // per head: M, then the chunk weights f_c = exp(M_c - M) (stored over M_c) and L
+    float* Lh = S.att;                       // [nh]
+    for (uint32_t h = (uint32_t)e.cw; h < nh; h += kComputeWaves) {
+        float* base = S.hf + (uint64_t)h * nc * st;
+        float M = -INFINITY;
+        for (uint32_t k = (uint32_t)lane_id(); k < nc; k += 64) M = fmaxf(M, base[k * st]);
+        M = wave_max_dpp(M);
+        float Ls = 0.f;
+        for (uint32_t k = (uint32_t)lane_id(); k < nc; k += 64) {
+            const float mk = base[k * st];
+            const float f = mk == -INFINITY ? 0.f : __expf(mk - M);
+            Ls += f * base[k * st + 1];
+            base[k * st] = f;
+        }
+        Ls = wave_sum_dpp(Ls);
+        if (lane_id() == 0) Lh[h] = Ls;
+    }
+    cbar();
+    // output words: G consecutive lanes share a word, each summing every G-th chunk, then the G
+    // partial sums are added across those lanes
+    u64* out = ll_layer(P, e.y, l) + e.y.o + (uint64_t)h0 * hd / vpw;
+    const uint32_t nwords = nh * hd / vpw;
+    uint32_t G = 1;
+    while (2 * G <= nc && 2 * G <= 64 && nwords * 2 * G <= (uint32_t)kComputeThreads) G *= 2;
+    for (uint32_t w0 = 0; w0 < nwords; w0 += kComputeThreads / G) {
+        const uint32_t i = w0 + (uint32_t)ctid / G, k0 = (uint32_t)ctid % G;
+        float v[2] = {0.f, 0.f};
+        if (i < nwords) {
+#pragma unroll
+            for (uint32_t j = 0; j < 2; ++j) {
+                if (j >= vpw) break;
+                const uint32_t t = i * vpw + j, h = t / hd, d = t % hd;
+                const float* base = S.hf + (uint64_t)h * nc * st;
+                float os = 0.f;
+                for (uint32_t k = k0; k < nc; k += G) os += base[k * st] * base[k * st + 2 + d];
+                v[j] = os;
+            }
+        }
+        for (uint32_t off = G >> 1; off >= 1; off >>= 1) {
+            v[0] += __shfl_xor(v[0], (int)off, 64);
+            v[1] += __shfl_xor(v[1], (int)off, 64);
+        }
+        if (i < nwords && k0 == 0) {
+            float r[2] = {0.f, 0.f};
+#pragma unroll
+            for (uint32_t j = 0; j < 2; ++j) {
+                if (j >= vpw) break;
+                r[j] = rA(P, v[j] / Lh[(i * vpw + j) / hd]);
+            }
+            ll_store(out + i, pack2(P, r[0], r[1]), P.flag);
+        }
+    }
 }
 
 // The greedy token: the argmax over the LM tiles' (max, index) pairs, lowest index among equal
 // maxima; a tile that saw a NaN makes the token -1.
-DEV void io_argmax(Io& io, const DevTask& T) {
-    const Ctx& c = *io.c;
-    CKP& P = *c.P;
+DEV void op_argmax(const TaskEnv& e, const DevTask& T) {
+    const Ctx& c = *e.c;
+    const KParams& P = *c.P;
+    Lds& S = *c.S;
+    const int ctid = e.ctid;
     const uint32_t nt = T.arg[2];
-    uint8_t* words = c.L.stage;
-    gather(io, 1, GSeg{P.ll + T.src, 2u * nt, words});
     float best = -INFINITY;
     int bi = 0x7fffffff;
     bool bad = false;
-    for (uint32_t t = (uint32_t)lane_id(); t < nt; t += 64u) {
-        const float v = __uint_as_float(wpl(words, 2u * t));
-        const int i = (int)wpl(words, 2u * t + 1u);
+    // word 2t: value bits, word 2t+1: index (or -1 for a tile with NaN)
+    (void)ll_gather(c, P.ll + e.y.lmpart, 2 * nt, ctid, [&](uint32_t i, uint32_t pl) {
+            if (i & 1) S.hf[i] = __int_as_float((int)pl);
+            else S.hf[i] = __uint_as_float(pl);
+        });
+    cbar();
+    mark(e, 1);
+    for (uint32_t t = (uint32_t)ctid; t < nt; t += kComputeThreads) {
+        const float v = S.hf[2 * t];
+        const int i = __float_as_int(S.hf[2 * t + 1]);
         if (i < 0) bad = true;
         else if (v > best || (v == best && i < bi)) { best = v; bi = i; }
     }
@@ -1306,141 +1142,107 @@ DEV void io_argmax(Io& io, const DevTask& T) {
         const int oi = __shfl_xor(bi, o, 64);
         if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
     }
-    const bool anybad = __builtin_amdgcn_ballot_w64(bad) != 0;
-    if (lane_id() == 0) P.tok_out[0] = anybad ? -1 : bi;
+    const int anybad = __any(bad);
+    if (lane_id() == 0) { S.fpart[e.cw] = best; S.ipart[e.cw] = anybad ? -1 : bi; }
+    cbar();
+    if (ctid == 0) {
+        float b = S.fpart[0];
+        int i0 = S.ipart[0];
+        bool badn = i0 < 0;
+        for (int w = 1; w < kComputeWaves; ++w) {
+            if (S.ipart[w] < 0) badn = true;
+            else if (S.fpart[w] > b || (S.fpart[w] == b && S.ipart[w] < i0)) { b = S.fpart[w]; i0 = S.ipart[w]; }
+        }
+        P.tok_out[0] = badn ? -1 : i0;
+    }
 }
 
-// ------------------------------------------------------------------ the two roles
-
-// Per task, every wave runs the same barriers: A1 (inputs gathered by the I/O wave), A1b (inside
-// the GEMV staging, between its reads and its writes; a lone barrier for other tasks), A2 (planes
-// written), then the compute (a merge has one more barrier inside), and B (results in LDS); an
-// attention task then combines the waves' states on every wave and has barrier C. The I/O wave
-// then writes the outputs while the compute waves go on to the next task's A1.
-template <int FMT>
-DEV void io_run(const Ctx& c0) {
-    Io io;
-    io.flag = c0.P->flag;
-    io.abort_ = false;
-    int tok = c0.P->tok_in[0];
-    if (tok < 0 || tok >= c0.P->V) {
-        if (lane_id() == 0)
-            __hip_atomic_store(&c0.P->status[1], kStatusBadToken, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+DEV void compute_run(const Ctx& c) {
+    const KParams& P = *c.P;
+    Lds& S = *c.S;
+    const int ctid = (int)threadIdx.x;
+    const int cw = __builtin_amdgcn_readfirstlane(ctid >> 6);
+    TaskEnv e;
+    e.c = &c;
+    e.ctid = ctid;
+    e.cw = cw;
+    e.y = ll_layout(P.H, P.L, P.nH, P.nKV, P.hd, P.I, P.act_f32, P.nchunks, P.lm_tiles);
+    int tok = P.tok_in[0];
+    if (tok < 0 || tok >= P.V) {
+        if (ctid == 0) __hip_atomic_store(&P.status[1], kStatusBadToken, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
         tok = 0;
     }
-    io.token = tok;
-    const int tid = kIoWave * 64 + lane_id();
-    for (uint32_t t = c0.q0; t < c0.q1; ++t) {
-        // the parameter block is re-read in every task through a pointer the compiler cannot
-        // follow across iterations, so it does not hold every parameter in registers for the
-        // whole queue (that exhausts the scalar registers)
-        Ctx c = c0;
-        asm volatile("" : "+s"(c.P));
-        CKP& P = *c.P;
-        io.c = &c;
-        const DevTask T = task_at(c, t);
-        io.tr = P.trace ? P.trace + (uint64_t)t * kTraceSlots : nullptr;
-        mark(io, 0);
-        const bool gemv = is_gemv_op(T.op);
-        if (gemv) {
-            const uint32_t K = T.k;
-            if (T.norm >= 0) io_gains(io, T.norm, K, n_planes(FMT) * plane_stride(FMT, K));
-            io_gemv_inputs(io, T, raw_off<FMT>(K, T.norm >= 0));
-        } else if (T.op == AMK_OP_ATTN) {
-            io_attn_inputs(io, T);
-        } else if (T.op == AMK_OP_MERGE) {
-            io_merge_inputs(io, T);
+    e.token = tok;
+    WBuf A, B;
+    const uint32_t q0 = P.queue_off[c.cu], q1 = P.queue_off[c.cu + 1];
+    // the first task's weights, if it has any
+    if (q0 < q1) {
+        const DevTask F = task_at(c, q0, q0);
+        if (is_gemv(F.op)) prefetch_task(c, F, cw, A, B);
+
+    }
+    for (uint32_t t = q0; t < q1; ++t) {
+        const DevTask T = task_at(c, q0, t);
+        const DevTask N = task_at(c, q0, t + 1 < q1 ? t + 1 : t);
+        const bool next_gemv = t + 1 < q1 && is_gemv(N.op);
+        e.tr = P.trace ? P.trace + (uint64_t)t * kTraceSlots : nullptr;
+        mark(e, 0);
+        // (after a timeout or an abort every wait returns at once, and the workgroup runs the rest
+        // of its queue without waiting, through the same barriers, so the launch ends)
+        if (is_gemv(T.op)) {
+            op_gemv(e, T, A, B);
         } else {
-            io_argmax(io, T);
+            switch (T.op) {
+            case AMK_OP_ATTN: op_attn(e, T, A, B); break;
+            case AMK_OP_MERGE: op_merge(e, T); break;
+            default: op_argmax(e, T); break;
+            }
         }
-        bar();                                   // A1
-        if (gemv) (void)stage_input<FMT>(c, T, tid);
-        else bar();
-        bar();                                   // A2
-        mark(io, 1);
-        if (T.op == AMK_OP_MERGE) merge_compute(c, T, (uint32_t)tid, FMT == AMK_F32);
-        bar();                                   // B
-        mark(io, 2);
-        if (io.tr && lane_id() == 0) io.tr[4] = c.L.misc->t_rows;
-        if (T.op == AMK_OP_ATTN) {
-            attn_combine(c, T, (uint32_t)tid, FMT == AMK_F32);
-            bar();                               // C: the combined results are in the row buffer
-        }
-        if (gemv) io_gemv_epilogue(io, T);
-        else if (T.op == AMK_OP_ATTN) attn_publish(io, T);
-        else if (T.op == AMK_OP_MERGE) merge_publish(io, T);
-        mark(io, 5);
-        mark(io, 3);
+        if (e.tr && ctid == 0) e.tr[5] = rt();
+        // every wave is done with this task's LDS data before the next task stages its input
+        cbar();
+        mark(e, 3);
+        // the task's outputs are out: start the next task's weights (behind those stores in the
+        // memory pipeline, so the outputs reach their consumers first)
+        if (next_gemv) prefetch_task(c, N, cw, A, B);
+
     }
 }
 
+// The kernel body for one weight format. The format (and with it the activation type: fp32
+// with fp32 weights, bf16 otherwise) is a compile-time constant, so each kernel carries only
+// its own code path.
 template <int FMT>
-DEV void comp_run(const Ctx& c0, uint32_t w) {
-    constexpr int R = ring_slots(FMT);
-    Ring<R> ring;
-    ring_init(c0, ring, w);
-    const int tid = (int)w * 64 + lane_id();
-    for (uint32_t t = c0.q0; t < c0.q1; ++t) {
-        Ctx c = c0;   // see io_run
-        asm volatile("" : "+s"(c.P));
-        CKP& P = *c.P;
-        const DevTask T = task_at(c, t);
-        const bool gemv = is_gemv_op(T.op);
-        bar();                                   // A1
-        int S = 0;
-        if (gemv) S = stage_input<FMT>(c, T, tid);
-        else bar();
-        bar();                                   // A2
-        if (gemv) gemv_compute<FMT, R>(c, ring, T, t, w, S);
-        else if (T.op == AMK_OP_ATTN) attn_compute<FMT>(c, ring, T, t, w);
-        else if (T.op == AMK_OP_MERGE) merge_compute(c, T, (uint32_t)tid, FMT == AMK_F32);
-        if (w == 0 && P.trace && lane_id() == 0) c.L.misc->t_rows = rt();
-        bar();                                   // B
-        if (T.op == AMK_OP_ATTN) {
-            attn_combine(c, T, (uint32_t)tid, FMT == AMK_F32);
-            bar();                               // C
-        }
-        // the lookahead: refill every free slot from the rest of the queue while the I/O wave
-        // writes this task's outputs and gathers the next inputs (a load issued into a busy
-        // memory system waits at issue; here that wait is off the task's critical path)
-        ring_refill(c, ring, w, c0.q1);
+DEV void megakernel_body(const KParams& Pin) {
+    __shared__ Lds S;
+    KParams P = Pin;
+    P.wfmt = FMT;
+    P.act_f32 = FMT == AMK_F32 ? 1 : 0;
+    const int tid = threadIdx.x;
+    if (tid == 0) S.abort_ = 0;
+    {   // copy the head of this CU's task queue to LDS (8 dwords per task)
+        const uint32_t q0 = P.queue_off[blockIdx.x], q1 = P.queue_off[blockIdx.x + 1];
+        const uint32_t n = min(q1 - q0, (uint32_t)kTaskCache) * (uint32_t)(sizeof(DevTask) / 4);
+        const uint32_t* src = (const uint32_t*)(P.tasks + q0);
+        uint32_t* dst = (uint32_t*)S.tcache;
+        for (uint32_t i = (uint32_t)tid; i < n; i += kThreads) dst[i] = src[i];
     }
-    // every ring load has landed before the workgroup leaves
-    __builtin_amdgcn_s_waitcnt(0);
-}
-
-template <int FMT>
-DEV void megakernel_body() {
-    constexpr int R = ring_slots(FMT);
-    __shared__ __attribute__((aligned(1024))) uint8_t ring[kCompWaves * R * 1024];
-    __shared__ __attribute__((aligned(16))) uint8_t stage[stage_bytes(FMT)];
-    __shared__ __attribute__((aligned(16))) double red[kRedRows];
-    __shared__ __attribute__((aligned(16))) Misc misc;
+    __syncthreads();
     Ctx c;
-    c.P = (CKP*)__builtin_amdgcn_kernarg_segment_ptr();
-    c.L.ring = ring;
-    c.L.stage = stage;
-    c.L.red = red;
-    c.L.misc = &misc;
+    c.P = &P;
+    c.S = &S;
     c.cu = blockIdx.x;
-    CKP& P = *c.P;
     c.deadline = rt() + P.watchdog_ticks;
-    c.pos = P.pos;
-    c.eps = P.eps;
-    c.wcu = P.wstream + *CONST4(uint64_t, P.cu_stream_off + blockIdx.x);
-    c.q0 = *CONST4(uint32_t, P.queue_off + blockIdx.x);
-    c.q1 = *CONST4(uint32_t, P.queue_off + blockIdx.x + 1);
-    const uint32_t w = (uint32_t)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (w == kIoWave) io_run<FMT>(c);
-    else comp_run<FMT>(c, w);
+    c.wcu = P.wstream + P.cu_stream_off[blockIdx.x];
+    compute_run(c);
 }
 
 }  // namespace
 
-extern "C" __global__ void __launch_bounds__(kThreads, 1) amk_megakernel_f32(KParams P) { (void)P; megakernel_body<AMK_F32>(); }
-extern "C" __global__ void __launch_bounds__(kThreads, 1) amk_megakernel_bf16(KParams P) { (void)P; megakernel_body<AMK_BF16>(); }
-extern "C" __global__ void __launch_bounds__(kThreads, 1) amk_megakernel_int8(KParams P) { (void)P; megakernel_body<AMK_INT8_PC>(); }
-extern "C" __global__ void __launch_bounds__(kThreads, 1) amk_megakernel_int4(KParams P) { (void)P; megakernel_body<AMK_INT4_G128>(); }
+extern "C" __global__ void __launch_bounds__(kThreads, 1) amk_megakernel_f32(KParams P) { megakernel_body<AMK_F32>(P); }
+extern "C" __global__ void __launch_bounds__(kThreads, 1) amk_megakernel_bf16(KParams P) { megakernel_body<AMK_BF16>(P); }
+extern "C" __global__ void __launch_bounds__(kThreads, 1) amk_megakernel_int8(KParams P) { megakernel_body<AMK_INT8_PC>(P); }
+extern "C" __global__ void __launch_bounds__(kThreads, 1) amk_megakernel_int4(KParams P) { megakernel_body<AMK_INT4_G128>(P); }
 
 namespace {
 const void* kernel_for(int wfmt) {
@@ -1451,6 +1253,13 @@ const void* kernel_for(int wfmt) {
     default: return (const void*)amk_megakernel_int4;
     }
 }
+}  // namespace
+
+}  // namespace amk
+
+namespace amk {
+
+namespace {
 
 // Per device: the device address of `scratch` and the epoch of the flags written into it.
 struct ScratchDev {
@@ -1470,6 +1279,7 @@ hipError_t clear_words(unsigned long long* p, uint64_t n, hipStream_t st) {
     hipLaunchKernelGGL(k_clear_words, dim3(1024), dim3(256), 0, st, p, n);
     return hipGetLastError();
 }
+
 }  // namespace
 
 hipError_t scratch_setup(int dev, hipStream_t st) {
