@@ -62,6 +62,8 @@ def lib() -> C.CDLL:
             L.orc_round.argtypes = [C.c_double, C.c_int]
             L.orc_quantize.restype = C.c_int
             L.orc_quantize.argtypes = [C.c_void_p, C.c_int64, C.c_int64, C.c_int, C.c_int, C.c_void_p, C.c_void_p]
+            L.orc_set_threads.argtypes = [C.c_int]
+            L.orc_set_threads.restype = C.c_int
             L.orc_rmsnorm.restype = None
             L.orc_rmsnorm.argtypes = [dp, dp, C.c_int, C.c_double, C.c_int, dp]
             L.orc_rope.restype = None
@@ -89,6 +91,11 @@ def lib() -> C.CDLL:
             L.orc_rounding_mode_is_nearest.restype = C.c_int
             _lib = L
     return _lib
+
+
+def set_threads(n: int) -> int:
+    """Threads of the oracle's OpenMP loops from now on; returns the count in effect."""
+    return int(lib().orc_set_threads(int(n)))
 
 
 def _dp(a):

@@ -29,6 +29,9 @@
 #include <stdlib.h>
 #include <string.h>
 #include <fenv.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define ORC_F32 0
 #define ORC_BF16 1
@@ -486,3 +489,16 @@ int orc_get_codes(const orc_ctx* c, int kind, int layer, int8_t* q, float* s) {
 }
 
 int orc_rounding_mode_is_nearest(void) { return fegetround() == FE_TONEAREST; }
+
+/* Threads of the OpenMP loops from now on (the CPU baseline's one-thread figure); returns the
+   count in effect. Results do not depend on it: every parallel loop writes disjoint outputs and
+   each output's sum runs in one thread in a fixed order. */
+int orc_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+    return omp_get_max_threads();
+#else
+    (void)n;
+    return 1;
+#endif
+}
