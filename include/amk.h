@@ -156,6 +156,11 @@ typedef struct {
                                   query head, 0: auto (grouped whenever KV heads are shared) */
     int32_t cu_assign;         /* 0 = XCD-aware (unchunked attention of one KV group on one XCD; chunked
                                   attention round robin), 1 = plain round robin */
+    int32_t prefetch_groups;   /* pipelining depth: groups of a GEMV task's weight loads (6 KiB per wave
+                                  each) a wave issues as soon as the previous task's outputs are out,
+                                  ahead of the task's inputs: 1 or 2, -1 for none, 0 = default (1).
+                                  Used by amk_create (the kernel's launch parameters); the lowering
+                                  only checks the range. */
 } amk_schedule_config;
 
 /* ---------------------------------------------------------------- calls */

@@ -88,7 +88,7 @@ class amk_schedule_config(C.Structure):
     _fields_ = [("struct_size", C.c_uint32), ("n_cu", C.c_int32), ("tasks_qkv", C.c_int32),
                 ("tasks_o", C.c_int32), ("tasks_gateup", C.c_int32), ("tasks_down", C.c_int32),
                 ("tasks_lm", C.c_int32), ("attn_chunks", C.c_int32), ("attn_group_tasks", C.c_int32),
-                ("cu_assign", C.c_int32)]
+                ("cu_assign", C.c_int32), ("prefetch_groups", C.c_int32)]
 
 
 class amk_vm_opts(C.Structure):

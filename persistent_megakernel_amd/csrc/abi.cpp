@@ -152,6 +152,9 @@ extern "C" amk_status amk_create(const amk_model_desc* desc, const amk_weights* 
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return AMK_E_HIP;
     int n_cu = (cfg && cfg->n_cu > 0) ? cfg->n_cu : prop.multiProcessorCount;
     if (n_cu > prop.multiProcessorCount) return AMK_E_NOT_RESIDENT;
+    const int pg = cfg ? cfg->prefetch_groups : 0;
+    if (pg < -1 || pg > 2) { logf("create", "prefetch_groups outside [-1, 2]"); return AMK_E_INVALID_ARG; }
+    const int ahead = pg == 0 ? kAheadGroupsDefault : pg < 0 ? 0 : pg;
 
     amk_ctx* c = new amk_ctx();
     c->d = d;
@@ -323,6 +326,7 @@ extern "C" amk_status amk_create(const amk_model_desc* desc, const amk_weights* 
     P.status = c->d_status;
     P.abort_flag = c->d_abort;
     P.watchdog_ticks = watchdog_ticks();
+    P.ahead_groups = ahead;
     c->last = stream;
     *out = c;
     return AMK_OK;

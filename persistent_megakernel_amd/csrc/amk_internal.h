@@ -31,12 +31,8 @@ constexpr int kTaskCache = 256;             // task descriptors of a CU's queue 
 #ifndef AMK_LOAD_SLOTS
 #define AMK_LOAD_SLOTS 6
 #endif
-#ifndef AMK_AHEAD_GROUPS
-#define AMK_AHEAD_GROUPS 1
-#endif
 constexpr int kLoadSlots = AMK_LOAD_SLOTS;  // 1 KiB (16 B per lane) weight loads per register buffer (2 buffers per wave)
-constexpr int kAheadGroups = AMK_AHEAD_GROUPS;   // groups of the next task's weights issued ahead (0, 1 or 2)
-static_assert(kAheadGroups >= 0 && kAheadGroups <= 2, "prefetch depth");
+constexpr int kAheadGroupsDefault = 1;      // groups of the next task's weights issued ahead (0, 1 or 2; a launch parameter)
 constexpr int kAttnBlock = 64;              // positions per attention unit
 constexpr int kMaxAttnHeads = 8;            // query heads per attention task
 constexpr int kChunkedCtx = 256;            // caches at least this long get context-split attention by default
@@ -135,6 +131,7 @@ struct KParams {
     uint32_t* status;                // host-visible status word
     uint32_t* abort_flag;            // device word: set on watchdog timeout
     uint64_t watchdog_ticks;         // s_memrealtime ticks (100 MHz) before a spin-wait gives up
+    int32_t ahead_groups;            // groups of the next GEMV task's weights each wave issues ahead (0, 1 or 2)
     uint64_t* trace;                 // optional per-task timestamps (kTraceSlots per device task) or null
 };
 

@@ -459,6 +459,10 @@ amk_status lower_model(const amk_model_desc& d, const amk_schedule_config* cfg, 
         if (cfg->struct_size != sizeof(amk_schedule_config)) return AMK_E_INVALID_ARG;
         C = *cfg;
     }
+    if (C.prefetch_groups < -1 || C.prefetch_groups > 2) {
+        if (msg) *msg = "prefetch_groups outside [-1, 2]";
+        return AMK_E_INVALID_ARG;
+    }
     Shape s = make_shape(d);
     const int nH = s.nH, nKV = s.nKV, gsz = nH / nKV, vpw = s.vpw;
     // attention grouping

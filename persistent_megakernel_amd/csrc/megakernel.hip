@@ -367,16 +367,17 @@ DEV void compute_group(const Lds& S_, const Geo& s, int cw, uint32_t K, uint32_t
 }
 
 // All groups of the wave's rows of task T, double-buffered: while one buffer is consumed the
-// other is in flight. On entry A holds group 0 (kAheadGroups >= 1) and B group 1
-// (kAheadGroups == 2), issued ahead and complete: the input staging waited for every load.
+// other is in flight. On entry A holds group 0 (ahead_groups >= 1) and B group 1
+// (ahead_groups == 2), issued ahead and complete: the input staging waited for every load.
 template <int FMT>
 DEV void gemv_rows_fmt(const Ctx& c, const DevTask& T, int cw, WBuf& A, WBuf& B) {
     const Geo s = geo_of(c, T, cw);
     const uint32_t K = K_of(*c.P, T.op);
     // nothing is in flight here; saying so lets the compiler count exactly from this point
     __builtin_amdgcn_s_waitcnt(kWaitVmem0);
-    if (kAheadGroups == 0 && s.ng > 0) issue_group(c, s, 0, A);
-    if (kAheadGroups <= 1 && s.ng > 1) issue_group(c, s, 1, B);
+    const int ag = c.P->ahead_groups;
+    if (ag == 0 && s.ng > 0) issue_group(c, s, 0, A);
+    if (ag <= 1 && s.ng > 1) issue_group(c, s, 1, B);
     float acc = 0.f;
     uint32_t g = 0;
     for (; g + 2 < s.ng; g += 2) {
@@ -391,10 +392,11 @@ DEV void gemv_rows_fmt(const Ctx& c, const DevTask& T, int cw, WBuf& A, WBuf& B)
 
 // Issue the first groups of task T's weights (the next task's, ahead of its inputs).
 DEV void prefetch_task(const Ctx& c, const DevTask& T, int cw, WBuf& A, WBuf& B) {
-    if (kAheadGroups == 0) return;
+    const int ag = c.P->ahead_groups;
+    if (ag == 0) return;
     const Geo s = geo_of(c, T, cw);
     if (s.ng > 0) issue_group(c, s, 0, A);
-    if (kAheadGroups == 2 && s.ng > 1) issue_group(c, s, 1, B);
+    if (ag == 2 && s.ng > 1) issue_group(c, s, 1, B);
 }
 
 DEV void gemv_rows(const Ctx& c, const DevTask& T, int cw, WBuf& A, WBuf& B) {

@@ -33,6 +33,9 @@ pytestmark = pytest.mark.gpu
 MARGIN = 2e-2
 FULL_DEPTH_ABS = 0.25
 FULL_DEPTH_RMS = 0.05
+# two layers deep: three one-ulp rounding flips of the first layer's outputs (pinned on the CPU by
+# test_oracle_sensitivity.py::test_one_ulp_flip_moves_two_layer_logits)
+TWO_LAYER_ABS = 0.075
 
 
 @pytest.fixture(scope="module")
@@ -132,10 +135,12 @@ def test_tiny_fp32_protocol(M):
 
 
 @pytest.mark.parametrize("cfg_kw", [dict(n_cu=1), dict(n_cu=7, cu_assign=1), dict(attn_chunks=3, attn_group_tasks=1),
-                                    dict(tasks_qkv=3, tasks_o=5, tasks_gateup=2, tasks_down=9, tasks_lm=4)])
+                                    dict(tasks_qkv=3, tasks_o=5, tasks_gateup=2, tasks_down=9, tasks_lm=4),
+                                    dict(prefetch_groups=-1, tasks_qkv=3), dict(prefetch_groups=2, tasks_gateup=2)])
 def test_tiny_fp32_schedules(M, cfg_kw):
-    """The same result under other valid lowerings: one CU, seven CUs round robin, split
-    context with a merge, uneven tiles."""
+    """The same result under other valid lowerings and launch parameters: one CU, seven CUs
+    round robin, split context with a merge, uneven tiles, no weight prefetch, two prefetched
+    load groups."""
     shape = I.SHAPES["tiny_fp32"].replace(n_generate=4)
     log(f"case tiny_fp32 schedule {cfg_kw}")
     r = _run(M, shape, I.make_weights(shape), I.prompt_tokens(shape), 4, cfg=M.schedule_config(**cfg_kw))
@@ -193,6 +198,22 @@ def test_depth1_full_width(M, name, pos0, prefill):
     assert max(r["errs"]) <= 2e-2
     _check_ids(r["gen"], r["tf"], r["margins"], name)
     _check_ids(r["gen"], r["fr"], r["margins"], name + " free-running")
+
+
+@pytest.mark.parametrize("prefetch", [-1, 2])
+def test_prefetch_depths_tinyllama_int8(M, prefetch):
+    """The run-time prefetch depth: no weight loads issued ahead, or two groups ahead, on two
+    TinyLlama-shaped int8 layers from position 512 (full width, so every GEMV task has more
+    than two load groups)."""
+    shape = I.SHAPES["tinyllama_int8"].replace(n_layers=2)
+    log(f"case tinyllama_int8 2 layers prefetch_groups={prefetch}")
+    w = I.make_weights(shape)
+    tok = int(I.prompt_tokens(shape, 1, stream=3)[0])
+    r = _run(M, shape, w, [tok], 4, pos0=512, prefill=512, cfg=M.schedule_config(prefetch_groups=prefetch))
+    log(f"prefetch {prefetch}: max abs err {max(r['errs']):.3e}, min margin {min(r['margins']):.3e}")
+    assert max(r["errs"]) <= TWO_LAYER_ABS
+    _check_ids(r["gen"], r["tf"], r["margins"], "prefetch", r["gen_errs"])
+    _check_ids(r["gen"], r["fr"], r["margins"], "prefetch free-running", r["gen_errs"])
 
 
 # ------------------------------------------------------------------ full depth
