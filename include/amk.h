@@ -165,8 +165,11 @@ typedef struct {
 
 /* ---------------------------------------------------------------- calls */
 
-/* Validate a schedule on the CPU. Reentrant, thread-safe, never touches a device. AMK_OK
- * means the call ran; the verdict is in *out. Rules (1 << k in rule_mask):
+/* Validate a schedule on the CPU: the pages' static safety gate, which refuses any schedule
+ * that could deadlock or race before it runs (pages: page 1, "Deadlock-free by construction";
+ * page 2, "1. Statically verified schedule IR"; page 4, "De Safety Gate"). Reentrant,
+ * thread-safe, never touches a device. AMK_OK means the call ran; the verdict is in *out.
+ * Rules (1 << k in rule_mask):
  *  V0 integrity: ids in range, every task in exactly one queue exactly once, lo < hi, no
  *     duplicate signal in a task, no write to a read-only region, no declared input/output
  *     and no post access on a flag-carrying region. When V0 fails nothing else is checked.
@@ -244,7 +247,11 @@ typedef struct amk_ctx amk_ctx;
 
 /* Build a context on the current device: lower (or take `sched`), validate, check that one
  * 512-thread workgroup per CU fits, quantise/repack the weights into library-owned device
- * memory, upload the task table and synchronise `stream`. The device watchdog (how long any
+ * memory, upload the task table and synchronise `stream`. This is the pages' compile step:
+ * a model becomes a static per-SM (here per-CU) task program that passes the safety gate
+ * before anything launches (AutoMegaKernel pages: page 2, "3. Agent-drivable compiler" and
+ * "1. Statically verified schedule IR"; page 4, "De Safety Gate"; the quantised formats, page
+ * 2, "Quantisation support and performance"). The device watchdog (how long any
  * single wait inside a step may last before the step gives up) is 2000 ms, or the value in
  * milliseconds of the environment variable AMK_WATCHDOG_MS when the context is created.
  *  desc      host; shape (AMK_E_UNSUPPORTED unless: head_dim in {16, 64, 128}; hidden and
@@ -267,7 +274,8 @@ amk_status amk_create(const amk_model_desc* desc, const amk_weights* weights, vo
                       amk_verdict* verdict, amk_ctx** out);
 
 /* One decode step: enqueue exactly one cooperative launch on `stream` and return without
- * synchronising.
+ * synchronising. One launch computes one forward pass and yields one greedy token (pages:
+ * page 1, author's note and "What's built"; page 3, "How it works", layers 0 and 1).
  *  token_in   device int32[1]: the input token (read at the start of the launch).
  *  pos        host int, 0 <= pos < max_ctx (else AMK_E_INVALID_ARG and no launch).
  *  token_out  device int32[1]: the greedy token (may equal token_in: decode chains on the
@@ -365,7 +373,8 @@ amk_status amk_set_trace(amk_ctx* ctx, uint64_t* trace, uint64_t capacity);
 amk_status amk_set_prefill_trace(amk_ctx* ctx, uint64_t* trace, uint64_t capacity);
 
 /* Synchronise the last stream, free every library-owned buffer; never touches caller
- * buffers. NULL-safe. */
+ * buffers. NULL-safe. (The end of the context amk_create built; the pages' runtime has the
+ * same create / step / destroy life cycle, page 1, "What's built".) */
 void amk_destroy(amk_ctx* ctx);
 
 /* The library's own weight quantiser, exposed for bit-exact comparison with other
