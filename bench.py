@@ -242,6 +242,30 @@ def verdict(dec, shape, w, pos0: int) -> dict:
 FULL_DEPTH_ABS = 0.25
 
 
+def read_ceiling_gbs(gib: int = 4, reps: int = 5) -> float:
+    """A measured HBM read rate on this GPU: the best of `reps` event-timed launches of the
+    library's read probe (amk_read_probe: the decode kernel's 16-byte non-temporal loads over
+    the whole grid) over a `gib` GiB buffer. The measured ceiling beside the 8 TB/s
+    specification."""
+    import torch
+    import persistent_megakernel_amd as M
+    n = gib << 30
+    x = torch.ones(n, dtype=torch.uint8, device="cuda")
+    out = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    best = 0.0
+    for _ in range(reps + 1):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        M.amk_read_probe(x.data_ptr(), n, out.data_ptr(), stream.cuda_stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        best = max(best, n / (a.elapsed_time(b) * 1e-3) / 1e9)
+    del x
+    torch.cuda.empty_cache()
+    return best
+
+
 def run_workload(name: str, K: int, W: int, traffic: dict, w=None, with_verdict: bool = True, prefill_tokens: int = 0):
     """Time K chained greedy decode launches (after W untimed) of one workload on cuda:0; the
     roofline of the kernel; the parity verdict; optionally the prefill leg."""
@@ -280,7 +304,11 @@ def run_workload(name: str, K: int, W: int, traffic: dict, w=None, with_verdict:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ev_ms = start.elapsed_time(stop)
-    launch_ms = sum(marks[2 * k].elapsed_time(marks[2 * k + 1]) for k in range(K)) / K
+    per = sorted(marks[2 * k].elapsed_time(marks[2 * k + 1]) for k in range(K))
+    launch_ms = sum(per) / K
+
+    def pct(q):
+        return per[min(K - 1, int(round(q * (K - 1))))] * 1e3
     status = dec.status()
     par = None
     if with_verdict and not status:
@@ -299,7 +327,9 @@ def run_workload(name: str, K: int, W: int, traffic: dict, w=None, with_verdict:
     per_launch = wb + kvb
     achieved = per_launch / (launch_ms * 1e-3) / 1e9
     rec = {"workload": desc, "name": name, "value": round(1e3 / ms_step, 2), "unit": "tokens/s",
-           "us_per_token": round(ms_step * 1e3, 2), "us_per_launch": round(launch_ms * 1e3, 2), "steps": K, "warmup": W,
+           "us_per_token": round(ms_step * 1e3, 2), "us_per_launch": round(launch_ms * 1e3, 2),
+           "us_per_launch_p10_p50_p90": [round(pct(0.1), 2), round(pct(0.5), 2), round(pct(0.9), 2)],
+           "steps": K, "warmup": W,
            "dtype": {I.WF_F32: "f32", I.WF_BF16: "bf16", I.WF_INT8: "w8a16", I.WF_INT4: "w4a16"}[shape.wfmt],
            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic.get(name)},
@@ -373,8 +403,15 @@ def main() -> int:
         "us_per_token": head["us_per_token"], "us_per_launch": head["us_per_launch"],
         "wall_s_timed": head["wall_s_timed"], "parity": head["parity"],
     }
+    rec["us_per_launch_p10_p50_p90"] = head["us_per_launch_p10_p50_p90"]
     if "prefill" in head:
         rec["prefill"] = head["prefill"]
+    # a measured read ceiling beside the specification's 8 TB/s
+    print("[bench] measured read rate (read probe over 4 GiB)", file=sys.stderr, flush=True)
+    ceil = read_ceiling_gbs()
+    rec["hbm_read_measured"] = {"value": round(ceil, 1), "unit": "GB/s",
+                                "how": "best of 5 launches of amk_read_probe over 4 GiB (16-byte non-temporal loads)",
+                                "decode_frac_of_it": round(head["roofline"]["achieved"] / ceil, 4)}
     if not args.no_per_model:
         per = []
         Kp, Wp = args.per_model_steps, 5

@@ -387,6 +387,18 @@ amk_status amk_quantize(int32_t wfmt, const void* master, int64_t rows, int64_t 
                         void* scales, void* stream);
 
 /* Library version string. */
+/* A measurement aid, not a step of the decode: read `bytes` of device memory once with the
+ * same 16-byte non-temporal loads the decode kernel streams its weights with (2048 workgroups of
+ * 512 threads), so that a caller timing the launch on `stream` gets the HBM read rate this GPU
+ * reaches, the measured ceiling beside the specification's one for the roofline the pages
+ * report (page 1, "Honesty rules"; page 3, "The results, read carefully").
+ *  buf    device, 16-byte aligned, borrowed until the launch completes; `bytes` a positive
+ *         multiple of 16 (else AMK_E_INVALID_ARG, nothing launched).
+ *  out    device uint32[1]: written only when the xor of a thread's words equals a fixed value
+ *         (it keeps the loads in the program); its content means nothing.
+ * Enqueues one launch and returns without synchronising. */
+amk_status amk_read_probe(const void* buf, uint64_t bytes, uint32_t* out, void* stream);
+
 const char* amk_version(void);
 
 #ifdef __cplusplus

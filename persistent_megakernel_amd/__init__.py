@@ -21,7 +21,7 @@ from ._abi import (AMK_BF16, AMK_F32, AMK_INT4_G128, AMK_INT8_PC, AmkError, STAT
                    STATUS_TIMEOUT, check, lib)
 
 __all__ = ["amk_validate", "amk_lower", "amk_create", "amk_decode_step", "amk_decode_step_static", "amk_destroy",
-           "amk_quantize", "amk_device_status", "amk_ctx_schedule", "amk_set_trace", "amk_version", "Decoder",
+           "amk_quantize", "amk_read_probe", "amk_device_status", "amk_ctx_schedule", "amk_set_trace", "amk_version", "Decoder",
            "model_desc", "schedule_config", "AmkError", "amk_vm_run",
            "amk_prefill", "amk_lower_prefill", "amk_set_prefill_trace"]
 
@@ -258,6 +258,11 @@ def amk_quantize(wfmt: int, master_ptr: int, rows: int, cols: int, codes_ptr: in
                  stream: int = 0) -> None:
     check("amk_quantize", lib().amk_quantize(int(wfmt), C.c_void_p(master_ptr), int(rows), int(cols),
                                              C.c_void_p(codes_ptr), C.c_void_p(scales_ptr), C.c_void_p(stream)))
+
+
+def amk_read_probe(buf_ptr: int, nbytes: int, out_ptr: int, stream: int = 0) -> None:
+    check("amk_read_probe", lib().amk_read_probe(C.c_void_p(buf_ptr), int(nbytes), C.c_void_p(out_ptr),
+                                                 C.c_void_p(stream)))
 
 
 # ---------------------------------------------------------------- a model on the device

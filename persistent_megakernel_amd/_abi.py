@@ -119,6 +119,7 @@ SIGNATURES = {
     "amk_set_trace": (C.c_int, [_P, _P, C.c_uint64]),
     "amk_destroy": (None, [_P]),
     "amk_quantize": (C.c_int, [C.c_int32, _P, C.c_int64, C.c_int64, _P, _P, _P]),
+    "amk_read_probe": (C.c_int, [_P, C.c_uint64, _P, _P]),
     "amk_version": (C.c_char_p, []),
     "amk_vm_run": (C.c_int, [C.POINTER(amk_schedule), C.POINTER(amk_vm_opts), C.POINTER(amk_vm_result)]),
     "amk_prefill": (C.c_int, [_P, _P, C.c_int32, C.c_int32, _P, _P, _P]),

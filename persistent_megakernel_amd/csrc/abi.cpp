@@ -526,6 +526,11 @@ extern "C" void amk_destroy(amk_ctx* c) {
     free_ctx(c);
 }
 
+extern "C" amk_status amk_read_probe(const void* buf, uint64_t bytes, uint32_t* out, void* stream_v) {
+    if (!buf || !out || bytes < 16 || bytes % 16 || ((uintptr_t)buf & 15u)) return AMK_E_INVALID_ARG;
+    return launch_read_probe(buf, bytes, out, (hipStream_t)stream_v) == hipSuccess ? AMK_OK : AMK_E_HIP;
+}
+
 extern "C" amk_status amk_quantize(int32_t wfmt, const void* master, int64_t rows, int64_t cols, void* codes, void* scales,
                                    void* stream_v) {
     if (!master || !codes || !scales || rows < 0 || cols <= 0) return AMK_E_INVALID_ARG;

@@ -13,6 +13,7 @@ hipError_t launch_repack(const RowMap* d_rows, uint32_t n_rows, const void* cons
 hipError_t launch_quantize(const uint16_t* master, int64_t rows, int64_t cols, int group, int qmax, int8_t* codes, float* scales,
                            hipStream_t st);
 hipError_t launch_norms(const void* src, int wfmt, uint32_t n, float* dst, hipStream_t st);
+hipError_t launch_read_probe(const void* buf, uint64_t bytes, uint32_t* out, hipStream_t st);
 
 // The persistent kernel: one cooperative launch of n_cu workgroups of kThreads.
 hipError_t launch_megakernel(const KParams& p, int n_cu, hipStream_t st);

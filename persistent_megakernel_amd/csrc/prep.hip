@@ -1,6 +1,7 @@
 // One-off set-up kernels (run at amk_create, not per token): the weight quantiser and the repack
 // of the canonical weights into the per-CU weight streams the megakernel reads, plus the
-// conversion of norm gains to fp32.
+// conversion of norm gains to fp32. Also the read probe, a measurement aid outside the decode
+// step (see amk_read_probe).
 //
 // Quantisation (the pages' int8 W8A16 and int4 weight-only kernels, page 2, "Quantisation
 // support and performance"; page 1, "Results"): symmetric absmax over an output row (int8) or a
@@ -114,7 +115,34 @@ __global__ void k_norms_to_f32(const void* src, int wfmt, uint32_t n, float* dst
     dst[i] = wfmt == AMK_F32 ? ((const float*)src)[i] : bf2f(((const uint16_t*)src)[i]);
 }
 
+// Read n16 16-byte segments once with the decode kernel's non-temporal weight loads: thread t of
+// the grid takes segments t, t + stride, ... four at a time. The xor of what a thread read is
+// stored only if it equals a fixed value, so the loads stay in the program.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr uint32_t kProbeMagic = 0x9e3779b9u;
+__global__ void __launch_bounds__(512) k_read_probe(const u32x4* p, uint64_t n16, uint32_t* out) {
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    uint32_t acc = 0;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const u32x4 a = __builtin_nontemporal_load(p + i), b = __builtin_nontemporal_load(p + i + stride);
+        const u32x4 c = __builtin_nontemporal_load(p + i + 2 * stride), d = __builtin_nontemporal_load(p + i + 3 * stride);
+        acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+    }
+    for (; i < n16; i += stride) {
+        const u32x4 a = __builtin_nontemporal_load(p + i);
+        acc ^= a.x ^ a.y ^ a.z ^ a.w;
+    }
+    if (acc == kProbeMagic) out[0] = acc;
+}
+
 }  // namespace
+
+hipError_t launch_read_probe(const void* buf, uint64_t bytes, uint32_t* out, hipStream_t st) {
+    // 8 workgroups of 512 threads per CU of a 256-CU part: enough loads in flight to cover HBM latency
+    hipLaunchKernelGGL(k_read_probe, dim3(2048), dim3(512), 0, st, (const u32x4*)buf, bytes / 16, out);
+    return hipGetLastError();
+}
 
 hipError_t launch_repack(const RowMap* d_rows, uint32_t n_rows, const void* const* d_src_tab, int L, int wfmt, uint8_t* d_stream,
                          hipStream_t st) {

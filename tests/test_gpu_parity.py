@@ -366,6 +366,22 @@ def test_decode_step_argument_errors(M):
     dec.close()
 
 
+def test_read_probe_arguments_and_launch(M):
+    """The read probe used for the measured read ceiling: a launch over a buffer completes, and
+    bad arguments are refused on the host before anything is launched."""
+    n = 1 << 24
+    buf = torch.ones(n, dtype=torch.uint8, device="cuda")
+    out = torch.zeros(1, dtype=torch.int32, device="cuda")
+    M.amk_read_probe(buf.data_ptr(), n, out.data_ptr())
+    M.amk_read_probe(buf.data_ptr(), 48, out.data_ptr())   # fewer segments than threads
+    torch.cuda.synchronize()
+    assert int(out.item()) == 0   # the xor of whole 16-byte runs of ones is never the fixed value
+    for ptr, nbytes in ((buf.data_ptr() + 1, 1 << 20), (buf.data_ptr(), 15), (buf.data_ptr(), 0),
+                        (buf.data_ptr(), (1 << 20) + 8), (0, 1 << 20)):
+        with pytest.raises(M.AmkError):
+            M.amk_read_probe(ptr, nbytes, out.data_ptr())
+
+
 def test_last_position(M):
     """A step at pos = max_ctx - 1 reads every cache row below it and writes the last row."""
     shape = I.tiny_shape(max_ctx=40)
