@@ -61,6 +61,7 @@ struct __attribute__((aligned(16))) Lds {
     float red[kRedRows];               // per-row GEMV results of the current task
     float att[kAttnLds / 4];           // attention q / current k, v; residual rows; reductions
     DevTask tcache[kTaskCache];        // the first kTaskCache tasks of this CU's queue
+    float hsum[kMaxInter / 2048 * 64]; // int4 tasks: per (load j, lane) the sum of the 32 input values the lane's codes meet
     uint32_t abort_;                   // this workgroup gives up
     float fpart[2 * kComputeWaves];
     int32_t ipart[2 * kComputeWaves];
@@ -320,7 +321,9 @@ DEV float dot16(const Lds& S, u32x4 w, uint32_t j, uint32_t lane, uint32_t row, 
                 const uint32_t wp = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
                 acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(wp), as_bf2(hh[2 * k + p]), acc, false);
             }
-    } else {   // int4 g128
+    } else {   // int4 g128: sum_b (n_b - 8) h_b = sum_b n_b h_b - 8 sum_b h_b, with n_b the stored
+               // nibble (0..15, exact in bf16) taken through the bf16 dot instruction in pairs and
+               // sum_b h_b the lane's input sum, computed once per task (S.hsum)
         const uint32_t c0 = 2048u * j + 32u * lane;
         const float sc = h2f(((const uint16_t*)S.kvb)[row * (K / 128) + c0 / 128]);
         const uint32_t a[4] = {w.x, w.y, w.z, w.w};
@@ -329,13 +332,16 @@ DEV float dot16(const Lds& S, u32x4 w, uint32_t j, uint32_t lane, uint32_t row, 
         for (int k = 0; k < 4; ++k) {
             const u32x4 hv = *(const u32x4*)(hb + c0 + 8 * k);
             const uint32_t hh[4] = {hv.x, hv.y, hv.z, hv.w};
+            // byte m of lo holds nibble 2m (the even code), byte m of hi nibble 2m + 1
+            const uint32_t lo = a[k] & 0x0f0f0f0fu, hi = (a[k] >> 4) & 0x0f0f0f0fu;
 #pragma unroll
-            for (int b = 0; b < 8; ++b) {
-                const uint32_t hw = hh[b >> 1];
-                p += (float)((int)((a[k] >> (4 * b)) & 0xfu) - 8) * bf2f((b & 1) ? (hw >> 16) : (hw & 0xffffu));
+            for (int m = 0; m < 4; ++m) {
+                const float f0 = (float)((lo >> (8 * m)) & 0xffu), f1 = (float)((hi >> (8 * m)) & 0xffu);
+                const uint32_t wp = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+                p = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(wp), as_bf2(hh[m]), p, false);
             }
         }
-        acc = sc * p;
+        acc = sc * (p - 8.f * S.hsum[64u * j + lane]);
     }
     return acc;
 }
@@ -609,6 +615,24 @@ DEV void op_gemv(const TaskEnv& e, const DevTask& T, WBuf& A, WBuf& B) {
         }
     }
     stage_input(c, ctid, src, emb, K, gains_of(P, T));   // ends with a barrier
+    if (P.wfmt == AMK_INT4_G128) {   // the input sums the int4 dot products take out (see dot16)
+        const uint16_t* hb = (const uint16_t*)S.hb;
+        for (uint32_t t = (uint32_t)ctid; t < ((K + 2047u) / 2048u) * 64u; t += kComputeThreads) {
+            const uint32_t c0 = 32u * t;   // = 2048 * (t / 64) + 32 * (t % 64)
+            float hs = 0.f;
+            if (c0 < K) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const u32x4 hv = *(const u32x4*)(hb + c0 + 8 * k);
+                    const uint32_t hh[4] = {hv.x, hv.y, hv.z, hv.w};
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) hs += bf2f(hh[m] & 0xffffu) + bf2f(hh[m] >> 16);
+                }
+            }
+            S.hsum[t] = hs;
+        }
+        cbar();
+    }
     mark(e, 1);
     gemv_rows(c, T, e.cw, A, B);
     if (e.tr && ctid == 0) e.tr[4] = rt();
