@@ -482,12 +482,15 @@ DEV const float* gains_of(const KParams& P, const DevTask& T) {
 }
 
 constexpr int kMaxGainsPerThread = kMaxHidden / kComputeThreads;
+// flag-carrying residual words per thread (a task's rows: at most kRedRows values)
+constexpr int kResidWords = kRedRows / kComputeThreads;
 
 // Stage the GEMV input of a task into S.hb (activation format), with RMSNorm when gains != 0.
 // Source: flag-carrying words (src) or, for layer 0, the embedding row of the input token. The
 // thread's norm gains are loaded before the wait so their latency overlaps it.
+template <typename H>
 DEV void stage_input(const Ctx& c, int ctid, const u64* src, const void* embed_row, uint32_t K,
-                     const float* gains) {
+                     const float* gains, H&& before_barrier) {
     const KParams& P = *c.P;
     Lds& S = *c.S;
     const uint32_t vpw = P.act_f32 ? 1u : 2u;
@@ -520,6 +523,7 @@ DEV void stage_input(const Ctx& c, int ctid, const u64* src, const void* embed_r
         }
     }
     if (!gains) {
+        before_barrier();
         cbar();
         return;
     }
@@ -539,6 +543,7 @@ DEV void stage_input(const Ctx& c, int ctid, const u64* src, const void* embed_r
             hput(P, S, i, rA(P, (x * r) * gr[k]));
         }
     }
+    before_barrier();
     cbar();
 }
 
@@ -600,21 +605,46 @@ DEV void op_gemv(const TaskEnv& e, const DevTask& T, WBuf& A, WBuf& B) {
             rc0 = cs.x; rs0 = cs.y; rc1 = cs.z; rs1 = cs.w;
         }
     }
-    // residual rows (O and down): from the previous x (or the embedding row at layer 0)
+    // residual rows (O and down): from the previous x (or the embedding row at layer 0). The
+    // flag-carrying words are loaded now and checked after the input gather, whose first wait
+    // covers them: the two take one memory round trip, not two.
+    const bool resid_ll = (op == AMK_OP_OPROJ && l > 0) || op == AMK_OP_DOWN;
+    const u64* rs = nullptr;
+    uint32_t nres = 0;
+    u64 rw[kResidWords];
     if (op == AMK_OP_OPROJ || op == AMK_OP_DOWN) {
         const uint32_t r0 = T.arg[0], n = T.arg[1];
-        if (op == AMK_OP_OPROJ && l == 0) {
+        if (!resid_ll) {
             const uint8_t* er = (const uint8_t*)P.embed + (uint64_t)e.token * P.H * esz;
             for (uint32_t i = (uint32_t)ctid; i < n; i += kComputeThreads)
                 S.att[i] = P.act_f32 ? ((const float*)er)[r0 + i] : bf2f(((const uint16_t*)er)[r0 + i]);
         } else {
-            const u64* rs = (op == AMK_OP_OPROJ ? ll_layer(P, e.y, l - 1) + e.y.xd : LLl + e.y.xo) + r0 / vpw;
-            (void)ll_gather(c, rs, n / vpw, ctid, [&](uint32_t i, uint32_t pl) {
-                    for (uint32_t j = 0; j < vpw; ++j) S.att[i * vpw + j] = word_val(P, pl, (int)j);
-                });
+            rs = (op == AMK_OP_OPROJ ? ll_layer(P, e.y, l - 1) + e.y.xd : LLl + e.y.xo) + r0 / vpw;
+            nres = n / vpw;
+#pragma unroll
+            for (int k = 0; k < kResidWords; ++k) {
+                const uint32_t i = (uint32_t)ctid + (uint32_t)k * kComputeThreads;
+                if (i < nres) rw[k] = ll_load(rs + i);
+            }
         }
     }
-    stage_input(c, ctid, src, emb, K, gains_of(P, T));   // ends with a barrier
+    stage_input(c, ctid, src, emb, K, gains_of(P, T), [&]() {
+            // the residual words (normally published long before: no further poll), stored before
+            // the barrier that ends the staging
+            if (!rs) return;
+            const uint32_t flag = P.flag;
+#pragma unroll
+            for (int k = 0; k < kResidWords; ++k) {
+                const uint32_t i = (uint32_t)ctid + (uint32_t)k * kComputeThreads;
+                if (i >= nres) continue;
+                uint32_t spins = 0;
+                while ((uint32_t)(rw[k] >> 32) != flag) {
+                    if (!spin_ok(c, spins)) break;
+                    rw[k] = ll_load(rs + i);
+                }
+                for (uint32_t j = 0; j < vpw; ++j) S.att[i * vpw + j] = word_val(P, (uint32_t)rw[k], (int)j);
+            }
+        });   // ends with a barrier
     if (P.wfmt == AMK_INT4_G128) {   // the input sums the int4 dot products take out (see dot16)
         const uint16_t* hb = (const uint16_t*)S.hb;
         for (uint32_t t = (uint32_t)ctid; t < ((K + 2047u) / 2048u) * 64u; t += kComputeThreads) {
