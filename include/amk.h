@@ -153,7 +153,8 @@ typedef struct {
                                   rows, else the least of: CUs per head group, cache rows / 32, and
                                   the chunks whose merge states fit LDS) */
     int32_t attn_group_tasks;  /* 1: one attention task per KV group (up to 8 query heads), 2: one per
-                                  query head, 0: auto (grouped whenever KV heads are shared) */
+                                  query head, 0: auto (grouped when KV heads are shared and the
+                                  cache holds at least 2048 positions) */
     int32_t cu_assign;         /* 0 = XCD-aware (unchunked attention of one KV group on one XCD; chunked
                                   attention round robin), 1 = plain round robin */
     int32_t prefetch_groups;   /* pipelining depth: groups of a GEMV task's weight loads (6 KiB per wave

@@ -36,6 +36,7 @@ constexpr int kAheadGroupsDefault = 1;      // groups of the next task's weights
 constexpr int kAttnBlock = 64;              // positions per attention unit
 constexpr int kMaxAttnHeads = 8;            // query heads per attention task
 constexpr int kChunkedCtx = 256;            // caches at least this long get context-split attention by default
+constexpr int kGroupedCtx = 2048;           // caches at least this long get one attention task per KV group by default
 constexpr int64_t kStageFloats = kHBytes / 4;   // fp32 values the input-vector stage holds
 // Flag-carrying words in the static per-device array of the allocation-free decode entry point
 // (64 MiB): a step whose layout needs more is refused.

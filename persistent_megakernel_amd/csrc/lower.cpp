@@ -467,7 +467,10 @@ amk_status lower_model(const amk_model_desc& d, const amk_schedule_config* cfg, 
     const int nH = s.nH, nKV = s.nKV, gsz = nH / nKV, vpw = s.vpw;
     // attention grouping
     // one attention task per KV group (its query heads share the K/V stream) unless asked not to
-    const bool group_tasks = C.attn_group_tasks == 1 || (C.attn_group_tasks == 0 && gsz > 1);   // 2: per query head
+    // by default the query heads of a KV group share one task (and one read of the group's K/V
+    // rows) only where the cache is long enough for those reads to matter; short caches get one
+    // task per query head, which spreads the work over more CUs
+    const bool group_tasks = C.attn_group_tasks == 1 || (C.attn_group_tasks == 0 && gsz > 1 && d.max_ctx >= kGroupedCtx);   // 2: per query head
     int heads_per_task = 1;
     if (group_tasks) {
         heads_per_task = gsz;

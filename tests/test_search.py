@@ -148,6 +148,7 @@ def test_refit_recovers_a_planted_cost_model():
     items = []
     for cfg in ({}, {"prefetch_groups": -1}, {"prefetch_groups": 2}, {"attn_chunks": 1}, {"attn_chunks": 8},
                 {"tasks_qkv": 32}, {"tasks_gateup": 64}, {"attn_group_tasks": 2}):
+        cfg = {"attn_group_tasks": 1, **cfg}   # grouped attention unless the case says otherwise
         ok, sc = S.lower(shape, cfg, shape.max_ctx)
         assert ok
         pl = S.Plan(shape, sc, 512)
