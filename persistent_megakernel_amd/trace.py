@@ -5,7 +5,9 @@ inputs observed, rows done, end, first wave's rows done (GEMV), outputs written 
 From them: per opcode the time spent waiting for inputs (producers on other CUs plus the
 staging prologue), computing, in the epilogue, the skew between the first wave and the whole
 workgroup at the end of the rows, and the closing barrier; per phase (opcode, layer) the moment
-the last CU finished, i.e. the critical path of the launch.
+the last CU finished, i.e. the critical path of the launch; and per consuming opcode the hop:
+from the last publication of a task's producers (their outputs written) to the task's inputs
+observed, the cross-CU synchronisation cost of each dependency.
 
     python -m persistent_megakernel_amd.trace --workload tinyllama_int8 --pos 512
 """
@@ -59,8 +61,42 @@ def summarize(sched, trace) -> dict:
         crit.append({"op": OPNAMES.get(op, str(op)), "layer": int(layer), "last_end_us": round(end, 3),
                      "span_us": round(end - prev, 3), "last_inputs_us": round(ready, 3)})
         prev = end
-    return {"launch_us": round(total, 3), "ops_mean_us": ops, "phases": crit,
+    return {"launch_us": round(total, 3), "ops_mean_us": ops, "phases": crit, "hops": hops(sched, tr),
             "n_cu": len(sched.queues), "cu_busy_end_us": round(float(np.median(rel[:, 3])), 3)}
+
+
+def hops(sched, trace) -> dict:
+    """Per consuming opcode: the hop of each task (inputs observed minus the latest 'outputs
+    written' stamp of the producers of the counters it waits on), as the median over tasks, the
+    median over phases of each phase's largest hop, and the share of phases whose slowest
+    consumer runs on the CU of the phase's last producer."""
+    tr = np.asarray(trace, dtype=np.int64)
+    order = [t for q in sched.queues for t in q]
+    row = {tid: k for k, tid in enumerate(order)}
+    cu_of = {tid: cu for cu, q in enumerate(sched.queues) for tid in q}
+    prods = defaultdict(list)
+    for tid, t in enumerate(sched.tasks):
+        for c in getattr(t, "signals", ()):
+            prods[c].append(tid)
+    per_task = defaultdict(list)
+    per_phase = defaultdict(list)   # (op, layer) -> [(hop, consumer cu, last producer cu)]
+    for tid, t in enumerate(sched.tasks):
+        src = [p for (c, _) in getattr(t, "waits", ()) for p in prods.get(c, [])]
+        if not src:
+            continue
+        last = max(src, key=lambda p: tr[row[p], 5])
+        hop = float(tr[row[tid], 1] - tr[row[last], 5]) * TICK_US
+        name = OPNAMES.get(t.opcode, str(t.opcode))
+        per_task[name].append(hop)
+        per_phase[(name, t.args[0])].append((hop, cu_of[tid], cu_of[last]))
+    out = {}
+    for name, v in per_task.items():
+        phases = [ph for (n, _), ph in per_phase.items() if n == name]
+        worst = [max(ph) for ph in phases]
+        out[name] = {"median_us": round(float(np.median(v)), 3),
+                     "phase_max_median_us": round(float(np.median([w[0] for w in worst])), 3),
+                     "slowest_on_last_producer_cu": round(float(np.mean([w[1] == w[2] for w in worst])), 3)}
+    return out
 
 
 def main(argv=None) -> int:

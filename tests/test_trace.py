@@ -19,9 +19,14 @@ from persistent_megakernel_amd import _abi as A
 from persistent_megakernel_amd.trace import TICK_US, summarize
 
 
-def _sched(tasks, queues):
-    """tasks: list of (opcode, layer); queues: list of lists of task ids."""
-    ts = [types.SimpleNamespace(opcode=op, args=(layer, 0, 0, 0, 0)) for op, layer in tasks]
+def _sched(tasks, queues, waits=None, signals=None):
+    """tasks: list of (opcode, layer); queues: list of lists of task ids; optional per-task waits
+    [(counter, threshold)] and signalled counters."""
+    n = len(tasks)
+    waits = waits or [[] for _ in range(n)]
+    signals = signals or [[] for _ in range(n)]
+    ts = [types.SimpleNamespace(opcode=op, args=(layer, 0, 0, 0, 0), waits=waits[i], signals=signals[i])
+          for i, (op, layer) in enumerate(tasks)]
     return types.SimpleNamespace(tasks=ts, queues=queues)
 
 
@@ -88,3 +93,25 @@ def test_merge_and_argmax_have_no_compute_split():
     assert ops["merge"]["epilogue"] == pytest.approx(60 * TICK_US)
     assert ops["argmax"]["epilogue"] == pytest.approx(20 * TICK_US)
     assert "wave_skew" not in ops["merge"]
+
+
+def test_hops_from_the_last_producer_to_each_consumer():
+    # two O tasks (CUs 0 and 1) signal counter 0; two gate/up tasks (CUs 1 and 2) wait on it
+    tasks = [(A.AMK_OP_OPROJ, 4), (A.AMK_OP_OPROJ, 4), (A.AMK_OP_GATEUP, 4), (A.AMK_OP_GATEUP, 4)]
+    queues = [[0], [1, 2], [3]]
+    waits = [[], [], [(0, 2)], [(0, 2)]]
+    signals = [[0], [0], [], []]
+    rows = {
+        0: _row(0, 10, 40, 60, out=50),
+        1: _row(0, 10, 60, 80, out=70),          # the last producer publishes at 70 (CU 1)
+        2: _row(80, 400, 500, 600),              # its own CU sees the inputs at 400: hop 330
+        3: _row(20, 300, 450, 500),              # CU 2: hop 230
+    }
+    order = [t for q in queues for t in q]
+    tr = np.array([rows[t] for t in order], dtype=np.int64)
+    res = summarize(_sched(tasks, queues, waits, signals), tr)
+    h = res["hops"]
+    assert set(h) == {"gateup"}    # the O tasks wait on nothing here
+    assert h["gateup"]["median_us"] == pytest.approx(280 * TICK_US)
+    assert h["gateup"]["phase_max_median_us"] == pytest.approx(330 * TICK_US)
+    assert h["gateup"]["slowest_on_last_producer_cu"] == 1.0
