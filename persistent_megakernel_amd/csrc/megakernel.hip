@@ -484,6 +484,8 @@ DEV const float* gains_of(const KParams& P, const DevTask& T) {
 constexpr int kMaxGainsPerThread = kMaxHidden / kComputeThreads;
 // flag-carrying residual words per thread (a task's rows: at most kRedRows values)
 constexpr int kResidWords = kRedRows / kComputeThreads;
+// 16-byte chunks of a tile's quantisation scales each thread holds in registers over the gather
+constexpr int kScaleRegs = 2;
 
 // Stage the GEMV input of a task into S.hb (activation format), with RMSNorm when gains != 0.
 // Source: flag-carrying words (src) or, for layer 0, the embedding row of the input token. The
@@ -588,14 +590,28 @@ DEV void op_gemv(const TaskEnv& e, const DevTask& T, WBuf& A, WBuf& B) {
     case AMK_OP_LM: src = ll_layer(P, e.y, P.L - 1) + e.y.xd; break;
     }
 
-    // quantised tiles: the row scales (int8) or group scales (int4) go to LDS. Any wait below
-    // waits for the weight loads already in flight too, so these loads cost no extra latency.
+    // quantised tiles: the row scales (int8) or group scales (int4) go to LDS. They are loaded
+    // into registers now and written to LDS only after the input gather: an LDS store here would
+    // wait for the loads, and with them for the weight loads in flight ahead of them, before the
+    // first poll of the inputs went out.
     const uint32_t sc_chunks = (uint32_t)((tile_bytes(P.wfmt, K, T.tile_rows) - tile_scale_off(P.wfmt, K, T.tile_rows)) / 16);
-    if (sc_chunks) {
-        const uint8_t* sb = c.wcu + T.wofs + tile_scale_off(P.wfmt, K, T.tile_rows);
-        for (uint32_t q = (uint32_t)ctid; q < sc_chunks; q += kComputeThreads)
-            *(u32x4*)(S.kvb + 16 * q) = *(const u32x4*)(sb + 16ull * q);
+    const uint8_t* sb = c.wcu + T.wofs + tile_scale_off(P.wfmt, K, T.tile_rows);
+    u32x4 scr[kScaleRegs];
+#pragma unroll
+    for (int k = 0; k < kScaleRegs; ++k) {
+        const uint32_t q = (uint32_t)ctid + (uint32_t)k * kComputeThreads;
+        if (q < sc_chunks) scr[k] = *(const u32x4*)(sb + 16ull * q);
     }
+    auto put_scales = [&]() {
+#pragma unroll
+        for (int k = 0; k < kScaleRegs; ++k) {
+            const uint32_t q = (uint32_t)ctid + (uint32_t)k * kComputeThreads;
+            if (q < sc_chunks) *(u32x4*)(S.kvb + 16 * q) = scr[k];
+        }
+        // (tiles with more scale chunks than the registers hold: the rest directly)
+        for (uint32_t q = (uint32_t)ctid + (uint32_t)kScaleRegs * kComputeThreads; q < sc_chunks; q += kComputeThreads)
+            *(u32x4*)(S.kvb + 16 * q) = *(const u32x4*)(sb + 16ull * q);
+    };
     // QKV: this thread's rotary cos/sin (quad ctid), loaded now so the load overlaps the input wait
     float rc0 = 1.f, rs0 = 0.f, rc1 = 1.f, rs1 = 0.f;
     if (op == AMK_OP_QKV && (uint32_t)ctid < T.arg[1]) {
@@ -629,6 +645,7 @@ DEV void op_gemv(const TaskEnv& e, const DevTask& T, WBuf& A, WBuf& B) {
         }
     }
     stage_input(c, ctid, src, emb, K, gains_of(P, T), [&]() {
+            put_scales();
             // the residual words (normally published long before: no further poll), stored before
             // the barrier that ends the staging
             if (!rs) return;
