@@ -200,20 +200,22 @@ def test_depth1_full_width(M, name, pos0, prefill):
     _check_ids(r["gen"], r["fr"], r["margins"], name + " free-running")
 
 
-@pytest.mark.parametrize("prefetch", [-1, 2])
-def test_prefetch_depths_tinyllama_int8(M, prefetch):
-    """The run-time prefetch depth: no weight loads issued ahead, or two groups ahead, on two
-    TinyLlama-shaped int8 layers from position 512 (full width, so every GEMV task has more
-    than two load groups)."""
+@pytest.mark.parametrize("cfg_kw", [dict(prefetch_groups=-1), dict(prefetch_groups=2), dict(attn_group_tasks=1)],
+                         ids=["no-prefetch", "prefetch-2", "grouped-attention"])
+def test_tinyllama_int8_two_layer_variants(M, cfg_kw):
+    """Launch parameters and lowerings beside the defaults, on two TinyLlama-shaped int8 layers
+    from position 512 (full width, so every GEMV task has more than two load groups): no weight
+    loads issued ahead, two groups ahead, and one attention task per KV group (the default at
+    this cache size is one per query head)."""
     shape = I.SHAPES["tinyllama_int8"].replace(n_layers=2)
-    log(f"case tinyllama_int8 2 layers prefetch_groups={prefetch}")
+    log(f"case tinyllama_int8 2 layers {cfg_kw}")
     w = I.make_weights(shape)
     tok = int(I.prompt_tokens(shape, 1, stream=3)[0])
-    r = _run(M, shape, w, [tok], 4, pos0=512, prefill=512, cfg=M.schedule_config(prefetch_groups=prefetch))
-    log(f"prefetch {prefetch}: max abs err {max(r['errs']):.3e}, min margin {min(r['margins']):.3e}")
+    r = _run(M, shape, w, [tok], 4, pos0=512, prefill=512, cfg=M.schedule_config(**cfg_kw))
+    log(f"{cfg_kw}: max abs err {max(r['errs']):.3e}, min margin {min(r['margins']):.3e}")
     assert max(r["errs"]) <= TWO_LAYER_ABS
-    _check_ids(r["gen"], r["tf"], r["margins"], "prefetch", r["gen_errs"])
-    _check_ids(r["gen"], r["fr"], r["margins"], "prefetch free-running", r["gen_errs"])
+    _check_ids(r["gen"], r["tf"], r["margins"], str(cfg_kw), r["gen_errs"])
+    _check_ids(r["gen"], r["fr"], r["margins"], f"{cfg_kw} free-running", r["gen_errs"])
 
 
 # ------------------------------------------------------------------ full depth
