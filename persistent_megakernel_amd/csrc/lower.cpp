@@ -192,11 +192,14 @@ bool derive_accesses(const Shape& s, const GenTask& t, uint64_t w_off, uint64_t 
         if (!nh || nh > (uint32_t)kMaxAttnHeads || nc != nchunks || c >= nc || h0 + nh > (uint32_t)s.nH) return false;
         const uint32_t g = (uint32_t)((uint64_t)h0 * s.nKV / s.nH);
         if ((uint64_t)(h0 + nh - 1) * s.nKV / s.nH != g) return false;   // one KV group per task
-        if ((uint64_t)kComputeWaves * nh * (s.hd + 2) > kStageFloats) return false;   // per-wave states in LDS
-        {   // dims per lane of the attention lane layout: hd / min(64 / nh rounded up to 2^k, hd) <= 8
+        {   // attention lane layout: hd / 8 lanes per head, nh rounded up to a power of two head
+            // places, all in one wave; the (wave, slot) states of every head staged in LDS
             uint32_t nhp = 1;
             while (nhp < nh) nhp <<= 1;
-            if ((uint32_t)s.hd / std::min<uint32_t>(64u / nhp, (uint32_t)s.hd) > 8u) return false;
+            const uint64_t lanes = (uint64_t)(s.hd / 8) * nhp;
+            if (lanes > 64) return false;
+            const uint64_t states = (uint64_t)kComputeWaves * (64 / lanes);
+            if (states * nh * (s.hd + 2) > (uint64_t)kStageFloats) return false;
         }
         add_acc(a, s.reg(l, L_QKV), 0, (uint64_t)h0 * s.hd, (uint64_t)(h0 + nh) * s.hd);
         if (c == nc - 1) {
@@ -480,7 +483,15 @@ amk_status lower_model(const amk_model_desc& d, const amk_schedule_config* cfg, 
             heads_per_task = h;
         }
     }
-    while (heads_per_task > 1 && (int64_t)kComputeWaves * heads_per_task * (s.hd + 2) > kStageFloats) {
+    // the task's heads must fit the attention lane layout (hd / 8 lanes per head, heads rounded up
+    // to a power of two, in one wave) and their per-state softmax states the LDS stage
+    auto attn_fits = [&](int hpt) {
+        int64_t nhp = 1;
+        while (nhp < hpt) nhp <<= 1;
+        const int64_t lanes = (int64_t)(s.hd / 8) * nhp;
+        return lanes <= 64 && (int64_t)kComputeWaves * (64 / lanes) * hpt * (s.hd + 2) <= kStageFloats;
+    };
+    while (heads_per_task > 1 && !attn_fits(heads_per_task)) {
         int h = heads_per_task - 1;
         while (gsz % h) --h;
         heads_per_task = h;

@@ -104,6 +104,25 @@ DEV float wave_sum_dpp(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
+// Sum (MAX = false) or maximum over aligned groups of G consecutive lanes (G = 1, 2, 4, 8 or 16),
+// every lane of a group receiving the group's result: DPP moves inside rows of 16 lanes (the two
+// quad permutations lane ^ 1 and lane ^ 2, then the half-row mirror and the row mirror, each of
+// which pairs a lane with one holding the other half's result), no LDS crossbar.
+template <bool MAX>
+DEV float group_reduce(float v, uint32_t G) {
+#define AMK_GRP(ctrl)                                                                                          \
+    {                                                                                                          \
+        const float o_ = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl, 0xf, 0xf, false)); \
+        v = MAX ? fmaxf(v, o_) : v + o_;                                                                       \
+    }
+    if (G >= 2) AMK_GRP(0xb1);    // quad_perm [1,0,3,2]
+    if (G >= 4) AMK_GRP(0x4e);    // quad_perm [2,3,0,1]
+    if (G >= 8) AMK_GRP(0x141);   // row_half_mirror
+    if (G >= 16) AMK_GRP(0x140);  // row_mirror
+#undef AMK_GRP
+    return v;
+}
+
 // Maximum over the 64 lanes with the same DPP pattern as wave_sum_dpp.
 DEV float wave_max_dpp(float v) {
 #define AMK_DPP_MAX(ctrl, rmask) \
@@ -801,11 +820,12 @@ DEV void op_gemv(const TaskEnv& e, const DevTask& T, WBuf& A, WBuf& B) {
 constexpr int kAttQ = 0;                          // [nh][hd], nh * hd <= 1024
 constexpr int kAttKc = kMaxAttnHeads * 128;       // [hd]
 constexpr int kAttVc = kAttKc + 128;              // [hd]
-constexpr int kAttF = kAttVc + 128;               // [kComputeWaves][kMaxAttnHeads] weights exp(m_w - M)
-constexpr int kAttM = kAttF + kComputeWaves * kMaxAttnHeads;   // [kMaxAttnHeads] maxima
-static_assert(kAttM + kMaxAttnHeads <= kAttnLds / 4, "attention LDS map");
+constexpr int kAttStates = 512;                   // (state, head) pairs: 8 waves * 64 / L slots * nh <= 512
+constexpr int kAttF = kAttVc + 128;               // [state][nh] weights exp(m_s - M)
+constexpr int kAttM = kAttF + kAttStates;         // [kMaxAttnHeads] maxima
+constexpr int kAttL = kAttM + kMaxAttnHeads;      // [kMaxAttnHeads] weighted sums of the states' l
+static_assert(kAttL + kMaxAttnHeads <= kAttnLds / 4, "attention LDS map");
 constexpr int kAttMaxD = 8;                       // dims per lane: hd / lanes-per-head (the lowering keeps it <= 8)
-constexpr int kAttBatch = 4;                      // history positions a wave scores at once
 constexpr int kKvRound = kKvBytes;               // bytes of K and V rows staged per round
 constexpr int kKvLoads = kKvRound / 16 / kComputeThreads;   // 16-byte K/V loads per thread per round
 
@@ -948,14 +968,23 @@ DEV void op_attn_d(const TaskEnv& e, const DevTask& T, WBuf& A, WBuf& B) {
     if (rn) kv_round_store(P, S, rn, ctid, A, B);
     cbar();
     mark(e, 1);
-    // lane layout (D, the dims per lane, is the template parameter: every per-dim loop below is
-    // fixed at compile time)
+    // lane layout: a lane owns D consecutive dims of one query head for one state slot, lane =
+    // (slot, head place, dim group) with L = hd / D lanes per head, nhp = nh rounded up to a power
+    // of two head places and S_ = 64 / (L * nhp) slots per wave. Each state (wave, slot) runs its
+    // own online softmax (running max m, running sum l, rescaled output o) over the positions
+    // dealt to it round robin; a position's score is the sum of q.K over the L lanes of its head,
+    // reduced with DPP moves inside the lane group.
     constexpr uint32_t D = (uint32_t)DT;
     const uint32_t L = hd / D;
-    const uint32_t hl = (uint32_t)lane / L, dg = (uint32_t)lane % L;
+    uint32_t nhp = 1;
+    while (nhp < nh) nhp <<= 1;
+    const uint32_t slots = max(1u, 64u / (L * nhp));   // the lowering keeps L * nhp <= 64
+    const uint32_t NS = (uint32_t)kComputeWaves * slots;   // states per head
+    const uint32_t dg = (uint32_t)lane % L, hl = ((uint32_t)lane / L) % nhp;
+    const uint32_t gs = (uint32_t)cw * slots + (uint32_t)lane / (L * nhp);   // this lane's state
     const bool active = hl < nh;
     const uint32_t hq = active ? hl : 0;   // inactive lanes shadow head 0 and never store
-    float qr[kAttMaxD], o[kAttMaxD], kv[kAttMaxD];
+    float qr[kAttMaxD], o[kAttMaxD];
 #pragma unroll
     for (int k = 0; k < kAttMaxD; ++k) {
         qr[k] = (uint32_t)k < D ? qs[hq * hd + dg * D + k] : 0.f;
@@ -963,74 +992,32 @@ DEV void op_attn_d(const TaskEnv& e, const DevTask& T, WBuf& A, WBuf& B) {
     }
     float m = -INFINITY, lsum = 0.f;
     const float scale = P.attn_scale;
-    // one position: score, online-softmax update; krow/vrow are the staged rows, or null for
-    // the current position (k, v in S.att)
-    auto step = [&](const uint8_t* krow, const uint8_t* vrow) {
-        if (krow) kv_slice(P, krow, dg * D, D, kv);
-        else
-#pragma unroll
-            for (int k = 0; k < kAttMaxD; ++k) kv[k] = (uint32_t)k < D ? kc[dg * D + k] : 0.f;
+    auto score = [&](const float (&kx)[kAttMaxD]) {
         float sdot = 0.f;
 #pragma unroll
         for (int k = 0; k < kAttMaxD; ++k)
-            if ((uint32_t)k < D) sdot += qr[k] * kv[k];
-        for (uint32_t off = L >> 1; off >= 1; off >>= 1) sdot += __shfl_xor(sdot, (int)off, 64);
-        const float sc = sdot * scale;
-        const float mn = fmaxf(m, sc);
-        const float alpha = __expf(m - mn), pw = __expf(sc - mn);
-        lsum = lsum * alpha + pw;
-        if (vrow) kv_slice(P, vrow, dg * D, D, kv);
-        else
-#pragma unroll
-            for (int k = 0; k < kAttMaxD; ++k) kv[k] = (uint32_t)k < D ? vc[dg * D + k] : 0.f;
-#pragma unroll
-        for (int k = 0; k < kAttMaxD; ++k)
-            if ((uint32_t)k < D) o[k] = o[k] * alpha + pw * kv[k];
-        m = mn;
+            if ((uint32_t)k < D) sdot += qr[k] * kx[k];
+        return group_reduce<false>(sdot, L) * scale;
     };
-    // history rounds: each wave takes kAttBatch positions at a time (positions w, w + 8, ...), so
-    // the lane-group reductions of their scores overlap and the running state is rescaled once
-    // per batch
+    // history rounds: the state takes positions gs, gs + NS, ..., two at a time (the second
+    // clamped to the first and weighted 0 past the round's end), so their scores overlap and the
+    // running state is rescaled once per pair
     while (rn) {
-        for (uint32_t i0 = (uint32_t)cw; i0 < rn; i0 += kComputeWaves * kAttBatch) {
-            float sc[kAttBatch];
+        for (uint32_t i = gs; i < rn; i += 2 * NS) {
+            const bool two = i + NS < rn;
+            const uint32_t i1 = two ? i + NS : i;
+            float k0[kAttMaxD], k1[kAttMaxD], v0[kAttMaxD], v1[kAttMaxD];
+            kv_slice(P, S.kvb + i * rowb, dg * D, D, k0);
+            kv_slice(P, S.kvb + i1 * rowb, dg * D, D, k1);
+            kv_slice(P, S.kvb + (rn + i) * rowb, dg * D, D, v0);
+            kv_slice(P, S.kvb + (rn + i1) * rowb, dg * D, D, v1);
+            const float s0 = score(k0), s1 = two ? score(k1) : -INFINITY;
+            const float mb = fmaxf(m, fmaxf(s0, s1));
+            const float alpha = __expf(m - mb), p0 = __expf(s0 - mb), p1 = two ? __expf(s1 - mb) : 0.f;
+            lsum = lsum * alpha + p0 + p1;
 #pragma unroll
-            for (int u = 0; u < kAttBatch; ++u) {
-                const uint32_t i = i0 + (uint32_t)u * kComputeWaves;
-                float sdot = 0.f;
-                if (i < rn) {
-                    kv_slice(P, S.kvb + i * rowb, dg * D, D, kv);
-#pragma unroll
-                    for (int k = 0; k < kAttMaxD; ++k)
-                        if ((uint32_t)k < D) sdot += qr[k] * kv[k];
-                }
-                sc[u] = sdot;
-            }
-            for (uint32_t off = L >> 1; off >= 1; off >>= 1)
-#pragma unroll
-                for (int u = 0; u < kAttBatch; ++u) sc[u] += __shfl_xor(sc[u], (int)off, 64);
-            float mb = m;
-#pragma unroll
-            for (int u = 0; u < kAttBatch; ++u) {
-                sc[u] = i0 + (uint32_t)u * kComputeWaves < rn ? sc[u] * scale : -INFINITY;
-                mb = fmaxf(mb, sc[u]);
-            }
-            const float alpha = __expf(m - mb);
-            lsum *= alpha;
-#pragma unroll
-            for (int k = 0; k < kAttMaxD; ++k) o[k] *= alpha;
-#pragma unroll
-            for (int u = 0; u < kAttBatch; ++u) {
-                const uint32_t i = i0 + (uint32_t)u * kComputeWaves;
-                if (i < rn) {
-                    const float pw = __expf(sc[u] - mb);
-                    lsum += pw;
-                    kv_slice(P, S.kvb + (rn + i) * rowb, dg * D, D, kv);
-#pragma unroll
-                    for (int k = 0; k < kAttMaxD; ++k)
-                        if ((uint32_t)k < D) o[k] += pw * kv[k];
-                }
-            }
+            for (int k = 0; k < kAttMaxD; ++k)
+                if ((uint32_t)k < D) o[k] = o[k] * alpha + p0 * v0[k] + p1 * v1[k];
             m = mb;
         }
         const uint32_t na = ra + rn, nn = min(per_round, p1 - na);
@@ -1042,12 +1029,28 @@ DEV void op_attn_d(const TaskEnv& e, const DevTask& T, WBuf& A, WBuf& B) {
         ra = na;
         rn = nn;
     }
-    // the current position: one wave
-    if (cur && (uint32_t)cw == nhist % kComputeWaves) step(nullptr, nullptr);
-    // per-wave states -> LDS: hf[(cw * nh + h) * (hd + 2) + {0: m, 1: l, 2 + d: o}]
+    // the current position (last chunk only): the state that would take the next history position
+    if (cur && gs == nhist % NS) {
+        float kx[kAttMaxD], vx[kAttMaxD];
+#pragma unroll
+        for (int k = 0; k < kAttMaxD; ++k) {
+            kx[k] = (uint32_t)k < D ? kc[dg * D + k] : 0.f;
+            vx[k] = (uint32_t)k < D ? vc[dg * D + k] : 0.f;
+        }
+        const float sc = score(kx);
+        const float mn = fmaxf(m, sc);
+        const float alpha = __expf(m - mn), pw = __expf(sc - mn);
+        lsum = lsum * alpha + pw;
+#pragma unroll
+        for (int k = 0; k < kAttMaxD; ++k)
+            if ((uint32_t)k < D) o[k] = o[k] * alpha + pw * vx[k];
+        m = mn;
+    }
+    if (e.tr && ctid == 0) e.tr[4] = rt();   // the first wave's positions done
+    // states -> LDS: hf[(state * nh + h) * (hd + 2) + {0: m, 1: l, 2 + d: o}]
     const uint32_t st = hd + 2;
     if (active) {
-        float* w = S.hf + ((uint32_t)cw * nh + hl) * st;
+        float* w = S.hf + ((uint64_t)gs * nh + hl) * st;
         if (dg == 0) { w[0] = m; w[1] = lsum; }
 #pragma unroll
         for (int k = 0; k < kAttMaxD; ++k)
@@ -1055,61 +1058,75 @@ DEV void op_attn_d(const TaskEnv& e, const DevTask& T, WBuf& A, WBuf& B) {
     }
     cbar();
     mark(e, 2);
-    // combination weights, once per (wave, head)
-    for (uint32_t t = (uint32_t)ctid; t < (uint32_t)kComputeWaves * nh; t += kComputeThreads) {
-        const uint32_t w = t / nh, h = t % nh;
-        float M = -INFINITY;
-        for (int v = 0; v < kComputeWaves; ++v) M = fmaxf(M, S.hf[((uint32_t)v * nh + h) * st]);
-        const float mw = S.hf[(w * nh + h) * st];
-        S.att[kAttF + w * kMaxAttnHeads + h] = mw == -INFINITY ? 0.f : __expf(mw - M);
-        if (w == 0) S.att[kAttM + h] = M;
+    // per head (one wave each): M = max over its states, the state weights f = exp(m_s - M) (0
+    // for a state that saw no position) and L = sum of f * l_s
+    float* F = S.att + kAttF;   // [state][nh]
+    for (uint32_t h = (uint32_t)cw; h < nh; h += kComputeWaves) {
+        float mx = -INFINITY;
+        for (uint32_t t = (uint32_t)lane; t < NS; t += 64) mx = fmaxf(mx, S.hf[((uint64_t)t * nh + h) * st]);
+        const float M = wave_max_dpp(mx);
+        float ls = 0.f;
+        for (uint32_t t = (uint32_t)lane; t < NS; t += 64) {
+            const float* w = S.hf + ((uint64_t)t * nh + h) * st;
+            const float f = w[0] == -INFINITY ? 0.f : __expf(w[0] - M);
+            F[t * nh + h] = f;
+            ls += f * w[1];
+        }
+        ls = wave_sum_dpp(ls);
+        if (lane == 0) { S.att[kAttM + h] = M; S.att[kAttL + h] = ls; }
     }
     cbar();
     const uint32_t flag = P.flag;
+    // output values: G consecutive lanes share a value (a word of the output rows, or one o value
+    // of the partial state), each summing every G-th state, then adding across the G lanes
+    const uint32_t nval = nc == 1 ? nh * hd / vpw : nh * hd;
+    uint32_t G = 1;
+    while (2 * G <= 16 && 2 * G <= NS && nval * 2 * G <= (uint32_t)kComputeThreads) G *= 2;
+    const uint32_t per_pass = (uint32_t)kComputeThreads / G;
     if (nc == 1) {   // the output rows, rounded once
         u64* out = ll_layer(P, e.y, l) + e.y.o + (uint64_t)h0 * hd / vpw;
-        for (uint32_t i = (uint32_t)ctid; i < nh * hd / vpw; i += kComputeThreads) {
+        for (uint32_t u0 = 0; u0 < nval; u0 += per_pass) {
+            const uint32_t u = u0 + (uint32_t)ctid / G, part = (uint32_t)ctid % G;
             float v[2] = {0.f, 0.f};
 #pragma unroll
             for (uint32_t j = 0; j < 2; ++j) {
                 if (j >= vpw) break;
-                const uint32_t t = i * vpw + j, h = t / hd, d = t % hd;
-                float os = 0.f, ls = 0.f;
-                for (int w = 0; w < kComputeWaves; ++w) {
-                    const float f = S.att[kAttF + w * kMaxAttnHeads + h];
-                    const float* ws = S.hf + ((uint32_t)w * nh + h) * st;
-                    ls += f * ws[1];
-                    os += f * ws[2 + d];
-                }
-                v[j] = rA(P, os / ls);
+                const uint32_t t = u * vpw + j, h = u < nval ? t / hd : 0, d = t % hd;
+                float os = 0.f;
+                if (u < nval)
+                    for (uint32_t q = part; q < NS; q += G) os += F[q * nh + h] * S.hf[((uint64_t)q * nh + h) * st + 2 + d];
+                os = group_reduce<false>(os, G);
+                v[j] = u < nval ? rA(P, os / S.att[kAttL + h]) : 0.f;
             }
-            ll_store(out + i, pack2(P, v[0], v[1]), flag);
+            if (u < nval && part == 0) ll_store(out + u, pack2(P, v[0], v[1]), flag);
         }
-    } else {   // partial state (M, L, o[hd]) per head, one fp32 per word
-        u64* part = ll_layer(P, e.y, l) + e.y.part;
-        for (uint32_t t = (uint32_t)ctid; t < nh * st; t += kComputeThreads) {
-            const uint32_t h = t / st, k = t % st;
-            float v;
-            if (k == 0) {
-                v = S.att[kAttM + h];
-            } else {
-                v = 0.f;
-                for (int w = 0; w < kComputeWaves; ++w)
-                    v += S.att[kAttF + w * kMaxAttnHeads + h] * S.hf[((uint32_t)w * nh + h) * st + k];
-            }
-            ll_store(part + ((uint64_t)(h0 + h) * nc + ch) * st + k, __float_as_uint(v), flag);
+    } else {   // partial state (M, L, o[hd]) per head, one fp32 per word: M and L first
+        u64* part_out = ll_layer(P, e.y, l) + e.y.part;
+        if ((uint32_t)ctid < 2 * nh) {
+            const uint32_t h = (uint32_t)ctid / 2, k = (uint32_t)ctid % 2;
+            ll_store(part_out + ((uint64_t)(h0 + h) * nc + ch) * st + k,
+                     __float_as_uint(S.att[(k ? kAttL : kAttM) + h]), flag);
+        }
+        for (uint32_t u0 = 0; u0 < nval; u0 += per_pass) {
+            const uint32_t u = u0 + (uint32_t)ctid / G, part = (uint32_t)ctid % G;
+            const uint32_t h = u < nval ? u / hd : 0, d = u % hd;
+            float os = 0.f;
+            if (u < nval)
+                for (uint32_t q = part; q < NS; q += G) os += F[q * nh + h] * S.hf[((uint64_t)q * nh + h) * st + 2 + d];
+            os = group_reduce<false>(os, G);
+            if (u < nval && part == 0)
+                ll_store(part_out + ((uint64_t)(h0 + h) * nc + ch) * st + 2 + d, __float_as_uint(os), flag);
         }
     }
 }
 
-// Attention with the lane layout's dims per lane as a compile-time constant: a head owns
-// min(64 / nh rounded up to a power of two, hd) lanes, so D = hd / lanes is 1, 2, 4 or 8 (the
-// lowering keeps it <= 8).
+// Attention with the dims per lane as a compile-time constant: D = the largest of 8, 4, 2, 1
+// that divides hd (the lowering keeps hd * nh <= 512, so a wave holds every head of the task).
 DEV void op_attn(const TaskEnv& e, const DevTask& T, WBuf& A, WBuf& B) {
-    const uint32_t nh = T.arg[1], hd = (uint32_t)e.c->P->hd;
-    uint32_t nhp = 1;
-    while (nhp < nh) nhp <<= 1;
-    switch (hd / min(64u / nhp, hd)) {
+    const uint32_t hd = (uint32_t)e.c->P->hd;
+    uint32_t D = 8;
+    while (D > 1 && hd % D) D >>= 1;
+    switch (D) {
     case 1: op_attn_d<1>(e, T, A, B); break;
     case 2: op_attn_d<2>(e, T, A, B); break;
     case 4: op_attn_d<4>(e, T, A, B); break;
@@ -1150,12 +1167,13 @@ DEV void op_merge(const TaskEnv& e, const DevTask& T) {
         if (lane_id() == 0) Lh[h] = Ls;
     }
     cbar();
+    mark(e, 2);
     // output words: G consecutive lanes share a word, each summing every G-th chunk, then the G
-    // partial sums are added across those lanes
+    // partial sums are added across those lanes (DPP moves inside the lane group)
     u64* out = ll_layer(P, e.y, l) + e.y.o + (uint64_t)h0 * hd / vpw;
     const uint32_t nwords = nh * hd / vpw;
     uint32_t G = 1;
-    while (2 * G <= nc && 2 * G <= 64 && nwords * 2 * G <= (uint32_t)kComputeThreads) G *= 2;
+    while (2 * G <= nc && 2 * G <= 16 && nwords * 2 * G <= (uint32_t)kComputeThreads) G *= 2;
     for (uint32_t w0 = 0; w0 < nwords; w0 += kComputeThreads / G) {
         const uint32_t i = w0 + (uint32_t)ctid / G, k0 = (uint32_t)ctid % G;
         float v[2] = {0.f, 0.f};
@@ -1170,10 +1188,8 @@ DEV void op_merge(const TaskEnv& e, const DevTask& T) {
                 v[j] = os;
             }
         }
-        for (uint32_t off = G >> 1; off >= 1; off >>= 1) {
-            v[0] += __shfl_xor(v[0], (int)off, 64);
-            v[1] += __shfl_xor(v[1], (int)off, 64);
-        }
+        v[0] = group_reduce<false>(v[0], G);
+        v[1] = group_reduce<false>(v[1], G);
         if (i < nwords && k0 == 0) {
             float r[2] = {0.f, 0.f};
 #pragma unroll

@@ -1,7 +1,9 @@
 """Per-task timestamp traces of the decode megakernel: where one launch spends its time.
 
 A trace row per task (queue order) holds six realtime-counter values (100 MHz): compute start,
-inputs observed, rows done, end, first wave's rows done (GEMV), outputs written (amk_set_trace).
+inputs observed, rows done (attention: the per-wave states stored; merge: the chunk weights
+computed), end, the first wave's rows (GEMV) or positions (attention) done, outputs written
+(amk_set_trace).
 From them: per opcode the time spent waiting for inputs (producers on other CUs plus the
 staging prologue), computing, in the epilogue, the skew between the first wave and the whole
 workgroup at the end of the rows, and the closing barrier; per phase (opcode, layer) the moment
@@ -42,8 +44,8 @@ def summarize(sched, trace) -> dict:
         s, ready, done, end, w0, out = rel[k]
         d = by_op[OPNAMES.get(op, str(op))]
         d["wait"].append(ready - s)
-        d["compute"].append(done - ready if op not in (A.AMK_OP_MERGE, A.AMK_OP_ARGMAX) else 0.0)
-        d["epilogue"].append(end - (done if op not in (A.AMK_OP_MERGE, A.AMK_OP_ARGMAX) else ready))
+        d["compute"].append(done - ready if op != A.AMK_OP_ARGMAX else 0.0)
+        d["epilogue"].append(end - (done if op != A.AMK_OP_ARGMAX else ready))
         if op in (A.AMK_OP_QKV, A.AMK_OP_OPROJ, A.AMK_OP_GATEUP, A.AMK_OP_DOWN, A.AMK_OP_LM):
             d["wave_skew"].append(max(0.0, done - w0))
         d["close"].append(max(0.0, end - out))

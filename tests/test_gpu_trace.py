@@ -3,8 +3,9 @@
 Tracing must not change what a launch computes: a traced decode launch and a traced prefill
 launch give logits and tokens bit-identical to untraced ones. Every task's timestamps must be
 ordered the way the kernels take them, and a CU's tasks must follow one another in queue order.
-Decode slots: 0 start, 1 inputs observed, 2 rows done (GEMV and attention), 3 end, 4 the first
-wave's rows done (GEMV), 5 outputs written. Prefill slots: 0 start, 1 inputs ready, 2 computed,
+Decode slots: 0 start, 1 inputs observed, 2 rows done (GEMV; attention: per-wave states stored;
+merge: chunk weights computed), 3 end, 4 the first wave's rows (GEMV) or positions (attention)
+done, 5 outputs written. Prefill slots: 0 start, 1 inputs ready, 2 computed,
 3 signalled. (The pages measure per-tile cross-SM synchronisation this way: AutoMegaKernel pages,
 page 2, "Performance ceiling and gap".)
 """
@@ -70,6 +71,8 @@ def test_traced_decode_is_bit_identical_and_ordered(M, name, pos0):
             if op in (1, 4, 5, 6, 7):   # GEMV ops
                 assert ready <= w0 <= done <= out, (op, tr[k - 1])
             elif op == 2:               # attention
+                assert ready <= w0 <= done <= out, (op, tr[k - 1])
+            elif op == 3:               # merge
                 assert ready <= done <= out, (op, tr[k - 1])
             if prev_end is not None:
                 assert prev_end <= s, "a CU's tasks overlap in its trace"

@@ -82,15 +82,16 @@ def test_phase_end_is_the_last_task_of_the_phase():
     assert res["ops_mean_us"]["gateup"]["wait"] == pytest.approx(np.mean([10, 40, 15]) * TICK_US, abs=1e-3)   # rounded to ns
 
 
-def test_merge_and_argmax_have_no_compute_split():
-    # merge and argmax: everything after the inputs counts as epilogue
+def test_merge_splits_at_its_chunk_weights_and_argmax_does_not_split():
+    # merge: compute = inputs -> chunk weights, epilogue = the rest; argmax: all epilogue
     tasks = [(A.AMK_OP_MERGE, 0), (A.AMK_OP_ARGMAX, 1)]
     queues = [[0, 1]]
-    tr = np.array([_row(0, 100, 0, 160, out=150), _row(160, 300, 0, 320, out=315)], dtype=np.int64)
+    tr = np.array([_row(0, 100, 120, 160, out=150), _row(160, 300, 0, 320, out=315)], dtype=np.int64)
     res = summarize(_sched(tasks, queues), tr)
     ops = res["ops_mean_us"]
-    assert ops["merge"]["compute"] == 0.0 and ops["argmax"]["compute"] == 0.0
-    assert ops["merge"]["epilogue"] == pytest.approx(60 * TICK_US)
+    assert ops["merge"]["compute"] == pytest.approx(20 * TICK_US)
+    assert ops["merge"]["epilogue"] == pytest.approx(40 * TICK_US)
+    assert ops["argmax"]["compute"] == 0.0
     assert ops["argmax"]["epilogue"] == pytest.approx(20 * TICK_US)
     assert "wave_skew" not in ops["merge"]
 
