@@ -107,7 +107,11 @@ enum {
     AMK_OP_GATEUP = 5,   /* layer, arg0 = first j, arg1 = count: RMSNorm + gate/up GEMV + SwiGLU */
     AMK_OP_DOWN = 6,     /* layer, arg0 = first row, arg1 = row count: down GEMV + residual */
     AMK_OP_LM = 7,       /* arg0 = first vocab row, arg1 = row count, arg2 = tile index: final RMSNorm + LM head + tile argmax */
-    AMK_OP_ARGMAX = 8    /* arg2 = number of LM tiles: greedy token */
+    AMK_OP_ARGMAX = 8,   /* arg2 = number of LM tiles: greedy token */
+    AMK_OP_ATTN_MERGE = 9 /* layer, arg0 = first query head, arg1 = head count, arg2 = chunk (the last),
+                             arg3 = chunks: attention over the last context chunk, then the merge of
+                             its state with the other chunks' states (AMK_OP_ATTN + AMK_OP_MERGE as
+                             one task) */
 };
 
 typedef struct {
@@ -162,6 +166,14 @@ typedef struct {
                                   ahead of the task's inputs: 1 or 2, -1 for none, 0 = default (1).
                                   Used by amk_create (the kernel's launch parameters); the lowering
                                   only checks the range. */
+    int32_t merge_fusion;      /* split-context attention (fusion grouping): 1 = the merge of a head
+                                  group runs inside the task of its last context chunk
+                                  (AMK_OP_ATTN_MERGE), which waits for the other chunks' states
+                                  after its own positions; 2 = separate merge tasks (AMK_OP_MERGE)
+                                  after every attention task; 0 = default (2, the faster of the two
+                                  on every workload measured). 1 is refused (AMK_E_UNSUPPORTED)
+                                  where the last chunk's LDS stage cannot hold every chunk state
+                                  of its heads. */
 } amk_schedule_config;
 
 /* ---------------------------------------------------------------- calls */

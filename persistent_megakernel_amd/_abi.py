@@ -28,6 +28,7 @@ AMK_SCHED_LL_PROTOCOL = 1
 # opcodes
 AMK_OP_QKV, AMK_OP_ATTN, AMK_OP_MERGE, AMK_OP_OPROJ = 1, 2, 3, 4
 AMK_OP_GATEUP, AMK_OP_DOWN, AMK_OP_LM, AMK_OP_ARGMAX = 5, 6, 7, 8
+AMK_OP_ATTN_MERGE = 9
 
 # device status bits
 STATUS_TIMEOUT, STATUS_BAD_TOKEN = 1, 2
@@ -88,7 +89,7 @@ class amk_schedule_config(C.Structure):
     _fields_ = [("struct_size", C.c_uint32), ("n_cu", C.c_int32), ("tasks_qkv", C.c_int32),
                 ("tasks_o", C.c_int32), ("tasks_gateup", C.c_int32), ("tasks_down", C.c_int32),
                 ("tasks_lm", C.c_int32), ("attn_chunks", C.c_int32), ("attn_group_tasks", C.c_int32),
-                ("cu_assign", C.c_int32), ("prefetch_groups", C.c_int32)]
+                ("cu_assign", C.c_int32), ("prefetch_groups", C.c_int32), ("merge_fusion", C.c_int32)]
 
 
 class amk_vm_opts(C.Structure):

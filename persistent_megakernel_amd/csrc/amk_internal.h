@@ -106,6 +106,28 @@ AMK_HD inline LLLayout ll_layout(int H, int L, int nH, int nKV, int hd, int I, i
     return y;
 }
 
+// Attention lane layout of a task with nh query heads: a lane owns D consecutive dims (the largest
+// of 8, 4, 2, 1 dividing hd), a head L = hd / D lanes, nh rounded up to a power of two head
+// places, and every wave 64 / (L * places) state slots. Returns the states per head (8 waves).
+AMK_HD inline uint32_t attn_states(int hd, uint32_t nh) {
+    uint32_t D = 8;
+    while (D > 1 && (uint32_t)hd % D) D >>= 1;
+    const uint32_t L = (uint32_t)hd / D;
+    uint32_t nhp = 1;
+    while (nhp < nh) nhp <<= 1;
+    const uint32_t slots = L * nhp >= 64 ? 1u : 64u / (L * nhp);
+    return (uint32_t)kComputeWaves * slots;
+}
+// Float offset, inside the input-vector stage, of the chunk states a fused attention + merge task
+// gathers: after its own (state, head) values, 16-byte aligned.
+AMK_HD inline uint64_t attn_merge_stage_off(int hd, uint32_t nh) {
+    return (((uint64_t)attn_states(hd, nh) * nh * (uint64_t)(hd + 2)) + 3) & ~3ull;
+}
+// The fused task fits when its own states and every chunk state of its heads share the stage.
+AMK_HD inline bool attn_merge_fits(int hd, uint32_t nh, uint32_t nc) {
+    return attn_merge_stage_off(hd, nh) + (uint64_t)nh * nc * (uint64_t)(hd + 2) <= (uint64_t)kStageFloats;
+}
+
 // Kernel parameters (passed by value).
 struct KParams {
     // shape

@@ -187,9 +187,12 @@ bool derive_accesses(const Shape& s, const GenTask& t, uint64_t w_off, uint64_t 
         }
         return true;
     }
-    case AMK_OP_ATTN: {
+    case AMK_OP_ATTN:
+    case AMK_OP_ATTN_MERGE: {
+        const bool fused = t.op == AMK_OP_ATTN_MERGE;
         const uint32_t h0 = t.arg[0], nh = t.arg[1], c = t.arg[2], nc = t.arg[3];
         if (!nh || nh > (uint32_t)kMaxAttnHeads || nc != nchunks || c >= nc || h0 + nh > (uint32_t)s.nH) return false;
+        if (fused && (nc < 2 || c != nc - 1 || !attn_merge_fits(s.hd, nh, nc))) return false;
         const uint32_t g = (uint32_t)((uint64_t)h0 * s.nKV / s.nH);
         if ((uint64_t)(h0 + nh - 1) * s.nKV / s.nH != g) return false;   // one KV group per task
         {   // attention lane layout: hd / 8 lanes per head, nh rounded up to a power of two head
@@ -207,7 +210,11 @@ bool derive_accesses(const Shape& s, const GenTask& t, uint64_t w_off, uint64_t 
             add_acc(a, s.reg(l, L_QKV), 0, qd + (uint64_t)(s.nKV + g) * s.hd, qd + (uint64_t)(s.nKV + g + 1) * s.hd);
         }
         add_acc(a, s.reg(l, L_KVHIST), 0, g, g + 1);
-        if (nc == 1) add_acc(a, s.reg(l, L_O), AMK_ACC_WRITE, (uint64_t)h0 * s.hd, (uint64_t)(h0 + nh) * s.hd);
+        if (fused) {   // the other chunks' states, then the merged output rows
+            for (uint32_t h = h0; h < h0 + nh; ++h)
+                add_acc(a, s.reg(l, L_PART), 0, (uint64_t)h * nc * (s.hd + 2), ((uint64_t)h * nc + nc - 1) * (s.hd + 2));
+            add_acc(a, s.reg(l, L_O), AMK_ACC_WRITE, (uint64_t)h0 * s.hd, (uint64_t)(h0 + nh) * s.hd);
+        } else if (nc == 1) add_acc(a, s.reg(l, L_O), AMK_ACC_WRITE, (uint64_t)h0 * s.hd, (uint64_t)(h0 + nh) * s.hd);
         else
             for (uint32_t h = h0; h < h0 + nh; ++h)
                 add_acc(a, s.reg(l, L_PART), AMK_ACC_WRITE, ((uint64_t)h * nc + c) * (s.hd + 2), ((uint64_t)h * nc + c + 1) * (s.hd + 2));
@@ -510,6 +517,18 @@ amk_status lower_model(const amk_model_desc& d, const amk_schedule_config* cfg, 
     }
     s.nchunks = nc;
     const bool xcd = C.cu_assign == 0 && nc == 1;   // chunked attention is spread over all CUs
+    if (C.merge_fusion < 0 || C.merge_fusion > 2) {
+        if (msg) *msg = "merge_fusion outside [0, 2]";
+        return AMK_E_INVALID_ARG;
+    }
+    // the merge of a head group inside the task of its last chunk, where its LDS stage holds the
+    // chunk states of the group's heads next to the task's own per-state values (on request:
+    // separate merge tasks measured faster)
+    const bool fuse_merge = nc > 1 && C.merge_fusion == 1 && attn_merge_fits(s.hd, heads_per_task, nc);
+    if (C.merge_fusion == 1 && nc > 1 && !fuse_merge) {
+        if (msg) *msg = "merge_fusion = 1: the chunk states of a head group do not fit the LDS stage";
+        return AMK_E_UNSUPPORTED;
+    }
 
     std::vector<GenTask> T;
     uint32_t nctr = 0;
@@ -552,30 +571,36 @@ amk_status lower_model(const amk_model_desc& d, const amk_schedule_config* cfg, 
         std::vector<uint32_t> c_part(n_head_tasks);
         if (nc > 1) for (auto& c : c_part) c = newc();
         std::vector<uint32_t> slot_in_xcd(8, 0), group_cu(n_head_tasks, 0);
-        for (int m = 0; m < n_head_tasks; ++m) {
-            const int h0 = m * heads_per_task;
-            const int g = (int)((int64_t)h0 * nKV / nH);
-            uint32_t first_cu = 0;
-            for (int c = 0; c < nc; ++c) {
-                uint32_t cu;
-                if (xcd) {
-                    uint32_t x = (uint32_t)g % 8, k = slot_in_xcd[x]++;
-                    cu = x + 8 * (k % (uint32_t)std::max(1, n_cu / 8));
-                } else {
-                    cu = (uint32_t)(m * nc + c);
+        // with the merge fused, every group's last chunk goes after all the other chunks (a CU's
+        // fused task waits for chunks that may sit in other CUs' queues; none of those may sit
+        // behind another fused task)
+        for (int pass = 0; pass < (fuse_merge ? 2 : 1); ++pass)
+            for (int m = 0; m < n_head_tasks; ++m) {
+                const int h0 = m * heads_per_task;
+                const int g = (int)((int64_t)h0 * nKV / nH);
+                for (int c = 0; c < nc; ++c) {
+                    const bool last = c == nc - 1;
+                    if (fuse_merge && last != (pass == 1)) continue;
+                    uint32_t cu;
+                    if (xcd) {
+                        uint32_t x = (uint32_t)g % 8, k = slot_in_xcd[x]++;
+                        cu = x + 8 * (k % (uint32_t)std::max(1, n_cu / 8));
+                    } else {
+                        cu = (uint32_t)(m * nc + c);
+                    }
+                    if (c == 0) group_cu[m] = cu;
+                    const bool fused = fuse_merge && last;
+                    uint32_t id = mk(fused ? AMK_OP_ATTN_MERGE : AMK_OP_ATTN, l, h0, heads_per_task, c, nc, cu);
+                    for (int h = h0; h < h0 + heads_per_task; ++h) T[id].waits.push_back({c_q[h], UINT32_MAX});
+                    if (last) T[id].waits.push_back({c_kv[g], UINT32_MAX});
+                    if (fused) T[id].waits.push_back({c_part[m], UINT32_MAX});
+                    T[id].sigs.push_back(nc == 1 || fused ? c_att : c_part[m]);
                 }
-                if (c == 0) first_cu = cu;
-                uint32_t id = mk(AMK_OP_ATTN, l, h0, heads_per_task, c, nc, cu);
-                for (int h = h0; h < h0 + heads_per_task; ++h) T[id].waits.push_back({c_q[h], UINT32_MAX});
-                if (c == nc - 1) T[id].waits.push_back({c_kv[g], UINT32_MAX});
-                T[id].sigs.push_back(nc == 1 ? c_att : c_part[m]);
             }
-            group_cu[m] = first_cu;
-        }
         // merges after every attention task of the layer: a CU's merge for one group must not
         // sit in its queue ahead of its attention chunk for another group (that would chain the
         // groups one after the other)
-        if (nc > 1)
+        if (nc > 1 && !fuse_merge)
             for (int m = 0; m < n_head_tasks; ++m) {
                 const int h0 = m * heads_per_task;
                 for (int h = h0; h < h0 + heads_per_task; ++h) {   // one merge per query head
@@ -642,7 +667,8 @@ amk_status lower_user(const amk_model_desc& d, const amk_schedule* us, const amk
     int nc = 0, lm_tiles = -1;
     for (uint32_t i = 0; i < us->n_tasks; ++i) {
         const amk_task& t = us->tasks[i];
-        if (t.opcode == AMK_OP_ATTN || t.opcode == AMK_OP_MERGE) nc = std::max<int>(nc, (int)t.arg[3]);
+        if (t.opcode == AMK_OP_ATTN || t.opcode == AMK_OP_MERGE || t.opcode == AMK_OP_ATTN_MERGE)
+            nc = std::max<int>(nc, (int)t.arg[3]);
         if (t.opcode == AMK_OP_ARGMAX) lm_tiles = (int)t.arg[2];
     }
     if (nc <= 0 || lm_tiles <= 0) { *mismatch = true; if (msg) *msg = "schedule lacks attention or argmax tasks"; return AMK_E_REJECTED; }

@@ -931,6 +931,9 @@ DEV AttnSpan attn_span(const KParams& P, const DevTask& T) {
 // current position (last chunk only) comes from the flag-carrying words. At the end the
 // per-wave states (m, l, o) are combined with weights exp(m_w - M) computed once per (wave,
 // head); a single chunk writes the output row, a split context writes its (M, L, o) state.
+DEV void merge_staged(const TaskEnv& e, int l, uint32_t h0, uint32_t nh, uint32_t nc, float* st_base, float* Lh,
+                      int mark_slot);
+
 template <int DT>
 DEV void op_attn_d(const TaskEnv& e, const DevTask& T, WBuf& A, WBuf& B) {
     const Ctx& c = *e.c;
@@ -1100,6 +1103,30 @@ DEV void op_attn_d(const TaskEnv& e, const DevTask& T, WBuf& A, WBuf& B) {
             }
             if (u < nval && part == 0) ll_store(out + u, pack2(P, v[0], v[1]), flag);
         }
+    } else if (T.op == AMK_OP_ATTN_MERGE) {
+        // the merge in this task: its own state goes to chunk slot nc - 1 of the merge stage (past
+        // the per-state values in the same LDS buffer), the other chunks' states are gathered
+        // beside it, then the heads are merged as a merge task would
+        float* ms = S.hf + attn_merge_stage_off((int)hd, nh);
+        if ((uint32_t)ctid < 2 * nh) {
+            const uint32_t h = (uint32_t)ctid / 2, k = (uint32_t)ctid % 2;
+            ms[((uint64_t)h * nc + nc - 1) * st + k] = S.att[(k ? kAttL : kAttM) + h];
+        }
+        for (uint32_t u0 = 0; u0 < nval; u0 += per_pass) {
+            const uint32_t u = u0 + (uint32_t)ctid / G, part = (uint32_t)ctid % G;
+            const uint32_t h = u < nval ? u / hd : 0, d = u % hd;
+            float os = 0.f;
+            if (u < nval)
+                for (uint32_t q = part; q < NS; q += G) os += F[q * nh + h] * S.hf[((uint64_t)q * nh + h) * st + 2 + d];
+            os = group_reduce<false>(os, G);
+            if (u < nval && part == 0) ms[((uint64_t)h * nc + nc - 1) * st + 2 + d] = os;
+        }
+        const u64* part_in = ll_layer(P, e.y, l) + e.y.part;
+        for (uint32_t h = 0; h < nh; ++h)
+            (void)ll_gather(c, part_in + (uint64_t)(h0 + h) * nc * st, (nc - 1) * st, ctid,
+                            [&](uint32_t i, uint32_t pl) { ms[(uint64_t)h * nc * st + i] = __uint_as_float(pl); });
+        cbar();
+        merge_staged(e, l, h0, nh, nc, ms, S.att + kAttQ, -1);
     } else {   // partial state (M, L, o[hd]) per head, one fp32 per word: M and L first
         u64* part_out = ll_layer(P, e.y, l) + e.y.part;
         if ((uint32_t)ctid < 2 * nh) {
@@ -1135,24 +1162,17 @@ DEV void op_attn(const TaskEnv& e, const DevTask& T, WBuf& A, WBuf& B) {
 }
 
 // Merge of the context chunks of query heads [h0, h0+nh): o = sum_c exp(M_c - M) o_c divided by
-// sum_c exp(M_c - M) L_c, M = max_c M_c (the split-context form of the same softmax). The
-// weights are computed once per (head, chunk).
-DEV void op_merge(const TaskEnv& e, const DevTask& T) {
-    const Ctx& c = *e.c;
-    const KParams& P = *c.P;
-    Lds& S = *c.S;
-    const int l = T.layer, ctid = e.ctid;
-    const uint32_t h0 = T.arg[0], nh = T.arg[1], nc = T.arg[3];
+// sum_c exp(M_c - M) L_c, M = max_c M_c (the split-context form of the same softmax). The chunk
+// states are staged in LDS at `st_base` as [head][chunk][M, L, o[hd]]; the weights are computed
+// once per (head, chunk) and stored over M_c. Lh receives each head's L.
+DEV void merge_staged(const TaskEnv& e, int l, uint32_t h0, uint32_t nh, uint32_t nc, float* st_base, float* Lh,
+                      int mark_slot) {
+    const KParams& P = *e.c->P;
+    const int ctid = e.ctid;
     const uint32_t hd = (uint32_t)P.hd, st = hd + 2;
     const uint32_t vpw = P.act_f32 ? 1u : 2u;
-    const u64* part = ll_layer(P, e.y, l) + e.y.part + (uint64_t)h0 * nc * st;
-    (void)ll_gather(c, part, nh * nc * st, ctid, [&](uint32_t i, uint32_t pl) { S.hf[i] = __uint_as_float(pl); });
-    cbar();
-    mark(e, 1);
-    // per head: M, then the chunk weights f_c = exp(M_c - M) (stored over M_c) and L
-    float* Lh = S.att;                       // [nh]
     for (uint32_t h = (uint32_t)e.cw; h < nh; h += kComputeWaves) {
-        float* base = S.hf + (uint64_t)h * nc * st;
+        float* base = st_base + (uint64_t)h * nc * st;
         float M = -INFINITY;
         for (uint32_t k = (uint32_t)lane_id(); k < nc; k += 64) M = fmaxf(M, base[k * st]);
         M = wave_max_dpp(M);
@@ -1167,7 +1187,7 @@ DEV void op_merge(const TaskEnv& e, const DevTask& T) {
         if (lane_id() == 0) Lh[h] = Ls;
     }
     cbar();
-    mark(e, 2);
+    if (mark_slot >= 0) mark(e, mark_slot);
     // output words: G consecutive lanes share a word, each summing every G-th chunk, then the G
     // partial sums are added across those lanes (DPP moves inside the lane group)
     u64* out = ll_layer(P, e.y, l) + e.y.o + (uint64_t)h0 * hd / vpw;
@@ -1182,7 +1202,7 @@ DEV void op_merge(const TaskEnv& e, const DevTask& T) {
             for (uint32_t j = 0; j < 2; ++j) {
                 if (j >= vpw) break;
                 const uint32_t t = i * vpw + j, h = t / hd, d = t % hd;
-                const float* base = S.hf + (uint64_t)h * nc * st;
+                const float* base = st_base + (uint64_t)h * nc * st;
                 float os = 0.f;
                 for (uint32_t k = k0; k < nc; k += G) os += base[k * st] * base[k * st + 2 + d];
                 v[j] = os;
@@ -1200,6 +1220,20 @@ DEV void op_merge(const TaskEnv& e, const DevTask& T) {
             ll_store(out + i, pack2(P, r[0], r[1]), P.flag);
         }
     }
+}
+
+// A merge task: gather every chunk state of its heads, then merge them.
+DEV void op_merge(const TaskEnv& e, const DevTask& T) {
+    const Ctx& c = *e.c;
+    const KParams& P = *c.P;
+    Lds& S = *c.S;
+    const uint32_t h0 = T.arg[0], nh = T.arg[1], nc = T.arg[3];
+    const uint32_t st = (uint32_t)P.hd + 2;
+    const u64* part = ll_layer(P, e.y, T.layer) + e.y.part + (uint64_t)h0 * nc * st;
+    (void)ll_gather(c, part, nh * nc * st, e.ctid, [&](uint32_t i, uint32_t pl) { S.hf[i] = __uint_as_float(pl); });
+    cbar();
+    mark(e, 1);
+    merge_staged(e, T.layer, h0, nh, nc, S.hf, S.att, 2);
 }
 
 // The greedy token: the argmax over the LM tiles' (max, index) pairs, lowest index among equal
@@ -1282,7 +1316,8 @@ DEV void compute_run(const Ctx& c) {
             op_gemv(e, T, A, B);
         } else {
             switch (T.op) {
-            case AMK_OP_ATTN: op_attn(e, T, A, B); break;
+            case AMK_OP_ATTN:
+            case AMK_OP_ATTN_MERGE: op_attn(e, T, A, B); break;
             case AMK_OP_MERGE: op_merge(e, T); break;
             default: op_argmax(e, T); break;
             }

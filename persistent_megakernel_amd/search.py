@@ -61,6 +61,7 @@ KNOBS: Dict[str, Tuple[int, ...]] = {
     "attn_group_tasks": (0, 2),
     "cu_assign": (0, 1),
     "prefetch_groups": (0, -1, 2),
+    "merge_fusion": (0, 1),
 }
 
 Config = Dict[str, int]
@@ -152,7 +153,7 @@ def task_cost(shape, task, pos: int, p: CostParams, ahead: int = 1) -> float:
         stream = rows * rb / (p.cu_gbps * 1e3)
         body = max(compute, stream)
         return p.task_us + max(0.0, body - ahead * p.ahead_us)
-    if op == A.AMK_OP_ATTN:
+    if op in (A.AMK_OP_ATTN, A.AMK_OP_ATTN_MERGE):
         n = pos + 1
         npos = n * (a2 + 1) // a3 - n * a2 // a3 if a3 else n
         nhp = 1
@@ -161,7 +162,9 @@ def task_cost(shape, task, pos: int, p: CostParams, ahead: int = 1) -> float:
         lanes = min(64 // nhp, shape.head_dim)
         levels = max(1, lanes.bit_length() - 1)
         macs = shape.head_dim * max(1, a1) / 64.0
-        return p.task_us + p.attn_fixed_us + -(-npos // p.waves) * (p.attn_mac_us * macs + p.attn_level_us * levels)
+        att = p.task_us + p.attn_fixed_us + -(-npos // p.waves) * (p.attn_mac_us * macs + p.attn_level_us * levels)
+        # the fused form also merges every chunk state of its heads (no task of its own)
+        return att + (max(1, a1) * a3 * p.merge_chunk_us if op == A.AMK_OP_ATTN_MERGE else 0.0)
     if op == A.AMK_OP_MERGE:
         return p.task_us + a1 * a3 * p.merge_chunk_us
     return p.task_us
@@ -562,6 +565,7 @@ CALIBRATION_CONFIGS: List[Config] = [
     {"tasks_qkv": 64}, {"tasks_o": 32}, {"tasks_gateup": 64}, {"tasks_down": 64}, {"tasks_lm": 64},
     {"tasks_qkv": 32, "tasks_gateup": 32, "tasks_down": 32, "tasks_o": 32},
     {"cu_assign": 1}, {"prefetch_groups": -1, "attn_chunks": 8},
+    {"merge_fusion": 1}, {"merge_fusion": 1, "attn_chunks": 4},
 ]
 
 

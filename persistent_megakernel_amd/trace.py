@@ -26,7 +26,8 @@ from . import _abi as A
 
 TICK_US = 0.01          # one tick of the 100 MHz realtime counter
 OPNAMES = {A.AMK_OP_QKV: "qkv", A.AMK_OP_ATTN: "attn", A.AMK_OP_MERGE: "merge", A.AMK_OP_OPROJ: "oproj",
-           A.AMK_OP_GATEUP: "gateup", A.AMK_OP_DOWN: "down", A.AMK_OP_LM: "lm", A.AMK_OP_ARGMAX: "argmax"}
+           A.AMK_OP_GATEUP: "gateup", A.AMK_OP_DOWN: "down", A.AMK_OP_LM: "lm", A.AMK_OP_ARGMAX: "argmax",
+           A.AMK_OP_ATTN_MERGE: "attn_merge"}
 
 
 def summarize(sched, trace) -> dict:

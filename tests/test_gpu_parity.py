@@ -200,13 +200,15 @@ def test_depth1_full_width(M, name, pos0, prefill):
     _check_ids(r["gen"], r["fr"], r["margins"], name + " free-running")
 
 
-@pytest.mark.parametrize("cfg_kw", [dict(prefetch_groups=-1), dict(prefetch_groups=2), dict(attn_group_tasks=1)],
-                         ids=["no-prefetch", "prefetch-2", "grouped-attention"])
+@pytest.mark.parametrize("cfg_kw", [dict(prefetch_groups=-1), dict(prefetch_groups=2), dict(attn_group_tasks=1),
+                                    dict(merge_fusion=1)],
+                         ids=["no-prefetch", "prefetch-2", "grouped-attention", "merge-fused"])
 def test_tinyllama_int8_two_layer_variants(M, cfg_kw):
     """Launch parameters and lowerings beside the defaults, on two TinyLlama-shaped int8 layers
     from position 512 (full width, so every GEMV task has more than two load groups): no weight
     loads issued ahead, two groups ahead, and one attention task per KV group (the default at
-    this cache size is one per query head)."""
+    this cache size is one per query head), and each head's merge inside the task of its last
+    context chunk (the default runs separate merge tasks)."""
     shape = I.SHAPES["tinyllama_int8"].replace(n_layers=2)
     log(f"case tinyllama_int8 2 layers {cfg_kw}")
     w = I.make_weights(shape)
@@ -216,6 +218,31 @@ def test_tinyllama_int8_two_layer_variants(M, cfg_kw):
     assert max(r["errs"]) <= TWO_LAYER_ABS
     _check_ids(r["gen"], r["tf"], r["margins"], str(cfg_kw), r["gen_errs"])
     _check_ids(r["gen"], r["fr"], r["margins"], f"{cfg_kw} free-running", r["gen_errs"])
+
+
+def test_merge_fusion_bit_identical(M):
+    """The merge inside the last chunk's task runs the same arithmetic on the same values as a
+    merge task (its own chunk state goes through LDS instead of flag-carrying words, both fp32):
+    logits of four teacher-forced steps from position 512 on two TinyLlama-shaped layers are
+    bit-identical between the two lowerings, and the fused one has no merge task."""
+    shape = I.SHAPES["tinyllama_int8"].replace(n_layers=2)
+    log("case merge fusion vs merge tasks, tinyllama_int8 2 layers from 512")
+    w = I.make_weights(shape)
+    toks = [int(t) for t in I.prompt_tokens(shape, 4, stream=5)]
+    outs = []
+    for mf in (1, 2):
+        dec = M.Decoder(shape, w, cfg=M.schedule_config(merge_fusion=mf))
+        ops = [t.opcode for t in dec.schedule().tasks]
+        assert (M.A.AMK_OP_ATTN_MERGE in ops) == (mf == 1) and (M.A.AMK_OP_MERGE in ops) == (mf == 2)
+        for l in range(shape.n_layers):
+            dec.set_kv_prefix(l, I.kv_prefill(shape, 512, l))
+        lg = torch.zeros((len(toks), shape.vocab), dtype=torch.float32, device="cuda")
+        M.run_steps(dec, toks, 512, logits=lg)
+        torch.cuda.synchronize()
+        assert dec.status() == 0
+        dec.close()
+        outs.append(lg.cpu().numpy())
+    np.testing.assert_array_equal(outs[0], outs[1])
 
 
 # ------------------------------------------------------------------ full depth

@@ -70,7 +70,7 @@ def test_traced_decode_is_bit_identical_and_ordered(M, name, pos0):
             assert s > 0 and s <= ready <= out <= end, (op, tr[k - 1])
             if op in (1, 4, 5, 6, 7):   # GEMV ops
                 assert ready <= w0 <= done <= out, (op, tr[k - 1])
-            elif op == 2:               # attention
+            elif op in (2, 9):          # attention (9: with the merge fused)
                 assert ready <= w0 <= done <= out, (op, tr[k - 1])
             elif op == 3:               # merge
                 assert ready <= done <= out, (op, tr[k - 1])

@@ -90,3 +90,36 @@ def test_unsupported_shapes_refused(M, kw, status):
     with pytest.raises(M.AmkError) as e:
         M.amk_lower(M.model_desc(shape))
     assert e.value.status == status
+
+
+def test_merge_fusion_lowering(M):
+    """The fusion-grouping knob for split-context attention: on request each head group's merge
+    runs inside its last chunk's task (AMK_OP_ATTN_MERGE, waiting on the other chunks' states);
+    the schedule is accepted by the validator and completes under the CPU executor with no race.
+    The default keeps separate merge tasks; the fused form is refused where the last chunk's LDS
+    stage cannot hold every chunk state of its heads (grouped Llama-3-8B heads at 4096), and
+    values outside the knob's range are refused."""
+    A = M.A
+    sh = I.SHAPES["tinyllama_int8"].replace(n_layers=2)
+    d = M.model_desc(sh, max_ctx=1024)
+    dflt = M.amk_lower(d, M.schedule_config(n_cu=64))
+    ops = [t.opcode for t in dflt.tasks]
+    assert A.AMK_OP_MERGE in ops and A.AMK_OP_ATTN_MERGE not in ops
+    fused = M.amk_lower(d, M.schedule_config(n_cu=64, merge_fusion=1))
+    ops = [t.opcode for t in fused.tasks]
+    n_att = ops.count(A.AMK_OP_ATTN) + ops.count(A.AMK_OP_ATTN_MERGE)
+    assert A.AMK_OP_MERGE not in ops and ops.count(A.AMK_OP_ATTN_MERGE) == sh.n_layers * sh.n_heads
+    assert n_att == [t.opcode for t in dflt.tasks].count(A.AMK_OP_ATTN)
+    for t in fused.tasks:
+        if t.opcode == A.AMK_OP_ATTN_MERGE:
+            nc = t.args[4]
+            assert nc > 1 and t.args[3] == nc - 1 and len(t.waits) == 3   # q, current k/v, other chunks
+    assert M.amk_validate(fused).accepted == 1
+    for seed in range(2):
+        r = M.amk_vm_run(fused, seed=seed, max_delay_us=30)
+        assert r["completed"] == 1 and r["races"] == 0 and r["uncovered_reads"] == 0, r
+    big = M.model_desc(I.SHAPES["llama3_8b_int4"], max_ctx=4128)
+    with pytest.raises(M.AmkError):
+        M.amk_lower(big, M.schedule_config(merge_fusion=1))
+    with pytest.raises(M.AmkError):
+        M.amk_lower(d, M.schedule_config(merge_fusion=3))
