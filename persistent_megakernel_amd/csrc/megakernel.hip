@@ -556,12 +556,22 @@ DEV void stage_input(const Ctx& c, int ctid, const u64* src, const void* embed_r
     float tot = 0.f;
     for (int w = 0; w < kComputeWaves; ++w) tot += S.fpart[w];
     const float r = 1.0f / __fsqrt_rn(tot / (float)K + P.eps);
+    // four values per thread at a time: their LDS reads go out together (indices below
+    // kMaxHidden stay inside the stage whatever K is), then the four are scaled and written back
+    static_assert(kMaxGainsPerThread % 4 == 0 && kMaxGainsPerThread * kComputeThreads <= kHBytes / 4, "norm groups");
 #pragma unroll
-    for (int k = 0; k < kMaxGainsPerThread; ++k) {
-        const uint32_t i = (uint32_t)ctid + (uint32_t)k * kComputeThreads;
-        if (i < K) {
-            const float x = P.act_f32 ? S.hf[i] : bf2f(((uint16_t*)S.hb)[i]);
-            hput(P, S, i, rA(P, (x * r) * gr[k]));
+    for (int k0 = 0; k0 < kMaxGainsPerThread; k0 += 4) {
+        if ((uint32_t)k0 * kComputeThreads >= K) break;
+        float x[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t i = (uint32_t)ctid + (uint32_t)(k0 + k) * kComputeThreads;
+            x[k] = P.act_f32 ? S.hf[i] : bf2f(((uint16_t*)S.hb)[i]);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t i = (uint32_t)ctid + (uint32_t)(k0 + k) * kComputeThreads;
+            if (i < K) hput(P, S, i, rA(P, (x[k] * r) * gr[k0 + k]));
         }
     }
     before_barrier();
