@@ -302,32 +302,55 @@ DEV bf16x2 as_bf2(uint32_t u) {
     return r;
 }
 
-// Dot product of lane l's 16 weight bytes of load j of a row with the matching slice of the
-// staged input. Weights are widened in registers: fp32 as is; bf16 pairs go through the bf16
-// dot instruction; int8 codes are converted to fp32 and their top halves (exactly the code as
-// bf16) packed in pairs for the same instruction; int4 codes are nibbles minus the bias 8, with
-// the lane's 32 codes (inside one 128-column group) scaled by the group's fp16 scale from LDS.
-// Products are exact in fp32; sums are fp32.
+// 16-byte LDS vectors of the staged input under one weight load of a lane: 4 fp32, 8 bf16, 16
+// (int8 codes) or 32 (int4 codes) input values.
 template <int FMT>
-DEV float dot16(const Lds& S, u32x4 w, uint32_t j, uint32_t lane, uint32_t row, uint32_t K) {
+constexpr int kInVecs = FMT == AMK_INT4_G128 ? 4 : FMT == AMK_INT8_PC ? 2 : 1;
+
+// The input values lane l's bytes of load j of a row meet. Every j below the row's load count
+// stays inside the stage for every input length the kernel takes (at most 8192 fp32 or 16384
+// 16-bit values), so a slot past the wave's last load can read them too and drop them.
+template <int FMT>
+DEV void in_slice(const Lds& S, uint32_t j, uint32_t lane, u32x4 (&h)[kInVecs<FMT>]) {
     const uint16_t* hb = (const uint16_t*)S.hb;
+    if constexpr (FMT == AMK_F32) {
+        h[0] = *(const u32x4*)(S.hf + 256u * j + 4u * lane);
+    } else if constexpr (FMT == AMK_BF16) {
+        h[0] = *(const u32x4*)(hb + 512u * j + 8u * lane);
+    } else if constexpr (FMT == AMK_INT8_PC) {
+        const uint16_t* p = hb + 1024u * j + 16u * lane;
+        h[0] = *(const u32x4*)p;
+        h[1] = *(const u32x4*)(p + 8);
+    } else {
+        const uint16_t* p = hb + 2048u * j + 32u * lane;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) h[k] = *(const u32x4*)(p + 8 * k);
+    }
+}
+
+// Dot product of lane l's 16 weight bytes of load j of a row with the matching slice of the
+// staged input (h, from in_slice). Weights are widened in registers: fp32 as is; bf16 pairs go
+// through the bf16 dot instruction; int8 codes are converted to fp32 and their top halves
+// (exactly the code as bf16) packed in pairs for the same instruction; int4 codes are nibbles
+// minus the bias 8, with the lane's 32 codes (inside one 128-column group) scaled by the group's
+// fp16 scale from LDS. Products are exact in fp32; sums are fp32.
+template <int FMT>
+DEV float dot16(const Lds& S, u32x4 w, const u32x4 (&h)[kInVecs<FMT>], uint32_t j, uint32_t lane, uint32_t row,
+                uint32_t K) {
     float acc = 0.f;
     if constexpr (FMT == AMK_F32) {
-        const uint32_t c0 = 256u * j + 4u * lane;
-        const u32x4 hv = *(const u32x4*)(S.hf + c0);
+        const u32x4 hv = h[0];
         acc += __uint_as_float(w.x) * __uint_as_float(hv.x);
         acc += __uint_as_float(w.y) * __uint_as_float(hv.y);
         acc += __uint_as_float(w.z) * __uint_as_float(hv.z);
         acc += __uint_as_float(w.w) * __uint_as_float(hv.w);
     } else if constexpr (FMT == AMK_BF16) {
-        const uint32_t c0 = 512u * j + 8u * lane;
-        const u32x4 hv = *(const u32x4*)(hb + c0);
-        const uint32_t a[4] = {w.x, w.y, w.z, w.w}, h[4] = {hv.x, hv.y, hv.z, hv.w};
+        const u32x4 hv = h[0];
+        const uint32_t a[4] = {w.x, w.y, w.z, w.w}, hh[4] = {hv.x, hv.y, hv.z, hv.w};
 #pragma unroll
-        for (int k = 0; k < 4; ++k) acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(a[k]), as_bf2(h[k]), acc, false);
+        for (int k = 0; k < 4; ++k) acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(a[k]), as_bf2(hh[k]), acc, false);
     } else if constexpr (FMT == AMK_INT8_PC) {
-        const uint32_t c0 = 1024u * j + 16u * lane;
-        const u32x4 h0 = *(const u32x4*)(hb + c0), h1 = *(const u32x4*)(hb + c0 + 8);
+        const u32x4 h0 = h[0], h1 = h[1];
         const uint32_t hh[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
         const uint32_t a[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
@@ -349,7 +372,7 @@ DEV float dot16(const Lds& S, u32x4 w, uint32_t j, uint32_t lane, uint32_t row, 
         float p = 0.f;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const u32x4 hv = *(const u32x4*)(hb + c0 + 8 * k);
+            const u32x4 hv = h[k];
             const uint32_t hh[4] = {hv.x, hv.y, hv.z, hv.w};
             // byte m of lo holds nibble 2m (the even code), byte m of hi nibble 2m + 1
             const uint32_t lo = a[k] & 0x0f0f0f0fu, hi = (a[k] >> 4) & 0x0f0f0f0fu;
@@ -374,11 +397,16 @@ DEV void compute_group(const Lds& S_, const Geo& s, int cw, uint32_t K, uint32_t
     const uint32_t lane = (uint32_t)lane_id();
     const uint32_t f0 = g * kLoadSlots;
     uint32_t i = f0 / s.nj, j = f0 - i * s.nj;
+    // the input slice of each slot is read from LDS one slot ahead, so its reads are in flight
+    // while the previous slot's products are formed
+    u32x4 hc[kInVecs<FMT>], hn[kInVecs<FMT>];
+    in_slice<FMT>(S, j, lane, hc);
 #pragma unroll
     for (int k = 0; k < kLoadSlots; ++k) {
+        if (k + 1 < kLoadSlots) in_slice<FMT>(S, j + 1 == s.nj ? 0u : j + 1, lane, hn);
         if (f0 + (uint32_t)k < s.nloads) {
             const uint32_t row = (uint32_t)cw + kComputeWaves * i;
-            const float d = dot16<FMT>(S, b.w[k], j, lane, row, K);
+            const float d = dot16<FMT>(S, b.w[k], hc, j, lane, row, K);
             acc += 1024u * j + 16u * lane < s.pitch ? d : 0.f;
             if (j + 1 == s.nj) {
                 float sum = wave_sum_dpp(acc);
@@ -388,6 +416,10 @@ DEV void compute_group(const Lds& S_, const Geo& s, int cw, uint32_t K, uint32_t
             }
         }
         if (++j == s.nj) { j = 0; ++i; }
+        if (k + 1 < kLoadSlots) {
+#pragma unroll
+            for (int v = 0; v < kInVecs<FMT>; ++v) hc[v] = hn[v];
+        }
     }
 }
 
