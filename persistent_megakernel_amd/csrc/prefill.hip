@@ -222,14 +222,22 @@ DEV void gemm_tile(const Ctx& c, const void* A, uint32_t lda, uint32_t m0, uint3
             ra[i] = u32x4{0, 0, 0, 0};
             if (r < mvalid && k < K) ra[i] = *(const u32x4*)((const uint8_t*)A + ((uint64_t)(m0 + r) * lda + k) * ES);
         }
+        // the row addresses first, all of them (a segment past the tile's rows reads row 0's and
+        // drops it), so their LDS reads are in flight together instead of one before each load
+        uint64_t rbase[SEGS_B];
 #pragma unroll
         for (int i = 0; i < SEGS_B; ++i) {
             const uint32_t g = (uint32_t)tid + (uint32_t)i * kPfThreads;
-            const uint32_t r = g / SPR, k = k0 + (g % SPR) * CPS;
+            rbase[i] = S.rows[g < segs_b ? g / SPR : 0u].codes;
+        }
+#pragma unroll
+        for (int i = 0; i < SEGS_B; ++i) {
+            const uint32_t g = (uint32_t)tid + (uint32_t)i * kPfThreads;
+            const uint32_t k = k0 + (g % SPR) * CPS;
             rb[i] = u32x4{0, 0, 0, 0};
             if (g < segs_b && k < K) {
-                const uint64_t off = S.rows[r].codes + (FMT == AMK_F32 ? 4ull * k : FMT == AMK_BF16 ? 2ull * k
-                                                       : FMT == AMK_INT8_PC ? (uint64_t)k : (uint64_t)k / 2);
+                const uint64_t off = rbase[i] + (FMT == AMK_F32 ? 4ull * k : FMT == AMK_BF16 ? 2ull * k
+                                                 : FMT == AMK_INT8_PC ? (uint64_t)k : (uint64_t)k / 2);
                 rb[i] = __builtin_nontemporal_load((const u32x4*)(P.wstream + off));
             }
         }
@@ -435,14 +443,22 @@ DEV void gemm_tile_wide(const Ctx& c, const void* A, uint32_t lda, uint32_t m0, 
             ra[i] = u32x4{0, 0, 0, 0};
             if (r < mvalid && k < K) ra[i] = *(const u32x4*)((const uint8_t*)A + ((uint64_t)(m0 + r) * lda + k) * ES);
         }
+        // the row addresses first, all of them (a segment past the tile's rows reads row 0's and
+        // drops it), so their LDS reads are in flight together instead of one before each load
+        uint64_t rbase[SEGS_B];
 #pragma unroll
         for (int i = 0; i < SEGS_B; ++i) {
             const uint32_t g = (uint32_t)tid + (uint32_t)i * kPfThreads;
-            const uint32_t r = g / SPR, k = k0 + (g % SPR) * CPS;
+            rbase[i] = S.rows[g < segs_b ? g / SPR : 0u].codes;
+        }
+#pragma unroll
+        for (int i = 0; i < SEGS_B; ++i) {
+            const uint32_t g = (uint32_t)tid + (uint32_t)i * kPfThreads;
+            const uint32_t k = k0 + (g % SPR) * CPS;
             rb[i] = u32x4{0, 0, 0, 0};
             if (g < segs_b && k < K) {
-                const uint64_t off = S.rows[r].codes + (FMT == AMK_F32 ? 4ull * k : FMT == AMK_BF16 ? 2ull * k
-                                                       : FMT == AMK_INT8_PC ? (uint64_t)k : (uint64_t)k / 2);
+                const uint64_t off = rbase[i] + (FMT == AMK_F32 ? 4ull * k : FMT == AMK_BF16 ? 2ull * k
+                                                 : FMT == AMK_INT8_PC ? (uint64_t)k : (uint64_t)k / 2);
                 rb[i] = __builtin_nontemporal_load((const u32x4*)(P.wstream + off));
             }
         }
